@@ -1,0 +1,24 @@
+"""CPU float64 oracle for decode-step attention over a paged KV cache.
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, by ``__graft_entry__.smoke()``
+and by the ``cpu_baseline`` leg of ``bench.py``; never by the library.
+
+Every function here is pinned by ``tests/test_oracle.py``; none is "parity
+unpinned".
+"""
+
+from .paged_attention import (  # noqa: F401
+    LN2,
+    attend,
+    decode_attention,
+    decode_bf16,
+    decode_e4m3fn,
+    decode_partials,
+    decode_step,
+    gather_sequence,
+    kv_append,
+    merge_partials,
+    partition_partials,
+    slot_of,
+    to_float64,
+)

@@ -1,0 +1,86 @@
+"""Algorithmic bytes and FLOPs of a decode step (host-side accounting).
+
+The roofline numbers the library reports are algorithmic: what the method must
+move and compute, not what a kernel happens to move.
+
+* KV bytes per token: ``2 * layers * n_kv * d_h * e`` (K and V).  The serving
+  lesson (learn.mohebi.ai, "KV-cache memory and the batch that fits") and the
+  KV-cache posts give 131,072 B for Llama-3-8B in bf16.
+* Decode-step proposition (serving lesson, "Proposition (decode step: bytes,
+  FLOPs, intensity and time)"): bytes >= W + B*C*k, FLOPs ~ B*W + g*B*C*k in
+  bf16, attention costs 4*C*d_h*a*L FLOPs per sequence, so g FLOP per cache
+  byte (2g/e_kv for other formats).
+* For one attention call (one layer) the algorithmic traffic is every
+  attended token's K and V row of every KV head, plus the queries, the
+  outputs, the block-table entries walked, the context lengths and, for e4m3,
+  one float32 scale per (block, kv head) for K and for V.  Partial results of
+  a split-KV launch and the unread tail of a sequence's last block are
+  implementation overhead and are not counted.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+ELEM_BYTES = {"f32": 4, "bf16": 2, "fp8_e4m3": 1}
+
+# MI355X published peaks used for roofline fractions.
+HBM_PEAK_GBPS = 8000.0
+FP32_VECTOR_PEAK_TFLOPS = 157.3
+
+
+def kv_bytes_per_token(layers: int, n_kv: int, d_h: int, e: float) -> float:
+    """K and V bytes one token adds to the cache over all layers."""
+    return 2 * layers * n_kv * d_h * e
+
+
+def blocks_needed(n_tokens, block_size: int):
+    """Whole blocks a sequence of n tokens occupies: ceil(n / block_size)."""
+    n = np.asarray(n_tokens, dtype=np.int64)
+    return -(-n // block_size)
+
+
+def paged_slots(live_lengths, block_size: int) -> int:
+    """Token slots held by paged sequences (whole blocks allocated on demand)."""
+    return int(block_size * blocks_needed(live_lengths, block_size).sum())
+
+
+def decode_step_model(*, W, B, C, k, layers, a, d_h, psi, peak_flops, bw):
+    """The serving lesson's decode-step roofline: bytes, FLOPs, intensity,
+    memory time and compute time for batch(es) ``B`` at context ``C``."""
+    B = np.asarray(B, dtype=np.float64)
+    kv = B * C * k
+    n_bytes = W + kv
+    flops = 2 * psi * B + 4 * B * C * layers * a * d_h
+    return dict(bytes=n_bytes, flops=flops, intensity=flops / n_bytes,
+                t_mem=n_bytes / bw, t_comp=flops / peak_flops,
+                tokens_per_s=B / np.maximum(n_bytes / bw, flops / peak_flops))
+
+
+def attention_call_traffic(context_lens, *, num_q_heads, num_kv_heads, head_dim,
+                           q_dtype, kv_dtype, block_size=16):
+    """Algorithmic bytes and FLOPs of one paged decode-attention call (one layer).
+
+    Returns a dict with ``kv_bytes`` (K+V rows of every attended token),
+    ``total_bytes`` (plus q, out, tables, lengths, e4m3 scales) and ``flops``
+    (4 * D * Hq per attended token: q.k and p.v).
+    """
+    ctx = np.asarray(context_lens, dtype=np.int64)
+    tokens = int(ctx.sum())
+    e_kv = ELEM_BYTES[kv_dtype]
+    e_q = ELEM_BYTES[q_dtype]
+    B = len(ctx)
+    kv = tokens * 2 * num_kv_heads * head_dim * e_kv
+    nblk = int(blocks_needed(ctx, block_size).sum())
+    scales = nblk * num_kv_heads * 4 * 2 if kv_dtype == "fp8_e4m3" else 0
+    qo = 2 * B * num_q_heads * head_dim * e_q
+    tables = 4 * nblk + 4 * B
+    return dict(tokens=tokens, kv_bytes=kv, scale_bytes=scales, qo_bytes=qo,
+                table_bytes=tables, total_bytes=kv + scales + qo + tables,
+                flops=4 * head_dim * num_q_heads * tokens)
+
+
+def append_traffic(num_seqs, *, num_kv_heads, head_dim, kv_dtype):
+    """Bytes the append moves: each new K and V row read once and written once."""
+    row = num_kv_heads * head_dim * ELEM_BYTES[kv_dtype]
+    return dict(bytes=num_seqs * row * 2 * 2)

@@ -1,0 +1,68 @@
+"""The bytes/FLOPs accounting against the numbers the pages print (CPU only)."""
+
+import json
+import os
+
+import numpy as np
+
+from paged_kv_cache_25_amd import traffic
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def test_serving_lesson_decode_table():
+    g = _golden("serving_lesson_numbers.json")
+    i = g["inputs"]
+    k = traffic.kv_bytes_per_token(i["L"], i["n_kv"], i["d_h"], i["e"])
+    assert k == g["kv_bytes_per_token"] and k // 1024 == g["kv_kib_per_token"]
+    assert int(i["M_kv"] // k) == g["tokens_fit"]
+    assert int(i["M_kv"] // (k * i["C"])) == g["batch_fit_at_2048"]
+    m = traffic.decode_step_model(W=i["e"] * i["psi"], B=i["B"], C=i["C"], k=k, layers=i["L"],
+                                  a=i["a"], d_h=i["d_h"], psi=i["psi"],
+                                  peak_flops=i["peak_flops"], bw=i["bw"])
+    assert list((m["bytes"] / 1e9).round(1)) == g["step_gb_round1"]
+    assert list(m["intensity"].round(1)) == g["intensity_round1"]
+    assert list((m["t_mem"] * 1e3).round(2)) == g["t_mem_ms_round2"]
+    assert list((m["t_comp"] * 1e3).round(2)) == g["t_comp_ms_round2"]
+    assert list(m["tokens_per_s"].round()) == g["tokens_per_s_round0"]
+
+
+def test_serving_lesson_paging_memory():
+    p = _golden("serving_lesson_numbers.json")["paging"]
+    live = np.random.default_rng(p["seed"]).integers(p["low"], p["high"], size=p["n"])
+    assert int(live.sum()) == p["live_sum"]
+    assert p["max_len"] * len(live) == p["reserved"]
+    assert traffic.paged_slots(live, p["block"]) == p["paged"]
+    assert round(100 * live.sum() / p["reserved"], 1) == p["used_share_reserved_pct"]
+    assert round(100 * live.sum() / p["paged"], 1) == p["used_share_paged_pct"]
+    assert (p["block"] * traffic.blocks_needed(live, p["block"]) - live).max() < p["block"]
+
+
+def test_kv_sizes_golden():
+    g = _golden("kv_sizes.json")
+    for model in ("llama3_8b", "llama2_7b"):
+        m = g[model]
+        assert traffic.kv_bytes_per_token(m["layers"], m["n_kv"], m["d_h"], m["e"]) == m["bytes_per_token"]
+    m = g["llama3_8b"]
+    for ctx, nbytes in m["context_bytes"].items():
+        assert int(ctx) * m["bytes_per_token"] == nbytes
+
+
+def test_attention_call_traffic_intensity():
+    """One layer's attention does g FLOP per cache byte in bf16 (2g/e in general)."""
+    ctx = np.array([512, 1000, 4096])
+    for kv, e in (("bf16", 2), ("fp8_e4m3", 1), ("f32", 4)):
+        for hq, hkv in ((32, 8), (32, 32)):
+            t = traffic.attention_call_traffic(ctx, num_q_heads=hq, num_kv_heads=hkv, head_dim=128,
+                                               q_dtype="bf16", kv_dtype=kv)
+            assert t["kv_bytes"] == ctx.sum() * 2 * hkv * 128 * e
+            assert t["flops"] / t["kv_bytes"] == 2 * (hq // hkv) / e
+    t = traffic.attention_call_traffic([17], num_q_heads=4, num_kv_heads=4, head_dim=64,
+                                       q_dtype="f32", kv_dtype="f32")
+    # 2 blocks walked: table 8 B + length 4 B; q and out 2*4*64*4 B
+    assert t["table_bytes"] == 12 and t["qo_bytes"] == 2048
