@@ -1,0 +1,271 @@
+#!/usr/bin/env python3
+"""Decode-step benchmark: paged KV append + split-KV decode attention + merge.
+
+One "step" is one pass of the whole hot path over one batch: ``pkv_kv_append``
+then ``pkv_paged_decode_attention`` (decode kernel + LSE merge) through the C
+ABI, on synthetic inputs already resident in HBM.  The default workload is
+the Llama-3-8B-shaped layer (batch 64, 32 query / 8 KV heads, head dim 128,
+bf16, 16-token blocks, context lengths uniform in [512, 4096]); ``--config``
+picks another named workload.  Inputs are rotated over enough copies to span
+more than the 256 MB last-level cache, so the timed steps read HBM.
+
+Prints one JSON line.  ``value`` is the step's algorithmic bytes (K/V rows of
+every attended token, the appended rows, q, out, block-table entries and
+lengths) divided by the measured step time, in GB/s.  ``roofline`` reports the
+decode kernel alone, timed live with HIP events (attention call minus merge
+call, both on the launch stream), against the 8 TB/s HBM peak.
+``cpu_baseline`` times the float64 CPU oracle on a bounded sample of the same
+workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+LLC_BYTES = 256 * 2 ** 20
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=2)
+    ap.add_argument("--seed", type=int, default=None)
+    ap.add_argument("--partition-size", type=int, default=None)
+    ap.add_argument("--kernel-reps", type=int, default=200)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget-s", type=float, default=15.0)
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only: the decode path "
+                          "shards by sequence or KV head with no exchange, so N GPUs run N "
+                          "independent copies of this benchmark; --gpus must be 1"}))
+        sys.exit(2)
+
+    import torch
+
+    from paged_kv_cache_25_amd import ops, traffic
+    from workloads import named_config
+
+    lib = ops.load()
+    if not torch.cuda.is_available():
+        raise SystemExit("no GPU visible")
+    dev = torch.device("cuda:0")
+
+    t0 = time.time()
+    inp = named_config(args.config, seed=args.seed)
+    P = inp.partition_size if args.partition_size is None else args.partition_size
+    print(f"[bench] workload {inp.name}: generated in {time.time() - t0:.1f}s", file=sys.stderr,
+          flush=True)
+
+    TD = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8_e4m3": torch.float8_e4m3fn}
+
+    def to_dev(arr, dt):
+        if dt is None:
+            return torch.from_numpy(np.ascontiguousarray(arr)).to(dev)
+        if dt == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(torch.bfloat16).to(dev)
+        if dt == "fp8_e4m3":
+            return torch.from_numpy(np.ascontiguousarray(arr)).view(torch.float8_e4m3fn).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(arr, dtype=np.float32)).to(dev)
+
+    base = dict(q=to_dev(inp.q, inp.q_dtype), k_pool=to_dev(inp.k_pool, inp.kv_dtype),
+                v_pool=to_dev(inp.v_pool, inp.kv_dtype), k_new=to_dev(inp.k_new, inp.kv_dtype),
+                v_new=to_dev(inp.v_new, inp.kv_dtype), tables=to_dev(inp.block_tables, None),
+                lens=to_dev(inp.context_lens, None),
+                k_scales=None if inp.k_scales is None else to_dev(inp.k_scales, None),
+                v_scales=None if inp.v_scales is None else to_dev(inp.v_scales, None))
+    footprint = sum(t.numel() * t.element_size() for t in base.values() if t is not None)
+    n_copies = max(1, math.ceil(1.5 * 2 ** 30 / footprint)) if footprint < 1.5 * 2 ** 30 else 1
+    if footprint * n_copies > 0.5 * torch.cuda.get_device_properties(0).total_memory:
+        n_copies = 1
+    copies = [base] + [{k: (None if v is None else v.clone()) for k, v in base.items()}
+                       for _ in range(n_copies - 1)]
+
+    B, Hq, Hkv, D = inp.num_seqs, inp.num_q_heads, inp.num_kv_heads, inp.head_dim
+    NB, MB = inp.num_blocks, inp.block_tables.shape[1]
+    mcl = inp.max_context_len
+    qcode, kvcode = ops.dtype_code(base["q"].dtype), ops.dtype_code(base["k_pool"].dtype)
+    ws_bytes = ops.workspace_bytes(B, Hq, D, mcl, P)
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    V = ctypes.c_void_p
+
+    def ptr(t):
+        return None if t is None else V(t.data_ptr())
+
+    calls = []
+    for c in copies:
+        c["out"] = torch.empty(B, Hq, D, dtype=c["q"].dtype, device=dev)
+        c["ws"] = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+        app = (ptr(c["k_pool"]), ptr(c["v_pool"]), ptr(c["k_new"]), ptr(c["v_new"]),
+               ptr(c["tables"]), ptr(c["lens"]), B, Hkv, D, 16, NB, MB, kvcode, sp)
+        att = (ptr(c["out"]), ptr(c["q"]), ptr(c["k_pool"]), ptr(c["v_pool"]),
+               ptr(c["k_scales"]), ptr(c["v_scales"]), ptr(c["tables"]), ptr(c["lens"]), B, Hq,
+               Hkv, D, 16, NB, MB, mcl, ctypes.c_float(inp.softmax_scale), P, ptr(c["ws"]),
+               ctypes.c_size_t(c["ws"].numel()), qcode, kvcode, sp)
+        maxp = max(1, -(-mcl // P)) if P else 1
+        lse_off = ((B * Hq * maxp * D * 4 + 255) // 256) * 256
+        mrg = (ptr(c["out"]), V(c["ws"].data_ptr()), V(c["ws"].data_ptr() + lse_off), None,
+               B, Hq, D, maxp, qcode, sp) if maxp > 1 else None
+        calls.append((app, att, mrg))
+
+    f_app, f_att, f_mrg = lib.pkv_kv_append, lib.pkv_paged_decode_attention, lib.pkv_merge_partials
+
+    def step(i):
+        app, att, _ = calls[i % n_copies]
+        if f_app(*app) != 0 or f_att(*att) != 0:
+            raise RuntimeError("libpkv call failed")
+
+    print(f"[bench] {n_copies} input copies of {footprint / 1e6:.1f} MB; warmup {args.warmup}",
+          file=sys.stderr, flush=True)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # ---- whole steps ----------------------------------------------------------
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    step_ms = ev0.elapsed_time(ev1) / args.steps
+    print(f"[bench] {args.steps} steps: {step_ms * 1e3:.1f} us/step", file=sys.stderr, flush=True)
+
+    # ---- the decode kernel alone: attention call minus merge call ------------
+    def timed(fn, reps):
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for i in range(reps):
+            fn(i)
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    def att_only(i):
+        if f_att(*calls[i % n_copies][1]) != 0:
+            raise RuntimeError("attention call failed")
+
+    def merge_only(i):
+        m = calls[i % n_copies][2]
+        if m is not None and f_mrg(*m) != 0:
+            raise RuntimeError("merge call failed")
+
+    def append_only(i):
+        if f_app(*calls[i % n_copies][0]) != 0:
+            raise RuntimeError("append call failed")
+
+    reps = args.kernel_reps
+    att_ms = timed(att_only, reps)
+    merge_ms = timed(merge_only, reps) if calls[0][2] is not None else 0.0
+    append_ms = timed(append_only, reps)
+    decode_ms = max(att_ms - merge_ms, 1e-9)
+
+    # ---- accounting ---------------------------------------------------------------
+    tr = traffic.attention_call_traffic(inp.context_lens, num_q_heads=Hq, num_kv_heads=Hkv,
+                                        head_dim=D, q_dtype=inp.q_dtype, kv_dtype=inp.kv_dtype)
+    ap = traffic.append_traffic(B, num_kv_heads=Hkv, head_dim=D, kv_dtype=inp.kv_dtype)
+    step_bytes = tr["total_bytes"] + ap["bytes"]
+    value = step_bytes / (step_ms * 1e-3) / 1e9
+    kernel_gbps = tr["kv_bytes"] / (decode_ms * 1e-3) / 1e9
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(inp, args.cpu_budget_s)
+
+    result = {
+        "metric": "paged decode attention achieved HBM GB/s (% of peak) and decode tokens/s",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": f"{inp.kv_dtype} kv, {inp.q_dtype} q, f32 accumulate",
+        "data": "synthetic (seeded N(0,1) K/V/q, random block placement)",
+        "config": {"workload": inp.name, "batch": B, "q_heads": Hq, "kv_heads": Hkv,
+                   "head_dim": D, "block_size": 16, "partition_size": P,
+                   "context_tokens": int(inp.context_lens.sum()), "max_context": mcl,
+                   "parallelism": "single GPU"},
+        "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
+        "decode_steps_per_s": round(1e3 / step_ms, 1),
+        "tokens_per_s": round(B * 1e3 / step_ms, 1),
+        "kernel_us": {"append": round(append_ms * 1e3, 2), "decode": round(decode_ms * 1e3, 2),
+                      "merge": round(merge_ms * 1e3, 2), "attention_call": round(att_ms * 1e3, 2)},
+        "roofline": {"kernel": "paged_decode_kernel", "bound": "hbm",
+                     "achieved": round(kernel_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(kernel_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "algorithmic_bytes_per_launch": tr["kv_bytes"]},
+        "cpu_baseline": cpu,
+        "input_copies": n_copies,
+    }
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(inp, budget_s):
+    """The float64 oracle, as it stands, on a bounded sample of sequences of
+    the same workload: append + attention for sequences taken in order until
+    about ``budget_s`` seconds of host work.  BLAS is held to one thread."""
+    import oracle.paged_attention as pa
+    from paged_kv_cache_25_amd import traffic
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(1):
+        return _cpu_baseline(inp, budget_s, pa, traffic)
+
+
+def _cpu_baseline(inp, budget_s, pa, traffic):
+    t_start = time.time()
+    done = []
+    elapsed = 0.0
+    for b in range(inp.num_seqs):
+        sub = inp.subset([b])
+        t = time.perf_counter()
+        kp, vp = pa.kv_append(sub.k_pool, sub.v_pool, sub.k_new, sub.v_new, sub.block_tables,
+                              sub.context_lens, sub.block_size, inplace=True)
+        pa.decode_attention(sub.q, kp, vp, sub.block_tables, sub.context_lens,
+                            block_size=sub.block_size, softmax_scale=sub.softmax_scale,
+                            q_dtype=sub.q_dtype, kv_dtype=sub.kv_dtype, k_scales=sub.k_scales,
+                            v_scales=sub.v_scales)
+        elapsed += time.perf_counter() - t
+        done.append(b)
+        if elapsed > budget_s:
+            break
+    tr = traffic.attention_call_traffic(inp.context_lens[done], num_q_heads=inp.num_q_heads,
+                                        num_kv_heads=inp.num_kv_heads, head_dim=inp.head_dim,
+                                        q_dtype=inp.q_dtype, kv_dtype=inp.kv_dtype)
+    ap = traffic.append_traffic(len(done), num_kv_heads=inp.num_kv_heads, head_dim=inp.head_dim,
+                                kv_dtype=inp.kv_dtype)
+    gbps = (tr["total_bytes"] + ap["bytes"]) / elapsed / 1e9
+    return {"value": round(gbps, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{len(done)} of {inp.num_seqs} sequences ({tr['tokens']} attended tokens), "
+                      f"append + attention, float64 NumPy, {elapsed:.1f} s",
+            "tokens_per_s": round(len(done) / elapsed, 3),
+            "wall_s": round(time.time() - t_start, 1)}
+
+
+if __name__ == "__main__":
+    main()

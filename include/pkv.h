@@ -1,0 +1,182 @@
+/*
+ * pkv.h - decode-step attention over a paged KV cache, for AMD MI355X (gfx950).
+ *
+ * One decode step: every sequence appends the K/V rows of its one new token,
+ * then its new query attends over all of its cached tokens.  The cache of
+ * every sequence lives in fixed-size physical blocks of a shared pool; a
+ * per-sequence block table maps logical block j (tokens j*bs .. j*bs+bs-1) to
+ * a physical block anywhere in the pool.
+ *   - KV-cache post (xuewyang.github.io/posts/kv), "Prefill and decode" and
+ *     "PagedAttention: the KV cache in blocks";
+ *   - brunomaga.github.io inference post, "PagedAttention: memory management
+ *     for the KV cache" (PagedKVCache, paged_decode_attention);
+ *   - learn.mohebi.ai serving lesson, "PagedAttention" (block-by-block reads
+ *     merged with the online-softmax update) and "Where it shows up"
+ *     (split-KV decoding).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Pointers marked [device] are device memory owned by the caller; the library
+ * allocates nothing, keeps no state between calls and never synchronises the
+ * host.  Every call enqueues its kernels on `stream` (a hipStream_t; NULL is
+ * the default stream) and returns.  Calls on one stream run in order; calls
+ * on different streams that touch the same memory race.
+ *
+ * Layouts (row-major, innermost last):
+ *   pools        [num_blocks, num_kv_heads, block_size, head_dim]  kv dtype
+ *   block_tables int32 [num_seqs, max_blocks_per_seq]; entries past a
+ *                sequence's ceil(ctx/block_size) blocks are never read
+ *   context_lens int32 [num_seqs]; ctx counts the token appended this step
+ *   q, out       [num_seqs, num_q_heads, head_dim] (the [B, Hq, 1, D] query
+ *                of one decode step with the length-1 axis dropped)
+ *   k_new, v_new [num_seqs, num_kv_heads, head_dim] in the pool's dtype
+ *   k_scales, v_scales float32 [num_blocks, num_kv_heads] (e4m3 pools only):
+ *                stored value * scale = the real value
+ * Query head i reads KV head i / (num_q_heads / num_kv_heads): consecutive
+ * grouping, as in 32 query heads sharing 8 KV heads in groups of 4.
+ *
+ * Device-side contract (not checked on the host, since the values live in
+ * device memory): 0 <= ctx <= max_blocks_per_seq * block_size,
+ * ctx <= max_context_len, and the first ceil(ctx/block_size) table entries of
+ * each sequence are in [0, num_blocks).  The kernels never read or write
+ * outside the buffers described here even when it is violated: a table entry
+ * outside [0, num_blocks) is treated as an empty block, ctx is clamped to
+ * the table's capacity, and tokens past max_context_len are ignored.  Results
+ * are then unspecified, but no fault follows.
+ *
+ * Errors are returned as pkv_status_t; nothing is launched when a call
+ * returns anything but PKV_OK, except PKV_ERR_HIP (a launch failed).
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PKV_ABI_VERSION 1
+
+typedef enum {
+  PKV_F32 = 0,       /* IEEE binary32                                        */
+  PKV_BF16 = 1,      /* bfloat16 (top half of a binary32)                    */
+  PKV_FP8_E4M3 = 2   /* OCP float8 e4m3fn: bias 7, max 448, no inf, NaN=0x7F */
+} pkv_dtype_t;
+
+typedef enum {
+  PKV_OK = 0,
+  PKV_ERR_INVALID_ARG = 1,   /* null pointer, non-positive size, bad relation */
+  PKV_ERR_UNSUPPORTED = 2,   /* valid but not built: head_dim, block_size, dtypes */
+  PKV_ERR_WORKSPACE = 3,     /* workspace missing or smaller than required */
+  PKV_ERR_HIP = 4            /* a HIP launch failed */
+} pkv_status_t;
+
+/* The version of this header the library was built from (PKV_ABI_VERSION). */
+int pkv_abi_version(void);
+
+/* A static, human-readable name for a status code. */
+const char* pkv_status_string(int status);
+
+/*
+ * pkv_kv_append - write each sequence's new K and V rows into its slot.
+ *
+ * For every sequence b with ctx_b = context_lens[b] >= 1: position
+ * pos = ctx_b - 1, physical block blk = block_tables[b][pos / block_size],
+ * slot off = pos % block_size; then for every KV head h,
+ * k_pool[blk][h][off][:] = k_new[b][h][:] and likewise for V.  A bitwise
+ * copy: e4m3 rows arrive already quantised with the block's scale.  The block
+ * must already be in the table (allocation is the caller's job; the pages'
+ * PagedKVCache.append takes a new block when pos % block_size == 0).  A
+ * sequence with ctx_b <= 0 is skipped.  Nothing else in the pools changes.
+ *   KV-cache post, "A toy vLLM" (write_kv) and "Reading the code";
+ *   brunomaga inference post, "PagedAttention..." (PagedKVCache.append).
+ *
+ * k_pool, v_pool [device, written]; k_new, v_new, block_tables, context_lens
+ * [device, read].  Sizes as in the header comment.  num_seqs == 0 is a no-op.
+ * Supported: head_dim in {64, 128}, block_size == 16, kv_dtype any.
+ */
+pkv_status_t pkv_kv_append(void* k_pool, void* v_pool, const void* k_new, const void* v_new,
+                           const int32_t* block_tables, const int32_t* context_lens,
+                           int32_t num_seqs, int32_t num_kv_heads, int32_t head_dim,
+                           int32_t block_size, int32_t num_blocks,
+                           int32_t max_blocks_per_seq, pkv_dtype_t kv_dtype, void* stream);
+
+/*
+ * pkv_decode_workspace_bytes - device workspace that
+ * pkv_paged_decode_attention needs for its split-KV partial results:
+ * float32 o [num_seqs, num_q_heads, maxP, head_dim] then, at the next
+ * 256-byte boundary, float32 lse [num_seqs, num_q_heads, maxP], where
+ * maxP = ceil(max_context_len / partition_size) (1 when partition_size == 0).
+ * Returns 0 when maxP <= 1 (no workspace is needed) or on invalid sizes.
+ */
+size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                  int32_t max_context_len, int32_t partition_size);
+
+/*
+ * pkv_paged_decode_attention - one query token per sequence attends over its
+ * whole paged cache (call pkv_kv_append first, on the same stream).
+ *
+ * out[b][i][:] = sum_t p_t * V[b][h][t][:],  p = softmax_t(softmax_scale *
+ * q[b][i] . K[b][h][t]),  h = i / (num_q_heads / num_kv_heads),  over the
+ * tokens t < ctx_b gathered through the block table; no other mask.  For
+ * e4m3 pools K and V are scaled by their (block, head) scale.  All arithmetic
+ * is float32; out is written in q_dtype (bfloat16 rounded to nearest even).
+ * A sequence with ctx_b == 0 gets zeros.
+ *   brunomaga inference post, paged_decode_attention (the definition);
+ *   serving lesson, "PagedAttention" (block-by-block, online softmax) and
+ *   "Where it shows up" (split-KV decoding over the whole GPU).
+ *
+ * The tokens of each sequence are split into partitions of partition_size
+ * tokens (a multiple of block_size; 0 = one partition per sequence).  One
+ * workgroup per (sequence, KV head, partition) streams the partition's blocks
+ * once for all the query heads of its group and writes a normalised partial
+ * output plus its natural-log log-sum-exp to `workspace`; a second kernel
+ * merges them (skipped when maxP == 1, where the first writes `out`).
+ *
+ * out [device, written]; q, pools, scales, tables, lens [device, read];
+ * workspace [device, scratch] of at least pkv_decode_workspace_bytes(...)
+ * bytes (may be NULL when that is 0).  max_context_len: a host-side upper
+ * bound of context_lens, used to size the grid.
+ * Supported: head_dim in {64, 128}; block_size == 16; any
+ * num_q_heads / num_kv_heads ratio; (q, kv) dtypes: q in {F32, BF16} with kv
+ * in {F32, BF16, FP8_E4M3}; e4m3 needs k_scales and v_scales.
+ */
+pkv_status_t pkv_paged_decode_attention(
+    void* out, const void* q, const void* k_pool, const void* v_pool,
+    const float* k_scales, const float* v_scales, const int32_t* block_tables,
+    const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+    int32_t head_dim, int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
+    int32_t max_context_len, float softmax_scale, int32_t partition_size, void* workspace,
+    size_t workspace_bytes, pkv_dtype_t q_dtype, pkv_dtype_t kv_dtype, void* stream);
+
+/*
+ * pkv_merge_partials - combine per-partition attention results.
+ *
+ * For each (b, i): M = max_p lse[b][i][p] over the partitions that count,
+ * w_p = exp(lse_p - M), out[b][i][:] = sum_p w_p o[b][i][p][:] / sum_p w_p.
+ * A partition counts if p < num_partitions[b] (all max_partitions when
+ * num_partitions is NULL) and its lse is not -inf; partitions that do not
+ * count are never multiplied (their o may hold anything).  With no counting
+ * partition the output is 0.  lse is the natural log of the partition's
+ * softmax denominator in the same units as its scores (m + ln sum exp(s - m)).
+ *   serving lesson, "PagedAttention" / "Where it shows up": partial results
+ *   of blocks or of a split cache merged by the online-softmax update.
+ *
+ * out [device, written] [num_seqs, num_q_heads, head_dim] in out_dtype
+ * (F32 or BF16); partial_out float32 [num_seqs, num_q_heads, max_partitions,
+ * head_dim] and partial_lse float32 [num_seqs, num_q_heads, max_partitions]
+ * [device, read]; num_partitions int32 [num_seqs] [device, read] or NULL.
+ * Supported: head_dim in {64, 128}.
+ */
+pkv_status_t pkv_merge_partials(void* out, const float* partial_out, const float* partial_lse,
+                                const int32_t* num_partitions, int32_t num_seqs,
+                                int32_t num_q_heads, int32_t head_dim, int32_t max_partitions,
+                                pkv_dtype_t out_dtype, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H */

@@ -223,7 +223,8 @@ def partition_partials(q, K, V, scale, partition_size):
 
 def merge_partials(o, lse):
     """o [..., nP, D], lse [..., nP] -> [..., D].  Partitions with lse = -inf
-    are empty and skipped; if all are empty the result is 0."""
+    are empty and skipped (never multiplied); if all are empty the result is 0.
+    Any other lse counts, so a NaN partial propagates."""
     o = np.asarray(o, np.float64)
     lse = np.asarray(lse, np.float64)
     out = np.zeros(o.shape[:-2] + (o.shape[-1],))
@@ -231,7 +232,7 @@ def merge_partials(o, lse):
     flat_l = lse.reshape(-1, lse.shape[-1])
     flat_out = out.reshape(-1, o.shape[-1])
     for r in range(flat_l.shape[0]):
-        valid = np.isfinite(flat_l[r])
+        valid = ~np.isneginf(flat_l[r])
         if not valid.any():
             continue
         M = flat_l[r][valid].max()

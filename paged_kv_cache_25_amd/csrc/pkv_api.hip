@@ -1,0 +1,210 @@
+// The C ABI of libpkv (declared in include/pkv.h): argument checks, workspace
+// layout and launch configuration.  Every check runs on the host before any
+// launch, so an invalid call enqueues nothing.
+#include "../../include/pkv.h"
+
+#include <hip/hip_runtime.h>
+
+#include "pkv_launch.h"
+
+namespace {
+
+using pkv::DType;
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool dtype_ok(pkv_dtype_t t) { return t == PKV_F32 || t == PKV_BF16 || t == PKV_FP8_E4M3; }
+DType to_internal(pkv_dtype_t t) {
+  return t == PKV_F32 ? DType::F32 : (t == PKV_BF16 ? DType::BF16 : DType::FP8);
+}
+bool head_dim_ok(int32_t d) { return d == 64 || d == 128; }
+
+// Partitions per sequence for a grid: ceil(max_ctx / P), or 1 when P == 0.
+int64_t max_partitions(int32_t max_context_len, int32_t partition_size) {
+  if (max_context_len <= 0) return 1;
+  if (partition_size == 0) return 1;
+  return (int64_t(max_context_len) + partition_size - 1) / partition_size;
+}
+
+// Query heads handled by one workgroup: the group size rounded up to a power
+// of two, at most 8 for head_dim 64 and 4 for head_dim 128 (the per-lane
+// accumulators must stay in registers); larger groups are split into tiles.
+int tile_heads(int group, int head_dim) {
+  const int cap = head_dim == 64 ? 8 : 4;
+  int t = 1;
+  while (t < group && t < cap) t *= 2;
+  return t;
+}
+
+struct PartLayout {
+  size_t o_bytes, lse_offset, lse_bytes, total;
+};
+
+PartLayout part_layout(int64_t B, int64_t Hq, int64_t D, int64_t maxp) {
+  PartLayout L;
+  L.o_bytes = size_t(B * Hq * maxp * D) * sizeof(float);
+  L.lse_offset = align_up(L.o_bytes);
+  L.lse_bytes = size_t(B * Hq * maxp) * sizeof(float);
+  L.total = L.lse_offset + align_up(L.lse_bytes);
+  return L;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pkv_abi_version(void) { return PKV_ABI_VERSION; }
+
+const char* pkv_status_string(int status) {
+  switch (status) {
+    case PKV_OK: return "PKV_OK";
+    case PKV_ERR_INVALID_ARG: return "PKV_ERR_INVALID_ARG";
+    case PKV_ERR_UNSUPPORTED: return "PKV_ERR_UNSUPPORTED";
+    case PKV_ERR_WORKSPACE: return "PKV_ERR_WORKSPACE";
+    case PKV_ERR_HIP: return "PKV_ERR_HIP";
+    default: return "PKV_UNKNOWN_STATUS";
+  }
+}
+
+pkv_status_t pkv_kv_append(void* k_pool, void* v_pool, const void* k_new, const void* v_new,
+                           const int32_t* block_tables, const int32_t* context_lens,
+                           int32_t num_seqs, int32_t num_kv_heads, int32_t head_dim,
+                           int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
+                           pkv_dtype_t kv_dtype, void* stream) {
+  if (num_seqs < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks <= 0 ||
+      max_blocks_per_seq <= 0 || !dtype_ok(kv_dtype))
+    return PKV_ERR_INVALID_ARG;
+  if (!head_dim_ok(head_dim) || block_size != pkv::kBlockSizeBuilt) return PKV_ERR_UNSUPPORTED;
+  if (num_seqs == 0) return PKV_OK;
+  if (!k_pool || !v_pool || !k_new || !v_new || !block_tables || !context_lens)
+    return PKV_ERR_INVALID_ARG;
+  pkv::AppendArgs a;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.num_seqs = num_seqs;
+  a.num_kv_heads = num_kv_heads;
+  a.row_bytes = head_dim * pkv::dtype_bytes(to_internal(kv_dtype));
+  a.num_blocks = num_blocks;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  return pkv::launch_kv_append(a, static_cast<hipStream_t>(stream)) == hipSuccess ? PKV_OK
+                                                                                  : PKV_ERR_HIP;
+}
+
+size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                  int32_t max_context_len, int32_t partition_size) {
+  if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 || partition_size < 0) return 0;
+  const int64_t maxp = max_partitions(max_context_len, partition_size);
+  if (maxp <= 1) return 0;
+  return part_layout(num_seqs, num_q_heads, head_dim, maxp).total;
+}
+
+pkv_status_t pkv_paged_decode_attention(
+    void* out, const void* q, const void* k_pool, const void* v_pool, const float* k_scales,
+    const float* v_scales, const int32_t* block_tables, const int32_t* context_lens,
+    int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len,
+    float softmax_scale, int32_t partition_size, void* workspace, size_t workspace_bytes,
+    pkv_dtype_t q_dtype, pkv_dtype_t kv_dtype, void* stream) {
+  if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
+      num_blocks <= 0 || max_blocks_per_seq <= 0 || max_context_len < 0 || partition_size < 0 ||
+      !dtype_ok(q_dtype) || !dtype_ok(kv_dtype) || !(softmax_scale == softmax_scale))
+    return PKV_ERR_INVALID_ARG;
+  if (num_q_heads % num_kv_heads != 0) return PKV_ERR_INVALID_ARG;
+  if (partition_size % block_size != 0) return PKV_ERR_INVALID_ARG;
+  if (!head_dim_ok(head_dim) || block_size != pkv::kBlockSizeBuilt) return PKV_ERR_UNSUPPORTED;
+  if (q_dtype == PKV_FP8_E4M3) return PKV_ERR_UNSUPPORTED;
+  if (num_seqs == 0) return PKV_OK;
+  if (!out || !q || !k_pool || !v_pool || !block_tables || !context_lens)
+    return PKV_ERR_INVALID_ARG;
+  if (kv_dtype == PKV_FP8_E4M3 && (!k_scales || !v_scales)) return PKV_ERR_INVALID_ARG;
+
+  const int64_t maxp = max_partitions(max_context_len, partition_size);
+  const int64_t blocks_per_part =
+      partition_size == 0 ? int64_t(max_blocks_per_seq) : int64_t(partition_size / block_size);
+  // A single partition per sequence also covers partition sizes past the table's capacity.
+  const bool single = maxp <= 1;
+  const int group = num_q_heads / num_kv_heads;
+  const int tile = tile_heads(group, head_dim);
+
+  pkv::DecodeArgs a;
+  a.out = out;
+  a.part_o = nullptr;
+  a.part_lse = nullptr;
+  if (!single) {
+    const PartLayout L = part_layout(num_seqs, num_q_heads, head_dim, maxp);
+    if (!workspace || workspace_bytes < L.total) return PKV_ERR_WORKSPACE;
+    a.part_o = static_cast<float*>(workspace);
+    a.part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + L.lse_offset);
+  }
+  a.q = q;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.k_scales = k_scales;
+  a.v_scales = v_scales;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.group = group;
+  a.head_chunks = (group + tile - 1) / tile;
+  a.num_blocks = num_blocks;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.blocks_per_partition = int(single ? max_blocks_per_seq : blocks_per_part);
+  a.max_partitions = int(maxp);
+  a.scale_log2 = softmax_scale * pkv::kLog2eHost;
+  a.write_final = single ? 1 : 0;
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (pkv::launch_paged_decode(a, head_dim, tile, to_internal(q_dtype), to_internal(kv_dtype), st) !=
+      hipSuccess)
+    return PKV_ERR_HIP;
+  if (single) return PKV_OK;
+
+  pkv::MergeArgs m;
+  m.out = out;
+  m.part_o = a.part_o;
+  m.part_lse = a.part_lse;
+  m.num_partitions = nullptr;
+  m.context_lens = context_lens;
+  m.partition_size = partition_size;
+  m.num_seqs = num_seqs;
+  m.num_q_heads = num_q_heads;
+  m.max_partitions = int(maxp);
+  return pkv::launch_merge(m, head_dim, to_internal(q_dtype), st) == hipSuccess ? PKV_OK
+                                                                                : PKV_ERR_HIP;
+}
+
+pkv_status_t pkv_merge_partials(void* out, const float* partial_out, const float* partial_lse,
+                                const int32_t* num_partitions, int32_t num_seqs,
+                                int32_t num_q_heads, int32_t head_dim, int32_t max_partitions,
+                                pkv_dtype_t out_dtype, void* stream) {
+  if (num_seqs < 0 || num_q_heads <= 0 || head_dim <= 0 || max_partitions <= 0 ||
+      !dtype_ok(out_dtype))
+    return PKV_ERR_INVALID_ARG;
+  if (!head_dim_ok(head_dim) || out_dtype == PKV_FP8_E4M3) return PKV_ERR_UNSUPPORTED;
+  if (num_seqs == 0) return PKV_OK;
+  if (!out || !partial_out || !partial_lse) return PKV_ERR_INVALID_ARG;
+  pkv::MergeArgs m;
+  m.out = out;
+  m.part_o = partial_out;
+  m.part_lse = partial_lse;
+  m.num_partitions = num_partitions;
+  m.context_lens = nullptr;
+  m.partition_size = 0;
+  m.num_seqs = num_seqs;
+  m.num_q_heads = num_q_heads;
+  m.max_partitions = max_partitions;
+  return pkv::launch_merge(m, head_dim, to_internal(out_dtype), static_cast<hipStream_t>(stream)) ==
+                 hipSuccess
+             ? PKV_OK
+             : PKV_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,60 @@
+// Host-side launchers of the libpkv kernels (internal; the public ABI is include/pkv.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pkv {
+
+enum class DType : int { F32 = 0, BF16 = 1, FP8 = 2 };
+
+constexpr int kBlockSizeBuilt = 16;                 // tokens per KV block
+constexpr float kLog2eHost = 1.4426950408889634f;
+
+inline int dtype_bytes(DType t) { return t == DType::F32 ? 4 : (t == DType::BF16 ? 2 : 1); }
+
+struct AppendArgs {
+  void* k_pool;
+  void* v_pool;
+  const void* k_new;
+  const void* v_new;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  int num_seqs, num_kv_heads, row_bytes, num_blocks, max_blocks_per_seq;
+};
+
+struct DecodeArgs {
+  void* out;               // final output (q dtype) when write_final
+  float* part_o;           // [B, Hq, maxP, D] when !write_final
+  float* part_lse;         // [B, Hq, maxP]
+  const void* q;
+  const void* k_pool;
+  const void* v_pool;
+  const float* k_scales;   // [NB, Hkv] (e4m3 only)
+  const float* v_scales;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  int num_seqs, num_q_heads, num_kv_heads, group, head_chunks;
+  int num_blocks, max_blocks_per_seq;
+  int blocks_per_partition;   // partition size / 16
+  int max_partitions;         // grid extent over partitions
+  float scale_log2;           // softmax_scale * log2(e)
+  int write_final;
+};
+
+struct MergeArgs {
+  void* out;
+  const float* part_o;
+  const float* part_lse;
+  const int32_t* num_partitions;   // may be null
+  const int32_t* context_lens;     // may be null: partitions = ceil(ctx / partition_size)
+  int partition_size;
+  int num_seqs, num_q_heads, max_partitions;
+};
+
+hipError_t launch_kv_append(const AppendArgs& a, hipStream_t stream);
+hipError_t launch_paged_decode(const DecodeArgs& a, int head_dim, int tile_heads, DType q_dtype,
+                               DType kv_dtype, hipStream_t stream);
+hipError_t launch_merge(const MergeArgs& a, int head_dim, DType out_dtype, hipStream_t stream);
+
+}  // namespace pkv

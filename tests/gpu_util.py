@@ -1,0 +1,109 @@
+"""Helpers for the GPU parity tests: move workload inputs to the device, run
+the HIP path through the C ABI, and compare against the oracle."""
+
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+import oracle.paged_attention as pa
+from paged_kv_cache_25_amd import ops
+
+TORCH_DT = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8_e4m3": torch.float8_e4m3fn}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def dev_tensor(arr: np.ndarray, dtype: str | None, device="cuda"):
+    """Storage numpy array -> device tensor of the matching torch dtype."""
+    if dtype is None:
+        return torch.from_numpy(np.ascontiguousarray(arr)).to(device)
+    if dtype == "bf16":
+        t = torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(torch.bfloat16)
+    elif dtype == "fp8_e4m3":
+        t = torch.from_numpy(np.ascontiguousarray(arr)).view(torch.float8_e4m3fn)
+    else:
+        t = torch.from_numpy(np.ascontiguousarray(arr, dtype=np.float32))
+    return t.to(device)
+
+
+def host_storage(t: torch.Tensor) -> np.ndarray:
+    """Device tensor -> numpy storage array (float32 / uint16 bits / uint8 codes)."""
+    t = t.detach().cpu().contiguous()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    if t.dtype == torch.float8_e4m3fn:
+        return t.view(torch.uint8).numpy()
+    return t.numpy()
+
+
+class DeviceStep:
+    """One workload on the device, ready to run append + decode."""
+
+    def __init__(self, inp, device="cuda"):
+        self.inp = inp
+        self.q = dev_tensor(inp.q, inp.q_dtype, device)
+        self.k_pool = dev_tensor(inp.k_pool, inp.kv_dtype, device)
+        self.v_pool = dev_tensor(inp.v_pool, inp.kv_dtype, device)
+        self.k_new = dev_tensor(inp.k_new, inp.kv_dtype, device)
+        self.v_new = dev_tensor(inp.v_new, inp.kv_dtype, device)
+        self.tables = dev_tensor(inp.block_tables, None, device)
+        self.lens = dev_tensor(inp.context_lens, None, device)
+        self.k_scales = None if inp.k_scales is None else dev_tensor(inp.k_scales, None, device)
+        self.v_scales = None if inp.v_scales is None else dev_tensor(inp.v_scales, None, device)
+        self.out = torch.empty(inp.num_seqs, inp.num_q_heads, inp.head_dim,
+                               dtype=TORCH_DT[inp.q_dtype], device=device)
+
+    def append(self):
+        ops.kv_append(self.k_pool, self.v_pool, self.k_new, self.v_new, self.tables, self.lens)
+
+    def decode(self, partition_size=None, max_context_len=None):
+        inp = self.inp
+        P = inp.partition_size if partition_size is None else partition_size
+        mcl = inp.max_context_len if max_context_len is None else max_context_len
+        ops.paged_decode_attention(self.out, self.q, self.k_pool, self.v_pool, self.tables,
+                                   self.lens, mcl, inp.softmax_scale, P, self.k_scales,
+                                   self.v_scales)
+        return self.out
+
+    def step(self, partition_size=None):
+        self.append()
+        out = self.decode(partition_size)
+        torch.cuda.synchronize()
+        return out
+
+    def out_f64(self):
+        return self.out.detach().float().cpu().double().numpy()
+
+
+def oracle_out(inp, seqs=None, pools=None):
+    """Oracle output (float64) after the append; ``pools`` = already-appended pools."""
+    if pools is None:
+        pools = pa.kv_append(inp.k_pool, inp.v_pool, inp.k_new, inp.v_new, inp.block_tables,
+                             inp.context_lens, inp.block_size)
+    return pa.decode_attention(inp.q, pools[0], pools[1], inp.block_tables, inp.context_lens,
+                               block_size=inp.block_size, softmax_scale=inp.softmax_scale,
+                               q_dtype=inp.q_dtype, kv_dtype=inp.kv_dtype,
+                               k_scales=inp.k_scales, v_scales=inp.v_scales, seqs=seqs)
+
+
+def check_tolerance(kv_dtype, gpu, ref, label=""):
+    """The bars: f32 KV max-abs 1e-5; bf16 KV |d| <= max(2e-2 |ref|, 1e-2);
+    e4m3 KV max-abs 6e-2 (against the oracle on the same dequantised values).
+    Returns the max abs error; asserts on the bar and on finiteness."""
+    assert np.isfinite(gpu).all(), f"{label}: non-finite output"
+    err = np.abs(gpu - ref)
+    mx = float(err.max()) if err.size else 0.0
+    if kv_dtype == "f32":
+        assert mx <= 1e-5, f"{label}: max abs err {mx}"
+    elif kv_dtype == "bf16":
+        bound = np.maximum(2e-2 * np.abs(ref), 1e-2)
+        assert (err <= bound).all(), f"{label}: max abs err {mx}"
+    else:
+        assert mx <= 6e-2, f"{label}: max abs err {mx}"
+    log(f"[parity] {label}: max|gpu-oracle| = {mx:.3e}")
+    return mx

@@ -151,14 +151,12 @@ def test_decode_mask_all_ones():
     one new one, the new query sees all 7 keys (4yush.com, 'Adding the cache to
     GPT-2').  A key placed at the newest position with a dominant score must
     therefore win."""
-    rng = np.random.default_rng(3)
     inp = make_inputs(num_seqs=1, num_q_heads=2, num_kv_heads=2, head_dim=64, ctx=("const", 7),
                       pool=("blocks", 4), q_dtype="f32", kv_dtype="f32", seed=3)
     qv = pa.to_float64(inp.q[0], "f32")
     inp.k_new[0] = (200.0 * qv / (qv * qv).sum(axis=1, keepdims=True) * 8).astype(np.float32)
     out = pins._step(inp)
     assert np.abs(out[0] - inp.v_new[0].astype(np.float64)).max() < 1e-12
-    del rng
 
 
 def test_empty_context_gives_zeros():

@@ -4,7 +4,8 @@ Nothing here computes attention.  The module draws:
 
 1. context lengths (tokens attended, counting the token appended this step),
 2. a random placement of every sequence's logical blocks in the shared pool,
-3. K pool values, then V pool values, then queries, all N(0, 1),
+3. K pool values, then V pool values (each from its own seed sequence,
+   [seed, 1] and [seed, 2], in chunks of 256 blocks), then queries, all N(0, 1),
 
 and stores them in the storage format of the requested dtype:
 
@@ -29,8 +30,10 @@ continuous-batching length mix and an fp8 multi-head case.
 
 from __future__ import annotations
 
+import concurrent.futures
 import dataclasses
 import math
+import os
 
 import numpy as np
 import torch
@@ -149,29 +152,52 @@ def _poison_value(dtype: str):
             "fp8_e4m3": np.uint8(E4M3_NAN_CODE)}[dtype]
 
 
-def _draw_pool(rng, num_blocks, hkv, bs, d, dtype, valid_count, poison, chunk=1024):
-    """Draw one pool (post-append contents) block-chunk by block-chunk."""
+_POOL_CHUNK_BLOCKS = 256
+
+
+def _draw_pool(seed_words, num_blocks, hkv, bs, d, dtype, valid_count, poison):
+    """Draw one pool (post-append contents).  Blocks are drawn in chunks of
+    256, chunk i from its own generator ``SeedSequence(seed_words).spawn(n)[i]``
+    (so the result does not depend on how many threads draw it)."""
     pool = np.empty((num_blocks, hkv, bs, d), STORAGE_NP[dtype])
     scales = np.full((num_blocks, hkv), np.nan, np.float32) if dtype == "fp8_e4m3" else None
     pv = _poison_value(dtype)
-    for c0 in range(0, num_blocks, chunk):
-        c1 = min(num_blocks, c0 + chunk)
-        x = rng.standard_normal((c1 - c0, hkv, bs, d), dtype=np.float32)
+    starts = list(range(0, num_blocks, _POOL_CHUNK_BLOCKS))
+    kids = np.random.SeedSequence(seed_words).spawn(len(starts))
+
+    def one(i):
+        c0 = starts[i]
+        c1 = min(num_blocks, c0 + _POOL_CHUNK_BLOCKS)
+        g = np.random.Generator(np.random.PCG64(kids[i]))
+        x = g.standard_normal((c1 - c0, hkv, bs, d), dtype=np.float32)
         vc = valid_count[c0:c1]
         slot_ok = np.arange(bs)[None, :] < vc[:, None]                     # [n, bs]
         if dtype == "fp8_e4m3":
-            amax = np.where(slot_ok[:, None, :, None], np.abs(x), np.float32(0)).max(axis=(2, 3))
+            mag = np.abs(x)
+            mag *= slot_ok[:, None, :, None]
+            amax = mag.max(axis=(2, 3))
             sc = np.where(amax > 0, amax / np.float32(E4M3_MAX), np.float32(1)).astype(np.float32)
-            y = np.clip(x / sc[:, :, None, None], -E4M3_MAX, E4M3_MAX)
-            pool[c0:c1] = _to_storage(y, dtype)
+            x /= sc[:, :, None, None]
+            np.clip(x, -E4M3_MAX, E4M3_MAX, out=x)
             scales[c0:c1] = np.where(vc[:, None] > 0, sc, np.float32(np.nan))
-        else:
-            pool[c0:c1] = _to_storage(x, dtype)
+        pool[c0:c1] = _to_storage(x, dtype)
         if poison:
             bad = ~slot_ok                                                   # [n, bs]
-            view = pool[c0:c1].transpose(0, 2, 1, 3)                         # [n, bs, hkv, d]
-            view[bad] = pv
+            if bad.any():
+                view = pool[c0:c1].transpose(0, 2, 1, 3)                     # [n, bs, hkv, d]
+                view[bad] = pv
+
+    with concurrent.futures.ThreadPoolExecutor(max_workers=_threads()) as ex:
+        list(ex.map(one, range(len(starts))))
     return pool, scales
+
+
+def _threads():
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
 
 
 def _context_lengths(rng, spec, num_seqs):
@@ -222,9 +248,9 @@ def make_inputs(*, num_seqs, num_q_heads, num_kv_heads, head_dim, ctx, pool,
             valid[-1] = ctx_lens[b] - (nblk[b] - 1) * block_size
         valid_count[ids] = valid
 
-    k_pool, k_scales = _draw_pool(rng, num_blocks, num_kv_heads, block_size, head_dim,
+    k_pool, k_scales = _draw_pool([seed, 1], num_blocks, num_kv_heads, block_size, head_dim,
                                   kv_dtype, valid_count, poison)
-    v_pool, v_scales = _draw_pool(rng, num_blocks, num_kv_heads, block_size, head_dim,
+    v_pool, v_scales = _draw_pool([seed, 2], num_blocks, num_kv_heads, block_size, head_dim,
                                   kv_dtype, valid_count, poison)
     q = _to_storage(rng.standard_normal((num_seqs, num_q_heads, head_dim), dtype=np.float32), q_dtype)
 
