@@ -327,7 +327,7 @@ __global__ __launch_bounds__(kWave) void paged_decode_kernel(DecodeArgs a) {
   for (int i = 0; i < G; ++i) {
     if (tg != i || i >= n_heads) continue;
     const int qh = qh0 + i;
-    const bool empty = !(lt[i] > 0.0f);
+    const bool empty = lt[i] == 0.0f;        // no valid token (a NaN sum is not empty)
     const float inv = empty ? 0.0f : 1.0f / lt[i];
     if (a.write_final) {
       char* orow = reinterpret_cast<char*>(a.out) + (size_t(b) * a.num_q_heads + qh) * size_t(D) * QT::kBytes;

@@ -1,0 +1,289 @@
+// Split-KV paged decode attention on the matrix cores (gfx950), for bf16
+// queries over a bf16 cache with query-head groups of 2..16 sharing a KV head.
+//
+// Same work split as the vector kernel: one 64-lane workgroup per (sequence,
+// KV head, tile of up to 16 query heads, partition) walks the partition's
+// block-table entries and reads each physical (block, KV head) slice
+// [16 tokens x D] once from HBM for every query head of its group.  The
+// quantity is the one the brunomaga inference post's paged_decode_attention
+// defines; blocks are merged with the online-softmax update (learn.mohebi.ai
+// serving lesson, "PagedAttention").
+//
+// Per 16-token block:
+//   S^T[16 tok x 16 heads] = K[16 x D] . Q^T      D/32 x mfma_f32_16x16x32_bf16
+//   online softmax on S^T in fp32 (log2 units; lazily raised maxima)
+//   O[16 heads x D] += P[16 x 16 tok] . V[16 x D]  D/16 x mfma_f32_16x16x16_bf16
+// The accumulator layout of the first product (lane l holds tokens 4*(l/16)+i
+// of head l%16) is exactly the A-operand layout the second needs, so P never
+// moves between lanes.  Unused head rows (group < 16) compute on zero queries
+// and are not written.  P is rounded to bf16 for the second product; scores,
+// weights, sums and O stay fp32.
+//
+// Loads (16 bytes per lane, straight into registers):
+//   K: lane l reads token l%16, bytes 64j + 16*(l/16) of its row for slab j:
+//      64 contiguous bytes per token per load.
+//   V: lane l reads rows 4*(l/16)+i, bytes 16*(l%16): each load covers four
+//      whole rows.  The B operand of tile e (dims 8c + e, c = l%16) is two
+//      v_perm_b32 of the four rows' words.
+#include "pkv_device.h"
+#include "pkv_launch.h"
+
+namespace pkv {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kRescaleThreshold = 8.0f;   // log2 units: weights <= 2^8
+constexpr int kHeadTile = 16;
+
+template <int D>
+struct MfmaTile {
+  static constexpr int kSlabs = D / 32;          // QK products per block
+  static constexpr int kTiles = D / 16;          // PV products per block
+  static constexpr int kRowBytes = D * 2;
+  static constexpr int kSliceBytes = 16 * kRowBytes;
+  static constexpr int kVChunkBytes = D / 8;     // bytes of one row a lane reads for V (16 or 8)
+  static constexpr int kVWords = kVChunkBytes / 4;
+};
+
+__device__ __forceinline__ uint32_t lo_pair(uint32_t a, uint32_t b) {   // (a.lo, b.lo)
+  return __builtin_amdgcn_perm(b, a, 0x05040100u);
+}
+__device__ __forceinline__ uint32_t hi_pair(uint32_t a, uint32_t b) {   // (a.hi, b.hi)
+  return __builtin_amdgcn_perm(b, a, 0x07060302u);
+}
+
+template <int D>
+struct BlockRegs {
+  uint4 k[MfmaTile<D>::kSlabs];                       // A operands of QK
+  uint32_t v[4][MfmaTile<D>::kVWords];                // rows 4r+i, this lane's bytes
+};
+
+template <int D>
+__device__ __forceinline__ void load_block(BlockRegs<D>& br, const char* kslice,
+                                           const char* vslice, int lane) {
+  using T = MfmaTile<D>;
+  const int r = lane >> 4, c = lane & 15;
+#pragma unroll
+  for (int j = 0; j < T::kSlabs; ++j)
+    br.k[j] = *reinterpret_cast<const uint4*>(kslice + c * T::kRowBytes + 64 * j + 16 * r);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const char* p = vslice + (4 * r + i) * T::kRowBytes + T::kVChunkBytes * c;
+    if constexpr (T::kVWords == 4) {
+      const uint4 w = *reinterpret_cast<const uint4*>(p);
+      br.v[i][0] = w.x; br.v[i][1] = w.y; br.v[i][2] = w.z; br.v[i][3] = w.w;
+    } else {
+      const uint2 w = *reinterpret_cast<const uint2*>(p);
+      br.v[i][0] = w.x; br.v[i][1] = w.y;
+    }
+  }
+}
+
+template <int D>
+struct MfmaDecode {
+  using T = MfmaTile<D>;
+  bf16x8 q[T::kSlabs];          // B operands of QK (head l%16)
+  f32x4 o[T::kTiles];           // O rows 4r+i, dims 8c+e (D=128) / 4c+e (D=64)
+  float m, l;                   // per head l%16 (log2 units)
+
+  __device__ __forceinline__ void block(BlockRegs<D>& br, int valid, float k_mul, int lane) {
+    const int r = lane >> 4;
+    f32x4 s = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int j = 0; j < T::kSlabs; ++j)
+      s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, br.k[j]), q[j], s,
+                                                  0, 0, 0);
+    float sc[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sc[i] = s[i] * k_mul;
+    if (valid < 16) {                       // wave-uniform: the sequence's last block
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bool ok = 4 * r + i < valid;
+        sc[i] = ok ? sc[i] : -INFINITY;
+#pragma unroll
+        for (int w = 0; w < T::kVWords; ++w) br.v[i][w] = ok ? br.v[i][w] : 0u;
+      }
+    }
+    const float bm = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+    if (__any(bm > m + kRescaleThreshold)) {     // rare: raise the reference maxima
+      float hm = fmaxf(bm, __shfl_xor(bm, 16));
+      hm = fmaxf(hm, __shfl_xor(hm, 32));
+      const float mn = fmaxf(m, hm);
+      const float alpha = __builtin_amdgcn_exp2f(m - mn);
+      l *= alpha;
+      m = mn;
+      float a_row[4];                        // alpha of head 4r+i, held by lane 4r+i
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a_row[i] = __shfl(alpha, 4 * r + i);
+#pragma unroll
+      for (int t = 0; t < T::kTiles; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[t][i] *= a_row[i];
+    }
+    float p[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(sc[i] - m);
+    l += (p[0] + p[1]) + (p[2] + p[3]);
+    const bf16x4 pa = {(__bf16)p[0], (__bf16)p[1], (__bf16)p[2], (__bf16)p[3]};
+#pragma unroll
+    for (int w = 0; w < T::kVWords; ++w) {
+      // tile 2w: low halves (dim 2w of this lane's chunk), tile 2w+1: high halves
+      const uint32_t b0lo = lo_pair(br.v[0][w], br.v[1][w]), b1lo = lo_pair(br.v[2][w], br.v[3][w]);
+      const uint32_t b0hi = hi_pair(br.v[0][w], br.v[1][w]), b1hi = hi_pair(br.v[2][w], br.v[3][w]);
+      const uint2 blo = {b0lo, b1lo}, bhi = {b0hi, b1hi};
+      o[2 * w] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, __builtin_bit_cast(bf16x4, blo),
+                                                           o[2 * w], 0, 0, 0);
+      o[2 * w + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+          pa, __builtin_bit_cast(bf16x4, bhi), o[2 * w + 1], 0, 0, 0);
+    }
+  }
+};
+
+// Three waves per SIMD: 151 VGPRs for head dim 128 with two blocks in flight.
+template <int D>
+__global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(3)))
+void paged_decode_mfma_kernel(DecodeArgs a) {
+  using T = MfmaTile<D>;
+  int idx = blockIdx.x;
+  const int part = idx % a.max_partitions; idx /= a.max_partitions;
+  const int chunk = idx % a.head_chunks;   idx /= a.head_chunks;
+  const int h = idx % a.num_kv_heads;
+  const int b = idx / a.num_kv_heads;
+
+  const int lane = threadIdx.x;
+  const int r = lane >> 4, c = lane & 15;
+
+  int ctx = a.context_lens[b];
+  ctx = ctx < 0 ? 0 : ctx;
+  const int cap = a.max_blocks_per_seq * kBlockSize;
+  ctx = ctx > cap ? cap : ctx;
+  const int n_blk_seq = (ctx + kBlockSize - 1) / kBlockSize;
+  const int blk_begin = part * a.blocks_per_partition;
+  int blk_end = blk_begin + a.blocks_per_partition;
+  blk_end = blk_end < n_blk_seq ? blk_end : n_blk_seq;
+  if (blk_begin >= blk_end && !(a.write_final && part == 0)) return;
+
+  const int head0 = chunk * kHeadTile;
+  int n_heads = a.group - head0;
+  n_heads = n_heads < kHeadTile ? n_heads : kHeadTile;
+  const int qh0 = h * a.group + head0;
+
+  MfmaDecode<D> dec;
+  {
+    const bool ok = c < n_heads;
+    const char* qrow = reinterpret_cast<const char*>(a.q) +
+                       (size_t(b) * a.num_q_heads + qh0 + (ok ? c : 0)) * T::kRowBytes;
+#pragma unroll
+    for (int j = 0; j < T::kSlabs; ++j) {
+      uint4 w = ok ? *reinterpret_cast<const uint4*>(qrow + 64 * j + 16 * r) : make_uint4(0, 0, 0, 0);
+      dec.q[j] = __builtin_bit_cast(bf16x8, w);
+    }
+#pragma unroll
+    for (int t = 0; t < T::kTiles; ++t) dec.o[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    dec.m = -INFINITY;
+    dec.l = 0.0f;
+  }
+
+  const int32_t* table = a.block_tables + size_t(b) * a.max_blocks_per_seq;
+  const char* kbase = reinterpret_cast<const char*>(a.k_pool);
+  const char* vbase = reinterpret_cast<const char*>(a.v_pool);
+  const size_t head_off = size_t(h) * T::kSliceBytes;
+  const size_t block_stride = size_t(a.num_kv_heads) * T::kSliceBytes;
+  const float k_mul = a.scale_log2;
+
+  BlockRegs<D> bA, bB;
+  for (int seg = blk_begin; seg < blk_end; seg += kWave) {
+    const int n = (blk_end - seg) < kWave ? (blk_end - seg) : kWave;
+    int my_id = lane < n ? table[seg + lane] : -1;
+    const bool my_ok = unsigned(my_id) < unsigned(a.num_blocks);
+    my_id = my_ok ? my_id : 0;
+    const uint64_t ok_mask = __ballot(my_ok);
+
+    auto fetch = [&](BlockRegs<D>& br, int k) {
+      const int phys = __builtin_amdgcn_readlane(my_id, k);
+      const size_t off = size_t(phys) * block_stride + head_off;
+      load_block<D>(br, kbase + off, vbase + off, lane);
+    };
+    auto consume = [&](BlockRegs<D>& br, int k) {
+      int valid = ctx - (seg + k) * kBlockSize;
+      valid = valid < kBlockSize ? valid : kBlockSize;
+      valid = ((ok_mask >> k) & 1) ? valid : 0;
+      dec.block(br, valid, k_mul, lane);
+    };
+
+    fetch(bA, 0);
+    int k = 0;
+    for (; k + 2 <= n; k += 2) {
+      fetch(bB, k + 1);
+      consume(bA, k);
+      if (k + 2 < n) fetch(bA, k + 2);
+      consume(bB, k + 1);
+    }
+    if (k < n) consume(bA, k);
+  }
+
+  // Denominator of head l%16 over the 4 lane rows; then that of head 4r+i.
+  float lt = dec.l + __shfl_xor(dec.l, 16);
+  lt += __shfl_xor(lt, 32);
+  float l_row[4], m_row[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    l_row[i] = __shfl(lt, 4 * r + i);
+    m_row[i] = __shfl(dec.m, 4 * r + i);
+  }
+  constexpr int kDimsPerLane = D / 16;       // dims dpl*c .. dpl*c + dpl-1 of each head row
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int hh = 4 * r + i;
+    if (hh >= n_heads) continue;
+    const int qh = qh0 + hh;
+    const bool empty = l_row[i] == 0.0f;
+    const float inv = empty ? 0.0f : 1.0f / l_row[i];
+    if (a.write_final) {
+      uint16_t* orow = reinterpret_cast<uint16_t*>(a.out) + (size_t(b) * a.num_q_heads + qh) * D +
+                       kDimsPerLane * c;
+      uint32_t packed[kDimsPerLane / 2];
+#pragma unroll
+      for (int e = 0; e < kDimsPerLane; e += 2)
+        packed[e / 2] = uint32_t(f32_to_bf16_rne(dec.o[e][i] * inv)) |
+                        (uint32_t(f32_to_bf16_rne(dec.o[e + 1][i] * inv)) << 16);
+      if constexpr (kDimsPerLane == 8)
+        *reinterpret_cast<uint4*>(orow) = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+      else
+        *reinterpret_cast<uint2*>(orow) = make_uint2(packed[0], packed[1]);
+    } else {
+      const size_t prow = (size_t(b) * a.num_q_heads + qh) * a.max_partitions + part;
+      float* op = a.part_o + prow * D + kDimsPerLane * c;
+#pragma unroll
+      for (int e = 0; e < kDimsPerLane; e += 4)
+        *reinterpret_cast<float4*>(op + e) = make_float4(dec.o[e][i] * inv, dec.o[e + 1][i] * inv,
+                                                         dec.o[e + 2][i] * inv, dec.o[e + 3][i] * inv);
+      if (c == 0)
+        a.part_lse[prow] = empty ? -INFINITY : (m_row[i] + __builtin_amdgcn_logf(l_row[i])) * kLn2;
+    }
+  }
+}
+
+template <int D>
+hipError_t launch_d(const DecodeArgs& a, hipStream_t stream) {
+  const size_t grid = size_t(a.num_seqs) * a.num_kv_heads * a.head_chunks * a.max_partitions;
+  if (grid == 0) return hipSuccess;
+  if (grid > 0x7fffffffu) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((paged_decode_mfma_kernel<D>), dim3(unsigned(grid)), dim3(kWave), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int mfma_head_tile() { return kHeadTile; }
+
+hipError_t launch_paged_decode_mfma(const DecodeArgs& a, int head_dim, hipStream_t stream) {
+  if (head_dim == 64) return launch_d<64>(a, stream);
+  return launch_d<128>(a, stream);
+}
+
+}  // namespace pkv

@@ -130,7 +130,10 @@ pkv_status_t pkv_paged_decode_attention(
   // A single partition per sequence also covers partition sizes past the table's capacity.
   const bool single = maxp <= 1;
   const int group = num_q_heads / num_kv_heads;
-  const int tile = tile_heads(group, head_dim);
+  // bf16 queries over a bf16 cache with a shared KV head run on the matrix
+  // cores; every other combination on the vector kernel.
+  const bool use_mfma = q_dtype == PKV_BF16 && kv_dtype == PKV_BF16 && group >= 2;
+  const int tile = use_mfma ? pkv::mfma_head_tile() : tile_heads(group, head_dim);
 
   pkv::DecodeArgs a;
   a.out = out;
@@ -162,9 +165,11 @@ pkv_status_t pkv_paged_decode_attention(
   a.write_final = single ? 1 : 0;
 
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (pkv::launch_paged_decode(a, head_dim, tile, to_internal(q_dtype), to_internal(kv_dtype), st) !=
-      hipSuccess)
-    return PKV_ERR_HIP;
+  const hipError_t err =
+      use_mfma ? pkv::launch_paged_decode_mfma(a, head_dim, st)
+               : pkv::launch_paged_decode(a, head_dim, tile, to_internal(q_dtype),
+                                          to_internal(kv_dtype), st);
+  if (err != hipSuccess) return PKV_ERR_HIP;
   if (single) return PKV_OK;
 
   pkv::MergeArgs m;

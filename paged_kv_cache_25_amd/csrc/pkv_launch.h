@@ -55,6 +55,9 @@ struct MergeArgs {
 hipError_t launch_kv_append(const AppendArgs& a, hipStream_t stream);
 hipError_t launch_paged_decode(const DecodeArgs& a, int head_dim, int tile_heads, DType q_dtype,
                                DType kv_dtype, hipStream_t stream);
+// Matrix-core variant for bf16 queries over a bf16 cache; heads in tiles of 16.
+hipError_t launch_paged_decode_mfma(const DecodeArgs& a, int head_dim, hipStream_t stream);
+int mfma_head_tile();
 hipError_t launch_merge(const MergeArgs& a, int head_dim, DType out_dtype, hipStream_t stream);
 
 }  // namespace pkv
