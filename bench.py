@@ -49,7 +49,30 @@ def parse():
     ap.add_argument("--kernel-reps", type=int, default=200)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=15.0)
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="only time a plain device-to-device copy of this many MiB (the "
+                         "reference kernel for scaling FETCH_SIZE / WRITE_SIZE counters)")
     return ap.parse_args()
+
+
+def copy_calibration(mib, reps):
+    """A plain copy of known size: under rocprofv3 --pmc its FETCH_SIZE and
+    WRITE_SIZE per dispatch, divided by ``mib`` MiB, give the counters' scale."""
+    import torch
+    n = mib * 2 ** 20 // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    print(json.dumps({"copy_mib": mib, "us_per_copy": round(ms * 1e3, 2),
+                      "copy_gbps_read_plus_write": round(2 * mib * 2 ** 20 / (ms * 1e-3) / 1e9, 1)}))
 
 
 def main():
@@ -59,6 +82,10 @@ def main():
                           "shards by sequence or KV head with no exchange, so N GPUs run N "
                           "independent copies of this benchmark; --gpus must be 1"}))
         sys.exit(2)
+
+    if args.copy_calibration_mib:
+        copy_calibration(args.copy_calibration_mib, max(1, args.steps))
+        return
 
     import torch
 

@@ -70,10 +70,10 @@ __device__ __forceinline__ void load_row(uint32_t (&w)[NW], const char* row, int
   for (int c = 0; c < TL::kChunks; ++c) {
     const char* p = row + TL::chunk_off(s, c);
     if constexpr (TL::kChunkBytes == 16) {
-      uint4 v = *reinterpret_cast<const uint4*>(p);
+      uint4 v = load_streamed<uint4>(p);
       w[c * 4 + 0] = v.x; w[c * 4 + 1] = v.y; w[c * 4 + 2] = v.z; w[c * 4 + 3] = v.w;
     } else {
-      uint2 v = *reinterpret_cast<const uint2*>(p);
+      uint2 v = load_streamed<uint2>(p);
       w[c * 2 + 0] = v.x; w[c * 2 + 1] = v.y;
     }
   }
@@ -222,12 +222,15 @@ __global__ __launch_bounds__(kWave) void paged_decode_kernel(DecodeArgs a) {
   constexpr int W = TL::kWords;
   constexpr int KD = TL::kDims;
 
-  // blockIdx.x -> (partition, head chunk, kv head, sequence), partition fastest.
+  // blockIdx.x -> (head chunk, kv head, sequence, partition), partition
+  // slowest.  Workgroups go to the 8 XCDs round-robin, so consecutive ids must
+  // carry equal work: every (sequence, head) has a partition 0, while only long
+  // sequences have high partitions.
   int idx = blockIdx.x;
-  const int part = idx % a.max_partitions; idx /= a.max_partitions;
   const int chunk = idx % a.head_chunks;   idx /= a.head_chunks;
-  const int h = idx % a.num_kv_heads;
-  const int b = idx / a.num_kv_heads;
+  const int h = idx % a.num_kv_heads;      idx /= a.num_kv_heads;
+  const int b = idx % a.num_seqs;
+  const int part = idx / a.num_seqs;
 
   const int lane = threadIdx.x;
   const int tg = lane / kLanesPerToken;

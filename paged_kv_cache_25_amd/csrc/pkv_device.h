@@ -87,4 +87,28 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
+// 8- and 16-byte loads of streamed K/V data.  With PKV_NT_LOADS (the default)
+// they carry the nontemporal hint: each slice is read once per step, so it
+// should not displace reusable lines from the caches.
+#ifndef PKV_NT_LOADS
+#define PKV_NT_LOADS 1
+#endif
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+template <typename T> struct VecOf;
+template <> struct VecOf<uint4> { using type = u32x4; };
+template <> struct VecOf<uint2> { using type = u32x2; };
+
+template <typename T>
+__device__ __forceinline__ T load_streamed(const char* p) {
+  using V = typename VecOf<T>::type;
+#if PKV_NT_LOADS
+  const V v = __builtin_nontemporal_load(reinterpret_cast<const V*>(p));
+#else
+  const V v = *reinterpret_cast<const V*>(p);
+#endif
+  return __builtin_bit_cast(T, v);
+}
+
 }  // namespace pkv
