@@ -217,6 +217,8 @@ def main():
     value = step_bytes / (step_ms * 1e-3) / 1e9
     kernel_gbps = tr["kv_bytes"] / (decode_ms * 1e-3) / 1e9
 
+    traffic_bytes = measured_traffic(inp.name) if (calls[0][2] is not None and
+                                                   P == 512 and args.seed is None) else None
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(inp, args.cpu_budget_s)
@@ -243,14 +245,45 @@ def main():
         "tokens_per_s": round(B * 1e3 / step_ms, 1),
         "kernel_us": {"append": round(append_ms * 1e3, 2), "decode": round(decode_ms * 1e3, 2),
                       "merge": round(merge_ms * 1e3, 2), "attention_call": round(att_ms * 1e3, 2)},
-        "roofline": {"kernel": "paged_decode_kernel", "bound": "hbm",
+        "roofline": {"kernel": ("paged_decode_mfma_kernel" if (inp.q_dtype == "bf16" and
+                                inp.kv_dtype == "bf16" and Hq // Hkv >= 2)
+                                else "paged_decode_kernel") + f"<{D}>",
+                     "bound": "hbm",
                      "achieved": round(kernel_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(kernel_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "frac": round(kernel_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic_bytes,
+                     "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, "
+                                     "copy-calibrated)",
                      "algorithmic_bytes_per_launch": tr["kv_bytes"]},
         "cpu_baseline": cpu,
         "input_copies": n_copies,
     }
     print(json.dumps(result), flush=True)
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "paged_decode_mfma_llama3_8b_b64_traffic.txt")
+KERNEL_SOURCES = ("paged_kv_cache_25_amd/csrc/paged_decode_mfma.hip",
+                  "paged_kv_cache_25_amd/csrc/pkv_device.h",
+                  "paged_kv_cache_25_amd/csrc/pkv_launch.h")
+
+
+def measured_traffic(workload):
+    """HBM bytes per decode launch from the committed rocprofv3 counter summary,
+    or None when the workload differs or the kernel sources changed since."""
+    import hashlib
+    if workload != "llama3_8b_b64" or not os.path.exists(TRAFFIC_FILE):
+        return None
+    fields = {}
+    for line in open(TRAFFIC_FILE):
+        if ":" in line and line.split(":", 1)[0].strip().replace("_", "").isalnum():
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    if fields.get("kernel_source_sha256") != h.hexdigest():
+        return None
+    return int(fields["traffic_bytes_per_launch"])
 
 
 def cpu_baseline(inp, budget_s):

@@ -250,7 +250,10 @@ __global__ __launch_bounds__(kWave) void paged_decode_kernel(DecodeArgs a) {
   n_heads = n_heads < G ? n_heads : G;
   const int qh0 = h * a.group + head0;                  // first query head of the tile
 
-  if (blk_begin >= blk_end && !(a.write_final && part == 0)) return;   // partition past the end
+  if (blk_begin >= blk_end && !(a.write_final && part == 0)) return;
+  // A sequence whose blocks fit one partition is finished here: write the
+  // final output instead of a partial (the merge skips it).
+  const bool final_out = a.write_final || n_blk_seq <= a.blocks_per_partition;   // partition past the end
 
   Dec dec;
   const size_t q_row_bytes = size_t(D) * QT::kBytes;
@@ -332,7 +335,7 @@ __global__ __launch_bounds__(kWave) void paged_decode_kernel(DecodeArgs a) {
     const int qh = qh0 + i;
     const bool empty = lt[i] == 0.0f;        // no valid token (a NaN sum is not empty)
     const float inv = empty ? 0.0f : 1.0f / lt[i];
-    if (a.write_final) {
+    if (final_out) {
       char* orow = reinterpret_cast<char*>(a.out) + (size_t(b) * a.num_q_heads + qh) * size_t(D) * QT::kBytes;
 #pragma unroll
       for (int k = 0; k < KD; ++k) {

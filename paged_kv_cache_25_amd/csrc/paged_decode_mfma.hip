@@ -189,6 +189,9 @@ void paged_decode_mfma_kernel(DecodeArgs a) {
   int blk_end = blk_begin + a.blocks_per_partition;
   blk_end = blk_end < n_blk_seq ? blk_end : n_blk_seq;
   if (blk_begin >= blk_end && !(a.write_final && part == 0)) return;
+  // A sequence whose blocks fit one partition is finished here: write the
+  // final output instead of a partial (the merge skips it).
+  const bool final_out = a.write_final || n_blk_seq <= a.blocks_per_partition;
 
   const int head0 = chunk * kHeadTile;
   int n_heads = a.group - head0;
@@ -270,7 +273,7 @@ void paged_decode_mfma_kernel(DecodeArgs a) {
     const int qh = qh0 + hh;
     const bool empty = l_row[i] == 0.0f;
     const float inv = empty ? 0.0f : 1.0f / l_row[i];
-    if (a.write_final) {
+    if (final_out) {
       uint16_t* orow = reinterpret_cast<uint16_t*>(a.out) + (size_t(b) * a.num_q_heads + qh) * D +
                        kDimsPerLane * c;
       uint32_t packed[kDimsPerLane / 2];

@@ -182,6 +182,7 @@ pkv_status_t pkv_paged_decode_attention(
   m.num_seqs = num_seqs;
   m.num_q_heads = num_q_heads;
   m.max_partitions = int(maxp);
+  m.skip_single = 1;
   return pkv::launch_merge(m, head_dim, to_internal(q_dtype), st) == hipSuccess ? PKV_OK
                                                                                 : PKV_ERR_HIP;
 }
@@ -206,6 +207,7 @@ pkv_status_t pkv_merge_partials(void* out, const float* partial_out, const float
   m.num_seqs = num_seqs;
   m.num_q_heads = num_q_heads;
   m.max_partitions = max_partitions;
+  m.skip_single = 0;
   return pkv::launch_merge(m, head_dim, to_internal(out_dtype), static_cast<hipStream_t>(stream)) ==
                  hipSuccess
              ? PKV_OK

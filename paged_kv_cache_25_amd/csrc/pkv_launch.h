@@ -50,6 +50,7 @@ struct MergeArgs {
   const int32_t* context_lens;     // may be null: partitions = ceil(ctx / partition_size)
   int partition_size;
   int num_seqs, num_q_heads, max_partitions;
+  int skip_single;                 // 1: sequences with one partition were written by the decode kernel
 };
 
 hipError_t launch_kv_append(const AppendArgs& a, hipStream_t stream);
