@@ -12,8 +12,9 @@ more than the 256 MB last-level cache, so the timed steps read HBM.
 Prints one JSON line.  ``value`` is the step's algorithmic bytes (K/V rows of
 every attended token, the appended rows, q, out, block-table entries and
 lengths) divided by the measured step time, in GB/s.  ``roofline`` reports the
-decode kernel alone, timed live with HIP events (attention call minus merge
-call, both on the launch stream), against the 8 TB/s HBM peak.
+decode kernel alone, timed live with HIP events on the launch stream through
+``pkv_paged_decode_partials`` (the same kernel and grid without the merge),
+against the 8 TB/s HBM peak.
 ``cpu_baseline`` times the float64 CPU oracle on a bounded sample of the same
 workload.
 """
@@ -150,15 +151,21 @@ def main():
                Hkv, D, 16, NB, MB, mcl, ctypes.c_float(inp.softmax_scale), P, ptr(c["ws"]),
                ctypes.c_size_t(c["ws"].numel()), qcode, kvcode, sp)
         maxp = max(1, -(-mcl // P)) if P else 1
+        c["parts"] = torch.empty(max(ops.workspace_bytes(B, Hq, D, mcl, P),
+                                     B * Hq * maxp * (D + 1) * 4 + 256), dtype=torch.uint8,
+                                 device=dev)
         lse_off = ((B * Hq * maxp * D * 4 + 255) // 256) * 256
-        mrg = (ptr(c["out"]), V(c["ws"].data_ptr()), V(c["ws"].data_ptr() + lse_off), None,
-               B, Hq, D, maxp, qcode, sp) if maxp > 1 else None
-        calls.append((app, att, mrg))
+        # the decode kernel alone, same grid and work, partials into its own buffer
+        prt = (V(c["parts"].data_ptr()), V(c["parts"].data_ptr() + lse_off), maxp, ptr(c["q"]),
+               ptr(c["k_pool"]), ptr(c["v_pool"]), ptr(c["k_scales"]), ptr(c["v_scales"]),
+               ptr(c["tables"]), ptr(c["lens"]), B, Hq, Hkv, D, 16, NB, MB,
+               ctypes.c_float(inp.softmax_scale), P, qcode, kvcode, sp)
+        calls.append((app, att, prt, maxp > 1))
 
-    f_app, f_att, f_mrg = lib.pkv_kv_append, lib.pkv_paged_decode_attention, lib.pkv_merge_partials
+    f_app, f_att, f_prt = lib.pkv_kv_append, lib.pkv_paged_decode_attention, lib.pkv_paged_decode_partials
 
     def step(i):
-        app, att, _ = calls[i % n_copies]
+        app, att, _, _ = calls[i % n_copies]
         if f_app(*app) != 0 or f_att(*att) != 0:
             raise RuntimeError("libpkv call failed")
 
@@ -179,7 +186,8 @@ def main():
     step_ms = ev0.elapsed_time(ev1) / args.steps
     print(f"[bench] {args.steps} steps: {step_ms * 1e3:.1f} us/step", file=sys.stderr, flush=True)
 
-    # ---- the decode kernel alone: attention call minus merge call ------------
+    # ---- per kernel: the decode kernel alone (partials call), the merge as the
+    # ---- attention call minus the decode kernel, the append alone ---------------
     def timed(fn, reps):
         torch.cuda.synchronize()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -194,10 +202,9 @@ def main():
         if f_att(*calls[i % n_copies][1]) != 0:
             raise RuntimeError("attention call failed")
 
-    def merge_only(i):
-        m = calls[i % n_copies][2]
-        if m is not None and f_mrg(*m) != 0:
-            raise RuntimeError("merge call failed")
+    def decode_only(i):
+        if f_prt(*calls[i % n_copies][2]) != 0:
+            raise RuntimeError("partials call failed")
 
     def append_only(i):
         if f_app(*calls[i % n_copies][0]) != 0:
@@ -205,9 +212,9 @@ def main():
 
     reps = args.kernel_reps
     att_ms = timed(att_only, reps)
-    merge_ms = timed(merge_only, reps) if calls[0][2] is not None else 0.0
+    decode_ms = timed(decode_only, reps)
     append_ms = timed(append_only, reps)
-    decode_ms = max(att_ms - merge_ms, 1e-9)
+    merge_ms = max(att_ms - decode_ms, 0.0) if calls[0][3] else 0.0
 
     # ---- accounting ---------------------------------------------------------------
     tr = traffic.attention_call_traffic(inp.context_lens, num_q_heads=Hq, num_kv_heads=Hkv,
@@ -217,8 +224,7 @@ def main():
     value = step_bytes / (step_ms * 1e-3) / 1e9
     kernel_gbps = tr["kv_bytes"] / (decode_ms * 1e-3) / 1e9
 
-    traffic_bytes = measured_traffic(inp.name) if (calls[0][2] is not None and
-                                                   P == 512 and args.seed is None) else None
+    traffic_bytes = measured_traffic(inp.name) if (P == 512 and args.seed is None) else None
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(inp, args.cpu_budget_s)

@@ -35,6 +35,10 @@
  * Query head i reads KV head i / (num_q_heads / num_kv_heads): consecutive
  * grouping, as in 32 query heads sharing 8 KV heads in groups of 4.
  *
+ * Alignment: pools, q, out, k_new, v_new, partial outputs and the workspace
+ * must be 16-byte aligned (the kernels move 16-byte vectors); int32 and
+ * float32 arrays 4-byte aligned.  A misaligned pointer is PKV_ERR_INVALID_ARG.
+ *
  * Device-side contract (not checked on the host, since the values live in
  * device memory): 0 <= ctx <= max_blocks_per_seq * block_size,
  * ctx <= max_context_len, and the first ceil(ctx/block_size) table entries of
@@ -121,9 +125,12 @@ size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t
  * out[b][i][:] = sum_t p_t * V[b][h][t][:],  p = softmax_t(softmax_scale *
  * q[b][i] . K[b][h][t]),  h = i / (num_q_heads / num_kv_heads),  over the
  * tokens t < ctx_b gathered through the block table; no other mask.  For
- * e4m3 pools K and V are scaled by their (block, head) scale.  All arithmetic
- * is float32; out is written in q_dtype (bfloat16 rounded to nearest even).
- * A sequence with ctx_b == 0 gets zeros.
+ * e4m3 pools K and V are scaled by their (block, head) scale.  Scores, the
+ * softmax, sums and accumulators are float32; with bf16 queries over a bf16
+ * cache and 2 or more query heads per KV head the product P.V runs on the
+ * matrix cores with the weights P rounded to bfloat16 (relative error at most
+ * 2^-9 per weight).  out is written in q_dtype (bfloat16 rounded to nearest
+ * even).  A sequence with ctx_b == 0 gets zeros.
  *   brunomaga inference post, paged_decode_attention (the definition);
  *   serving lesson, "PagedAttention" (block-by-block, online softmax) and
  *   "Where it shows up" (split-KV decoding over the whole GPU).
@@ -150,6 +157,35 @@ pkv_status_t pkv_paged_decode_attention(
     int32_t head_dim, int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
     int32_t max_context_len, float softmax_scale, int32_t partition_size, void* workspace,
     size_t workspace_bytes, pkv_dtype_t q_dtype, pkv_dtype_t kv_dtype, void* stream);
+
+/*
+ * pkv_paged_decode_partials - the split-KV half of pkv_paged_decode_attention
+ * on its own: per-partition attention results, not merged.
+ *
+ * Partition p of sequence b covers its tokens [p*P, min((p+1)*P, ctx_b))
+ * (P = partition_size; 0 means one partition holding the whole sequence).
+ * For p < ceil(ctx_b / P) it writes the normalised partial output
+ * partial_out[b][i][p][:] = sum_t p_t V_t / sum_t p_t over the partition's
+ * tokens and partial_lse[b][i][p] = ln sum_t exp(s_t) (s_t the scaled scores,
+ * natural log); for the partitions ceil(ctx_b / P) <= p < max_partitions it
+ * writes partial_lse = -inf and leaves partial_out untouched.  Tokens at or
+ * beyond max_partitions * P are not read.  pkv_merge_partials on the result
+ * gives pkv_paged_decode_attention's output.  This is the piece each GPU runs
+ * over its own token range when one sequence's cache is split across GPUs.
+ *   serving lesson, "PagedAttention" and "Where it shows up" (partial results
+ *   of split-KV decoding, merged afterwards).
+ *
+ * partial_out float32 [num_seqs, num_q_heads, max_partitions, head_dim] and
+ * partial_lse float32 [num_seqs, num_q_heads, max_partitions] [device,
+ * written]; the other arguments as for pkv_paged_decode_attention.
+ */
+pkv_status_t pkv_paged_decode_partials(
+    float* partial_out, float* partial_lse, int32_t max_partitions, const void* q,
+    const void* k_pool, const void* v_pool, const float* k_scales, const float* v_scales,
+    const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+    int32_t num_blocks, int32_t max_blocks_per_seq, float softmax_scale, int32_t partition_size,
+    pkv_dtype_t q_dtype, pkv_dtype_t kv_dtype, void* stream);
 
 /*
  * pkv_merge_partials - combine per-partition attention results.

@@ -1,12 +1,15 @@
 // Log-sum-exp merge of split-KV partial results, for gfx950.
 //
-// One 64-lane workgroup per (sequence, query head).  The lanes find
-// M = max lse over the partitions that count, lane i computes the weight
-// exp(lse_i - M) of partition i, and every lane accumulates sum_p w_p o_p over
-// its D/64 dims with eight partial rows in flight, then divides by the summed
-// weights.  Partitions that do not count (past the sequence's count, or with
-// lse = -inf) are skipped, never multiplied by a zero weight, so whatever they
-// hold cannot reach the output.
+// One workgroup per (sequence, query head): one wave when every sequence's
+// partition rows fit in one batch or the batch is large, else 256 threads.  A row group of D/4
+// threads reads one partition row with float4 loads and keeps eight rows in
+// flight (64 rows per 256 threads for D=128); the
+// first batch is issued together with the pass that finds M = max lse over the
+// partitions that count.  Each group accumulates sum_p exp(lse_p - M) o_p over
+// its partitions, and the groups are summed in LDS and divided by the summed
+// weights.  Partitions that do not count (past
+// the sequence's count, or with lse = -inf) are skipped, never multiplied by a
+// zero weight, so whatever they hold cannot reach the output.
 //   learn.mohebi.ai serving lesson, "PagedAttention" and "Where it shows up":
 //   partial attention results merged with the online-softmax update.
 #include "pkv_device.h"
@@ -15,13 +18,23 @@
 namespace pkv {
 namespace {
 
+constexpr int kThreads = 256;
+
 template <int D, typename OT>
-__global__ __launch_bounds__(kWave) void merge_kernel(MergeArgs a) {
-  constexpr int kPer = D / kWave;                 // dims per lane: 1 or 2
-  constexpr int kUnroll = 8;                      // partial rows in flight per lane
+__global__ __launch_bounds__(kThreads) void merge_kernel(MergeArgs a) {
+  constexpr int kRowThreads = D / 4;              // float4 per thread covers one partition row
+  constexpr int kMaxGroups = kThreads / kRowThreads;
+  constexpr int kUnroll = 8;                      // rows in flight per row group
+  __shared__ float4 s_acc[kMaxGroups][kRowThreads];
+  __shared__ float s_w[kMaxGroups];
+  __shared__ float s_max[kThreads / kWave];
+  const int kGroups = blockDim.x / kRowThreads;   // row groups in this launch
+  const int n_waves = blockDim.x / kWave;
+
   const int qh = blockIdx.x % a.num_q_heads;
   const int b = blockIdx.x / a.num_q_heads;
-  const int lane = threadIdx.x;
+  const int t = threadIdx.x;
+  const int g = t / kRowThreads, c = t % kRowThreads;
 
   int np = a.max_partitions;
   if (a.num_partitions) {
@@ -31,55 +44,72 @@ __global__ __launch_bounds__(kWave) void merge_kernel(MergeArgs a) {
     np = ctx <= 0 ? 0 : (ctx + a.partition_size - 1) / a.partition_size;
   }
   np = np < 0 ? 0 : (np > a.max_partitions ? a.max_partitions : np);
-  if (a.skip_single && np == 1) return;           // already final
+  if (a.skip_single && np == 1) return;           // already final (uniform: whole block)
 
   const size_t row = size_t(b) * a.num_q_heads + qh;
   const float* lse = a.part_lse + row * a.max_partitions;
-  const float* o = a.part_o + row * a.max_partitions * D + lane * kPer;
+  const float* o = a.part_o + row * a.max_partitions * D + 4 * c;
 
-  float M = -INFINITY;
-  for (int p = lane; p < np; p += kWave) M = fmaxf(M, lse[p]);
-  M = wave_max(M);
-
-  float acc[kPer];
+  // First batch of rows and their lse, issued together with the max pass.
+  float4 rowv[kUnroll];
+  float lp[kUnroll];
 #pragma unroll
-  for (int k = 0; k < kPer; ++k) acc[k] = 0.0f;
+  for (int u = 0; u < kUnroll; ++u) {
+    const int p = g + u * kGroups;
+    lp[u] = p < np ? lse[p] : -INFINITY;
+    rowv[u] = p < np ? *reinterpret_cast<const float4*>(o + size_t(p) * D)
+                     : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  }
+  float M = -INFINITY;
+  for (int p = t; p < np; p += blockDim.x) M = fmaxf(M, lse[p]);
+  M = wave_max(M);
+  if ((t & (kWave - 1)) == 0) s_max[t / kWave] = M;
+  __syncthreads();
+  M = s_max[0];
+  for (int w = 1; w < n_waves; ++w) M = fmaxf(M, s_max[w]);
+
+  // Row group g takes partitions g, g + kGroups, ...; -inf partitions never count.
+  float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
   float wsum = 0.0f;
   if (M > -INFINITY) {
-    for (int p0 = 0; p0 < np; p0 += kWave) {
-      // Lane i holds the weight of partition p0 + i; -inf partitions never count.
-      const float lp = p0 + lane < np ? lse[p0 + lane] : -INFINITY;
-      const uint64_t counts = __ballot(lp != -INFINITY);
-      const float w_lane = lp != -INFINITY ? __expf(lp - M) : 0.0f;
-      wsum += w_lane;
-      const int cnt = np - p0 < kWave ? np - p0 : kWave;
-      for (int k0 = 0; k0 < cnt; k0 += kUnroll) {
-        float part[kUnroll][kPer];
+    for (int p0 = g;; ) {
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-          const int k = k0 + u;
-          const bool use = k < cnt && ((counts >> k) & 1);
+      for (int u = 0; u < kUnroll; ++u) {
+        if (lp[u] == -INFINITY) continue;
+        const float w = __expf(lp[u] - M);
+        wsum += w;
+        acc.x = fmaf(w, rowv[u].x, acc.x);
+        acc.y = fmaf(w, rowv[u].y, acc.y);
+        acc.z = fmaf(w, rowv[u].z, acc.z);
+        acc.w = fmaf(w, rowv[u].w, acc.w);
+      }
+      p0 += kGroups * kUnroll;
+      if (p0 >= np) break;
 #pragma unroll
-          for (int e = 0; e < kPer; ++e)
-            part[u][e] = use ? o[size_t(p0 + k) * D + e] : 0.0f;
-        }
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-          const int k = k0 + u;
-          const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w_lane),
-                                                                   k < kWave ? k : 0));
-          const bool use = k < cnt && ((counts >> k) & 1);
-#pragma unroll
-          for (int e = 0; e < kPer; ++e) acc[e] = use ? fmaf(w, part[u][e], acc[e]) : acc[e];
-        }
+      for (int u = 0; u < kUnroll; ++u) {
+        const int p = p0 + u * kGroups;
+        lp[u] = p < np ? lse[p] : -INFINITY;
+        rowv[u] = p < np ? *reinterpret_cast<const float4*>(o + size_t(p) * D)
+                         : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
       }
     }
   }
-  wsum = wave_sum(wsum);
-  const float inv = wsum > 0.0f ? 1.0f / wsum : 0.0f;
+  s_acc[g][c] = acc;
+  if (c == 0) s_w[g] = wsum;
+  __syncthreads();
+  if (g != 0) return;
+  float W = 0.0f;
+  for (int k = 0; k < kGroups; ++k) {
+    const float4 v = s_acc[k][c];
+    acc = k == 0 ? v : make_float4(acc.x + v.x, acc.y + v.y, acc.z + v.z, acc.w + v.w);
+    W += s_w[k];
+  }
+  const float inv = W > 0.0f ? 1.0f / W : 0.0f;
   char* orow = reinterpret_cast<char*>(a.out) + row * D * sizeof(typename OT::Storage);
-#pragma unroll
-  for (int k = 0; k < kPer; ++k) OT::store(orow, lane * kPer + k, acc[k] * inv);
+  OT::store(orow, 4 * c + 0, acc.x * inv);
+  OT::store(orow, 4 * c + 1, acc.y * inv);
+  OT::store(orow, 4 * c + 2, acc.z * inv);
+  OT::store(orow, 4 * c + 3, acc.w * inv);
 }
 
 struct OutF32 {
@@ -98,10 +128,15 @@ hipError_t launch_d(const MergeArgs& a, DType out_dtype, hipStream_t stream) {
   const size_t grid = size_t(a.num_seqs) * a.num_q_heads;
   if (grid == 0) return hipSuccess;
   if (grid > 0x7fffffffu) return hipErrorInvalidConfiguration;
+  // One wave per (sequence, head) when its rows fit one batch (8 rows per
+  // row group), or when there are enough (sequence, head) pairs to fill the
+  // chip with single waves; four waves for few, long sequences.
+  const bool one_batch = a.max_partitions * (D / 4) <= 8 * kWave;
+  const int threads = (one_batch || grid >= 4096) ? kWave : kThreads;
   if (out_dtype == DType::F32)
-    hipLaunchKernelGGL((merge_kernel<D, OutF32>), dim3(unsigned(grid)), dim3(kWave), 0, stream, a);
+    hipLaunchKernelGGL((merge_kernel<D, OutF32>), dim3(unsigned(grid)), dim3(threads), 0, stream, a);
   else
-    hipLaunchKernelGGL((merge_kernel<D, OutBF16>), dim3(unsigned(grid)), dim3(kWave), 0, stream, a);
+    hipLaunchKernelGGL((merge_kernel<D, OutBF16>), dim3(unsigned(grid)), dim3(threads), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -250,10 +250,14 @@ __global__ __launch_bounds__(kWave) void paged_decode_kernel(DecodeArgs a) {
   n_heads = n_heads < G ? n_heads : G;
   const int qh0 = h * a.group + head0;                  // first query head of the tile
 
-  if (blk_begin >= blk_end && !(a.write_final && part == 0)) return;
+  if (blk_begin >= blk_end && !(a.write_final && part == 0)) {   // partition past the end
+    if (a.mark_empty && lane < n_heads)
+      a.part_lse[(size_t(b) * a.num_q_heads + qh0 + lane) * a.max_partitions + part] = -INFINITY;
+    return;
+  }
   // A sequence whose blocks fit one partition is finished here: write the
   // final output instead of a partial (the merge skips it).
-  const bool final_out = a.write_final || n_blk_seq <= a.blocks_per_partition;   // partition past the end
+  const bool final_out = a.write_final || (a.final_single && n_blk_seq <= a.blocks_per_partition);
 
   Dec dec;
   const size_t q_row_bytes = size_t(D) * QT::kBytes;

@@ -188,15 +188,19 @@ void paged_decode_mfma_kernel(DecodeArgs a) {
   const int n_blk_seq = (ctx + kBlockSize - 1) / kBlockSize;
   int blk_end = blk_begin + a.blocks_per_partition;
   blk_end = blk_end < n_blk_seq ? blk_end : n_blk_seq;
-  if (blk_begin >= blk_end && !(a.write_final && part == 0)) return;
-  // A sequence whose blocks fit one partition is finished here: write the
-  // final output instead of a partial (the merge skips it).
-  const bool final_out = a.write_final || n_blk_seq <= a.blocks_per_partition;
-
   const int head0 = chunk * kHeadTile;
   int n_heads = a.group - head0;
   n_heads = n_heads < kHeadTile ? n_heads : kHeadTile;
   const int qh0 = h * a.group + head0;
+
+  if (blk_begin >= blk_end && !(a.write_final && part == 0)) {   // partition past the end
+    if (a.mark_empty && lane < n_heads)
+      a.part_lse[(size_t(b) * a.num_q_heads + qh0 + lane) * a.max_partitions + part] = -INFINITY;
+    return;
+  }
+  // A sequence whose blocks fit one partition is finished here: write the
+  // final output instead of a partial (the merge skips it).
+  const bool final_out = a.write_final || (a.final_single && n_blk_seq <= a.blocks_per_partition);
 
   MfmaDecode<D> dec;
   {

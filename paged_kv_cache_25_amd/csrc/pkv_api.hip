@@ -4,6 +4,7 @@
 #include "../../include/pkv.h"
 
 #include <hip/hip_runtime.h>
+#include <stdint.h>
 
 #include "pkv_launch.h"
 
@@ -20,6 +21,10 @@ DType to_internal(pkv_dtype_t t) {
   return t == PKV_F32 ? DType::F32 : (t == PKV_BF16 ? DType::BF16 : DType::FP8);
 }
 bool head_dim_ok(int32_t d) { return d == 64 || d == 128; }
+
+// The kernels move data in 16-byte vectors.
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
 // Partitions per sequence for a grid: ceil(max_ctx / P), or 1 when P == 0.
 int64_t max_partitions(int32_t max_context_len, int32_t partition_size) {
@@ -80,6 +85,9 @@ pkv_status_t pkv_kv_append(void* k_pool, void* v_pool, const void* k_new, const 
   if (num_seqs == 0) return PKV_OK;
   if (!k_pool || !v_pool || !k_new || !v_new || !block_tables || !context_lens)
     return PKV_ERR_INVALID_ARG;
+  if (!aligned16(k_pool) || !aligned16(v_pool) || !aligned16(k_new) || !aligned16(v_new) ||
+      !aligned4(block_tables) || !aligned4(context_lens))
+    return PKV_ERR_INVALID_ARG;
   pkv::AppendArgs a;
   a.k_pool = k_pool;
   a.v_pool = v_pool;
@@ -104,47 +112,49 @@ size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t
   return part_layout(num_seqs, num_q_heads, head_dim, maxp).total;
 }
 
-pkv_status_t pkv_paged_decode_attention(
-    void* out, const void* q, const void* k_pool, const void* v_pool, const float* k_scales,
-    const float* v_scales, const int32_t* block_tables, const int32_t* context_lens,
-    int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-    int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len,
-    float softmax_scale, int32_t partition_size, void* workspace, size_t workspace_bytes,
-    pkv_dtype_t q_dtype, pkv_dtype_t kv_dtype, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Checks shared by the two decode entry points (everything but the output
+// and workspace pointers).
+pkv_status_t check_decode(const void* q, const void* k_pool, const void* v_pool,
+                          const float* k_scales, const float* v_scales,
+                          const int32_t* block_tables, const int32_t* context_lens,
+                          int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                          int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                          int32_t max_blocks_per_seq, float softmax_scale,
+                          int32_t partition_size, pkv_dtype_t q_dtype, pkv_dtype_t kv_dtype) {
   if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
-      num_blocks <= 0 || max_blocks_per_seq <= 0 || max_context_len < 0 || partition_size < 0 ||
-      !dtype_ok(q_dtype) || !dtype_ok(kv_dtype) || !(softmax_scale == softmax_scale))
+      num_blocks <= 0 || max_blocks_per_seq <= 0 || partition_size < 0 || !dtype_ok(q_dtype) ||
+      !dtype_ok(kv_dtype) || !(softmax_scale == softmax_scale))
     return PKV_ERR_INVALID_ARG;
   if (num_q_heads % num_kv_heads != 0) return PKV_ERR_INVALID_ARG;
   if (partition_size % block_size != 0) return PKV_ERR_INVALID_ARG;
   if (!head_dim_ok(head_dim) || block_size != pkv::kBlockSizeBuilt) return PKV_ERR_UNSUPPORTED;
   if (q_dtype == PKV_FP8_E4M3) return PKV_ERR_UNSUPPORTED;
   if (num_seqs == 0) return PKV_OK;
-  if (!out || !q || !k_pool || !v_pool || !block_tables || !context_lens)
-    return PKV_ERR_INVALID_ARG;
+  if (!q || !k_pool || !v_pool || !block_tables || !context_lens) return PKV_ERR_INVALID_ARG;
   if (kv_dtype == PKV_FP8_E4M3 && (!k_scales || !v_scales)) return PKV_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned4(block_tables) ||
+      !aligned4(context_lens) || !aligned4(k_scales) || !aligned4(v_scales))
+    return PKV_ERR_INVALID_ARG;
+  return PKV_OK;
+}
 
-  const int64_t maxp = max_partitions(max_context_len, partition_size);
-  const int64_t blocks_per_part =
-      partition_size == 0 ? int64_t(max_blocks_per_seq) : int64_t(partition_size / block_size);
-  // A single partition per sequence also covers partition sizes past the table's capacity.
-  const bool single = maxp <= 1;
-  const int group = num_q_heads / num_kv_heads;
-  // bf16 queries over a bf16 cache with a shared KV head run on the matrix
-  // cores; every other combination on the vector kernel.
-  const bool use_mfma = q_dtype == PKV_BF16 && kv_dtype == PKV_BF16 && group >= 2;
-  const int tile = use_mfma ? pkv::mfma_head_tile() : tile_heads(group, head_dim);
+// bf16 queries over a bf16 cache with a shared KV head run on the matrix
+// cores; every other combination on the vector kernel.
+bool uses_mfma(pkv_dtype_t q_dtype, pkv_dtype_t kv_dtype, int group) {
+  return q_dtype == PKV_BF16 && kv_dtype == PKV_BF16 && group >= 2;
+}
 
-  pkv::DecodeArgs a;
-  a.out = out;
-  a.part_o = nullptr;
-  a.part_lse = nullptr;
-  if (!single) {
-    const PartLayout L = part_layout(num_seqs, num_q_heads, head_dim, maxp);
-    if (!workspace || workspace_bytes < L.total) return PKV_ERR_WORKSPACE;
-    a.part_o = static_cast<float*>(workspace);
-    a.part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + L.lse_offset);
-  }
+pkv::DecodeArgs decode_args(const void* q, const void* k_pool, const void* v_pool,
+                            const float* k_scales, const float* v_scales,
+                            const int32_t* block_tables, const int32_t* context_lens,
+                            int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                            int32_t head_dim, int32_t num_blocks, int32_t max_blocks_per_seq,
+                            float softmax_scale, int tile) {
+  pkv::DecodeArgs a{};
   a.q = q;
   a.k_pool = k_pool;
   a.v_pool = v_pool;
@@ -155,21 +165,69 @@ pkv_status_t pkv_paged_decode_attention(
   a.num_seqs = num_seqs;
   a.num_q_heads = num_q_heads;
   a.num_kv_heads = num_kv_heads;
-  a.group = group;
-  a.head_chunks = (group + tile - 1) / tile;
+  a.group = num_q_heads / num_kv_heads;
+  a.head_chunks = (a.group + tile - 1) / tile;
   a.num_blocks = num_blocks;
   a.max_blocks_per_seq = max_blocks_per_seq;
+  a.scale_log2 = softmax_scale * pkv::kLog2eHost;
+  (void)head_dim;
+  return a;
+}
+
+hipError_t launch_decode(const pkv::DecodeArgs& a, int head_dim, int tile, bool mfma,
+                         pkv_dtype_t q_dtype, pkv_dtype_t kv_dtype, hipStream_t st) {
+  return mfma ? pkv::launch_paged_decode_mfma(a, head_dim, st)
+              : pkv::launch_paged_decode(a, head_dim, tile, to_internal(q_dtype),
+                                         to_internal(kv_dtype), st);
+}
+
+}  // namespace
+
+extern "C" {
+
+pkv_status_t pkv_paged_decode_attention(
+    void* out, const void* q, const void* k_pool, const void* v_pool, const float* k_scales,
+    const float* v_scales, const int32_t* block_tables, const int32_t* context_lens,
+    int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len,
+    float softmax_scale, int32_t partition_size, void* workspace, size_t workspace_bytes,
+    pkv_dtype_t q_dtype, pkv_dtype_t kv_dtype, void* stream) {
+  if (max_context_len < 0) return PKV_ERR_INVALID_ARG;
+  const pkv_status_t st0 = check_decode(q, k_pool, v_pool, k_scales, v_scales, block_tables,
+                                        context_lens, num_seqs, num_q_heads, num_kv_heads,
+                                        head_dim, block_size, num_blocks, max_blocks_per_seq,
+                                        softmax_scale, partition_size, q_dtype, kv_dtype);
+  if (st0 != PKV_OK || num_seqs == 0) return st0;
+  if (!out || !aligned16(out) || !aligned16(workspace)) return PKV_ERR_INVALID_ARG;
+
+  const int64_t maxp = max_partitions(max_context_len, partition_size);
+  const int64_t blocks_per_part =
+      partition_size == 0 ? int64_t(max_blocks_per_seq) : int64_t(partition_size / block_size);
+  // A single partition per sequence also covers partition sizes past the table's capacity.
+  const bool single = maxp <= 1;
+  const int group = num_q_heads / num_kv_heads;
+  const bool mfma = uses_mfma(q_dtype, kv_dtype, group);
+  const int tile = mfma ? pkv::mfma_head_tile() : tile_heads(group, head_dim);
+
+  pkv::DecodeArgs a = decode_args(q, k_pool, v_pool, k_scales, v_scales, block_tables,
+                                  context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                  num_blocks, max_blocks_per_seq, softmax_scale, tile);
+  a.out = out;
+  if (!single) {
+    const PartLayout L = part_layout(num_seqs, num_q_heads, head_dim, maxp);
+    if (!workspace || workspace_bytes < L.total) return PKV_ERR_WORKSPACE;
+    a.part_o = static_cast<float*>(workspace);
+    a.part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + L.lse_offset);
+  }
   a.blocks_per_partition = int(single ? max_blocks_per_seq : blocks_per_part);
   a.max_partitions = int(maxp);
-  a.scale_log2 = softmax_scale * pkv::kLog2eHost;
   a.write_final = single ? 1 : 0;
+  a.final_single = 1;
+  a.mark_empty = 0;
 
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const hipError_t err =
-      use_mfma ? pkv::launch_paged_decode_mfma(a, head_dim, st)
-               : pkv::launch_paged_decode(a, head_dim, tile, to_internal(q_dtype),
-                                          to_internal(kv_dtype), st);
-  if (err != hipSuccess) return PKV_ERR_HIP;
+  if (launch_decode(a, head_dim, tile, mfma, q_dtype, kv_dtype, st) != hipSuccess)
+    return PKV_ERR_HIP;
   if (single) return PKV_OK;
 
   pkv::MergeArgs m;
@@ -187,6 +245,42 @@ pkv_status_t pkv_paged_decode_attention(
                                                                                 : PKV_ERR_HIP;
 }
 
+pkv_status_t pkv_paged_decode_partials(
+    float* partial_out, float* partial_lse, int32_t max_partitions_, const void* q,
+    const void* k_pool, const void* v_pool, const float* k_scales, const float* v_scales,
+    const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+    int32_t num_blocks, int32_t max_blocks_per_seq, float softmax_scale, int32_t partition_size,
+    pkv_dtype_t q_dtype, pkv_dtype_t kv_dtype, void* stream) {
+  if (max_partitions_ <= 0) return PKV_ERR_INVALID_ARG;
+  const pkv_status_t st0 = check_decode(q, k_pool, v_pool, k_scales, v_scales, block_tables,
+                                        context_lens, num_seqs, num_q_heads, num_kv_heads,
+                                        head_dim, block_size, num_blocks, max_blocks_per_seq,
+                                        softmax_scale, partition_size, q_dtype, kv_dtype);
+  if (st0 != PKV_OK || num_seqs == 0) return st0;
+  if (!partial_out || !partial_lse || !aligned16(partial_out) || !aligned4(partial_lse))
+    return PKV_ERR_INVALID_ARG;
+  const int group = num_q_heads / num_kv_heads;
+  const bool mfma = uses_mfma(q_dtype, kv_dtype, group);
+  const int tile = mfma ? pkv::mfma_head_tile() : tile_heads(group, head_dim);
+  pkv::DecodeArgs a = decode_args(q, k_pool, v_pool, k_scales, v_scales, block_tables,
+                                  context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                  num_blocks, max_blocks_per_seq, softmax_scale, tile);
+  a.out = nullptr;
+  a.part_o = partial_out;
+  a.part_lse = partial_lse;
+  a.blocks_per_partition =
+      partition_size == 0 ? max_blocks_per_seq : partition_size / block_size;
+  a.max_partitions = max_partitions_;
+  a.write_final = 0;
+  a.final_single = 0;
+  a.mark_empty = 1;
+  return launch_decode(a, head_dim, tile, mfma, q_dtype, kv_dtype,
+                       static_cast<hipStream_t>(stream)) == hipSuccess
+             ? PKV_OK
+             : PKV_ERR_HIP;
+}
+
 pkv_status_t pkv_merge_partials(void* out, const float* partial_out, const float* partial_lse,
                                 const int32_t* num_partitions, int32_t num_seqs,
                                 int32_t num_q_heads, int32_t head_dim, int32_t max_partitions,
@@ -197,6 +291,9 @@ pkv_status_t pkv_merge_partials(void* out, const float* partial_out, const float
   if (!head_dim_ok(head_dim) || out_dtype == PKV_FP8_E4M3) return PKV_ERR_UNSUPPORTED;
   if (num_seqs == 0) return PKV_OK;
   if (!out || !partial_out || !partial_lse) return PKV_ERR_INVALID_ARG;
+  if (!aligned16(out) || !aligned16(partial_out) || !aligned4(partial_lse) ||
+      !aligned4(num_partitions))
+    return PKV_ERR_INVALID_ARG;
   pkv::MergeArgs m;
   m.out = out;
   m.part_o = partial_out;

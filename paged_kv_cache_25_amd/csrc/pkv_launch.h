@@ -39,7 +39,9 @@ struct DecodeArgs {
   int blocks_per_partition;   // partition size / 16
   int max_partitions;         // grid extent over partitions
   float scale_log2;           // softmax_scale * log2(e)
-  int write_final;
+  int write_final;            // every sequence has one partition: write `out`
+  int final_single;           // a sequence with one partition writes `out` (the merge skips it)
+  int mark_empty;             // partitions past a sequence's end write lse = -inf
 };
 
 struct MergeArgs {

@@ -50,6 +50,9 @@ def load():
     L.pkv_paged_decode_attention.restype = ctypes.c_int
     L.pkv_paged_decode_attention.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, F, I,
                                              P, Z, ctypes.c_int, ctypes.c_int, P]
+    L.pkv_paged_decode_partials.restype = ctypes.c_int
+    L.pkv_paged_decode_partials.argtypes = [P, P, I, P, P, P, P, P, P, P, I, I, I, I, I, I, I, F, I,
+                                            ctypes.c_int, ctypes.c_int, P]
     L.pkv_merge_partials.restype = ctypes.c_int
     L.pkv_merge_partials.argtypes = [P, P, P, P, I, I, I, I, ctypes.c_int, P]
     _lib = L
@@ -124,6 +127,24 @@ def paged_decode_attention(out, q, k_pool, v_pool, block_tables, context_lens, m
         int(max_context_len), float(softmax_scale), int(partition_size), _ptr(workspace),
         workspace.numel(), dtype_code(q.dtype), dtype_code(k_pool.dtype), _stream(stream)))
     return out
+
+
+def paged_decode_partials(partial_out, partial_lse, q, k_pool, v_pool, block_tables,
+                          context_lens, softmax_scale, partition_size=512, k_scales=None,
+                          v_scales=None, stream=None):
+    """Unmerged split-KV results: partial_out [B, Hq, P, D] fp32, partial_lse [B, Hq, P] fp32."""
+    _need_cuda(partial_out, partial_lse, q, k_pool, v_pool, block_tables, context_lens,
+               k_scales, v_scales)
+    if partial_out.dtype != torch.float32 or partial_lse.dtype != torch.float32:
+        raise TypeError("partials are float32")
+    B, hq, d = q.shape
+    nb, hkv, bs, _ = k_pool.shape
+    _check("pkv_paged_decode_partials", load().pkv_paged_decode_partials(
+        _ptr(partial_out), _ptr(partial_lse), partial_out.shape[2], _ptr(q), _ptr(k_pool),
+        _ptr(v_pool), _ptr(k_scales), _ptr(v_scales), _ptr(block_tables), _ptr(context_lens), B,
+        hq, hkv, d, bs, nb, block_tables.shape[1], float(softmax_scale), int(partition_size),
+        dtype_code(q.dtype), dtype_code(k_pool.dtype), _stream(stream)))
+    return partial_out, partial_lse
 
 
 def merge_partials(out, partial_out, partial_lse, num_partitions=None, stream=None):

@@ -33,7 +33,7 @@ def lib():
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted([
         "pkv_abi_version", "pkv_status_string", "pkv_kv_append", "pkv_decode_workspace_bytes",
-        "pkv_paged_decode_attention", "pkv_merge_partials"])
+        "pkv_paged_decode_attention", "pkv_paged_decode_partials", "pkv_merge_partials"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -100,6 +100,41 @@ def test_decode_validation(lib):
     need = lib.pkv_decode_workspace_bytes(2, 8, 128, 64, 16)
     assert _decode(lib, ws=FAKE, wsb=need - 1) == WORKSPACE
     assert _decode(lib, B=0, q=None) == OK
+
+
+def test_alignment_checked(lib):
+    odd = ctypes.c_void_p(0x10008)                        # 8-byte aligned only
+    assert _append(lib, k_pool=odd) == INVALID
+    assert _append(lib, tables=ctypes.c_void_p(0x10002)) == INVALID
+    need = lib.pkv_decode_workspace_bytes(2, 8, 128, 64, 16)
+    assert _decode(lib, q=odd, ws=FAKE, wsb=need) == INVALID
+    assert _decode(lib, out=odd, ws=FAKE, wsb=need) == INVALID
+    assert _decode(lib, ws=odd, wsb=need) == INVALID
+    f = lib.pkv_merge_partials
+    assert f(FAKE, odd, FAKE, None, 2, 4, 128, 3, ops.PKV_BF16, None) == INVALID
+
+
+def _partials(lib, **over):
+    a = dict(po=FAKE, pl=FAKE, maxp=4, q=FAKE, kp=FAKE, vp=FAKE, ks=None, vs=None, tables=FAKE,
+             lens=FAKE, B=2, hq=8, hkv=2, d=128, bs=16, nb=8, mbps=4, scale=0.088, P=16,
+             qt=ops.PKV_BF16, kvt=ops.PKV_BF16)
+    a.update(over)
+    return lib.pkv_paged_decode_partials(
+        a["po"], a["pl"], a["maxp"], a["q"], a["kp"], a["vp"], a["ks"], a["vs"], a["tables"],
+        a["lens"], a["B"], a["hq"], a["hkv"], a["d"], a["bs"], a["nb"], a["mbps"], a["scale"],
+        a["P"], a["qt"], a["kvt"], None)
+
+
+def test_partials_validation(lib):
+    assert _partials(lib, po=None) == INVALID
+    assert _partials(lib, pl=None) == INVALID
+    assert _partials(lib, maxp=0) == INVALID
+    assert _partials(lib, po=ctypes.c_void_p(0x10008)) == INVALID
+    assert _partials(lib, hq=6, hkv=4) == INVALID
+    assert _partials(lib, P=24) == INVALID
+    assert _partials(lib, d=96) == UNSUPPORTED
+    assert _partials(lib, kvt=ops.PKV_FP8_E4M3) == INVALID
+    assert _partials(lib, B=0, po=None) == OK
 
 
 def test_workspace_size(lib):

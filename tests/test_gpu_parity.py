@@ -235,6 +235,47 @@ def test_fp8_decode_all_codes():
     assert set(np.concatenate([rows[0], rows[1]]).tolist()) == set(codes.tolist())
 
 
+# --- partials entry point: the decode kernel alone ---------------------------
+
+@pytest.mark.parametrize("kv,q,P", [("f32", "f32", 64), ("bf16", "bf16", 512), ("bf16", "bf16", 0),
+                                    ("fp8_e4m3", "bf16", 128)])
+def test_partials_match_oracle_and_merge(kv, q, P):
+    """pkv_paged_decode_partials against the oracle's per-partition outputs and
+    log-sum-exps; partitions past a sequence's end carry lse = -inf; merging
+    the partials reproduces the attention call."""
+    inp = make_inputs(num_seqs=5, num_q_heads=8, num_kv_heads=2, head_dim=128,
+                      ctx=("fixed", [1, 700, 63, 1500, 0]), pool=("used_fraction", 0.8),
+                      q_dtype=q, kv_dtype=kv, seed=31)
+    maxp = max(1, -(-inp.max_context_len // P)) if P else 1
+    log(f"[case] partials kv={kv} q={q} P={P} maxP={maxp}")
+    d = DeviceStep(inp)
+    d.append()
+    po = torch.full((5, 8, maxp, 128), float("nan"), device="cuda")
+    pl = torch.full((5, 8, maxp), float("nan"), device="cuda")
+    ops.paged_decode_partials(po, pl, d.q, d.k_pool, d.v_pool, d.tables, d.lens,
+                              inp.softmax_scale, P, d.k_scales, d.v_scales)
+    torch.cuda.synchronize()
+    kp, vp = pa.kv_append(inp.k_pool, inp.v_pool, inp.k_new, inp.v_new, inp.block_tables,
+                          inp.context_lens, inp.block_size)
+    o_ref, l_ref = pa.decode_partials(inp.q, kp, vp, inp.block_tables, inp.context_lens,
+                                      block_size=16, softmax_scale=inp.softmax_scale,
+                                      q_dtype=q, kv_dtype=kv, partition_size=P or inp.max_context_len,
+                                      max_partitions=maxp, k_scales=inp.k_scales,
+                                      v_scales=inp.v_scales)
+    got_l = pl.cpu().double().numpy()
+    got_o = po.cpu().double().numpy()
+    valid = np.isfinite(l_ref)
+    assert np.array_equal(np.isneginf(got_l), ~valid)
+    tol_l = 1e-5 if kv == "f32" else 2e-3
+    assert np.abs(got_l[valid] - l_ref[valid]).max() < tol_l
+    o_err = np.abs(got_o[valid] - o_ref[valid]).max()
+    assert o_err < (1e-5 if kv == "f32" else 2e-2), o_err
+    out = torch.empty_like(d.q)
+    ops.merge_partials(out, po, pl)
+    ref = oracle_out(inp, pools=(kp, vp))
+    check_tolerance(kv, out.float().cpu().double().numpy(), ref, f"partials+merge {kv}", out_dtype=q)
+
+
 # --- merge kernel on its own -------------------------------------------------
 
 def test_merge_partials_kernel():
