@@ -1,9 +1,11 @@
 #!/usr/bin/env python3
 """Decode-step benchmark: paged KV append + split-KV decode attention + merge.
 
-One "step" is one pass of the whole hot path over one batch: ``pkv_kv_append``
-then ``pkv_paged_decode_attention`` (decode kernel + LSE merge) through the C
-ABI, on synthetic inputs already resident in HBM.  The default workload is
+One "step" is one pass of the whole hot path over one batch: the new token's
+K/V appended, then decode attention and the LSE merge, through the C ABI's
+``pkv_paged_decode_step`` (the append runs inside the decode kernel), on
+synthetic inputs already resident in HBM.  The same step as two calls
+(``pkv_kv_append`` then ``pkv_paged_decode_attention``) is timed alongside.  The default workload is
 the Llama-3-8B-shaped layer (batch 64, 32 query / 8 KV heads, head dim 128,
 bf16, 16-token blocks, context lengths uniform in [512, 4096]); ``--config``
 picks another named workload.  Inputs are rotated over enough copies to span
@@ -160,12 +162,22 @@ def main():
                ptr(c["k_pool"]), ptr(c["v_pool"]), ptr(c["k_scales"]), ptr(c["v_scales"]),
                ptr(c["tables"]), ptr(c["lens"]), B, Hq, Hkv, D, 16, NB, MB,
                ctypes.c_float(inp.softmax_scale), P, qcode, kvcode, sp)
-        calls.append((app, att, prt, maxp > 1))
+        stp = (ptr(c["out"]), ptr(c["q"]), ptr(c["k_pool"]), ptr(c["v_pool"]), ptr(c["k_new"]),
+               ptr(c["v_new"]), ptr(c["k_scales"]), ptr(c["v_scales"]), ptr(c["tables"]),
+               ptr(c["lens"]), B, Hq, Hkv, D, 16, NB, MB, mcl, ctypes.c_float(inp.softmax_scale),
+               P, ptr(c["ws"]), ctypes.c_size_t(c["ws"].numel()), qcode, kvcode, sp)
+        calls.append((app, att, prt, maxp > 1, stp))
 
     f_app, f_att, f_prt = lib.pkv_kv_append, lib.pkv_paged_decode_attention, lib.pkv_paged_decode_partials
+    f_stp = lib.pkv_paged_decode_step
 
     def step(i):
-        app, att, _, _ = calls[i % n_copies]
+        # one decode step: append + attention (+ merge), the append fused into the decode kernel
+        if f_stp(*calls[i % n_copies][4]) != 0:
+            raise RuntimeError("libpkv call failed")
+
+    def step_two_calls(i):
+        app, att = calls[i % n_copies][0], calls[i % n_copies][1]
         if f_app(*app) != 0 or f_att(*att) != 0:
             raise RuntimeError("libpkv call failed")
 
@@ -211,6 +223,7 @@ def main():
             raise RuntimeError("append call failed")
 
     reps = args.kernel_reps
+    two_call_ms = timed(step_two_calls, reps)
     att_ms = timed(att_only, reps)
     decode_ms = timed(decode_only, reps)
     append_ms = timed(append_only, reps)
@@ -250,7 +263,8 @@ def main():
         "decode_steps_per_s": round(1e3 / step_ms, 1),
         "tokens_per_s": round(B * 1e3 / step_ms, 1),
         "kernel_us": {"append": round(append_ms * 1e3, 2), "decode": round(decode_ms * 1e3, 2),
-                      "merge": round(merge_ms * 1e3, 2), "attention_call": round(att_ms * 1e3, 2)},
+                      "merge": round(merge_ms * 1e3, 2), "attention_call": round(att_ms * 1e3, 2),
+                      "step_as_two_calls": round(two_call_ms * 1e3, 2)},
         "roofline": {"kernel": ("paged_decode_mfma_kernel" if (inp.q_dtype == "bf16" and
                                 inp.kv_dtype == "bf16" and Hq // Hkv >= 2)
                                 else "paged_decode_kernel") + f"<{D}>",

@@ -159,6 +159,30 @@ pkv_status_t pkv_paged_decode_attention(
     size_t workspace_bytes, pkv_dtype_t q_dtype, pkv_dtype_t kv_dtype, void* stream);
 
 /*
+ * pkv_paged_decode_step - one whole decode step: exactly pkv_kv_append
+ * followed by pkv_paged_decode_attention, with the append done inside the
+ * decode kernel.  The workgroup that reads a sequence's last block takes the
+ * new token's K/V rows from k_new/v_new and writes them into their pool slot
+ * (slot ctx-1, bit for bit), so the step costs one decode launch (plus the
+ * merge) instead of a separate append launch.  Pools and outputs afterwards
+ * are those of the two separate calls.
+ *   KV-cache post, "Prefill and decode": the token's own K/V are appended
+ *   first, then everything cached is attended.
+ *
+ * Arguments as for pkv_kv_append and pkv_paged_decode_attention; k_pool and
+ * v_pool are [device, read and written].  The append of a sequence happens
+ * only if 1 <= ctx <= max_blocks_per_seq * block_size and ctx <=
+ * max_context_len (the launched partitions cover its last block).
+ */
+pkv_status_t pkv_paged_decode_step(
+    void* out, const void* q, void* k_pool, void* v_pool, const void* k_new, const void* v_new,
+    const float* k_scales, const float* v_scales, const int32_t* block_tables,
+    const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+    int32_t head_dim, int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
+    int32_t max_context_len, float softmax_scale, int32_t partition_size, void* workspace,
+    size_t workspace_bytes, pkv_dtype_t q_dtype, pkv_dtype_t kv_dtype, void* stream);
+
+/*
  * pkv_paged_decode_partials - the split-KV half of pkv_paged_decode_attention
  * on its own: per-partition attention results, not merged.
  *

@@ -79,6 +79,20 @@ __device__ __forceinline__ void load_row(uint32_t (&w)[NW], const char* row, int
   }
 }
 
+// Store one lane's chunks of a row (the inverse of load_row).
+template <int D, typename KV, int NW>
+__device__ __forceinline__ void store_row(const uint32_t (&w)[NW], char* row, int s) {
+  using TL = Tile<D, KV>;
+#pragma unroll
+  for (int c = 0; c < TL::kChunks; ++c) {
+    char* p = row + TL::chunk_off(s, c);
+    if constexpr (TL::kChunkBytes == 16)
+      *reinterpret_cast<uint4*>(p) = make_uint4(w[c * 4 + 0], w[c * 4 + 1], w[c * 4 + 2], w[c * 4 + 3]);
+    else
+      *reinterpret_cast<uint2*>(p) = make_uint2(w[c * 2 + 0], w[c * 2 + 1]);
+  }
+}
+
 // Storage words of one lane's slice of a row -> kDims floats (in dim order k).
 template <int D, typename KV, int NW, int ND>
 __device__ __forceinline__ void to_float(const uint32_t (&w)[NW], float (&f)[ND]) {
@@ -236,14 +250,18 @@ __global__ __launch_bounds__(kWave) void paged_decode_kernel(DecodeArgs a) {
   const int tg = lane / kLanesPerToken;
   const int s = lane % kLanesPerToken;
 
-  int ctx = a.context_lens[b];
-  ctx = ctx < 0 ? 0 : ctx;
+  const int raw_ctx = a.context_lens[b];
+  int ctx = raw_ctx < 0 ? 0 : raw_ctx;
   const int cap = a.max_blocks_per_seq * kBlockSize;
   ctx = ctx > cap ? cap : ctx;
   const int n_blk_seq = (ctx + kBlockSize - 1) / kBlockSize;
   const int blk_begin = part * a.blocks_per_partition;
   int blk_end = blk_begin + a.blocks_per_partition;
   blk_end = blk_end < n_blk_seq ? blk_end : n_blk_seq;
+  // Fused append: the block of position ctx-1 takes its new row from k_new/v_new
+  // (a sequence outside 1 <= ctx <= capacity appends nothing, as pkv_kv_append).
+  const int append_blk = (a.k_new && raw_ctx >= 1 && raw_ctx <= cap) ? (raw_ctx - 1) / kBlockSize : -1;
+  const int t_new = (raw_ctx - 1) % kBlockSize;
 
   const int head0 = chunk * G;                          // first head of the tile within the group
   int n_heads = a.group - head0;
@@ -299,11 +317,29 @@ __global__ __launch_bounds__(kWave) void paged_decode_kernel(DecodeArgs a) {
         load_row<D, KV>(vw[j], vslice + t * TL::kRowBytes, s);
       }
     };
-    auto consume = [&](const uint32_t (&kw)[kTokPerLane][W], uint32_t (&vw)[kTokPerLane][W], int k) {
+    auto consume = [&](uint32_t (&kw)[kTokPerLane][W], uint32_t (&vw)[kTokPerLane][W], int k) {
       const int blk = seg + k;
       int valid = ctx - blk * kBlockSize;
       valid = valid < kBlockSize ? valid : kBlockSize;
-      valid = ((ok_mask >> k) & 1) ? valid : 0;
+      const bool ok = (ok_mask >> k) & 1;
+      valid = ok ? valid : 0;
+      if (blk == append_blk && ok) {
+        // Fused append: the lanes owning the new token's row take it from
+        // k_new/v_new and (one writer per sequence and KV head) store it.
+        const size_t nrow = (size_t(b) * a.num_kv_heads + h) * TL::kRowBytes;
+        const int phys = __builtin_amdgcn_readlane(my_id, k);
+        const size_t off = size_t(phys) * block_stride + head_off + size_t(t_new) * TL::kRowBytes;
+#pragma unroll
+        for (int j = 0; j < kTokPerLane; ++j) {
+          if (tg + kGroups * j != t_new) continue;
+          load_row<D, KV>(kw[j], reinterpret_cast<const char*>(a.k_new) + nrow, s);
+          load_row<D, KV>(vw[j], reinterpret_cast<const char*>(a.v_new) + nrow, s);
+          if (chunk == 0) {
+            store_row<D, KV>(kw[j], reinterpret_cast<char*>(a.k_pool_w) + off, s);
+            store_row<D, KV>(vw[j], reinterpret_cast<char*>(a.v_pool_w) + off, s);
+          }
+        }
+      }
       float km = a.scale_log2, vm = 1.0f;
       if constexpr (kFp8) {
         km *= __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_ks), k));

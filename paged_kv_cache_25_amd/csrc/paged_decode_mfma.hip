@@ -48,7 +48,12 @@ constexpr int kHeadTile = 16;
 #ifndef PKV_MFMA_WAVES_PER_EU
 #define PKV_MFMA_WAVES_PER_EU 3
 #endif
+// Independent work items (waves) packed in one workgroup; they share nothing.
+#ifndef PKV_MFMA_ITEMS_PER_WG
+#define PKV_MFMA_ITEMS_PER_WG 1
+#endif
 constexpr int kDepth = PKV_MFMA_DEPTH;
+constexpr int kItemsPerWg = PKV_MFMA_ITEMS_PER_WG;
 
 template <int D>
 struct MfmaTile {
@@ -91,6 +96,53 @@ __device__ __forceinline__ void load_block(BlockRegs<D>& br, const char* kslice,
       const uint2 w = load_streamed<uint2>(p);
       br.v[i][0] = w.x; br.v[i][1] = w.y;
     }
+  }
+}
+
+// The fused append, for the block holding a sequence's new token (row t_new):
+// the lanes that own that row replace it with the new K/V row, then store it
+// into its pool slot.  Static register indexes only.
+template <int D>
+__device__ __forceinline__ void take_new_row(BlockRegs<D>& br, const char* knew, const char* vnew,
+                                             int t_new, int lane) {
+  using T = MfmaTile<D>;
+  const int r = lane >> 4, c = lane & 15;
+  if (c == t_new) {
+#pragma unroll
+    for (int j = 0; j < T::kSlabs; ++j) br.k[j] = *reinterpret_cast<const uint4*>(knew + 64 * j + 16 * r);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (4 * r + i != t_new) continue;
+    const char* p = vnew + T::kVChunkBytes * c;
+    if constexpr (T::kVWords == 4) {
+      const uint4 w = *reinterpret_cast<const uint4*>(p);
+      br.v[i][0] = w.x; br.v[i][1] = w.y; br.v[i][2] = w.z; br.v[i][3] = w.w;
+    } else {
+      const uint2 w = *reinterpret_cast<const uint2*>(p);
+      br.v[i][0] = w.x; br.v[i][1] = w.y;
+    }
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void store_new_row(const BlockRegs<D>& br, char* kslice, char* vslice,
+                                              int t_new, int lane) {
+  using T = MfmaTile<D>;
+  const int r = lane >> 4, c = lane & 15;
+  if (c == t_new) {
+#pragma unroll
+    for (int j = 0; j < T::kSlabs; ++j)
+      *reinterpret_cast<uint4*>(kslice + c * T::kRowBytes + 64 * j + 16 * r) = br.k[j];
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {                  // static register index: no scratch copy
+    if (4 * r + i != t_new) continue;
+    char* p = vslice + t_new * T::kRowBytes + T::kVChunkBytes * c;
+    if constexpr (T::kVWords == 4)
+      *reinterpret_cast<uint4*>(p) = make_uint4(br.v[i][0], br.v[i][1], br.v[i][2], br.v[i][3]);
+    else
+      *reinterpret_cast<uint2*>(p) = make_uint2(br.v[i][0], br.v[i][1]);
   }
 }
 
@@ -157,20 +209,21 @@ struct MfmaDecode {
 
 // Three waves per SIMD: 151 VGPRs for head dim 128 with two blocks in registers.
 template <int D>
-__global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(PKV_MFMA_WAVES_PER_EU)))
+__global__ __launch_bounds__(kWave * kItemsPerWg) __attribute__((amdgpu_waves_per_eu(PKV_MFMA_WAVES_PER_EU)))
 void paged_decode_mfma_kernel(DecodeArgs a) {
   using T = MfmaTile<D>;
   // blockIdx.x -> (head chunk, kv head, sequence, partition), partition
   // slowest.  Workgroups go to the 8 XCDs round-robin, so consecutive ids must
   // carry equal work: every (sequence, head) has a partition 0, while only long
   // sequences have high partitions.
-  int idx = blockIdx.x;
+  int idx = blockIdx.x * kItemsPerWg + int(threadIdx.x / kWave);
+  if (idx >= a.num_seqs * a.num_kv_heads * a.head_chunks * a.max_partitions) return;
   const int chunk = idx % a.head_chunks;   idx /= a.head_chunks;
   const int h = idx % a.num_kv_heads;      idx /= a.num_kv_heads;
   const int b = idx % a.num_seqs;
   const int part = idx / a.num_seqs;
 
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x % kWave;
   const int r = lane >> 4, c = lane & 15;
 
   const int32_t* table = a.block_tables + size_t(b) * a.max_blocks_per_seq;
@@ -181,13 +234,17 @@ void paged_decode_mfma_kernel(DecodeArgs a) {
   const int first_n = a.max_blocks_per_seq - blk_begin;
   int id0 = (lane < first_n && lane < a.blocks_per_partition) ? table[blk_begin + lane] : -1;
 
-  int ctx = a.context_lens[b];
-  ctx = ctx < 0 ? 0 : ctx;
+  const int raw_ctx = a.context_lens[b];
+  int ctx = raw_ctx < 0 ? 0 : raw_ctx;
   const int cap = a.max_blocks_per_seq * kBlockSize;
   ctx = ctx > cap ? cap : ctx;
   const int n_blk_seq = (ctx + kBlockSize - 1) / kBlockSize;
   int blk_end = blk_begin + a.blocks_per_partition;
   blk_end = blk_end < n_blk_seq ? blk_end : n_blk_seq;
+  // Fused append: the block of position ctx-1 takes its new row from k_new/v_new
+  // (a sequence outside 1 <= ctx <= capacity appends nothing, as pkv_kv_append).
+  const int append_blk = (a.k_new && raw_ctx >= 1 && raw_ctx <= cap) ? (raw_ctx - 1) / kBlockSize : -1;
+  const int t_new = (raw_ctx - 1) % kBlockSize;
   const int head0 = chunk * kHeadTile;
   int n_heads = a.group - head0;
   n_heads = n_heads < kHeadTile ? n_heads : kHeadTile;
@@ -241,7 +298,19 @@ void paged_decode_mfma_kernel(DecodeArgs a) {
     auto consume = [&](BlockRegs<D>& br, int k) {
       int valid = ctx - (seg + k) * kBlockSize;
       valid = valid < kBlockSize ? valid : kBlockSize;
-      valid = ((ok_mask >> k) & 1) ? valid : 0;
+      const bool ok = (ok_mask >> k) & 1;
+      valid = ok ? valid : 0;
+      if (seg + k == append_blk && ok) {
+        const size_t nrow = (size_t(b) * a.num_kv_heads + h) * T::kRowBytes;
+        take_new_row<D>(br, reinterpret_cast<const char*>(a.k_new) + nrow,
+                        reinterpret_cast<const char*>(a.v_new) + nrow, t_new, lane);
+        if (chunk == 0) {                                // one writer per (sequence, KV head)
+          const int phys = __builtin_amdgcn_readlane(my_id, k);
+          const size_t off = size_t(phys) * block_stride + head_off;
+          store_new_row<D>(br, reinterpret_cast<char*>(a.k_pool_w) + off,
+                           reinterpret_cast<char*>(a.v_pool_w) + off, t_new, lane);
+        }
+      }
       dec.block(br, valid, k_mul, lane);
     };
 
@@ -307,7 +376,9 @@ hipError_t launch_d(const DecodeArgs& a, hipStream_t stream) {
   const size_t grid = size_t(a.num_seqs) * a.num_kv_heads * a.head_chunks * a.max_partitions;
   if (grid == 0) return hipSuccess;
   if (grid > 0x7fffffffu) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((paged_decode_mfma_kernel<D>), dim3(unsigned(grid)), dim3(kWave), 0, stream, a);
+  const size_t wgs = (grid + kItemsPerWg - 1) / kItemsPerWg;
+  hipLaunchKernelGGL((paged_decode_mfma_kernel<D>), dim3(unsigned(wgs)), dim3(kWave * kItemsPerWg), 0,
+                     stream, a);
   return hipGetLastError();
 }
 

@@ -181,17 +181,14 @@ hipError_t launch_decode(const pkv::DecodeArgs& a, int head_dim, int tile, bool 
                                          to_internal(kv_dtype), st);
 }
 
-}  // namespace
-
-extern "C" {
-
-pkv_status_t pkv_paged_decode_attention(
+pkv_status_t attention_impl(
     void* out, const void* q, const void* k_pool, const void* v_pool, const float* k_scales,
     const float* v_scales, const int32_t* block_tables, const int32_t* context_lens,
     int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
     int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len,
     float softmax_scale, int32_t partition_size, void* workspace, size_t workspace_bytes,
-    pkv_dtype_t q_dtype, pkv_dtype_t kv_dtype, void* stream) {
+    pkv_dtype_t q_dtype, pkv_dtype_t kv_dtype, void* stream, const void* k_new,
+    const void* v_new, void* k_pool_w, void* v_pool_w) {
   if (max_context_len < 0) return PKV_ERR_INVALID_ARG;
   const pkv_status_t st0 = check_decode(q, k_pool, v_pool, k_scales, v_scales, block_tables,
                                         context_lens, num_seqs, num_q_heads, num_kv_heads,
@@ -213,6 +210,10 @@ pkv_status_t pkv_paged_decode_attention(
                                   context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim,
                                   num_blocks, max_blocks_per_seq, softmax_scale, tile);
   a.out = out;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.k_pool_w = k_pool_w;
+  a.v_pool_w = v_pool_w;
   if (!single) {
     const PartLayout L = part_layout(num_seqs, num_q_heads, head_dim, maxp);
     if (!workspace || workspace_bytes < L.total) return PKV_ERR_WORKSPACE;
@@ -243,6 +244,40 @@ pkv_status_t pkv_paged_decode_attention(
   m.skip_single = 1;
   return pkv::launch_merge(m, head_dim, to_internal(q_dtype), st) == hipSuccess ? PKV_OK
                                                                                 : PKV_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+pkv_status_t pkv_paged_decode_attention(
+    void* out, const void* q, const void* k_pool, const void* v_pool, const float* k_scales,
+    const float* v_scales, const int32_t* block_tables, const int32_t* context_lens,
+    int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len,
+    float softmax_scale, int32_t partition_size, void* workspace, size_t workspace_bytes,
+    pkv_dtype_t q_dtype, pkv_dtype_t kv_dtype, void* stream) {
+  return attention_impl(out, q, k_pool, v_pool, k_scales, v_scales, block_tables, context_lens,
+                        num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                        max_blocks_per_seq, max_context_len, softmax_scale, partition_size,
+                        workspace, workspace_bytes, q_dtype, kv_dtype, stream, nullptr, nullptr,
+                        nullptr, nullptr);
+}
+
+pkv_status_t pkv_paged_decode_step(
+    void* out, const void* q, void* k_pool, void* v_pool, const void* k_new, const void* v_new,
+    const float* k_scales, const float* v_scales, const int32_t* block_tables,
+    const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+    int32_t head_dim, int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
+    int32_t max_context_len, float softmax_scale, int32_t partition_size, void* workspace,
+    size_t workspace_bytes, pkv_dtype_t q_dtype, pkv_dtype_t kv_dtype, void* stream) {
+  if (num_seqs > 0 && (!k_new || !v_new || !aligned16(k_new) || !aligned16(v_new)))
+    return PKV_ERR_INVALID_ARG;
+  return attention_impl(out, q, k_pool, v_pool, k_scales, v_scales, block_tables, context_lens,
+                        num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                        max_blocks_per_seq, max_context_len, softmax_scale, partition_size,
+                        workspace, workspace_bytes, q_dtype, kv_dtype, stream, k_new, v_new,
+                        k_pool, v_pool);
 }
 
 pkv_status_t pkv_paged_decode_partials(

@@ -34,6 +34,13 @@ struct DecodeArgs {
   const float* v_scales;
   const int32_t* block_tables;
   const int32_t* context_lens;
+  // Fused append (null otherwise): the new token's K/V rows [B, Hkv, D] are
+  // read from here instead of the pool, and written into the pool slot by the
+  // workgroup that reads the sequence's last block.
+  const void* k_new;
+  const void* v_new;
+  void* k_pool_w;
+  void* v_pool_w;
   int num_seqs, num_q_heads, num_kv_heads, group, head_chunks;
   int num_blocks, max_blocks_per_seq;
   int blocks_per_partition;   // partition size / 16

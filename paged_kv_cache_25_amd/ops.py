@@ -50,6 +50,9 @@ def load():
     L.pkv_paged_decode_attention.restype = ctypes.c_int
     L.pkv_paged_decode_attention.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, F, I,
                                              P, Z, ctypes.c_int, ctypes.c_int, P]
+    L.pkv_paged_decode_step.restype = ctypes.c_int
+    L.pkv_paged_decode_step.argtypes = [P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, F, I,
+                                        P, Z, ctypes.c_int, ctypes.c_int, P]
     L.pkv_paged_decode_partials.restype = ctypes.c_int
     L.pkv_paged_decode_partials.argtypes = [P, P, I, P, P, P, P, P, P, P, I, I, I, I, I, I, I, F, I,
                                             ctypes.c_int, ctypes.c_int, P]
@@ -159,9 +162,27 @@ def merge_partials(out, partial_out, partial_lse, num_partitions=None, stream=No
 
 def decode_step(out, q, k_pool, v_pool, k_new, v_new, block_tables, context_lens,
                 max_context_len, softmax_scale, partition_size=512, k_scales=None,
-                v_scales=None, workspace=None, stream=None):
-    """One decode step: append the new K/V, then attend (same stream, in order)."""
-    kv_append(k_pool, v_pool, k_new, v_new, block_tables, context_lens, stream)
-    return paged_decode_attention(out, q, k_pool, v_pool, block_tables, context_lens,
-                                  max_context_len, softmax_scale, partition_size, k_scales,
-                                  v_scales, workspace, stream)
+                v_scales=None, workspace=None, stream=None, fused=True):
+    """One decode step: append the new K/V, then attend.  ``fused`` runs it as
+    pkv_paged_decode_step (the append inside the decode kernel); otherwise as
+    pkv_kv_append then pkv_paged_decode_attention on the same stream."""
+    if not fused:
+        kv_append(k_pool, v_pool, k_new, v_new, block_tables, context_lens, stream)
+        return paged_decode_attention(out, q, k_pool, v_pool, block_tables, context_lens,
+                                      max_context_len, softmax_scale, partition_size, k_scales,
+                                      v_scales, workspace, stream)
+    _need_cuda(out, q, k_pool, v_pool, k_new, v_new, block_tables, context_lens, k_scales,
+               v_scales, workspace)
+    if k_new.dtype != k_pool.dtype or v_new.dtype != v_pool.dtype:
+        raise TypeError("k_new/v_new must have the pool's dtype")
+    B, hq, d = q.shape
+    nb, hkv, bs, _ = k_pool.shape
+    if workspace is None:
+        workspace = alloc_workspace(B, hq, d, max_context_len, partition_size, q.device)
+    _check("pkv_paged_decode_step", load().pkv_paged_decode_step(
+        _ptr(out), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(k_new), _ptr(v_new), _ptr(k_scales),
+        _ptr(v_scales), _ptr(block_tables), _ptr(context_lens), B, hq, hkv, d, bs, nb,
+        block_tables.shape[1], int(max_context_len), float(softmax_scale), int(partition_size),
+        _ptr(workspace), workspace.numel(), dtype_code(q.dtype), dtype_code(k_pool.dtype),
+        _stream(stream)))
+    return out

@@ -70,9 +70,18 @@ class DeviceStep:
                                    self.v_scales)
         return self.out
 
-    def step(self, partition_size=None):
-        self.append()
-        out = self.decode(partition_size)
+    def step(self, partition_size=None, fused=False):
+        """Append then attend: two ABI calls, or pkv_paged_decode_step when fused."""
+        if fused:
+            inp = self.inp
+            P = inp.partition_size if partition_size is None else partition_size
+            ops.decode_step(self.out, self.q, self.k_pool, self.v_pool, self.k_new, self.v_new,
+                            self.tables, self.lens, inp.max_context_len, inp.softmax_scale, P,
+                            self.k_scales, self.v_scales, fused=True)
+            out = self.out
+        else:
+            self.append()
+            out = self.decode(partition_size)
         torch.cuda.synchronize()
         return out
 

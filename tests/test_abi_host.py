@@ -33,7 +33,8 @@ def lib():
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted([
         "pkv_abi_version", "pkv_status_string", "pkv_kv_append", "pkv_decode_workspace_bytes",
-        "pkv_paged_decode_attention", "pkv_paged_decode_partials", "pkv_merge_partials"])
+        "pkv_paged_decode_attention", "pkv_paged_decode_step", "pkv_paged_decode_partials",
+        "pkv_merge_partials"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -112,6 +113,27 @@ def test_alignment_checked(lib):
     assert _decode(lib, ws=odd, wsb=need) == INVALID
     f = lib.pkv_merge_partials
     assert f(FAKE, odd, FAKE, None, 2, 4, 128, 3, ops.PKV_BF16, None) == INVALID
+
+
+def _step(lib, **over):
+    a = dict(out=FAKE, q=FAKE, kp=FAKE, vp=FAKE, kn=FAKE, vn=FAKE, ks=None, vs=None, tables=FAKE,
+             lens=FAKE, B=2, hq=8, hkv=2, d=128, bs=16, nb=8, mbps=4, maxctx=64, scale=0.088,
+             P=16, ws=None, wsb=0, qt=ops.PKV_BF16, kvt=ops.PKV_BF16)
+    a.update(over)
+    return lib.pkv_paged_decode_step(
+        a["out"], a["q"], a["kp"], a["vp"], a["kn"], a["vn"], a["ks"], a["vs"], a["tables"],
+        a["lens"], a["B"], a["hq"], a["hkv"], a["d"], a["bs"], a["nb"], a["mbps"], a["maxctx"],
+        a["scale"], a["P"], a["ws"], a["wsb"], a["qt"], a["kvt"], None)
+
+
+def test_step_validation(lib):
+    assert _step(lib, kn=None) == INVALID
+    assert _step(lib, vn=ctypes.c_void_p(0x10008)) == INVALID
+    assert _step(lib, q=None) == INVALID
+    assert _step(lib, hq=6, hkv=4) == INVALID
+    assert _step(lib, d=96) == UNSUPPORTED
+    assert _step(lib) == WORKSPACE
+    assert _step(lib, B=0, kn=None, q=None) == OK
 
 
 def _partials(lib, **over):

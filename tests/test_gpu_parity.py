@@ -32,12 +32,13 @@ def _pool_bytes(a):
     return np.ascontiguousarray(a).view(np.uint8)
 
 
-def run_and_check(inp, label, seqs=None, partition_size=None, check_pools=True):
+def run_and_check(inp, label, seqs=None, partition_size=None, check_pools=True, fused=False):
+    label = label + (" [fused step]" if fused else "")
     log(f"[case] {label}: B={inp.num_seqs} Hq={inp.num_q_heads} Hkv={inp.num_kv_heads} "
         f"D={inp.head_dim} kv={inp.kv_dtype} q={inp.q_dtype} max_ctx={inp.max_context_len} "
         f"P={inp.partition_size if partition_size is None else partition_size}")
     d = DeviceStep(inp)
-    d.step(partition_size)
+    d.step(partition_size, fused=fused)
     kp, vp = pa.kv_append(inp.k_pool, inp.v_pool, inp.k_new, inp.v_new, inp.block_tables,
                           inp.context_lens, inp.block_size)
     if check_pools:
@@ -52,40 +53,50 @@ def run_and_check(inp, label, seqs=None, partition_size=None, check_pools=True):
 
 # --- the five workloads at their full sizes -------------------------------
 
-def test_config1_tiny_fp32_full():
-    run_and_check(named_config(1), "config1 tiny fp32")
+FUSED = pytest.mark.parametrize("fused", [False, True], ids=["two_calls", "fused_step"])
 
 
-def test_config2_llama3_8b_b64_full():
-    run_and_check(named_config(2), "config2 llama3-8b b64")
+@FUSED
+def test_config1_tiny_fp32_full(fused):
+    run_and_check(named_config(1), "config1 tiny fp32", fused=fused)
 
 
-def test_config3_long_context_sampled():
+@FUSED
+def test_config2_llama3_8b_b64_full(fused):
+    run_and_check(named_config(2), "config2 llama3-8b b64", fused=fused)
+
+
+@FUSED
+def test_config3_long_context_sampled(fused):
     inp = named_config(3)
-    run_and_check(inp, "config3 131072 ctx (seqs 0,3)", seqs=[0, 3])
+    run_and_check(inp, "config3 131072 ctx (seqs 0,3)", seqs=[0, 3], fused=fused)
 
 
-def test_config4_continuous_batching_full():
-    run_and_check(named_config(4), "config4 lognormal mix b256")
+@FUSED
+def test_config4_continuous_batching_full(fused):
+    run_and_check(named_config(4), "config4 lognormal mix b256", fused=fused)
 
 
-def test_config5_fp8_sampled():
+@FUSED
+def test_config5_fp8_sampled(fused):
     inp = named_config(5)
-    run_and_check(inp, "config5 fp8 b128 (8 seqs)", seqs=[0, 1, 17, 40, 63, 64, 100, 127])
+    run_and_check(inp, "config5 fp8 b128 (8 seqs)", seqs=[0, 1, 17, 40, 63, 64, 100, 127],
+                  fused=fused)
 
 
 # --- float32 twins: the same shapes at the 1e-5 bar ------------------------
 
+@FUSED
 @pytest.mark.parametrize("config,over", [
     (2, dict(num_seqs=12)),
     (3, dict(num_seqs=1)),
     (4, dict(num_seqs=48)),
     (5, dict(num_seqs=6)),
 ])
-def test_fp32_twin(config, over):
+def test_fp32_twin(config, over, fused):
     inp = named_config(config, q_dtype="f32", kv_dtype="f32", **over)
     seqs = [0] if config == 3 else None
-    run_and_check(inp, f"config{config} f32 twin", seqs=seqs)
+    run_and_check(inp, f"config{config} f32 twin", seqs=seqs, fused=fused)
 
 
 # --- partitions, placement, determinism, poison ----------------------------
@@ -163,11 +174,12 @@ def test_group_sizes(hq, hkv, d):
 @pytest.mark.parametrize("hq,hkv", [(4, 2), (6, 2), (8, 2), (10, 2), (16, 2), (32, 2), (48, 2)])
 @pytest.mark.parametrize("d", [64, 128])
 def test_group_sizes_bf16(hq, hkv, d):
-    """bf16 queries and cache: the matrix-core kernel, heads in tiles of 16."""
+    """bf16 queries and cache: the matrix-core kernel, heads in tiles of 16
+    (three tiles for a group of 24, all reading the fused step's new row)."""
     inp = make_inputs(num_seqs=3, num_q_heads=hq, num_kv_heads=hkv, head_dim=d,
                       ctx=("uniform", 1, 700), pool=("used_fraction", 0.8), q_dtype="bf16",
                       kv_dtype="bf16", seed=hq * 10 + d)
-    run_and_check(inp, f"bf16 g={hq // hkv} D={d}")
+    run_and_check(inp, f"bf16 g={hq // hkv} D={d}", fused=hq // hkv >= 16)
 
 
 @pytest.mark.parametrize("config,P", [(2, 512), (2, 0), (4, 512), (3, 512)])
@@ -180,25 +192,27 @@ def test_peaky_softmax_bf16(config, P):
     run_and_check(inp, f"config{config}-shape peaky P={P}", partition_size=P)
 
 
+@FUSED
 @pytest.mark.parametrize("q,kv", [("f32", "f32"), ("f32", "bf16"), ("f32", "fp8_e4m3"),
                                   ("bf16", "f32"), ("bf16", "bf16"), ("bf16", "fp8_e4m3")])
 @pytest.mark.parametrize("d", [64, 128])
-def test_dtype_combinations(q, kv, d):
+def test_dtype_combinations(q, kv, d, fused):
     inp = make_inputs(num_seqs=5, num_q_heads=8, num_kv_heads=2, head_dim=d,
                       ctx=("uniform", 1, 1200), pool=("used_fraction", 0.6), q_dtype=q,
                       kv_dtype=kv, seed=7 + d)
-    run_and_check(inp, f"q={q} kv={kv} D={d}")
+    run_and_check(inp, f"q={q} kv={kv} D={d}", fused=fused)
 
 
 # --- edge cases -------------------------------------------------------------
 
-def test_single_token_and_empty_contexts():
+@FUSED
+def test_single_token_and_empty_contexts(fused):
     inp = make_inputs(num_seqs=5, num_q_heads=8, num_kv_heads=2, head_dim=128,
                       ctx=("fixed", [1, 0, 17, 1, 16]), pool=("blocks", 12), q_dtype="f32",
                       kv_dtype="f32", seed=3, extra_table_cols=2)
-    run_and_check(inp, "ctx {1,0,17,1,16}")
+    run_and_check(inp, "ctx {1,0,17,1,16}", fused=fused)
     d = DeviceStep(inp)
-    out = d.step().cpu().numpy()
+    out = d.step(fused=fused).cpu().numpy()
     assert (out[1] == 0).all()
     # ctx = 1: exactly the appended V row
     assert np.array_equal(out[0], np.repeat(inp.v_new[0], 4, axis=0))
