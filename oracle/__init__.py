@@ -17,8 +17,11 @@ from .paged_attention import (  # noqa: F401
     decode_step,
     gather_sequence,
     kv_append,
+    kv_append_tokens,
     merge_partials,
+    multi_query_attention,
     partition_partials,
     slot_of,
     to_float64,
+    visible_tokens,
 )

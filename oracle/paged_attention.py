@@ -34,6 +34,13 @@ What it computes, written out plainly and slowly from the pages:
   in decode the newest token may look at every cached token (4yush.com,
   "Adding the cache to GPT-2": the decode mask is all ones).
 
+* ``kv_append_tokens`` / ``multi_query_attention``: several new tokens per
+  sequence (chunked prefill, a prefix-cache tail, a speculative verify pass).
+  The t newest tokens are appended, then query j of them attends over the
+  tokens up to its own position: ``ctx - t + j + 1`` of them (the shifted
+  causal mask of the KV post's ``attn_cached``, the brunomaga post's
+  ``causal_mask`` and the 4yush post's mask with a start offset).
+
 * ``partition_partials`` / ``merge_partials``: the softmax over a range of
   tokens splits into per-range normalised outputs ``o_p`` and their
   log-sum-exp ``lse_p = m_p + ln sum exp(s - m_p)``; the whole-range output is
@@ -260,6 +267,63 @@ def decode_partials(q, k_pool, v_pool, block_tables, context_lens, *, block_size
         o[b, :, :ob.shape[1]] = ob
         lse[b, :, :lb.shape[1]] = lb
     return o, lse
+
+
+# --------------------------------------------------------------------------
+# Several new tokens per sequence: the shifted causal mask
+# --------------------------------------------------------------------------
+
+def visible_tokens(ctx: int, t: int, j: int) -> int:
+    """How many cached tokens query j (0-based) of a sequence's t newest tokens
+    sees: the tokens up to its own position ctx - t + j (KV post, "A KV cache in
+    PyTorch": mask tril(T - t); brunomaga post, causal_mask(Sq, Sk) =
+    tril(Sk - Sq); 4yush post, "Adding the cache to GPT-2": new token r at
+    position start + r sees keys 0 .. start + r)."""
+    return ctx - t + j + 1
+
+
+def kv_append_tokens(k_pool, v_pool, k_new, v_new, block_tables, context_lens, query_start_loc,
+                     block_size, inplace=False):
+    """Write the t_b = qsl[b+1] - qsl[b] newest rows of every sequence: row
+    qsl[b] + j of k_new/v_new ([total, Hkv, D]) goes to position ctx_b - t_b + j."""
+    if not inplace:
+        k_pool = k_pool.copy()
+        v_pool = v_pool.copy()
+    for b in range(len(context_lens)):
+        ctx = int(context_lens[b])
+        q0, q1 = int(query_start_loc[b]), int(query_start_loc[b + 1])
+        t = q1 - q0
+        for j in range(t):
+            pos = ctx - t + j
+            if pos < 0:
+                continue
+            blk, off = slot_of(block_tables[b], pos, block_size)
+            k_pool[blk, :, off, :] = k_new[q0 + j]
+            v_pool[blk, :, off, :] = v_new[q0 + j]
+    return k_pool, v_pool
+
+
+def multi_query_attention(q, k_pool, v_pool, block_tables, context_lens, query_start_loc, *,
+                          block_size, softmax_scale, q_dtype, kv_dtype, k_scales=None,
+                          v_scales=None):
+    """q [total, Hq, D]: rows qsl[b] .. qsl[b+1]-1 are sequence b's newest
+    tokens, in order.  Query j of sequence b attends over its first
+    visible_tokens(ctx_b, t_b, j) cached tokens.  Returns float64 [total, Hq, D]."""
+    total = int(query_start_loc[-1])
+    out = np.zeros((total,) + q.shape[1:])
+    for b in range(len(context_lens)):
+        ctx = int(context_lens[b])
+        q0, q1 = int(query_start_loc[b]), int(query_start_loc[b + 1])
+        if q1 == q0 or ctx <= 0:
+            continue
+        K = gather_sequence(k_pool, block_tables[b], ctx, block_size, kv_dtype, k_scales)
+        V = gather_sequence(v_pool, block_tables[b], ctx, block_size, kv_dtype, v_scales)
+        for j in range(q1 - q0):
+            n = visible_tokens(ctx, q1 - q0, j)
+            if n <= 0:
+                continue
+            out[q0 + j] = attend(to_float64(q[q0 + j], q_dtype), K[:, :n], V[:, :n], softmax_scale)
+    return out
 
 
 def decode_step(q, k_pool, v_pool, k_new, v_new, block_tables, context_lens, *,

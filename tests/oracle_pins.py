@@ -356,3 +356,99 @@ def pin_weights_sum_to_one(seed=19):
 
 def pin_config_crosscheck(config, seqs=None, **overrides):
     return pin_library_crosscheck(named_config(config, **overrides), seqs)
+
+
+# --------------------------------------------------------------------------
+# Several new tokens per sequence (chunked prefill / verify): shifted causal mask
+# --------------------------------------------------------------------------
+
+def pin_chunked_vs_causal(*, schedules, Hq=4, Hkv=2, D=16, bs=4, seed=23):
+    """Each sequence s processes its T_s tokens in chunks schedules[s] (all
+    sequences advance one chunk per step, ragged): append the chunk's K/V,
+    then every query of the chunk attends.  The outputs, in token order, must
+    equal full causal attention over the T_s tokens (the KV post's check: a
+    6-token prefill then 4 single-token decodes against attention over all 10)."""
+    rng = np.random.default_rng(seed)
+    n = len(schedules)
+    T = [sum(sc) for sc in schedules]
+    Tm = max(T)
+    q_all = rng.standard_normal((n, Hq, Tm, D)).astype(np.float32)
+    k_all = rng.standard_normal((n, Hkv, Tm, D)).astype(np.float32)
+    v_all = rng.standard_normal((n, Hkv, Tm, D)).astype(np.float32)
+    worst = 0.0
+    refs = [_sdpa(torch.from_numpy(q_all[s:s + 1, :, :T[s]]).double(),
+                  torch.from_numpy(k_all[s:s + 1, :, :T[s]]).double(),
+                  torch.from_numpy(v_all[s:s + 1, :, :T[s]]).double(), is_causal=True).numpy()[0]
+            for s in range(n)]
+    nbmax = -(-Tm // bs)
+    NB = n * nbmax + 3
+    free = [int(x) for x in rng.permutation(NB)]
+    k_pool = np.full((NB, Hkv, bs, D), np.nan, np.float32)
+    v_pool = np.full((NB, Hkv, bs, D), np.nan, np.float32)
+    tables = np.full((n, nbmax + 1), -1, np.int32)
+    used = [0] * n
+    done = [0] * n
+    for step in range(max(len(sc) for sc in schedules)):
+        t = [schedules[s][step] if step < len(schedules[s]) else 0 for s in range(n)]
+        ctx = np.array([done[s] + t[s] for s in range(n)], np.int32)
+        for s in range(n):
+            while used[s] * bs < ctx[s]:
+                tables[s, used[s]] = free.pop()
+                used[s] += 1
+        qsl = np.concatenate([[0], np.cumsum(t)]).astype(np.int32)
+        rows_q = np.concatenate([q_all[s, :, done[s]:done[s] + t[s]].transpose(1, 0, 2) for s in range(n)])
+        rows_k = np.concatenate([k_all[s, :, done[s]:done[s] + t[s]].transpose(1, 0, 2) for s in range(n)])
+        rows_v = np.concatenate([v_all[s, :, done[s]:done[s] + t[s]].transpose(1, 0, 2) for s in range(n)])
+        pa.kv_append_tokens(k_pool, v_pool, rows_k, rows_v, tables, ctx, qsl, bs, inplace=True)
+        out = pa.multi_query_attention(rows_q, k_pool, v_pool, tables, ctx, qsl, block_size=bs,
+                                       softmax_scale=1.0 / math.sqrt(D), q_dtype="f32",
+                                       kv_dtype="f32")
+        for s in range(n):
+            got = out[qsl[s]:qsl[s + 1]]                              # [t, Hq, D]
+            ref = refs[s][:, done[s]:done[s] + t[s]].transpose(1, 0, 2)
+            if got.size:
+                worst = max(worst, float(np.nan_to_num(np.abs(got - ref), nan=np.inf).max()))
+        done = [done[s] + t[s] for s in range(n)]
+    return worst
+
+
+def torch_padded_multi_query(inp, k_pool, v_pool):
+    """Padded torch gather + float64 SDPA with each query's mask
+    arange(L) < ctx - t + j + 1."""
+    bs, D = inp.block_size, inp.head_dim
+    qsl = inp.query_start_loc
+    out = np.zeros((inp.total_queries, inp.num_q_heads, D))
+    kp = torch_decode_storage(k_pool, inp.kv_dtype)
+    vp = torch_decode_storage(v_pool, inp.kv_dtype)
+    if inp.k_scales is not None:
+        kp = kp * torch.from_numpy(inp.k_scales).double()[:, :, None, None]
+        vp = vp * torch.from_numpy(inp.v_scales).double()[:, :, None, None]
+    q_all = torch_decode_storage(inp.q, inp.q_dtype)
+    for b in range(inp.num_seqs):
+        ctx = int(inp.context_lens[b])
+        t = int(qsl[b + 1] - qsl[b])
+        nb = -(-ctx // bs)
+        ids = torch.from_numpy(inp.block_tables[b, :nb].astype(np.int64))
+        L = nb * bs
+        k = kp[ids].permute(1, 0, 2, 3).reshape(inp.num_kv_heads, L, D)[None]
+        v = vp[ids].permute(1, 0, 2, 3).reshape(inp.num_kv_heads, L, D)[None]
+        keep = torch.arange(L)[None, :] < torch.arange(ctx - t + 1, ctx + 1)[:, None]  # [t, L]
+        valid = torch.arange(L) < ctx
+        k = torch.where(valid[None, None, :, None], k, torch.zeros_like(k))
+        v = torch.where(valid[None, None, :, None], v, torch.zeros_like(v))
+        q = q_all[qsl[b]:qsl[b + 1]].permute(1, 0, 2)[None]                            # [1, Hq, t, D]
+        o = _sdpa(q, k, v, attn_mask=keep[None, None], scale=inp.softmax_scale)
+        out[qsl[b]:qsl[b + 1]] = o[0].permute(1, 0, 2).numpy()
+    return out
+
+
+def pin_multi_query_library(inp):
+    kp, vp = pa.kv_append_tokens(inp.k_pool, inp.v_pool, inp.k_new, inp.v_new, inp.block_tables,
+                                 inp.context_lens, inp.query_start_loc, inp.block_size)
+    ref = torch_padded_multi_query(inp, kp, vp)
+    out = pa.multi_query_attention(inp.q, kp, vp, inp.block_tables, inp.context_lens,
+                                   inp.query_start_loc, block_size=inp.block_size,
+                                   softmax_scale=inp.softmax_scale, q_dtype=inp.q_dtype,
+                                   kv_dtype=inp.kv_dtype, k_scales=inp.k_scales,
+                                   v_scales=inp.v_scales)
+    return float(np.nan_to_num(np.abs(out - ref), nan=np.inf).max())

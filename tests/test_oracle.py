@@ -183,3 +183,42 @@ def test_workload_recipes_shapes():
     assert 700 < np.median(c4.context_lens) < 1400
     c5 = named_config(5, num_seqs=2, ctx=("const", 64))
     assert c5.k_scales.shape == (c5.num_blocks, 32) and c5.k_pool.dtype == np.uint8
+
+
+# Several new tokens per sequence ----------------------------------------------
+
+@pytest.mark.parametrize("schedules,Hq,Hkv,bs", [
+    ([[6, 1, 1, 1, 1]], 4, 4, 4),                                   # the KV post's own check
+    ([[6, 1, 1, 1, 1], [3, 3, 3, 1], [1, 1, 8, 2]], 4, 2, 4),       # ragged chunks, GQA
+    ([[17, 16, 1, 5], [40], [1] * 12], 8, 2, 16),                   # a whole prefill, blocks of 16
+])
+def test_chunked_equals_full_causal(schedules, Hq, Hkv, bs):
+    assert pins.pin_chunked_vs_causal(schedules=schedules, Hq=Hq, Hkv=Hkv, bs=bs) < 1e-12
+
+
+def test_visibility_golden():
+    g = _golden("gpt2_cache_masks.json")
+    for case in g["cases"]:
+        start, t = case["start"], case["new"]
+        for j, row in enumerate(case["mask"]):
+            assert pa.visible_tokens(start + t, t, j) == sum(row)
+            assert row == [1] * sum(row) + [0] * (len(row) - sum(row))
+
+
+@pytest.mark.parametrize("kv,q", [("bf16", "bf16"), ("fp8_e4m3", "bf16"), ("f32", "f32")])
+def test_multi_query_library_crosscheck(kv, q):
+    inp = make_inputs(num_seqs=4, num_q_heads=32, num_kv_heads=8, head_dim=128,
+                      ctx=("uniform", 1, 700), pool=("used_fraction", 0.8), q_dtype=q,
+                      kv_dtype=kv, seed=41, new_tokens=("uniform", 1, 9))
+    assert pins.pin_multi_query_library(inp) < 1e-12
+
+
+def test_one_new_token_is_decode():
+    inp = named_config(2, num_seqs=3)
+    qsl = np.arange(4, dtype=np.int32)
+    kp, vp = pa.kv_append(inp.k_pool, inp.v_pool, inp.k_new, inp.v_new, inp.block_tables,
+                          inp.context_lens, 16)
+    kw = dict(block_size=16, softmax_scale=inp.softmax_scale, q_dtype="bf16", kv_dtype="bf16")
+    a = pa.decode_attention(inp.q, kp, vp, inp.block_tables, inp.context_lens, **kw)
+    b = pa.multi_query_attention(inp.q, kp, vp, inp.block_tables, inp.context_lens, qsl, **kw)
+    assert np.array_equal(a, b)

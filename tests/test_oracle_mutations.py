@@ -113,6 +113,17 @@ def _mut_partition_overlap(monkeypatch):
                         lambda q, K, V, scale, P: orig(q, K[:, 1:], V[:, 1:], scale, P))
 
 
+def _mut_visibility(monkeypatch):
+    monkeypatch.setattr(pa, "visible_tokens", lambda ctx, t, j: ctx - t + j + 2)
+
+
+def _mut_append_tokens_order(monkeypatch):
+    orig = pa.kv_append_tokens
+    def app(kp, vp, kn, vn, tab, ctx, qsl, bs, inplace=False):
+        return orig(kp, vp, kn[::-1].copy(), vn[::-1].copy(), tab, ctx, qsl, bs, inplace)
+    monkeypatch.setattr(pa, "kv_append_tokens", app)
+
+
 def _caught(check):
     with np.errstate(all="ignore"):
         try:
@@ -130,13 +141,16 @@ PIN_SUITE = {
     "bf16": lambda: pins.pin_bf16_table() > 0,
     "split_merge": lambda: pins.pin_split_merge(named_config(1), (16, 64)) > 1e-9,
     "closed_forms": lambda: pins.pin_closed_forms() > 1e-9,
+    "chunked": lambda: pins.pin_chunked_vs_causal(schedules=[[6, 1, 1, 1, 1], [3, 3, 3, 1]],
+                                                  Hkv=2) > 1e-9,
 }
 
 
 @pytest.mark.parametrize("mutant", [
     _mut_gqa_modulo, _mut_append_slot, _mut_no_scale, _mut_keep_tail, _mut_block_order,
     _mut_v_from_k, _mut_no_max_shift_sign, _mut_merge_weights, _mut_e4m3_bias,
-    _mut_fp8_scale_transposed, _mut_bf16_shift, _mut_partition_overlap,
+    _mut_fp8_scale_transposed, _mut_bf16_shift, _mut_partition_overlap, _mut_visibility,
+    _mut_append_tokens_order,
 ])
 def test_planted_mistake_is_caught(monkeypatch, mutant):
     mutant(monkeypatch)

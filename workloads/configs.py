@@ -106,6 +106,19 @@ class PagedDecodeInputs:
     k_scales: np.ndarray | None   # float32 [NB, Hkv] (fp8 only)
     v_scales: np.ndarray | None
     seed: int = 0
+    # Several new tokens per sequence: rows qsl[b] .. qsl[b+1]-1 of q, k_new and
+    # v_new belong to sequence b (its newest tokens, in order).  None: one each.
+    query_start_loc: np.ndarray | None = None
+
+    @property
+    def total_queries(self) -> int:
+        return int(self.q.shape[0])
+
+    @property
+    def max_new_tokens(self) -> int:
+        if self.query_start_loc is None:
+            return 1
+        return int(np.diff(self.query_start_loc).max()) if self.num_seqs else 0
 
     @property
     def max_context_len(self) -> int:
@@ -122,7 +135,10 @@ class PagedDecodeInputs:
         return -(-self.context_lens.astype(np.int64) // p)
 
     def subset(self, seqs) -> "PagedDecodeInputs":
-        """The same pools, with only the chosen sequences in the batch."""
+        """The same pools, with only the chosen sequences in the batch (one new
+        token per sequence)."""
+        if self.query_start_loc is not None:
+            raise ValueError("subset() is for one new token per sequence")
         seqs = np.asarray(seqs, dtype=np.int64)
         return dataclasses.replace(
             self,
@@ -220,12 +236,24 @@ def _context_lengths(rng, spec, num_seqs):
 
 def make_inputs(*, num_seqs, num_q_heads, num_kv_heads, head_dim, ctx, pool,
                 q_dtype, kv_dtype, partition_size=512, block_size=16, seed=0,
-                poison=True, extra_table_cols=0, name="custom", softmax_scale=None):
-    """Draw one decode step's inputs.  See the module docstring for the recipe."""
+                poison=True, extra_table_cols=0, name="custom", softmax_scale=None,
+                new_tokens=None):
+    """Draw one decode step's inputs.  See the module docstring for the recipe.
+
+    ``new_tokens`` (a length spec like ``ctx``, or None for one per sequence)
+    gives each sequence several new tokens: they are its newest positions, and
+    a context shorter than its new tokens is raised to their count."""
     if q_dtype not in ("f32", "bf16") or kv_dtype not in DTYPES:
         raise ValueError((q_dtype, kv_dtype))
     rng = np.random.default_rng(seed)
     ctx_lens = _context_lengths(rng, ctx, num_seqs)
+    if new_tokens is None:
+        t_new = np.ones(num_seqs, dtype=np.int64) * (ctx_lens > 0)
+        qsl = None
+    else:
+        t_new = _context_lengths(rng, new_tokens, num_seqs)
+        ctx_lens = np.maximum(ctx_lens, t_new)
+        qsl = np.concatenate([[0], np.cumsum(t_new)]).astype(np.int32)
     nblk = -(-ctx_lens // block_size)
     total = int(nblk.sum())
     if pool[0] == "blocks":
@@ -252,25 +280,31 @@ def make_inputs(*, num_seqs, num_q_heads, num_kv_heads, head_dim, ctx, pool,
                                   kv_dtype, valid_count, poison)
     v_pool, v_scales = _draw_pool([seed, 2], num_blocks, num_kv_heads, block_size, head_dim,
                                   kv_dtype, valid_count, poison)
-    q = _to_storage(rng.standard_normal((num_seqs, num_q_heads, head_dim), dtype=np.float32), q_dtype)
+    n_rows = num_seqs if qsl is None else int(qsl[-1])
+    q = _to_storage(rng.standard_normal((n_rows, num_q_heads, head_dim), dtype=np.float32), q_dtype)
 
-    # Take the new token's rows out of their slot, and poison the slot.
-    k_new = np.empty((num_seqs, num_kv_heads, head_dim), STORAGE_NP[kv_dtype])
+    # Take the new tokens' rows out of their slots, and poison the slots.
+    k_new = np.empty((n_rows, num_kv_heads, head_dim), STORAGE_NP[kv_dtype])
     v_new = np.empty_like(k_new)
     pv = _poison_value(kv_dtype)
+    row = 0
     for b in range(num_seqs):
-        if ctx_lens[b] <= 0:
+        t = int(t_new[b]) if qsl is not None else 1
+        if qsl is None and ctx_lens[b] <= 0:
             k_new[b] = pv
             v_new[b] = pv
+            row += 1
             continue
-        pos = ctx_lens[b] - 1
-        blk = tables[b, pos // block_size]
-        off = pos % block_size
-        k_new[b] = k_pool[blk, :, off]
-        v_new[b] = v_pool[blk, :, off]
-        if poison:
-            k_pool[blk, :, off] = pv
-            v_pool[blk, :, off] = pv
+        for j in range(t):
+            pos = ctx_lens[b] - t + j
+            blk = tables[b, pos // block_size]
+            off = pos % block_size
+            k_new[row] = k_pool[blk, :, off]
+            v_new[row] = v_pool[blk, :, off]
+            if poison:
+                k_pool[blk, :, off] = pv
+                v_pool[blk, :, off] = pv
+            row += 1
 
     return PagedDecodeInputs(
         name=name, num_seqs=num_seqs, num_q_heads=num_q_heads, num_kv_heads=num_kv_heads,
@@ -280,7 +314,7 @@ def make_inputs(*, num_seqs, num_q_heads, num_kv_heads, head_dim, ctx, pool,
         softmax_scale=(1.0 / math.sqrt(head_dim)) if softmax_scale is None else softmax_scale,
         context_lens=ctx_lens.astype(np.int32), block_tables=tables, q=q,
         k_pool=k_pool, v_pool=v_pool, k_new=k_new, v_new=v_new,
-        k_scales=k_scales, v_scales=v_scales, seed=seed)
+        k_scales=k_scales, v_scales=v_scales, seed=seed, query_start_loc=qsl)
 
 
 def recipe(config: int) -> dict:
