@@ -235,6 +235,97 @@ pkv_status_t pkv_merge_partials(void* out, const float* partial_out, const float
                                 int32_t num_q_heads, int32_t head_dim, int32_t max_partitions,
                                 pkv_dtype_t out_dtype, void* stream);
 
+/*
+ * Several new tokens per sequence
+ * -------------------------------
+ * The entry points below serve a step in which sequence b brings t_b >= 0 new
+ * tokens instead of one: a chunk of a long prompt (chunked prefill), the
+ * uncached tail of a prompt whose prefix is cached, or draft tokens checked
+ * in one pass.  Their rows are stacked over sequences:
+ *   query_start_loc int32 [num_seqs + 1], non-decreasing, query_start_loc[0]
+ *                = 0 and query_start_loc[num_seqs] = num_tokens; rows
+ *                query_start_loc[b] .. query_start_loc[b+1]-1 are sequence
+ *                b's new tokens in order, t_b their count
+ *   q, out       [num_tokens, num_q_heads, head_dim]
+ *   k_new, v_new [num_tokens, num_kv_heads, head_dim] in the pool's dtype
+ * context_lens[b] counts the t_b new tokens: they take positions
+ * ctx_b - t_b .. ctx_b - 1.  Device-side contract, beyond the one above:
+ * query_start_loc as described and t_b <= max_query_len.
+ */
+
+/*
+ * pkv_kv_append_tokens - write each sequence's t_b new K and V rows into
+ * their slots: row query_start_loc[b] + j goes to position ctx_b - t_b + j
+ * (block block_tables[b][pos / block_size], slot pos % block_size), for every
+ * KV head, bit for bit.  Rows whose position would be negative, and every row
+ * of a sequence with ctx_b <= 0 or ctx_b past the table's capacity, are
+ * skipped.  With t_b = 1 for all b this is pkv_kv_append.
+ *   KV-cache post, "A KV cache in PyTorch" (the t new keys and values are
+ *   concatenated after the cached ones); 4yush post, "Adding the cache to
+ *   GPT-2" (new token r takes position start + r).
+ *
+ * k_pool, v_pool [device, written]; k_new, v_new, block_tables, context_lens,
+ * query_start_loc [device, read].  num_tokens == 0 or num_seqs == 0 is a
+ * no-op.  Supported as for pkv_kv_append.
+ */
+pkv_status_t pkv_kv_append_tokens(void* k_pool, void* v_pool, const void* k_new,
+                                  const void* v_new, const int32_t* block_tables,
+                                  const int32_t* context_lens, const int32_t* query_start_loc,
+                                  int32_t num_seqs, int32_t num_tokens, int32_t num_kv_heads,
+                                  int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                  int32_t max_blocks_per_seq, pkv_dtype_t kv_dtype,
+                                  void* stream);
+
+/*
+ * pkv_multi_query_workspace_bytes - device workspace of
+ * pkv_paged_multi_query_attention: float32 o [num_tokens, num_q_heads, maxP,
+ * head_dim] then, at the next 256-byte boundary, float32 lse [num_tokens,
+ * num_q_heads, maxP], maxP = ceil(max_context_len / partition_size) (1 when
+ * partition_size == 0).  Returns 0 when maxP <= 1 or on invalid sizes.
+ */
+size_t pkv_multi_query_workspace_bytes(int32_t num_tokens, int32_t num_q_heads,
+                                       int32_t head_dim, int32_t max_context_len,
+                                       int32_t partition_size);
+
+/*
+ * pkv_paged_multi_query_attention - every new token attends over the cached
+ * tokens up to and including its own position (call pkv_kv_append_tokens
+ * first, on the same stream): the causal mask shifted by the cache length.
+ *
+ * For row r = query_start_loc[b] + j (0 <= j < t_b) and query head i:
+ * out[r][i][:] = sum_{s < n} p_s V[b][h][s][:], p = softmax_s(softmax_scale *
+ * q[r][i] . K[b][h][s]), h = i / (num_q_heads / num_kv_heads), over the
+ * n = ctx_b - t_b + j + 1 tokens before and at its position.  A row with
+ * n <= 0 gets zeros.  Precision and dtypes as for pkv_paged_decode_attention
+ * (the matrix cores run bf16 over bf16 with 2 or more query heads per KV
+ * head); with t_b = 1 for all b the result is that of
+ * pkv_paged_decode_attention.
+ *   KV-cache post, "A KV cache in PyTorch" (the mask tril(T - t) over the
+ *   cached plus new keys); brunomaga inference post, causal_mask(Sq, Sk) =
+ *   tril(Sk - Sq); 4yush post, "Adding the cache to GPT-2".
+ *
+ * One workgroup per (sequence, KV head, tile of query columns, partition):
+ * column n of sequence b is new token n / g and head n % g of the KV head's
+ * group (g = num_q_heads / num_kv_heads), so the g*t_b queries that share a
+ * KV head read each cached block once per partition.  Partitions are merged
+ * as in pkv_paged_decode_attention.
+ *
+ * out [device, written] in q_dtype; q, pools, scales, tables, lens,
+ * query_start_loc [device, read]; workspace [device, scratch] of at least
+ * pkv_multi_query_workspace_bytes(num_tokens, ...) bytes (may be NULL when
+ * that is 0).  max_query_len: a host-side upper bound of every t_b (>= 1),
+ * used to size the grid; max_context_len as for pkv_paged_decode_attention.
+ * Supported as for pkv_paged_decode_attention.
+ */
+pkv_status_t pkv_paged_multi_query_attention(
+    void* out, const void* q, const void* k_pool, const void* v_pool, const float* k_scales,
+    const float* v_scales, const int32_t* block_tables, const int32_t* context_lens,
+    const int32_t* query_start_loc, int32_t num_seqs, int32_t num_tokens, int32_t max_query_len,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+    int32_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len,
+    float softmax_scale, int32_t partition_size, void* workspace, size_t workspace_bytes,
+    pkv_dtype_t q_dtype, pkv_dtype_t kv_dtype, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

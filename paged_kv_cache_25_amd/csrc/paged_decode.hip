@@ -132,11 +132,13 @@ struct Decode {
   float qf[kDot2 ? 1 : G][kDot2 ? 1 : KD];
   float m[G], l[G], acc[G][KD];
 
-  __device__ __forceinline__ void load_q(const char* q_base, size_t q_head_stride, int n_heads, int s) {
+  // Columns n0 .. n0+G-1 of the tile; a missing column gets a zero query.
+  __device__ __forceinline__ void load_q(const char* q, const Columns& cols, int n0, int s) {
+    constexpr size_t kQRowBytes = size_t(D) * QT::kBytes;
 #pragma unroll
     for (int i = 0; i < G; ++i) {
-      const char* row = q_base + i * q_head_stride;
-      const bool ok = i < n_heads;
+      const bool ok = cols.valid(n0 + i);
+      const char* row = q + (ok ? cols.row(n0 + i) : 0) * kQRowBytes;
       if constexpr (kDot2) {
         uint32_t tmp[W];
         if (ok) load_row<D, QT>(tmp, row, s);
@@ -154,8 +156,11 @@ struct Decode {
   }
 
   // One 16-token block: kw/vw hold this lane's two tokens (tg, tg+8).
+  // valid_toks: tokens of the block inside the context (V past it is zeroed);
+  // vis[i]: tokens of the block column i may see (uniform; used when need_mask).
   __device__ __forceinline__ void block(const uint32_t (&kw)[kTokPerLane][W],
                                         uint32_t (&vw)[kTokPerLane][W], int valid_toks,
+                                        const int (&vis)[G], bool need_mask,
                                         float k_mul, float v_mul, int tg) {
     float sc[kTokPerLane][G];
 #pragma unroll
@@ -183,12 +188,16 @@ struct Decode {
 #pragma unroll
       for (int i = 0; i < G; ++i) sc[j][i] = sum8(part[i]) * k_mul;
     }
-    if (valid_toks < kBlockSize) {            // wave-uniform: a partial or skipped block
+    if (need_mask) {                          // wave-uniform: the sequence's last block(s)
+#pragma unroll
+      for (int j = 0; j < kTokPerLane; ++j)
+#pragma unroll
+        for (int i = 0; i < G; ++i) sc[j][i] = tg + kGroups * j < vis[i] ? sc[j][i] : -INFINITY;
+    }
+    if (valid_toks < kBlockSize) {            // wave-uniform: rows past the context hold poison
 #pragma unroll
       for (int j = 0; j < kTokPerLane; ++j) {
         const bool ok = tg + kGroups * j < valid_toks;
-#pragma unroll
-        for (int i = 0; i < G; ++i) sc[j][i] = ok ? sc[j][i] : -INFINITY;
 #pragma unroll
         for (int w = 0; w < W; ++w) vw[j][w] = ok ? vw[j][w] : 0u;
       }
@@ -206,7 +215,8 @@ struct Decode {
         for (int j = 1; j < kTokPerLane; ++j) bm = fmaxf(bm, sc[j][i]);
         bm = max_over_groups8(bm);
         const float mn = fmaxf(m[i], bm);
-        const float alpha = __builtin_amdgcn_exp2f(m[i] - mn);
+        // a column with nothing visible yet keeps m = -inf (and alpha = 1)
+        const float alpha = mn == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m[i] - mn);
         l[i] *= alpha;
 #pragma unroll
         for (int k = 0; k < KD; ++k) acc[i][k] *= alpha;
@@ -219,7 +229,8 @@ struct Decode {
       to_float<D, KV>(vw[j], vf);
 #pragma unroll
       for (int i = 0; i < G; ++i) {
-        const float p = __builtin_amdgcn_exp2f(sc[j][i] - m[i]);
+        // all scores -inf so far: weight 0, not exp2(NaN)
+        const float p = __builtin_amdgcn_exp2f(sc[j][i] - (m[i] == -INFINITY ? 0.0f : m[i]));
         l[i] += p;
         const float pv = p * v_mul;
 #pragma unroll
@@ -263,24 +274,39 @@ __global__ __launch_bounds__(kWave) void paged_decode_kernel(DecodeArgs a) {
   const int append_blk = (a.k_new && raw_ctx >= 1 && raw_ctx <= cap) ? (raw_ctx - 1) / kBlockSize : -1;
   const int t_new = (raw_ctx - 1) % kBlockSize;
 
-  const int head0 = chunk * G;                          // first head of the tile within the group
-  int n_heads = a.group - head0;
-  n_heads = n_heads < G ? n_heads : G;
-  const int qh0 = h * a.group + head0;                  // first query head of the tile
+  // Column n of the tile is new token n / group, head n % group (one new token:
+  // the group's heads), n = chunk*G + i.
+  Columns cols;
+  cols.group = a.group;
+  cols.num_q_heads = a.num_q_heads;
+  cols.kv_head = h;
+  if (a.q_start) {
+    cols.row0 = a.q_start[b];
+    cols.t = a.q_start[b + 1] - cols.row0;
+  } else {
+    cols.row0 = b;
+    cols.t = 1;
+  }
+  const int n0 = chunk * G;
+  if (!cols.valid(n0)) return;                          // no column of this tile exists
 
   if (blk_begin >= blk_end && !(a.write_final && part == 0)) {   // partition past the end
-    if (a.mark_empty && lane < n_heads)
-      a.part_lse[(size_t(b) * a.num_q_heads + qh0 + lane) * a.max_partitions + part] = -INFINITY;
+    if (a.mark_empty && lane < G && cols.valid(n0 + lane))
+      a.part_lse[cols.row(n0 + lane) * a.max_partitions + part] = -INFINITY;
     return;
   }
+  // Tokens each column attends to (all ctx for a single new token); the
+  // tile's first column sees the fewest.
+  int vis_all[G];
+#pragma unroll
+  for (int i = 0; i < G; ++i) vis_all[i] = cols.valid(n0 + i) ? cols.visible(n0 + i, ctx) : ctx;
+  const int min_vis = vis_all[0];
   // A sequence whose blocks fit one partition is finished here: write the
   // final output instead of a partial (the merge skips it).
   const bool final_out = a.write_final || (a.final_single && n_blk_seq <= a.blocks_per_partition);
 
   Dec dec;
-  const size_t q_row_bytes = size_t(D) * QT::kBytes;
-  dec.load_q(reinterpret_cast<const char*>(a.q) + (size_t(b) * a.num_q_heads + qh0) * q_row_bytes,
-             q_row_bytes, n_heads, s);
+  dec.load_q(reinterpret_cast<const char*>(a.q), cols, n0, s);
 
   const int32_t* table = a.block_tables + size_t(b) * a.max_blocks_per_seq;
   const char* kbase = reinterpret_cast<const char*>(a.k_pool);
@@ -319,10 +345,15 @@ __global__ __launch_bounds__(kWave) void paged_decode_kernel(DecodeArgs a) {
     };
     auto consume = [&](uint32_t (&kw)[kTokPerLane][W], uint32_t (&vw)[kTokPerLane][W], int k) {
       const int blk = seg + k;
-      int valid = ctx - blk * kBlockSize;
+      const int first = blk * kBlockSize;
+      int valid = ctx - first;
       valid = valid < kBlockSize ? valid : kBlockSize;
       const bool ok = (ok_mask >> k) & 1;
       valid = ok ? valid : 0;
+      const bool need_mask = valid < kBlockSize || first + kBlockSize > min_vis;
+      int vis[G];
+#pragma unroll
+      for (int i = 0; i < G; ++i) vis[i] = vis_all[i] - first < valid ? vis_all[i] - first : valid;
       if (blk == append_blk && ok) {
         // Fused append: the lanes owning the new token's row take it from
         // k_new/v_new and (one writer per sequence and KV head) store it.
@@ -345,7 +376,7 @@ __global__ __launch_bounds__(kWave) void paged_decode_kernel(DecodeArgs a) {
         km *= __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_ks), k));
         vm = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_vs), k));
       }
-      dec.block(kw, vw, valid, km, vm, tg);
+      dec.block(kw, vw, valid, vis, need_mask, km, vm, tg);
     };
 
     fetch(kA, vA, 0);
@@ -368,15 +399,15 @@ __global__ __launch_bounds__(kWave) void paged_decode_kernel(DecodeArgs a) {
     for (int k = 0; k < KD; ++k) dec.acc[i][k] = sum_over_groups8(dec.acc[i][k]);
   }
 
-  // Token group i writes head i of the tile.
+  // Token group i writes column i of the tile.
 #pragma unroll
   for (int i = 0; i < G; ++i) {
-    if (tg != i || i >= n_heads) continue;
-    const int qh = qh0 + i;
+    if (tg != i || !cols.valid(n0 + i)) continue;
+    const size_t qrow = cols.row(n0 + i);
     const bool empty = lt[i] == 0.0f;        // no valid token (a NaN sum is not empty)
     const float inv = empty ? 0.0f : 1.0f / lt[i];
     if (final_out) {
-      char* orow = reinterpret_cast<char*>(a.out) + (size_t(b) * a.num_q_heads + qh) * size_t(D) * QT::kBytes;
+      char* orow = reinterpret_cast<char*>(a.out) + qrow * size_t(D) * QT::kBytes;
 #pragma unroll
       for (int k = 0; k < KD; ++k) {
         const float v = dec.acc[i][k] * inv;
@@ -384,7 +415,7 @@ __global__ __launch_bounds__(kWave) void paged_decode_kernel(DecodeArgs a) {
         else reinterpret_cast<uint16_t*>(orow)[TL::dim(s, k)] = f32_to_bf16_rne(v);
       }
     } else {
-      const size_t prow = (size_t(b) * a.num_q_heads + qh) * a.max_partitions + part;
+      const size_t prow = qrow * a.max_partitions + part;
       float* o = a.part_o + prow * D;
 #pragma unroll
       for (int k = 0; k < KD; ++k) o[TL::dim(s, k)] = dec.acc[i][k] * inv;

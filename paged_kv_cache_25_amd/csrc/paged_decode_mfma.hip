@@ -153,7 +153,11 @@ struct MfmaDecode {
   f32x4 o[T::kTiles];           // O rows 4r+i, dims 8c+e (D=128) / 4c+e (D=64)
   float m, l;                   // per head l%16 (log2 units)
 
-  __device__ __forceinline__ void block(BlockRegs<D>& br, int valid, float k_mul, int lane) {
+  // valid: tokens of the block inside the context (rows past it hold poison and
+  // are zeroed in V); vis: tokens of the block this lane's column may see
+  // (uniform need_mask says whether any column sees fewer than 16).
+  __device__ __forceinline__ void block(BlockRegs<D>& br, int valid, int vis, bool need_mask,
+                                        float k_mul, int lane) {
     const int r = lane >> 4;
     f32x4 s = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
@@ -163,11 +167,14 @@ struct MfmaDecode {
     float sc[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) sc[i] = s[i] * k_mul;
-    if (valid < 16) {                       // wave-uniform: the sequence's last block
+    if (need_mask) {                        // wave-uniform: the sequence's last block(s)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sc[i] = 4 * r + i < vis ? sc[i] : -INFINITY;
+    }
+    if (valid < 16) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const bool ok = 4 * r + i < valid;
-        sc[i] = ok ? sc[i] : -INFINITY;
 #pragma unroll
         for (int w = 0; w < T::kVWords; ++w) br.v[i][w] = ok ? br.v[i][w] : 0u;
       }
@@ -177,7 +184,8 @@ struct MfmaDecode {
       float hm = fmaxf(bm, __shfl_xor(bm, 16));
       hm = fmaxf(hm, __shfl_xor(hm, 32));
       const float mn = fmaxf(m, hm);
-      const float alpha = __builtin_amdgcn_exp2f(m - mn);
+      // a column with nothing visible yet keeps m = -inf (and alpha = 1)
+      const float alpha = mn == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m - mn);
       l *= alpha;
       m = mn;
       float a_row[4];                        // alpha of head 4r+i, held by lane 4r+i
@@ -189,8 +197,9 @@ struct MfmaDecode {
         for (int i = 0; i < 4; ++i) o[t][i] *= a_row[i];
     }
     float p[4];
+    const float m_eff = m == -INFINITY ? 0.0f : m;     // all scores -inf: weights 0, not NaN
 #pragma unroll
-    for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(sc[i] - m);
+    for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(sc[i] - m_eff);
     l += (p[0] + p[1]) + (p[2] + p[3]);
     const bf16x4 pa = {(__bf16)p[0], (__bf16)p[1], (__bf16)p[2], (__bf16)p[3]};
 #pragma unroll
@@ -208,7 +217,9 @@ struct MfmaDecode {
 };
 
 // Three waves per SIMD: 151 VGPRs for head dim 128 with two blocks in registers.
-template <int D>
+// kMulti: several new tokens per sequence (per-column visibility); otherwise
+// one new token, whose column sees the whole context.
+template <int D, bool kMulti>
 __global__ __launch_bounds__(kWave * kItemsPerWg) __attribute__((amdgpu_waves_per_eu(PKV_MFMA_WAVES_PER_EU)))
 void paged_decode_mfma_kernel(DecodeArgs a) {
   using T = MfmaTile<D>;
@@ -245,25 +256,38 @@ void paged_decode_mfma_kernel(DecodeArgs a) {
   // (a sequence outside 1 <= ctx <= capacity appends nothing, as pkv_kv_append).
   const int append_blk = (a.k_new && raw_ctx >= 1 && raw_ctx <= cap) ? (raw_ctx - 1) / kBlockSize : -1;
   const int t_new = (raw_ctx - 1) % kBlockSize;
-  const int head0 = chunk * kHeadTile;
-  int n_heads = a.group - head0;
-  n_heads = n_heads < kHeadTile ? n_heads : kHeadTile;
-  const int qh0 = h * a.group + head0;
+  // Column c of this tile: new token n / group, head n % group, n = chunk*16 + c.
+  Columns cols;
+  cols.group = a.group;
+  cols.num_q_heads = a.num_q_heads;
+  cols.kv_head = h;
+  if constexpr (kMulti) {
+    cols.row0 = a.q_start[b];
+    cols.t = a.q_start[b + 1] - cols.row0;
+  } else {
+    cols.row0 = b;
+    cols.t = 1;
+  }
+  const int n0 = chunk * kHeadTile;
+  if (!cols.valid(n0)) return;                        // no column of this tile exists
+  const int my_n = n0 + c;
+  const bool my_col = cols.valid(my_n);
 
   if (blk_begin >= blk_end && !(a.write_final && part == 0)) {   // partition past the end
-    if (a.mark_empty && lane < n_heads)
-      a.part_lse[(size_t(b) * a.num_q_heads + qh0 + lane) * a.max_partitions + part] = -INFINITY;
+    if (a.mark_empty && lane < kHeadTile && my_col)
+      a.part_lse[cols.row(my_n) * a.max_partitions + part] = -INFINITY;
     return;
   }
+  const int my_vis = kMulti && my_col ? cols.visible(my_n, ctx) : ctx;   // tokens my column attends to
+  const int min_vis = kMulti ? cols.visible(n0, ctx) : ctx;     // fewest: the tile's first column
   // A sequence whose blocks fit one partition is finished here: write the
   // final output instead of a partial (the merge skips it).
   const bool final_out = a.write_final || (a.final_single && n_blk_seq <= a.blocks_per_partition);
 
   MfmaDecode<D> dec;
   {
-    const bool ok = c < n_heads;
-    const char* qrow = reinterpret_cast<const char*>(a.q) +
-                       (size_t(b) * a.num_q_heads + qh0 + (ok ? c : 0)) * T::kRowBytes;
+    const bool ok = my_col;
+    const char* qrow = reinterpret_cast<const char*>(a.q) + (ok ? cols.row(my_n) : 0) * T::kRowBytes;
 #pragma unroll
     for (int j = 0; j < T::kSlabs; ++j) {
       uint4 w = ok ? *reinterpret_cast<const uint4*>(qrow + 64 * j + 16 * r) : make_uint4(0, 0, 0, 0);
@@ -296,10 +320,17 @@ void paged_decode_mfma_kernel(DecodeArgs a) {
       load_block<D>(br, kbase + off, vbase + off, lane);
     };
     auto consume = [&](BlockRegs<D>& br, int k) {
-      int valid = ctx - (seg + k) * kBlockSize;
+      const int first = (seg + k) * kBlockSize;
+      int valid = ctx - first;
       valid = valid < kBlockSize ? valid : kBlockSize;
       const bool ok = (ok_mask >> k) & 1;
       valid = ok ? valid : 0;
+      int vis = valid;
+      bool need_mask = valid < kBlockSize;
+      if constexpr (kMulti) {
+        vis = ok ? my_vis - first : 0;
+        need_mask = !ok || first + kBlockSize > min_vis;
+      }
       if (seg + k == append_blk && ok) {
         const size_t nrow = (size_t(b) * a.num_kv_heads + h) * T::kRowBytes;
         take_new_row<D>(br, reinterpret_cast<const char*>(a.k_new) + nrow,
@@ -311,7 +342,7 @@ void paged_decode_mfma_kernel(DecodeArgs a) {
                            reinterpret_cast<char*>(a.v_pool_w) + off, t_new, lane);
         }
       }
-      dec.block(br, valid, k_mul, lane);
+      dec.block(br, valid, vis, need_mask, k_mul, lane);
     };
 
     // Ring of kDepth register buffers: block k+kDepth-1 is requested before
@@ -329,7 +360,7 @@ void paged_decode_mfma_kernel(DecodeArgs a) {
     }
   }
 
-  // Denominator of head l%16 over the 4 lane rows; then that of head 4r+i.
+  // Denominator of column l%16 over the 4 lane rows; then that of column 4r+i.
   float lt = dec.l + __shfl_xor(dec.l, 16);
   lt += __shfl_xor(lt, 32);
   float l_row[4], m_row[4];
@@ -341,14 +372,13 @@ void paged_decode_mfma_kernel(DecodeArgs a) {
   constexpr int kDimsPerLane = D / 16;       // dims dpl*c .. dpl*c + dpl-1 of each head row
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int hh = 4 * r + i;
-    if (hh >= n_heads) continue;
-    const int qh = qh0 + hh;
+    const int n = n0 + 4 * r + i;                      // output row 4r+i is column n
+    if (!cols.valid(n)) continue;
+    const size_t qrow = cols.row(n);
     const bool empty = l_row[i] == 0.0f;
     const float inv = empty ? 0.0f : 1.0f / l_row[i];
     if (final_out) {
-      uint16_t* orow = reinterpret_cast<uint16_t*>(a.out) + (size_t(b) * a.num_q_heads + qh) * D +
-                       kDimsPerLane * c;
+      uint16_t* orow = reinterpret_cast<uint16_t*>(a.out) + qrow * D + kDimsPerLane * c;
       uint32_t packed[kDimsPerLane / 2];
 #pragma unroll
       for (int e = 0; e < kDimsPerLane; e += 2)
@@ -359,7 +389,7 @@ void paged_decode_mfma_kernel(DecodeArgs a) {
       else
         *reinterpret_cast<uint2*>(orow) = make_uint2(packed[0], packed[1]);
     } else {
-      const size_t prow = (size_t(b) * a.num_q_heads + qh) * a.max_partitions + part;
+      const size_t prow = qrow * a.max_partitions + part;
       float* op = a.part_o + prow * D + kDimsPerLane * c;
 #pragma unroll
       for (int e = 0; e < kDimsPerLane; e += 4)
@@ -377,8 +407,12 @@ hipError_t launch_d(const DecodeArgs& a, hipStream_t stream) {
   if (grid == 0) return hipSuccess;
   if (grid > 0x7fffffffu) return hipErrorInvalidConfiguration;
   const size_t wgs = (grid + kItemsPerWg - 1) / kItemsPerWg;
-  hipLaunchKernelGGL((paged_decode_mfma_kernel<D>), dim3(unsigned(wgs)), dim3(kWave * kItemsPerWg), 0,
-                     stream, a);
+  if (a.q_start)
+    hipLaunchKernelGGL((paged_decode_mfma_kernel<D, true>), dim3(unsigned(wgs)),
+                       dim3(kWave * kItemsPerWg), 0, stream, a);
+  else
+    hipLaunchKernelGGL((paged_decode_mfma_kernel<D, false>), dim3(unsigned(wgs)),
+                       dim3(kWave * kItemsPerWg), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -33,9 +33,10 @@ int64_t max_partitions(int32_t max_context_len, int32_t partition_size) {
   return (int64_t(max_context_len) + partition_size - 1) / partition_size;
 }
 
-// Query heads handled by one workgroup: the group size rounded up to a power
-// of two, at most 8 for head_dim 64 and 4 for head_dim 128 (the per-lane
-// accumulators must stay in registers); larger groups are split into tiles.
+// Query columns (heads of a group, times new tokens) handled by one vector
+// workgroup: their count rounded up to a power of two, at most 8 for head_dim
+// 64 and 4 for head_dim 128 (the per-lane accumulators must stay in
+// registers); more columns are split into tiles.
 int tile_heads(int group, int head_dim) {
   const int cap = head_dim == 64 ? 8 : 4;
   int t = 1;
@@ -73,22 +74,28 @@ const char* pkv_status_string(int status) {
   }
 }
 
-pkv_status_t pkv_kv_append(void* k_pool, void* v_pool, const void* k_new, const void* v_new,
-                           const int32_t* block_tables, const int32_t* context_lens,
-                           int32_t num_seqs, int32_t num_kv_heads, int32_t head_dim,
-                           int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
-                           pkv_dtype_t kv_dtype, void* stream) {
-  if (num_seqs < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks <= 0 ||
-      max_blocks_per_seq <= 0 || !dtype_ok(kv_dtype))
+}  // extern "C"
+
+namespace {
+
+// Both appends: q_start == nullptr means one new row per sequence.
+pkv_status_t append_impl(void* k_pool, void* v_pool, const void* k_new, const void* v_new,
+                         const int32_t* block_tables, const int32_t* context_lens,
+                         const int32_t* q_start, int32_t num_seqs, int32_t num_rows,
+                         int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                         int32_t num_blocks, int32_t max_blocks_per_seq, pkv_dtype_t kv_dtype,
+                         void* stream) {
+  if (num_seqs < 0 || num_rows < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
+      num_blocks <= 0 || max_blocks_per_seq <= 0 || !dtype_ok(kv_dtype))
     return PKV_ERR_INVALID_ARG;
   if (!head_dim_ok(head_dim) || block_size != pkv::kBlockSizeBuilt) return PKV_ERR_UNSUPPORTED;
-  if (num_seqs == 0) return PKV_OK;
+  if (num_seqs == 0 || num_rows == 0) return PKV_OK;
   if (!k_pool || !v_pool || !k_new || !v_new || !block_tables || !context_lens)
     return PKV_ERR_INVALID_ARG;
   if (!aligned16(k_pool) || !aligned16(v_pool) || !aligned16(k_new) || !aligned16(v_new) ||
-      !aligned4(block_tables) || !aligned4(context_lens))
+      !aligned4(block_tables) || !aligned4(context_lens) || !aligned4(q_start))
     return PKV_ERR_INVALID_ARG;
-  pkv::AppendArgs a;
+  pkv::AppendArgs a{};
   a.k_pool = k_pool;
   a.v_pool = v_pool;
   a.k_new = k_new;
@@ -100,8 +107,37 @@ pkv_status_t pkv_kv_append(void* k_pool, void* v_pool, const void* k_new, const 
   a.row_bytes = head_dim * pkv::dtype_bytes(to_internal(kv_dtype));
   a.num_blocks = num_blocks;
   a.max_blocks_per_seq = max_blocks_per_seq;
+  a.q_start = q_start;
+  a.num_rows = num_rows;
   return pkv::launch_kv_append(a, static_cast<hipStream_t>(stream)) == hipSuccess ? PKV_OK
                                                                                   : PKV_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+pkv_status_t pkv_kv_append(void* k_pool, void* v_pool, const void* k_new, const void* v_new,
+                           const int32_t* block_tables, const int32_t* context_lens,
+                           int32_t num_seqs, int32_t num_kv_heads, int32_t head_dim,
+                           int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
+                           pkv_dtype_t kv_dtype, void* stream) {
+  return append_impl(k_pool, v_pool, k_new, v_new, block_tables, context_lens, nullptr, num_seqs,
+                     num_seqs, num_kv_heads, head_dim, block_size, num_blocks,
+                     max_blocks_per_seq, kv_dtype, stream);
+}
+
+pkv_status_t pkv_kv_append_tokens(void* k_pool, void* v_pool, const void* k_new,
+                                  const void* v_new, const int32_t* block_tables,
+                                  const int32_t* context_lens, const int32_t* query_start_loc,
+                                  int32_t num_seqs, int32_t num_tokens, int32_t num_kv_heads,
+                                  int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                  int32_t max_blocks_per_seq, pkv_dtype_t kv_dtype,
+                                  void* stream) {
+  if (num_seqs > 0 && num_tokens > 0 && !query_start_loc) return PKV_ERR_INVALID_ARG;
+  return append_impl(k_pool, v_pool, k_new, v_new, block_tables, context_lens, query_start_loc,
+                     num_seqs, num_tokens, num_kv_heads, head_dim, block_size, num_blocks,
+                     max_blocks_per_seq, kv_dtype, stream);
 }
 
 size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
@@ -110,6 +146,15 @@ size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t
   const int64_t maxp = max_partitions(max_context_len, partition_size);
   if (maxp <= 1) return 0;
   return part_layout(num_seqs, num_q_heads, head_dim, maxp).total;
+}
+
+size_t pkv_multi_query_workspace_bytes(int32_t num_tokens, int32_t num_q_heads,
+                                       int32_t head_dim, int32_t max_context_len,
+                                       int32_t partition_size) {
+  // The partial results are laid out per query row, exactly as the
+  // one-token workspace is per sequence.
+  return pkv_decode_workspace_bytes(num_tokens, num_q_heads, head_dim, max_context_len,
+                                    partition_size);
 }
 
 }  // extern "C"
@@ -142,10 +187,11 @@ pkv_status_t check_decode(const void* q, const void* k_pool, const void* v_pool,
   return PKV_OK;
 }
 
-// bf16 queries over a bf16 cache with a shared KV head run on the matrix
-// cores; every other combination on the vector kernel.
-bool uses_mfma(pkv_dtype_t q_dtype, pkv_dtype_t kv_dtype, int group) {
-  return q_dtype == PKV_BF16 && kv_dtype == PKV_BF16 && group >= 2;
+// bf16 queries over a bf16 cache run on the matrix cores when 2 or more
+// queries share each KV head (the group's heads times the new tokens); every
+// other combination on the vector kernel.
+bool uses_mfma(pkv_dtype_t q_dtype, pkv_dtype_t kv_dtype, int64_t columns) {
+  return q_dtype == PKV_BF16 && kv_dtype == PKV_BF16 && columns >= 2;
 }
 
 pkv::DecodeArgs decode_args(const void* q, const void* k_pool, const void* v_pool,
@@ -314,6 +360,79 @@ pkv_status_t pkv_paged_decode_partials(
                        static_cast<hipStream_t>(stream)) == hipSuccess
              ? PKV_OK
              : PKV_ERR_HIP;
+}
+
+pkv_status_t pkv_paged_multi_query_attention(
+    void* out, const void* q, const void* k_pool, const void* v_pool, const float* k_scales,
+    const float* v_scales, const int32_t* block_tables, const int32_t* context_lens,
+    const int32_t* query_start_loc, int32_t num_seqs, int32_t num_tokens, int32_t max_query_len,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+    int32_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len,
+    float softmax_scale, int32_t partition_size, void* workspace, size_t workspace_bytes,
+    pkv_dtype_t q_dtype, pkv_dtype_t kv_dtype, void* stream) {
+  if (max_context_len < 0 || num_tokens < 0 || max_query_len < 0) return PKV_ERR_INVALID_ARG;
+  // No new token anywhere: sizes are checked, pointers are not needed.
+  const pkv_status_t st0 = check_decode(q, k_pool, v_pool, k_scales, v_scales, block_tables,
+                                        context_lens, num_tokens == 0 ? 0 : num_seqs,
+                                        num_q_heads, num_kv_heads,
+                                        head_dim, block_size, num_blocks, max_blocks_per_seq,
+                                        softmax_scale, partition_size, q_dtype, kv_dtype);
+  if (st0 != PKV_OK || num_seqs == 0 || num_tokens == 0) return st0;
+  if (max_query_len < 1) return PKV_ERR_INVALID_ARG;
+  if (!out || !query_start_loc || !aligned16(out) || !aligned16(workspace) ||
+      !aligned4(query_start_loc))
+    return PKV_ERR_INVALID_ARG;
+
+  const int64_t maxp = max_partitions(max_context_len, partition_size);
+  const bool single = maxp <= 1;
+  const int group = num_q_heads / num_kv_heads;
+  const int64_t columns = int64_t(max_query_len) * group;     // queries per KV head
+  const bool mfma = uses_mfma(q_dtype, kv_dtype, columns);
+  const int tile = mfma ? pkv::mfma_head_tile()
+                        : tile_heads(columns < (1 << 20) ? int(columns) : (1 << 20), head_dim);
+  const int64_t chunks = (columns + tile - 1) / tile;
+  if (chunks > 0x7fffffff) return PKV_ERR_INVALID_ARG;
+
+  pkv::DecodeArgs a = decode_args(q, k_pool, v_pool, k_scales, v_scales, block_tables,
+                                  context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                  num_blocks, max_blocks_per_seq, softmax_scale, tile);
+  a.out = out;
+  a.q_start = query_start_loc;
+  a.max_q = max_query_len;
+  a.head_chunks = int(chunks);
+  if (!single) {
+    const PartLayout L = part_layout(num_tokens, num_q_heads, head_dim, maxp);
+    if (!workspace || workspace_bytes < L.total) return PKV_ERR_WORKSPACE;
+    a.part_o = static_cast<float*>(workspace);
+    a.part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + L.lse_offset);
+  }
+  a.blocks_per_partition =
+      single ? max_blocks_per_seq : partition_size / block_size;
+  a.max_partitions = int(maxp);
+  a.write_final = single ? 1 : 0;
+  // Every (row, partition) of the workspace is written, empty ones as lse =
+  // -inf, so the merge below needs no per-row partition count.
+  a.final_single = 0;
+  a.mark_empty = 1;
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (launch_decode(a, head_dim, tile, mfma, q_dtype, kv_dtype, st) != hipSuccess)
+    return PKV_ERR_HIP;
+  if (single) return PKV_OK;
+
+  pkv::MergeArgs m;
+  m.out = out;
+  m.part_o = a.part_o;
+  m.part_lse = a.part_lse;
+  m.num_partitions = nullptr;
+  m.context_lens = nullptr;
+  m.partition_size = partition_size;
+  m.num_seqs = num_tokens;
+  m.num_q_heads = num_q_heads;
+  m.max_partitions = int(maxp);
+  m.skip_single = 0;
+  return pkv::launch_merge(m, head_dim, to_internal(q_dtype), st) == hipSuccess ? PKV_OK
+                                                                                : PKV_ERR_HIP;
 }
 
 pkv_status_t pkv_merge_partials(void* out, const float* partial_out, const float* partial_lse,

@@ -21,6 +21,10 @@ struct AppendArgs {
   const int32_t* block_tables;
   const int32_t* context_lens;
   int num_seqs, num_kv_heads, row_bytes, num_blocks, max_blocks_per_seq;
+  // Several new tokens per sequence: rows q_start[b] .. q_start[b+1]-1 of
+  // k_new/v_new (num_rows rows in all) belong to sequence b.  Null: one row each.
+  const int32_t* q_start;
+  int num_rows;
 };
 
 struct DecodeArgs {
@@ -41,6 +45,10 @@ struct DecodeArgs {
   const void* v_new;
   void* k_pool_w;
   void* v_pool_w;
+  // Several new tokens per sequence (null: one each, row b of q and out).
+  // Rows q_start[b] .. q_start[b+1]-1 of q/out are sequence b's newest tokens.
+  const int32_t* q_start;
+  int max_q;                  // most new tokens of any sequence (1 without q_start)
   int num_seqs, num_q_heads, num_kv_heads, group, head_chunks;
   int num_blocks, max_blocks_per_seq;
   int blocks_per_partition;   // partition size / 16
@@ -49,6 +57,20 @@ struct DecodeArgs {
   int write_final;            // every sequence has one partition: write `out`
   int final_single;           // a sequence with one partition writes `out` (the merge skips it)
   int mark_empty;             // partitions past a sequence's end write lse = -inf
+};
+
+// The columns of one (sequence, KV head) work item: column n is new token
+// j = n / group of the sequence (of t) and query head i = n % group of the KV
+// head's group.  Token j sees the cached tokens up to its own position.
+struct Columns {
+  int group, t, row0, num_q_heads, kv_head;
+  __host__ __device__ bool valid(int n) const { return n < t * group; }
+  // row of the [tokens, q heads] arrays (q, out, partials)
+  __host__ __device__ size_t row(int n) const {
+    return size_t(row0 + n / group) * num_q_heads + size_t(kv_head) * group + n % group;
+  }
+  // cached tokens column n attends to
+  __host__ __device__ int visible(int n, int ctx) const { return ctx - t + n / group + 1; }
 };
 
 struct MergeArgs {

@@ -58,6 +58,14 @@ def load():
                                             ctypes.c_int, ctypes.c_int, P]
     L.pkv_merge_partials.restype = ctypes.c_int
     L.pkv_merge_partials.argtypes = [P, P, P, P, I, I, I, I, ctypes.c_int, P]
+    L.pkv_kv_append_tokens.restype = ctypes.c_int
+    L.pkv_kv_append_tokens.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, ctypes.c_int, P]
+    L.pkv_multi_query_workspace_bytes.restype = Z
+    L.pkv_multi_query_workspace_bytes.argtypes = [I, I, I, I, I]
+    L.pkv_paged_multi_query_attention.restype = ctypes.c_int
+    L.pkv_paged_multi_query_attention.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I,
+                                                  I, I, I, F, I, P, Z, ctypes.c_int,
+                                                  ctypes.c_int, P]
     _lib = L
     return L
 
@@ -185,4 +193,52 @@ def decode_step(out, q, k_pool, v_pool, k_new, v_new, block_tables, context_lens
         block_tables.shape[1], int(max_context_len), float(softmax_scale), int(partition_size),
         _ptr(workspace), workspace.numel(), dtype_code(q.dtype), dtype_code(k_pool.dtype),
         _stream(stream)))
+    return out
+
+
+def kv_append_tokens(k_pool, v_pool, k_new, v_new, block_tables, context_lens, query_start_loc,
+                     stream=None):
+    """Write rows qsl[b] .. qsl[b+1]-1 of k_new/v_new [T, Hkv, D] into positions
+    ctx_b - t_b .. ctx_b - 1 of sequence b (pkv_kv_append_tokens)."""
+    _need_cuda(k_pool, v_pool, k_new, v_new, block_tables, context_lens, query_start_loc)
+    nb, hkv, bs, d = k_pool.shape
+    B = block_tables.shape[0]
+    if k_new.dtype != k_pool.dtype or v_new.dtype != v_pool.dtype or k_pool.dtype != v_pool.dtype:
+        raise TypeError("k_new/v_new must have the pool's dtype")
+    if query_start_loc.shape[0] != B + 1 or k_new.shape[0] != v_new.shape[0]:
+        raise ValueError("query_start_loc must have num_seqs + 1 entries")
+    _check("pkv_kv_append_tokens", load().pkv_kv_append_tokens(
+        _ptr(k_pool), _ptr(v_pool), _ptr(k_new), _ptr(v_new), _ptr(block_tables),
+        _ptr(context_lens), _ptr(query_start_loc), B, k_new.shape[0], hkv, d, bs, nb,
+        block_tables.shape[1], dtype_code(k_pool.dtype), _stream(stream)))
+
+
+def multi_query_workspace_bytes(num_tokens, num_q_heads, head_dim, max_context_len,
+                                partition_size):
+    return int(load().pkv_multi_query_workspace_bytes(num_tokens, num_q_heads, head_dim,
+                                                      max_context_len, partition_size))
+
+
+def paged_multi_query_attention(out, q, k_pool, v_pool, block_tables, context_lens,
+                                query_start_loc, max_query_len, max_context_len, softmax_scale,
+                                partition_size=512, k_scales=None, v_scales=None, workspace=None,
+                                stream=None):
+    """out[T, Hq, D] (q's dtype): row qsl[b] + j attends over the first
+    ctx_b - t_b + j + 1 cached tokens of sequence b (pkv_paged_multi_query_attention)."""
+    _need_cuda(out, q, k_pool, v_pool, block_tables, context_lens, query_start_loc, k_scales,
+               v_scales, workspace)
+    T, hq, d = q.shape
+    nb, hkv, bs, _ = k_pool.shape
+    B = block_tables.shape[0]
+    if query_start_loc.shape[0] != B + 1:
+        raise ValueError("query_start_loc must have num_seqs + 1 entries")
+    if workspace is None:
+        n = multi_query_workspace_bytes(T, hq, d, max_context_len, partition_size)
+        workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=q.device)
+    _check("pkv_paged_multi_query_attention", load().pkv_paged_multi_query_attention(
+        _ptr(out), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(k_scales), _ptr(v_scales),
+        _ptr(block_tables), _ptr(context_lens), _ptr(query_start_loc), B, T, int(max_query_len),
+        hq, hkv, d, bs, nb, block_tables.shape[1], int(max_context_len), float(softmax_scale),
+        int(partition_size), _ptr(workspace), workspace.numel(), dtype_code(q.dtype),
+        dtype_code(k_pool.dtype), _stream(stream)))
     return out

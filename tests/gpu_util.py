@@ -152,3 +152,59 @@ def check_tolerance(kv_dtype, gpu, ref, label="", out_dtype="f32"):
         assert mx <= 6e-2, f"{label}: max abs err {mx}"
     log(f"[parity] {label}: max|gpu-oracle| = {mx:.3e}")
     return mx
+
+
+class DeviceMultiStep:
+    """A workload with several new tokens per sequence on the device: append
+    them (pkv_kv_append_tokens), then attend (pkv_paged_multi_query_attention)."""
+
+    def __init__(self, inp, device="cuda"):
+        assert inp.query_start_loc is not None
+        self.inp = inp
+        self.q = dev_tensor(inp.q, inp.q_dtype, device)
+        self.k_pool = dev_tensor(inp.k_pool, inp.kv_dtype, device)
+        self.v_pool = dev_tensor(inp.v_pool, inp.kv_dtype, device)
+        self.k_new = dev_tensor(inp.k_new, inp.kv_dtype, device)
+        self.v_new = dev_tensor(inp.v_new, inp.kv_dtype, device)
+        self.tables = dev_tensor(inp.block_tables, None, device)
+        self.lens = dev_tensor(inp.context_lens, None, device)
+        self.qsl = dev_tensor(inp.query_start_loc.astype(np.int32), None, device)
+        self.k_scales = None if inp.k_scales is None else dev_tensor(inp.k_scales, None, device)
+        self.v_scales = None if inp.v_scales is None else dev_tensor(inp.v_scales, None, device)
+        self.out = torch.empty(inp.total_queries, inp.num_q_heads, inp.head_dim,
+                               dtype=TORCH_DT[inp.q_dtype], device=device)
+
+    def append(self):
+        ops.kv_append_tokens(self.k_pool, self.v_pool, self.k_new, self.v_new, self.tables,
+                             self.lens, self.qsl)
+
+    def attend(self, partition_size=None, max_query_len=None):
+        inp = self.inp
+        P = inp.partition_size if partition_size is None else partition_size
+        mq = max(inp.max_new_tokens, 1) if max_query_len is None else max_query_len
+        ops.paged_multi_query_attention(self.out, self.q, self.k_pool, self.v_pool, self.tables,
+                                        self.lens, self.qsl, mq, inp.max_context_len,
+                                        inp.softmax_scale, P, self.k_scales, self.v_scales)
+        return self.out
+
+    def step(self, partition_size=None):
+        self.append()
+        out = self.attend(partition_size)
+        torch.cuda.synchronize()
+        return out
+
+    def out_f64(self):
+        return self.out.detach().float().cpu().double().numpy()
+
+
+def oracle_multi(inp, pools=None):
+    """Oracle output (float64, [total, Hq, D]) after appending the new tokens."""
+    if pools is None:
+        pools = pa.kv_append_tokens(inp.k_pool, inp.v_pool, inp.k_new, inp.v_new,
+                                    inp.block_tables, inp.context_lens, inp.query_start_loc,
+                                    inp.block_size)
+    return pa.multi_query_attention(inp.q, pools[0], pools[1], inp.block_tables,
+                                    inp.context_lens, inp.query_start_loc,
+                                    block_size=inp.block_size, softmax_scale=inp.softmax_scale,
+                                    q_dtype=inp.q_dtype, kv_dtype=inp.kv_dtype,
+                                    k_scales=inp.k_scales, v_scales=inp.v_scales)

@@ -34,7 +34,8 @@ def test_header_declares_the_entry_points():
     assert declared_functions() == sorted([
         "pkv_abi_version", "pkv_status_string", "pkv_kv_append", "pkv_decode_workspace_bytes",
         "pkv_paged_decode_attention", "pkv_paged_decode_step", "pkv_paged_decode_partials",
-        "pkv_merge_partials"])
+        "pkv_merge_partials", "pkv_kv_append_tokens", "pkv_multi_query_workspace_bytes",
+        "pkv_paged_multi_query_attention"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -174,6 +175,58 @@ def test_merge_validation(lib):
     assert f(FAKE, FAKE, FAKE, None, 2, 4, 96, 3, ops.PKV_BF16, None) == UNSUPPORTED
     assert f(FAKE, FAKE, FAKE, None, 2, 4, 128, 3, ops.PKV_FP8_E4M3, None) == UNSUPPORTED
     assert f(None, None, None, None, 0, 4, 128, 3, ops.PKV_F32, None) == OK
+
+
+def _append_tokens(lib, **over):
+    a = dict(k_pool=FAKE, v_pool=FAKE, k_new=FAKE, v_new=FAKE, tables=FAKE, lens=FAKE, qsl=FAKE,
+             B=2, T=5, hkv=2, d=128, bs=16, nb=8, mbps=4, kv=ops.PKV_BF16)
+    a.update(over)
+    return lib.pkv_kv_append_tokens(a["k_pool"], a["v_pool"], a["k_new"], a["v_new"],
+                                    a["tables"], a["lens"], a["qsl"], a["B"], a["T"], a["hkv"],
+                                    a["d"], a["bs"], a["nb"], a["mbps"], a["kv"], None)
+
+
+def test_append_tokens_validation(lib):
+    assert _append_tokens(lib, qsl=None) == INVALID
+    assert _append_tokens(lib, qsl=ctypes.c_void_p(0x10002)) == INVALID
+    assert _append_tokens(lib, k_new=ctypes.c_void_p(0x10008)) == INVALID
+    assert _append_tokens(lib, T=-1) == INVALID
+    assert _append_tokens(lib, hkv=0) == INVALID
+    assert _append_tokens(lib, d=96) == UNSUPPORTED
+    assert _append_tokens(lib, T=0, k_pool=None, qsl=None) == OK     # no new rows
+    assert _append_tokens(lib, B=0, k_pool=None, qsl=None) == OK
+
+
+def _multi(lib, **over):
+    a = dict(out=FAKE, q=FAKE, kp=FAKE, vp=FAKE, ks=None, vs=None, tables=FAKE, lens=FAKE,
+             qsl=FAKE, B=2, T=6, maxq=4, hq=8, hkv=2, d=128, bs=16, nb=8, mbps=4, maxctx=64,
+             scale=0.088, P=16, ws=None, wsb=0, qt=ops.PKV_BF16, kvt=ops.PKV_BF16)
+    a.update(over)
+    return lib.pkv_paged_multi_query_attention(
+        a["out"], a["q"], a["kp"], a["vp"], a["ks"], a["vs"], a["tables"], a["lens"], a["qsl"],
+        a["B"], a["T"], a["maxq"], a["hq"], a["hkv"], a["d"], a["bs"], a["nb"], a["mbps"],
+        a["maxctx"], a["scale"], a["P"], a["ws"], a["wsb"], a["qt"], a["kvt"], None)
+
+
+def test_multi_query_validation(lib):
+    need = lib.pkv_multi_query_workspace_bytes(6, 8, 128, 64, 16)
+    assert need == lib.pkv_decode_workspace_bytes(6, 8, 128, 64, 16) > 0
+    assert _multi(lib, qsl=None, ws=FAKE, wsb=need) == INVALID
+    assert _multi(lib, qsl=ctypes.c_void_p(0x10002), ws=FAKE, wsb=need) == INVALID
+    assert _multi(lib, maxq=0, ws=FAKE, wsb=need) == INVALID
+    assert _multi(lib, maxq=-1) == INVALID
+    assert _multi(lib, T=-1) == INVALID
+    assert _multi(lib, maxctx=-1) == INVALID
+    assert _multi(lib, hq=6, hkv=4) == INVALID
+    assert _multi(lib, P=24) == INVALID
+    assert _multi(lib, d=96) == UNSUPPORTED
+    assert _multi(lib, qt=ops.PKV_FP8_E4M3) == UNSUPPORTED
+    assert _multi(lib, kvt=ops.PKV_FP8_E4M3) == INVALID        # e4m3 without scales
+    assert _multi(lib, out=ctypes.c_void_p(0x10008), ws=FAKE, wsb=need) == INVALID
+    assert _multi(lib) == WORKSPACE                            # 4 partitions, no workspace
+    assert _multi(lib, ws=FAKE, wsb=need - 1) == WORKSPACE
+    assert _multi(lib, B=0, q=None, qsl=None) == OK
+    assert _multi(lib, T=0, q=None, qsl=None) == OK
 
 
 def test_binding_refuses_cpu_tensors():

@@ -1,0 +1,195 @@
+"""GPU parity of several new tokens per sequence: pkv_kv_append_tokens then
+pkv_paged_multi_query_attention, against the oracle's kv_append_tokens and
+multi_query_attention (the causal mask shifted by the cache length).
+
+Covers both kernels (matrix cores for bf16 over bf16 with 2+ queries per KV
+head, the vector kernel otherwise), column tiles that span several new tokens
+and a ragged last tile, partition boundaries inside the new tokens,
+sequences with no new token, rows that see nothing, a prompt prefilled in
+chunks, and the one-token case against the decode entry point bit for bit."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.paged_attention as pa
+from tests.gpu_util import (DeviceMultiStep, DeviceStep, check_tolerance, host_storage, log,
+                            oracle_multi)
+from workloads import make_inputs, named_config
+
+pytestmark = pytest.mark.gpu
+
+
+def _shape(config, **over):
+    """A named workload's head layout and dtypes, with a small batch."""
+    from workloads.configs import recipe
+    r = recipe(config)
+    r.update(over)
+    return r
+
+
+def _same_bits(a, b):
+    """Bitwise equality (the pools hold NaN poison, which == would reject)."""
+    return a.dtype == b.dtype and a.shape == b.shape and np.array_equal(
+        np.ascontiguousarray(a).view(np.uint8), np.ascontiguousarray(b).view(np.uint8))
+
+
+def _check(inp, label, partition_size=None):
+    log(f"[case] {label}: B={inp.num_seqs} T={inp.total_queries} maxq={inp.max_new_tokens} "
+        f"g={inp.group_size} D={inp.head_dim} {inp.q_dtype}/{inp.kv_dtype} "
+        f"P={inp.partition_size if partition_size is None else partition_size}")
+    dev = DeviceMultiStep(inp)
+    gpu = dev.step(partition_size).detach().float().cpu().double().numpy()
+    pools = pa.kv_append_tokens(inp.k_pool, inp.v_pool, inp.k_new, inp.v_new, inp.block_tables,
+                                inp.context_lens, inp.query_start_loc, inp.block_size)
+    ref = oracle_multi(inp, pools)
+    check_tolerance(inp.kv_dtype, gpu, ref, label, out_dtype=inp.q_dtype)
+    # the append is a bitwise scatter: the pools match the oracle's exactly
+    assert _same_bits(host_storage(dev.k_pool), pools[0])
+    assert _same_bits(host_storage(dev.v_pool), pools[1])
+    return dev, gpu, ref
+
+
+@pytest.mark.parametrize("t", [1, 2, 4, 5, 8, 16])
+def test_fixed_new_tokens_f32(t):
+    """Tiny f32 MHA workload (vector kernel), every sequence with t new tokens."""
+    r = _shape(1)
+    r["ctx"] = ("fixed", [17, 33, 64, 100])
+    inp = make_inputs(seed=10 + t, name=f"tiny_f32_t{t}", new_tokens=("const", t), **r)
+    _check(inp, f"f32 t={t}")
+    _check(inp, f"f32 t={t} P=32", partition_size=32)
+
+
+@pytest.mark.parametrize("t", [1, 2, 4, 5, 8, 16])
+def test_fixed_new_tokens_gqa_bf16(t):
+    """Llama-3-8B heads (g=4) in bf16: the matrix-core kernel; 16-column tiles
+    hold 4 new tokens, so t=5 leaves a ragged tile."""
+    inp = named_config(2, seed=20 + t, num_seqs=6, ctx=("uniform", 16, 1400),
+                       new_tokens=("const", t), name=f"gqa_bf16_t{t}")
+    _check(inp, f"gqa bf16 t={t}")
+    _check(inp, f"gqa bf16 t={t} P=64", partition_size=64)
+
+
+@pytest.mark.parametrize("group,head_dim,dtypes", [
+    (1, 128, ("bf16", "bf16")),      # MHA: the matrix cores serve t tokens of one head
+    (1, 128, ("bf16", "fp8_e4m3")),  # fp8 MHA (vector kernel)
+    (4, 128, ("f32", "bf16")),
+    (8, 64, ("bf16", "bf16")),
+    (8, 64, ("f32", "f32")),
+    (2, 64, ("bf16", "fp8_e4m3")),
+])
+def test_group_and_dtype_mix(group, head_dim, dtypes):
+    qd, kd = dtypes
+    hkv = 4
+    inp = make_inputs(num_seqs=5, num_q_heads=hkv * group, num_kv_heads=hkv, head_dim=head_dim,
+                      ctx=("uniform", 1, 700), pool=("used_fraction", 0.8), q_dtype=qd,
+                      kv_dtype=kd, partition_size=128, seed=30 + group,
+                      new_tokens=("uniform", 1, 9), name=f"g{group}_d{head_dim}_{qd}_{kd}")
+    _check(inp, inp.name)
+
+
+def test_ragged_new_tokens_and_empty_sequences():
+    """t_b from 0 to 33 in one batch: sequences with no new token produce no
+    rows; a 33-token tail spans three 16-column tiles even at g=1 ... g=4."""
+    r = _shape(2, num_seqs=7, ctx=("fixed", [5, 300, 40, 1030, 33, 600, 100]))
+    r["new_tokens"] = ("fixed", [3, 0, 33, 1, 16, 0, 7])
+    inp = make_inputs(seed=41, name="ragged", **r)
+    assert inp.total_queries == 60
+    _check(inp, "ragged bf16 P=512")
+    _check(inp, "ragged bf16 P=32", partition_size=32)
+    r.update(q_dtype="f32", kv_dtype="f32")
+    _check(make_inputs(seed=41, name="ragged_f32", **r), "ragged f32", partition_size=48)
+
+
+def test_prefill_from_empty_cache():
+    """ctx == t: the whole prompt is new (plain causal attention)."""
+    inp = named_config(2, seed=50, num_seqs=3, ctx=("fixed", [40, 77, 16]),
+                       new_tokens=("fixed", [40, 77, 16]), name="prefill")
+    _check(inp, "prefill bf16")
+    _check(inp, "prefill bf16 P=16", partition_size=16)
+
+
+def test_rows_that_see_nothing():
+    """A context shorter than the new tokens (ctx < t): rows whose position
+    would be negative are not appended and attend to nothing (zeros)."""
+    r = _shape(1)
+    inp = make_inputs(seed=60, name="short", ctx=("fixed", [20, 40, 64, 100]),
+                      new_tokens=("fixed", [6, 2, 9, 4]),
+                      **{k: v for k, v in r.items() if k != "ctx"})
+    inp.context_lens[0] = 3          # 6 new rows, 3 positions: rows 0..2 see nothing
+    inp.context_lens[2] = 5
+    _, gpu, ref = _check(inp, "ctx < t")
+    assert np.all(gpu[0:3] == 0) and np.all(ref[0:3] == 0)
+
+
+def test_one_token_matches_decode_entry_point():
+    """With t_b = 1 everywhere the multi-token entry point computes exactly
+    what the decode entry point does (same kernels, same rounding)."""
+    for cfg, label in ((2, "gqa bf16"), (5, "fp8 mha"), (1, "f32")):
+        over = dict(num_seqs=8) if cfg != 1 else {}
+        if cfg == 5:
+            over["ctx"] = ("uniform", 100, 1500)
+        one = named_config(cfg, seed=70 + cfg, **over)
+        multi = named_config(cfg, seed=70 + cfg, new_tokens=("const", 1), **over)
+        assert np.array_equal(one.context_lens, multi.context_lens)
+        assert _same_bits(one.q, multi.q) and _same_bits(one.k_new, multi.k_new)
+        a = DeviceStep(one).step().detach().cpu()
+        dm = DeviceMultiStep(multi)
+        b = dm.step().detach().cpu()
+        log(f"[case] t=1 {label}: bit-identical {torch.equal(a, b)}")
+        assert torch.equal(a, b), label
+
+
+def test_chunked_prefill_equals_one_pass():
+    """A prompt written and attended in chunks (6, 1, 1, 9, 16, 3 tokens) gives
+    the oracle's one-pass causal attention over the whole prompt, row by row."""
+    chunks = [6, 1, 1, 9, 16, 3]
+    total = sum(chunks)
+    full = named_config(2, seed=80, num_seqs=1, ctx=("const", total),
+                        new_tokens=("const", total), name="prefill_one_pass")
+    ref = oracle_multi(full)
+    dev = DeviceMultiStep(full)
+    rows = []
+    done = 0
+    qsl = torch.zeros(2, dtype=torch.int32, device="cuda")
+    lens = torch.zeros(1, dtype=torch.int32, device="cuda")
+    from paged_kv_cache_25_amd import ops
+    for c in chunks:
+        qsl[1] = c
+        lens[0] = done + c
+        sl = slice(done, done + c)
+        q = dev.q[sl].contiguous()
+        out = torch.empty_like(q)
+        ops.kv_append_tokens(dev.k_pool, dev.v_pool, dev.k_new[sl].contiguous(),
+                             dev.v_new[sl].contiguous(), dev.tables, lens, qsl)
+        ops.paged_multi_query_attention(out, q, dev.k_pool, dev.v_pool, dev.tables, lens, qsl,
+                                        c, done + c, full.softmax_scale, 16)
+        torch.cuda.synchronize()
+        rows.append(out.float().cpu().double().numpy())
+        done += c
+    gpu = np.concatenate(rows)
+    check_tolerance("bf16", gpu, ref, "chunked prefill")
+
+
+def test_speculative_verify_workload_sampled():
+    """The Llama-3-8B batch-64 layer with 4 new tokens per sequence (three
+    drafts and the token before them, as a verify pass sees them), at full
+    size in the launch configuration the benchmark times; sampled rows
+    against the oracle."""
+    inp = named_config(2, new_tokens=("const", 4), name="llama3_8b_b64_t4")
+    dev = DeviceMultiStep(inp)
+    gpu = dev.step().detach().float().cpu().double().numpy()
+    rng = np.random.default_rng(0)
+    seqs = sorted(rng.choice(inp.num_seqs, 6, replace=False).tolist())
+    pools = pa.kv_append_tokens(inp.k_pool, inp.v_pool, inp.k_new, inp.v_new, inp.block_tables,
+                                inp.context_lens, inp.query_start_loc, inp.block_size)
+    assert _same_bits(host_storage(dev.k_pool), pools[0])
+    assert _same_bits(host_storage(dev.v_pool), pools[1])
+    for b in seqs:
+        q0, q1 = int(inp.query_start_loc[b]), int(inp.query_start_loc[b + 1])
+        ref = pa.multi_query_attention(inp.q[q0:q1], pools[0], pools[1],
+                                       inp.block_tables[b:b + 1], inp.context_lens[b:b + 1],
+                                       np.array([0, q1 - q0]), block_size=inp.block_size,
+                                       softmax_scale=inp.softmax_scale, q_dtype=inp.q_dtype,
+                                       kv_dtype=inp.kv_dtype)
+        check_tolerance("bf16", gpu[q0:q1], ref, f"verify t=4 seq {b} ctx {inp.context_lens[b]}")
