@@ -52,6 +52,9 @@ def parse():
     ap.add_argument("--kernel-reps", type=int, default=200)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=15.0)
+    ap.add_argument("--new-tokens", type=int, default=0,
+                    help="time the multi-token path instead: every sequence of the workload "
+                         "brings this many new tokens (append + shifted-causal attention)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only time a plain device-to-device copy of this many MiB (the "
                          "reference kernel for scaling FETCH_SIZE / WRITE_SIZE counters)")
@@ -88,6 +91,9 @@ def main():
 
     if args.copy_calibration_mib:
         copy_calibration(args.copy_calibration_mib, max(1, args.steps))
+        return
+    if args.new_tokens:
+        main_multi(args)
         return
 
     import torch
@@ -278,6 +284,232 @@ def main():
         "input_copies": n_copies,
     }
     print(json.dumps(result), flush=True)
+
+
+def to_device(arr, dt, dev):
+    import torch
+    if dt is None:
+        return torch.from_numpy(np.ascontiguousarray(arr)).to(dev)
+    if dt == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(torch.bfloat16).to(dev)
+    if dt == "fp8_e4m3":
+        return torch.from_numpy(np.ascontiguousarray(arr)).view(torch.float8_e4m3fn).to(dev)
+    return torch.from_numpy(np.ascontiguousarray(arr, dtype=np.float32)).to(dev)
+
+
+def rotated_copies(base):
+    """The inputs plus enough clones to span well over the last-level cache."""
+    import torch
+    footprint = sum(t.numel() * t.element_size() for t in base.values() if t is not None)
+    n = max(1, math.ceil(1.5 * 2 ** 30 / footprint)) if footprint < 1.5 * 2 ** 30 else 1
+    if footprint * n > 0.5 * torch.cuda.get_device_properties(0).total_memory:
+        n = 1
+    return [base] + [{k: (None if v is None else v.clone()) for k, v in base.items()}
+                     for _ in range(n - 1)], footprint
+
+
+def event_timer(stream):
+    """ms per call of fn(i) over reps calls, with HIP events on ``stream``."""
+    import torch
+
+    def timed(fn, reps):
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for i in range(reps):
+            fn(i)
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+    return timed
+
+
+def main_multi(args):
+    """Several new tokens per sequence (chunked prefill, a verify pass): one
+    step is pkv_kv_append_tokens then pkv_paged_multi_query_attention over the
+    workload's sequences, each bringing ``--new-tokens`` tokens."""
+    import torch
+
+    from paged_kv_cache_25_amd import ops, traffic
+    from workloads import named_config
+
+    lib = ops.load()
+    if not torch.cuda.is_available():
+        raise SystemExit("no GPU visible")
+    dev = torch.device("cuda:0")
+    T = args.new_tokens
+    t0 = time.time()
+    from workloads.configs import CONFIG_NAMES
+    inp = named_config(args.config, seed=args.seed, new_tokens=("const", T),
+                       name=f"{CONFIG_NAMES[args.config]}_t{T}")
+    P = inp.partition_size if args.partition_size is None else args.partition_size
+    print(f"[bench] workload {inp.name}: generated in {time.time() - t0:.1f}s", file=sys.stderr,
+          flush=True)
+    base = dict(q=to_device(inp.q, inp.q_dtype, dev),
+                k_pool=to_device(inp.k_pool, inp.kv_dtype, dev),
+                v_pool=to_device(inp.v_pool, inp.kv_dtype, dev),
+                k_new=to_device(inp.k_new, inp.kv_dtype, dev),
+                v_new=to_device(inp.v_new, inp.kv_dtype, dev),
+                tables=to_device(inp.block_tables, None, dev),
+                lens=to_device(inp.context_lens, None, dev),
+                qsl=to_device(inp.query_start_loc.astype(np.int32), None, dev),
+                k_scales=None if inp.k_scales is None else to_device(inp.k_scales, None, dev),
+                v_scales=None if inp.v_scales is None else to_device(inp.v_scales, None, dev))
+    copies, footprint = rotated_copies(base)
+    n_copies = len(copies)
+
+    B, Hq, Hkv, D = inp.num_seqs, inp.num_q_heads, inp.num_kv_heads, inp.head_dim
+    NB, MB = inp.num_blocks, inp.block_tables.shape[1]
+    R = inp.total_queries
+    mcl, mq = inp.max_context_len, inp.max_new_tokens
+    qcode, kvcode = ops.dtype_code(base["q"].dtype), ops.dtype_code(base["k_pool"].dtype)
+    ws_bytes = ops.multi_query_workspace_bytes(R, Hq, D, mcl, P)
+    maxp = max(1, -(-mcl // P)) if P else 1
+    lse_off = ((R * Hq * maxp * D * 4 + 255) // 256) * 256
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    V = ctypes.c_void_p
+
+    def ptr(t):
+        return None if t is None else V(t.data_ptr())
+
+    calls = []
+    for c in copies:
+        c["out"] = torch.empty(R, Hq, D, dtype=c["q"].dtype, device=dev)
+        c["ws"] = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+        app = (ptr(c["k_pool"]), ptr(c["v_pool"]), ptr(c["k_new"]), ptr(c["v_new"]),
+               ptr(c["tables"]), ptr(c["lens"]), ptr(c["qsl"]), B, R, Hkv, D, 16, NB, MB,
+               kvcode, sp)
+        att = (ptr(c["out"]), ptr(c["q"]), ptr(c["k_pool"]), ptr(c["v_pool"]),
+               ptr(c["k_scales"]), ptr(c["v_scales"]), ptr(c["tables"]), ptr(c["lens"]),
+               ptr(c["qsl"]), B, R, mq, Hq, Hkv, D, 16, NB, MB, mcl,
+               ctypes.c_float(inp.softmax_scale), P, ptr(c["ws"]),
+               ctypes.c_size_t(c["ws"].numel()), qcode, kvcode, sp)
+        # the decode kernel alone (same grid and work, partials for every row)
+        c["parts"] = torch.empty(lse_off + R * Hq * maxp * 4, dtype=torch.uint8, device=dev)
+        prt = (V(c["parts"].data_ptr()), V(c["parts"].data_ptr() + lse_off), maxp, ptr(c["q"]),
+               ptr(c["k_pool"]), ptr(c["v_pool"]), ptr(c["k_scales"]), ptr(c["v_scales"]),
+               ptr(c["tables"]), ptr(c["lens"]), ptr(c["qsl"]), B, R, mq, Hq, Hkv, D, 16, NB, MB,
+               ctypes.c_float(inp.softmax_scale), P, qcode, kvcode, sp)
+        calls.append((app, att, prt))
+
+    f_app, f_att = lib.pkv_kv_append_tokens, lib.pkv_paged_multi_query_attention
+    f_prt = lib.pkv_paged_multi_query_partials
+
+    def step(i):
+        app, att, _ = calls[i % n_copies]
+        if f_app(*app) != 0 or f_att(*att) != 0:
+            raise RuntimeError("libpkv call failed")
+
+    print(f"[bench] {n_copies} input copies of {footprint / 1e6:.1f} MB; warmup {args.warmup}",
+          file=sys.stderr, flush=True)
+    for i in range(args.warmup):
+        step(i)
+    timed = event_timer(stream)
+    step_ms = timed(step, args.steps)
+    print(f"[bench] {args.steps} steps: {step_ms * 1e3:.1f} us/step", file=sys.stderr, flush=True)
+
+    def att_only(i):
+        if f_att(*calls[i % n_copies][1]) != 0:
+            raise RuntimeError("attention call failed")
+
+    def decode_only(i):
+        if f_prt(*calls[i % n_copies][2]) != 0:
+            raise RuntimeError("partials call failed")
+
+    def append_only(i):
+        if f_app(*calls[i % n_copies][0]) != 0:
+            raise RuntimeError("append call failed")
+
+    reps = args.kernel_reps
+    att_ms = timed(att_only, reps)
+    decode_ms = timed(decode_only, reps)
+    append_ms = timed(append_only, reps)
+    merge_ms = max(att_ms - decode_ms, 0.0) if maxp > 1 else 0.0
+
+    t_new = np.diff(inp.query_start_loc)
+    tr = traffic.multi_query_traffic(inp.context_lens, t_new, num_q_heads=Hq, num_kv_heads=Hkv,
+                                     head_dim=D, q_dtype=inp.q_dtype, kv_dtype=inp.kv_dtype)
+    ap = traffic.append_traffic(R, num_kv_heads=Hkv, head_dim=D, kv_dtype=inp.kv_dtype)
+    step_bytes = tr["total_bytes"] + ap["bytes"] + 4 * (B + 1)
+    value = step_bytes / (step_ms * 1e-3) / 1e9
+    kernel_gbps = tr["kv_bytes"] / (decode_ms * 1e-3) / 1e9
+    mfma = inp.q_dtype == "bf16" and inp.kv_dtype == "bf16" and (Hq // Hkv) * mq >= 2
+    cpu = None if args.no_cpu_baseline else cpu_baseline_multi(inp, args.cpu_budget_s)
+    result = {
+        "metric": "paged multi-token attention achieved HBM GB/s (% of peak) and new tokens/s",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": f"{inp.kv_dtype} kv, {inp.q_dtype} q, f32 accumulate",
+        "data": "synthetic (seeded N(0,1) K/V/q, random block placement)",
+        "config": {"workload": inp.name, "batch": B, "new_tokens_per_seq": T, "q_heads": Hq,
+                   "kv_heads": Hkv, "head_dim": D, "block_size": 16, "partition_size": P,
+                   "context_tokens": int(inp.context_lens.sum()), "max_context": mcl,
+                   "parallelism": "single GPU"},
+        "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
+        "steps_per_s": round(1e3 / step_ms, 1),
+        "new_tokens_per_s": round(R * 1e3 / step_ms, 1),
+        "kernel_us": {"append": round(append_ms * 1e3, 2), "decode": round(decode_ms * 1e3, 2),
+                      "merge": round(merge_ms * 1e3, 2), "attention_call": round(att_ms * 1e3, 2)},
+        "roofline": {"kernel": ("paged_decode_mfma_kernel" if mfma else "paged_decode_kernel")
+                               + f"<{D}> (several new tokens)",
+                     "bound": "hbm", "achieved": round(kernel_gbps, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(kernel_gbps / HBM_PEAK_GBPS, 4),
+                     "traffic": None, "algorithmic_bytes_per_launch": tr["kv_bytes"],
+                     "flops_per_launch": tr["flops"]},
+        "cpu_baseline": cpu,
+        "input_copies": n_copies,
+    }
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline_multi(inp, budget_s):
+    """The float64 oracle on a bounded sample of the multi-token workload:
+    append + attention for whole sequences in order, BLAS on one thread."""
+    import oracle.paged_attention as pa
+    from paged_kv_cache_25_amd import traffic
+    from threadpoolctl import threadpool_limits
+    qsl = inp.query_start_loc
+    done, elapsed = [], 0.0
+    with threadpool_limits(1):
+        for b in range(inp.num_seqs):
+            q0, q1 = int(qsl[b]), int(qsl[b + 1])
+            tab = inp.block_tables[b:b + 1]
+            lens = inp.context_lens[b:b + 1]
+            loc = np.array([0, q1 - q0])
+            ids = tab[0][tab[0] >= 0]
+            kp, vp = inp.k_pool[ids], inp.v_pool[ids]          # the sequence's own blocks
+            local = np.arange(len(ids), dtype=np.int32)[None, :]
+            t = time.perf_counter()
+            kp, vp = pa.kv_append_tokens(kp, vp, inp.k_new[q0:q1], inp.v_new[q0:q1], local, lens,
+                                         loc, inp.block_size, inplace=True)
+            pa.multi_query_attention(inp.q[q0:q1], kp, vp, local, lens, loc,
+                                     block_size=inp.block_size, softmax_scale=inp.softmax_scale,
+                                     q_dtype=inp.q_dtype, kv_dtype=inp.kv_dtype,
+                                     k_scales=None if inp.k_scales is None else inp.k_scales[ids],
+                                     v_scales=None if inp.v_scales is None else inp.v_scales[ids])
+            elapsed += time.perf_counter() - t
+            done.append(b)
+            if elapsed > budget_s:
+                break
+    t_new = np.diff(qsl)[done]
+    tr = traffic.multi_query_traffic(inp.context_lens[done], t_new, num_q_heads=inp.num_q_heads,
+                                     num_kv_heads=inp.num_kv_heads, head_dim=inp.head_dim,
+                                     q_dtype=inp.q_dtype, kv_dtype=inp.kv_dtype)
+    ap = traffic.append_traffic(int(t_new.sum()), num_kv_heads=inp.num_kv_heads,
+                                head_dim=inp.head_dim, kv_dtype=inp.kv_dtype)
+    return {"value": round((tr["total_bytes"] + ap["bytes"]) / elapsed / 1e9, 4), "unit": "GB/s",
+            "cores": 1, "kind": "oracle",
+            "sample": f"{len(done)} of {inp.num_seqs} sequences ({tr['rows']} new tokens over "
+                      f"{tr['tokens']} cached), append + attention, float64 NumPy, {elapsed:.1f} s",
+            "new_tokens_per_s": round(int(t_new.sum()) / elapsed, 3)}
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "paged_decode_mfma_llama3_8b_b64_traffic.txt")

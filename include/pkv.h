@@ -326,6 +326,30 @@ pkv_status_t pkv_paged_multi_query_attention(
     float softmax_scale, int32_t partition_size, void* workspace, size_t workspace_bytes,
     pkv_dtype_t q_dtype, pkv_dtype_t kv_dtype, void* stream);
 
+/*
+ * pkv_paged_multi_query_partials - the split-KV half of
+ * pkv_paged_multi_query_attention on its own, as pkv_paged_decode_partials is
+ * for one new token: for row r of sequence b, query head i and partition p <
+ * ceil(ctx_b / P), the normalised partial output over the partition's tokens
+ * that the row sees and its natural-log log-sum-exp (-inf when the row sees
+ * none of them; partial_out then carries no meaning); partitions
+ * ceil(ctx_b / P) <= p < max_partitions get lse = -inf and leave partial_out
+ * untouched.  pkv_merge_partials
+ * over the num_tokens rows gives pkv_paged_multi_query_attention's output.
+ *
+ * partial_out float32 [num_tokens, num_q_heads, max_partitions, head_dim] and
+ * partial_lse float32 [num_tokens, num_q_heads, max_partitions] [device,
+ * written]; the other arguments as for pkv_paged_multi_query_attention.
+ */
+pkv_status_t pkv_paged_multi_query_partials(
+    float* partial_out, float* partial_lse, int32_t max_partitions, const void* q,
+    const void* k_pool, const void* v_pool, const float* k_scales, const float* v_scales,
+    const int32_t* block_tables, const int32_t* context_lens, const int32_t* query_start_loc,
+    int32_t num_seqs, int32_t num_tokens, int32_t max_query_len, int32_t num_q_heads,
+    int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
+    int32_t max_blocks_per_seq, float softmax_scale, int32_t partition_size,
+    pkv_dtype_t q_dtype, pkv_dtype_t kv_dtype, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -40,7 +40,16 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(MergeArgs a) {
   if (a.num_partitions) {
     np = a.num_partitions[b];
   } else if (a.context_lens) {
-    const int ctx = a.context_lens[b];
+    int seq = b;
+    if (a.q_start) {                              // last s with q_start[s] <= b
+      int lo = 0, hi = a.num_batch - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (a.q_start[mid] <= b) lo = mid; else hi = mid - 1;
+      }
+      seq = lo;
+    }
+    const int ctx = a.context_lens[seq];
     np = ctx <= 0 ? 0 : (ctx + a.partition_size - 1) / a.partition_size;
   }
   np = np < 0 ? 0 : (np > a.max_partitions ? a.max_partitions : np);

@@ -247,12 +247,11 @@ __global__ __launch_bounds__(kWave) void paged_decode_kernel(DecodeArgs a) {
   constexpr int W = TL::kWords;
   constexpr int KD = TL::kDims;
 
-  // blockIdx.x -> (head chunk, kv head, sequence, partition), partition
-  // slowest.  Workgroups go to the 8 XCDs round-robin, so consecutive ids must
-  // carry equal work: every (sequence, head) has a partition 0, while only long
-  // sequences have high partitions.
-  int idx = blockIdx.x;
-  const int chunk = idx % a.head_chunks;   idx /= a.head_chunks;
+  // blockIdx.x -> (column chunk, unit = (kv head, sequence, partition)).
+  int chunk, idx;
+  if (!decode_unit(blockIdx.x, a.head_chunks, a.num_seqs * a.num_kv_heads * a.max_partitions,
+                   chunk, idx))
+    return;
   const int h = idx % a.num_kv_heads;      idx /= a.num_kv_heads;
   const int b = idx % a.num_seqs;
   const int part = idx / a.num_seqs;
@@ -427,8 +426,10 @@ __global__ __launch_bounds__(kWave) void paged_decode_kernel(DecodeArgs a) {
 
 template <int D, int G, typename QT, typename KV>
 hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
-  const size_t grid = size_t(a.num_seqs) * a.num_kv_heads * a.head_chunks * a.max_partitions;
-  if (grid == 0) return hipSuccess;
+  const size_t units = size_t(a.num_seqs) * a.num_kv_heads * a.max_partitions;
+  if (units == 0 || a.head_chunks == 0) return hipSuccess;
+  if (units > 0x7fffffffu) return hipErrorInvalidConfiguration;
+  const size_t grid = decode_grid(units, a.head_chunks);
   if (grid > 0x7fffffffu) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL((paged_decode_kernel<D, G, QT, KV>), dim3(unsigned(grid)), dim3(kWave), 0,
                      stream, a);

@@ -48,12 +48,7 @@ constexpr int kHeadTile = 16;
 #ifndef PKV_MFMA_WAVES_PER_EU
 #define PKV_MFMA_WAVES_PER_EU 3
 #endif
-// Independent work items (waves) packed in one workgroup; they share nothing.
-#ifndef PKV_MFMA_ITEMS_PER_WG
-#define PKV_MFMA_ITEMS_PER_WG 1
-#endif
 constexpr int kDepth = PKV_MFMA_DEPTH;
-constexpr int kItemsPerWg = PKV_MFMA_ITEMS_PER_WG;
 
 template <int D>
 struct MfmaTile {
@@ -78,22 +73,22 @@ struct BlockRegs {
   uint32_t v[4][MfmaTile<D>::kVWords];                // rows 4r+i, this lane's bytes
 };
 
-template <int D>
+template <int D, bool kNT>
 __device__ __forceinline__ void load_block(BlockRegs<D>& br, const char* kslice,
                                            const char* vslice, int lane) {
   using T = MfmaTile<D>;
   const int r = lane >> 4, c = lane & 15;
 #pragma unroll
   for (int j = 0; j < T::kSlabs; ++j)
-    br.k[j] = load_streamed<uint4>(kslice + c * T::kRowBytes + 64 * j + 16 * r);
+    br.k[j] = load_streamed<uint4, kNT>(kslice + c * T::kRowBytes + 64 * j + 16 * r);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const char* p = vslice + (4 * r + i) * T::kRowBytes + T::kVChunkBytes * c;
     if constexpr (T::kVWords == 4) {
-      const uint4 w = load_streamed<uint4>(p);
+      const uint4 w = load_streamed<uint4, kNT>(p);
       br.v[i][0] = w.x; br.v[i][1] = w.y; br.v[i][2] = w.z; br.v[i][3] = w.w;
     } else {
-      const uint2 w = load_streamed<uint2>(p);
+      const uint2 w = load_streamed<uint2, kNT>(p);
       br.v[i][0] = w.x; br.v[i][1] = w.y;
     }
   }
@@ -216,25 +211,25 @@ struct MfmaDecode {
   }
 };
 
-// Three waves per SIMD: 151 VGPRs for head dim 128 with two blocks in registers.
+// Three waves per SIMD: about 150 VGPRs for head dim 128 with two blocks in registers.
 // kMulti: several new tokens per sequence (per-column visibility); otherwise
-// one new token, whose column sees the whole context.
-template <int D, bool kMulti>
-__global__ __launch_bounds__(kWave * kItemsPerWg) __attribute__((amdgpu_waves_per_eu(PKV_MFMA_WAVES_PER_EU)))
+// one new token, whose column sees the whole context.  kNT: K/V loads carry the
+// nontemporal hint; off when several column tiles read the same blocks, so the
+// later tiles find them in L2.
+template <int D, bool kMulti, bool kNT>
+__global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(PKV_MFMA_WAVES_PER_EU)))
 void paged_decode_mfma_kernel(DecodeArgs a) {
   using T = MfmaTile<D>;
-  // blockIdx.x -> (head chunk, kv head, sequence, partition), partition
-  // slowest.  Workgroups go to the 8 XCDs round-robin, so consecutive ids must
-  // carry equal work: every (sequence, head) has a partition 0, while only long
-  // sequences have high partitions.
-  int idx = blockIdx.x * kItemsPerWg + int(threadIdx.x / kWave);
-  if (idx >= a.num_seqs * a.num_kv_heads * a.head_chunks * a.max_partitions) return;
-  const int chunk = idx % a.head_chunks;   idx /= a.head_chunks;
+  // blockIdx.x -> (column chunk, unit = (kv head, sequence, partition)).
+  int chunk, idx;
+  if (!decode_unit(blockIdx.x, a.head_chunks, a.num_seqs * a.num_kv_heads * a.max_partitions,
+                   chunk, idx))
+    return;
   const int h = idx % a.num_kv_heads;      idx /= a.num_kv_heads;
   const int b = idx % a.num_seqs;
   const int part = idx / a.num_seqs;
 
-  const int lane = threadIdx.x % kWave;
+  const int lane = threadIdx.x;
   const int r = lane >> 4, c = lane & 15;
 
   const int32_t* table = a.block_tables + size_t(b) * a.max_blocks_per_seq;
@@ -317,7 +312,7 @@ void paged_decode_mfma_kernel(DecodeArgs a) {
     auto fetch = [&](BlockRegs<D>& br, int k) {
       const int phys = __builtin_amdgcn_readlane(my_id, k);
       const size_t off = size_t(phys) * block_stride + head_off;
-      load_block<D>(br, kbase + off, vbase + off, lane);
+      load_block<D, kNT>(br, kbase + off, vbase + off, lane);
     };
     auto consume = [&](BlockRegs<D>& br, int k) {
       const int first = (seg + k) * kBlockSize;
@@ -403,16 +398,27 @@ void paged_decode_mfma_kernel(DecodeArgs a) {
 
 template <int D>
 hipError_t launch_d(const DecodeArgs& a, hipStream_t stream) {
-  const size_t grid = size_t(a.num_seqs) * a.num_kv_heads * a.head_chunks * a.max_partitions;
-  if (grid == 0) return hipSuccess;
+  const size_t units = size_t(a.num_seqs) * a.num_kv_heads * a.max_partitions;
+  if (units == 0 || a.head_chunks == 0) return hipSuccess;
+  if (units > 0x7fffffffu) return hipErrorInvalidConfiguration;
+  const size_t grid = decode_grid(units, a.head_chunks);
   if (grid > 0x7fffffffu) return hipErrorInvalidConfiguration;
-  const size_t wgs = (grid + kItemsPerWg - 1) / kItemsPerWg;
-  if (a.q_start)
-    hipLaunchKernelGGL((paged_decode_mfma_kernel<D, true>), dim3(unsigned(wgs)),
-                       dim3(kWave * kItemsPerWg), 0, stream, a);
-  else
-    hipLaunchKernelGGL((paged_decode_mfma_kernel<D, false>), dim3(unsigned(wgs)),
-                       dim3(kWave * kItemsPerWg), 0, stream, a);
+  const bool nt = a.head_chunks == 1 && PKV_NT_LOADS;
+  if (a.q_start) {
+    if (nt)
+      hipLaunchKernelGGL((paged_decode_mfma_kernel<D, true, true>), dim3(unsigned(grid)),
+                         dim3(kWave), 0, stream, a);
+    else
+      hipLaunchKernelGGL((paged_decode_mfma_kernel<D, true, false>), dim3(unsigned(grid)),
+                         dim3(kWave), 0, stream, a);
+  } else {
+    if (nt)
+      hipLaunchKernelGGL((paged_decode_mfma_kernel<D, false, true>), dim3(unsigned(grid)),
+                         dim3(kWave), 0, stream, a);
+    else
+      hipLaunchKernelGGL((paged_decode_mfma_kernel<D, false, false>), dim3(unsigned(grid)),
+                         dim3(kWave), 0, stream, a);
+  }
   return hipGetLastError();
 }
 

@@ -288,8 +288,55 @@ pkv_status_t attention_impl(
   m.num_q_heads = num_q_heads;
   m.max_partitions = int(maxp);
   m.skip_single = 1;
+  m.q_start = nullptr;
+  m.num_batch = num_seqs;
   return pkv::launch_merge(m, head_dim, to_internal(q_dtype), st) == hipSuccess ? PKV_OK
                                                                                 : PKV_ERR_HIP;
+}
+
+// Checks and kernel set-up shared by the two multi-token entry points.
+struct MultiSetup {
+  pkv::DecodeArgs a;
+  bool mfma = false, nothing = false;
+  int tile = 1;
+};
+
+pkv_status_t multi_setup(MultiSetup& ms, const void* q, const void* k_pool, const void* v_pool,
+                         const float* k_scales, const float* v_scales,
+                         const int32_t* block_tables, const int32_t* context_lens,
+                         const int32_t* query_start_loc, int32_t num_seqs, int32_t num_tokens,
+                         int32_t max_query_len, int32_t num_q_heads, int32_t num_kv_heads,
+                         int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                         int32_t max_blocks_per_seq, float softmax_scale,
+                         int32_t partition_size, pkv_dtype_t q_dtype, pkv_dtype_t kv_dtype) {
+  if (num_tokens < 0 || max_query_len < 0) return PKV_ERR_INVALID_ARG;
+  // No new token anywhere: sizes are checked, pointers are not needed.
+  const pkv_status_t st0 = check_decode(q, k_pool, v_pool, k_scales, v_scales, block_tables,
+                                        context_lens, num_tokens == 0 ? 0 : num_seqs,
+                                        num_q_heads, num_kv_heads, head_dim, block_size,
+                                        num_blocks, max_blocks_per_seq, softmax_scale,
+                                        partition_size, q_dtype, kv_dtype);
+  if (st0 != PKV_OK) return st0;
+  if (num_seqs == 0 || num_tokens == 0) {
+    ms.nothing = true;
+    return PKV_OK;
+  }
+  if (max_query_len < 1 || !query_start_loc || !aligned4(query_start_loc))
+    return PKV_ERR_INVALID_ARG;
+  const int group = num_q_heads / num_kv_heads;
+  const int64_t columns = int64_t(max_query_len) * group;     // queries per KV head
+  ms.mfma = uses_mfma(q_dtype, kv_dtype, columns);
+  ms.tile = ms.mfma ? pkv::mfma_head_tile()
+                    : tile_heads(columns < (1 << 20) ? int(columns) : (1 << 20), head_dim);
+  const int64_t chunks = (columns + ms.tile - 1) / ms.tile;
+  if (chunks > 0x7fffffff) return PKV_ERR_INVALID_ARG;
+  ms.a = decode_args(q, k_pool, v_pool, k_scales, v_scales, block_tables, context_lens,
+                     num_seqs, num_q_heads, num_kv_heads, head_dim, num_blocks,
+                     max_blocks_per_seq, softmax_scale, ms.tile);
+  ms.a.q_start = query_start_loc;
+  ms.a.max_q = max_query_len;
+  ms.a.head_chunks = int(chunks);
+  return PKV_OK;
 }
 
 }  // namespace
@@ -370,36 +417,19 @@ pkv_status_t pkv_paged_multi_query_attention(
     int32_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len,
     float softmax_scale, int32_t partition_size, void* workspace, size_t workspace_bytes,
     pkv_dtype_t q_dtype, pkv_dtype_t kv_dtype, void* stream) {
-  if (max_context_len < 0 || num_tokens < 0 || max_query_len < 0) return PKV_ERR_INVALID_ARG;
-  // No new token anywhere: sizes are checked, pointers are not needed.
-  const pkv_status_t st0 = check_decode(q, k_pool, v_pool, k_scales, v_scales, block_tables,
-                                        context_lens, num_tokens == 0 ? 0 : num_seqs,
-                                        num_q_heads, num_kv_heads,
-                                        head_dim, block_size, num_blocks, max_blocks_per_seq,
-                                        softmax_scale, partition_size, q_dtype, kv_dtype);
-  if (st0 != PKV_OK || num_seqs == 0 || num_tokens == 0) return st0;
-  if (max_query_len < 1) return PKV_ERR_INVALID_ARG;
-  if (!out || !query_start_loc || !aligned16(out) || !aligned16(workspace) ||
-      !aligned4(query_start_loc))
-    return PKV_ERR_INVALID_ARG;
+  if (max_context_len < 0) return PKV_ERR_INVALID_ARG;
+  MultiSetup ms;
+  const pkv_status_t st0 = multi_setup(
+      ms, q, k_pool, v_pool, k_scales, v_scales, block_tables, context_lens, query_start_loc,
+      num_seqs, num_tokens, max_query_len, num_q_heads, num_kv_heads, head_dim, block_size,
+      num_blocks, max_blocks_per_seq, softmax_scale, partition_size, q_dtype, kv_dtype);
+  if (st0 != PKV_OK || ms.nothing) return st0;
+  if (!out || !aligned16(out) || !aligned16(workspace)) return PKV_ERR_INVALID_ARG;
 
   const int64_t maxp = max_partitions(max_context_len, partition_size);
   const bool single = maxp <= 1;
-  const int group = num_q_heads / num_kv_heads;
-  const int64_t columns = int64_t(max_query_len) * group;     // queries per KV head
-  const bool mfma = uses_mfma(q_dtype, kv_dtype, columns);
-  const int tile = mfma ? pkv::mfma_head_tile()
-                        : tile_heads(columns < (1 << 20) ? int(columns) : (1 << 20), head_dim);
-  const int64_t chunks = (columns + tile - 1) / tile;
-  if (chunks > 0x7fffffff) return PKV_ERR_INVALID_ARG;
-
-  pkv::DecodeArgs a = decode_args(q, k_pool, v_pool, k_scales, v_scales, block_tables,
-                                  context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim,
-                                  num_blocks, max_blocks_per_seq, softmax_scale, tile);
+  pkv::DecodeArgs& a = ms.a;
   a.out = out;
-  a.q_start = query_start_loc;
-  a.max_q = max_query_len;
-  a.head_chunks = int(chunks);
   if (!single) {
     const PartLayout L = part_layout(num_tokens, num_q_heads, head_dim, maxp);
     if (!workspace || workspace_bytes < L.total) return PKV_ERR_WORKSPACE;
@@ -410,13 +440,14 @@ pkv_status_t pkv_paged_multi_query_attention(
       single ? max_blocks_per_seq : partition_size / block_size;
   a.max_partitions = int(maxp);
   a.write_final = single ? 1 : 0;
-  // Every (row, partition) of the workspace is written, empty ones as lse =
-  // -inf, so the merge below needs no per-row partition count.
-  a.final_single = 0;
-  a.mark_empty = 1;
+  // Rows of a sequence whose blocks fit one partition are written final by
+  // the decode kernel; the merge finds each row's sequence and its partition
+  // count from query_start_loc and context_lens, and skips those rows.
+  a.final_single = 1;
+  a.mark_empty = 0;
 
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (launch_decode(a, head_dim, tile, mfma, q_dtype, kv_dtype, st) != hipSuccess)
+  if (launch_decode(a, head_dim, ms.tile, ms.mfma, q_dtype, kv_dtype, st) != hipSuccess)
     return PKV_ERR_HIP;
   if (single) return PKV_OK;
 
@@ -425,14 +456,49 @@ pkv_status_t pkv_paged_multi_query_attention(
   m.part_o = a.part_o;
   m.part_lse = a.part_lse;
   m.num_partitions = nullptr;
-  m.context_lens = nullptr;
+  m.context_lens = context_lens;
   m.partition_size = partition_size;
   m.num_seqs = num_tokens;
   m.num_q_heads = num_q_heads;
   m.max_partitions = int(maxp);
-  m.skip_single = 0;
+  m.skip_single = 1;
+  m.q_start = query_start_loc;
+  m.num_batch = num_seqs;
   return pkv::launch_merge(m, head_dim, to_internal(q_dtype), st) == hipSuccess ? PKV_OK
                                                                                 : PKV_ERR_HIP;
+}
+
+pkv_status_t pkv_paged_multi_query_partials(
+    float* partial_out, float* partial_lse, int32_t max_partitions_, const void* q,
+    const void* k_pool, const void* v_pool, const float* k_scales, const float* v_scales,
+    const int32_t* block_tables, const int32_t* context_lens, const int32_t* query_start_loc,
+    int32_t num_seqs, int32_t num_tokens, int32_t max_query_len, int32_t num_q_heads,
+    int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
+    int32_t max_blocks_per_seq, float softmax_scale, int32_t partition_size,
+    pkv_dtype_t q_dtype, pkv_dtype_t kv_dtype, void* stream) {
+  if (max_partitions_ <= 0) return PKV_ERR_INVALID_ARG;
+  MultiSetup ms;
+  const pkv_status_t st0 = multi_setup(
+      ms, q, k_pool, v_pool, k_scales, v_scales, block_tables, context_lens, query_start_loc,
+      num_seqs, num_tokens, max_query_len, num_q_heads, num_kv_heads, head_dim, block_size,
+      num_blocks, max_blocks_per_seq, softmax_scale, partition_size, q_dtype, kv_dtype);
+  if (st0 != PKV_OK || ms.nothing) return st0;
+  if (!partial_out || !partial_lse || !aligned16(partial_out) || !aligned4(partial_lse))
+    return PKV_ERR_INVALID_ARG;
+  pkv::DecodeArgs& a = ms.a;
+  a.out = nullptr;
+  a.part_o = partial_out;
+  a.part_lse = partial_lse;
+  a.blocks_per_partition =
+      partition_size == 0 ? max_blocks_per_seq : partition_size / block_size;
+  a.max_partitions = max_partitions_;
+  a.write_final = 0;
+  a.final_single = 0;
+  a.mark_empty = 1;
+  return launch_decode(a, head_dim, ms.tile, ms.mfma, q_dtype, kv_dtype,
+                       static_cast<hipStream_t>(stream)) == hipSuccess
+             ? PKV_OK
+             : PKV_ERR_HIP;
 }
 
 pkv_status_t pkv_merge_partials(void* out, const float* partial_out, const float* partial_lse,
@@ -459,6 +525,8 @@ pkv_status_t pkv_merge_partials(void* out, const float* partial_out, const float
   m.num_q_heads = num_q_heads;
   m.max_partitions = max_partitions;
   m.skip_single = 0;
+  m.q_start = nullptr;
+  m.num_batch = num_seqs;
   return pkv::launch_merge(m, head_dim, to_internal(out_dtype), static_cast<hipStream_t>(stream)) ==
                  hipSuccess
              ? PKV_OK

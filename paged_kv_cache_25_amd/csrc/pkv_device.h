@@ -89,7 +89,8 @@ __device__ __forceinline__ float wave_sum(float x) {
 
 // 8- and 16-byte loads of streamed K/V data.  With PKV_NT_LOADS (the default)
 // they carry the nontemporal hint: each slice is read once per step, so it
-// should not displace reusable lines from the caches.
+// should not displace reusable lines from the caches.  kNT = false gives plain
+// loads, for data that other workgroups read again soon through the same L2.
 #ifndef PKV_NT_LOADS
 #define PKV_NT_LOADS 1
 #endif
@@ -100,14 +101,12 @@ template <typename T> struct VecOf;
 template <> struct VecOf<uint4> { using type = u32x4; };
 template <> struct VecOf<uint2> { using type = u32x2; };
 
-template <typename T>
+template <typename T, bool kNT = bool(PKV_NT_LOADS)>
 __device__ __forceinline__ T load_streamed(const char* p) {
   using V = typename VecOf<T>::type;
-#if PKV_NT_LOADS
-  const V v = __builtin_nontemporal_load(reinterpret_cast<const V*>(p));
-#else
-  const V v = *reinterpret_cast<const V*>(p);
-#endif
+  V v;
+  if constexpr (kNT) v = __builtin_nontemporal_load(reinterpret_cast<const V*>(p));
+  else v = *reinterpret_cast<const V*>(p);
   return __builtin_bit_cast(T, v);
 }
 

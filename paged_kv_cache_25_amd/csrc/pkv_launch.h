@@ -73,6 +73,28 @@ struct Columns {
   __host__ __device__ int visible(int n, int ctx) const { return ctx - t + n / group + 1; }
 };
 
+// Grid order of the decode kernels.  The hardware hands workgroup ids to the
+// 8 XCDs round-robin (id % 8), and each XCD has its own L2.  A unit is one
+// (KV head, sequence, partition), KV head fastest and partition slowest, so
+// consecutive units carry equal work (every sequence has a partition 0, only
+// long ones have high partitions).  The column tiles ("chunks") of one unit
+// read the same K/V blocks: they take ids 8 apart, i.e. run back to back on
+// one XCD, so the blocks come from HBM once and from that L2 after.
+constexpr int kXcds = 8;
+
+inline size_t decode_grid(size_t units, int chunks) {
+  return (units + kXcds - 1) / kXcds * kXcds * size_t(chunks);
+}
+
+// Workgroup id -> (chunk, unit); false for the padding ids past the last unit.
+__device__ inline bool decode_unit(int id, int chunks, int units, int& chunk, int& unit) {
+  const int xcd = id % kXcds;
+  const int r = id / kXcds;
+  chunk = r % chunks;
+  unit = (r / chunks) * kXcds + xcd;
+  return unit < units;
+}
+
 struct MergeArgs {
   void* out;
   const float* part_o;
@@ -82,6 +104,11 @@ struct MergeArgs {
   int partition_size;
   int num_seqs, num_q_heads, max_partitions;
   int skip_single;                 // 1: sequences with one partition were written by the decode kernel
+  // Several new tokens per sequence: row r (num_seqs above counts rows) belongs
+  // to the sequence s with q_start[s] <= r < q_start[s+1], whose context_lens
+  // entry sets its partition count.  Null: row r is sequence r.
+  const int32_t* q_start;
+  int num_batch;                   // sequences, when q_start is set
 };
 
 hipError_t launch_kv_append(const AppendArgs& a, hipStream_t stream);

@@ -66,6 +66,9 @@ def load():
     L.pkv_paged_multi_query_attention.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I,
                                                   I, I, I, F, I, P, Z, ctypes.c_int,
                                                   ctypes.c_int, P]
+    L.pkv_paged_multi_query_partials.restype = ctypes.c_int
+    L.pkv_paged_multi_query_partials.argtypes = [P, P, I, P, P, P, P, P, P, P, P, I, I, I, I, I,
+                                                 I, I, I, I, F, I, ctypes.c_int, ctypes.c_int, P]
     _lib = L
     return L
 
@@ -242,3 +245,24 @@ def paged_multi_query_attention(out, q, k_pool, v_pool, block_tables, context_le
         int(partition_size), _ptr(workspace), workspace.numel(), dtype_code(q.dtype),
         dtype_code(k_pool.dtype), _stream(stream)))
     return out
+
+
+def paged_multi_query_partials(partial_out, partial_lse, q, k_pool, v_pool, block_tables,
+                               context_lens, query_start_loc, max_query_len, softmax_scale,
+                               partition_size=512, k_scales=None, v_scales=None, stream=None):
+    """Unmerged split-KV results of the multi-token attention: partial_out
+    [T, Hq, P, D] fp32, partial_lse [T, Hq, P] fp32 (pkv_paged_multi_query_partials)."""
+    _need_cuda(partial_out, partial_lse, q, k_pool, v_pool, block_tables, context_lens,
+               query_start_loc, k_scales, v_scales)
+    if partial_out.dtype != torch.float32 or partial_lse.dtype != torch.float32:
+        raise TypeError("partials are float32")
+    T, hq, d = q.shape
+    nb, hkv, bs, _ = k_pool.shape
+    B = block_tables.shape[0]
+    _check("pkv_paged_multi_query_partials", load().pkv_paged_multi_query_partials(
+        _ptr(partial_out), _ptr(partial_lse), partial_out.shape[2], _ptr(q), _ptr(k_pool),
+        _ptr(v_pool), _ptr(k_scales), _ptr(v_scales), _ptr(block_tables), _ptr(context_lens),
+        _ptr(query_start_loc), B, T, int(max_query_len), hq, hkv, d, bs, nb,
+        block_tables.shape[1], float(softmax_scale), int(partition_size), dtype_code(q.dtype),
+        dtype_code(k_pool.dtype), _stream(stream)))
+    return partial_out, partial_lse

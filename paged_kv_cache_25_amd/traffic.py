@@ -84,3 +84,29 @@ def append_traffic(num_seqs, *, num_kv_heads, head_dim, kv_dtype):
     """Bytes the append moves: each new K and V row read once and written once."""
     row = num_kv_heads * head_dim * ELEM_BYTES[kv_dtype]
     return dict(bytes=num_seqs * row * 2 * 2)
+
+
+def multi_query_traffic(context_lens, new_tokens, *, num_q_heads, num_kv_heads, head_dim,
+                        q_dtype, kv_dtype, block_size=16):
+    """Algorithmic bytes and FLOPs of one multi-token attention call: sequence b
+    brings new_tokens[b] queries that share one read of its ctx_b cached K/V
+    rows (the newest sees them all, and the others a prefix of them).  Bytes:
+    those rows, q and out of every new token, the tables and lengths (and the
+    query offsets); FLOPs: 4 * D * Hq per (query, visible token) pair, where
+    query j of t sees ctx - t + j + 1 tokens."""
+    ctx = np.asarray(context_lens, dtype=np.int64)
+    t = np.asarray(new_tokens, dtype=np.int64)
+    base = attention_call_traffic(ctx, num_q_heads=num_q_heads, num_kv_heads=num_kv_heads,
+                                  head_dim=head_dim, q_dtype=q_dtype, kv_dtype=kv_dtype,
+                                  block_size=block_size)
+    rows = int(t.sum())
+    qo = 2 * rows * num_q_heads * head_dim * ELEM_BYTES[q_dtype]
+    tables = base["table_bytes"] + 4 * (len(ctx) + 1)
+    # sum over j < t of max(ctx - t + j + 1, 0)
+    pairs = 0
+    for c, n in zip(ctx.tolist(), t.tolist()):
+        pairs += sum(max(c - n + j + 1, 0) for j in range(n))
+    return dict(tokens=base["tokens"], rows=rows, kv_bytes=base["kv_bytes"],
+                scale_bytes=base["scale_bytes"], qo_bytes=qo, table_bytes=tables,
+                total_bytes=base["kv_bytes"] + base["scale_bytes"] + qo + tables,
+                flops=4 * head_dim * num_q_heads * pairs)

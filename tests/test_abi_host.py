@@ -35,7 +35,7 @@ def test_header_declares_the_entry_points():
         "pkv_abi_version", "pkv_status_string", "pkv_kv_append", "pkv_decode_workspace_bytes",
         "pkv_paged_decode_attention", "pkv_paged_decode_step", "pkv_paged_decode_partials",
         "pkv_merge_partials", "pkv_kv_append_tokens", "pkv_multi_query_workspace_bytes",
-        "pkv_paged_multi_query_attention"])
+        "pkv_paged_multi_query_attention", "pkv_paged_multi_query_partials"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -227,6 +227,30 @@ def test_multi_query_validation(lib):
     assert _multi(lib, ws=FAKE, wsb=need - 1) == WORKSPACE
     assert _multi(lib, B=0, q=None, qsl=None) == OK
     assert _multi(lib, T=0, q=None, qsl=None) == OK
+
+
+def _multi_partials(lib, **over):
+    a = dict(po=FAKE, pl=FAKE, maxp=4, q=FAKE, kp=FAKE, vp=FAKE, ks=None, vs=None, tables=FAKE,
+             lens=FAKE, qsl=FAKE, B=2, T=6, maxq=4, hq=8, hkv=2, d=128, bs=16, nb=8, mbps=4,
+             scale=0.088, P=16, qt=ops.PKV_BF16, kvt=ops.PKV_BF16)
+    a.update(over)
+    return lib.pkv_paged_multi_query_partials(
+        a["po"], a["pl"], a["maxp"], a["q"], a["kp"], a["vp"], a["ks"], a["vs"], a["tables"],
+        a["lens"], a["qsl"], a["B"], a["T"], a["maxq"], a["hq"], a["hkv"], a["d"], a["bs"],
+        a["nb"], a["mbps"], a["scale"], a["P"], a["qt"], a["kvt"], None)
+
+
+def test_multi_query_partials_validation(lib):
+    assert _multi_partials(lib, po=None) == INVALID
+    assert _multi_partials(lib, pl=None) == INVALID
+    assert _multi_partials(lib, maxp=0) == INVALID
+    assert _multi_partials(lib, qsl=None) == INVALID
+    assert _multi_partials(lib, maxq=0) == INVALID
+    assert _multi_partials(lib, po=ctypes.c_void_p(0x10008)) == INVALID
+    assert _multi_partials(lib, P=24) == INVALID
+    assert _multi_partials(lib, d=96) == UNSUPPORTED
+    assert _multi_partials(lib, kvt=ops.PKV_FP8_E4M3) == INVALID
+    assert _multi_partials(lib, T=0, po=None, qsl=None) == OK
 
 
 def test_binding_refuses_cpu_tensors():

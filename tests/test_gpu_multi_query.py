@@ -193,3 +193,56 @@ def test_speculative_verify_workload_sampled():
                                        softmax_scale=inp.softmax_scale, q_dtype=inp.q_dtype,
                                        kv_dtype=inp.kv_dtype)
         check_tolerance("bf16", gpu[q0:q1], ref, f"verify t=4 seq {b} ctx {inp.context_lens[b]}")
+
+
+@pytest.mark.parametrize("kv,q,P", [("bf16", "bf16", 64), ("f32", "f32", 32),
+                                    ("fp8_e4m3", "bf16", 128)])
+def test_partials_match_oracle_and_merge(kv, q, P):
+    """pkv_paged_multi_query_partials against the oracle's per-partition
+    results of each row's visible prefix; partitions a row does not see carry
+    lse = -inf; merging the partials gives the attention call bit for bit."""
+    from paged_kv_cache_25_amd import ops
+    inp = make_inputs(num_seqs=4, num_q_heads=8, num_kv_heads=2, head_dim=128,
+                      ctx=("fixed", [3, 300, 40, 520]), pool=("used_fraction", 0.8),
+                      q_dtype=q, kv_dtype=kv, seed=90, new_tokens=("fixed", [5, 1, 19, 8]))
+    inp.context_lens[0] = 3               # ctx < t: two rows see nothing
+    maxp = -(-inp.max_context_len // P)
+    log(f"[case] multi partials kv={kv} q={q} P={P} maxP={maxp}")
+    dev = DeviceMultiStep(inp)
+    dev.append()
+    R = inp.total_queries
+    po = torch.full((R, 8, maxp, 128), float("nan"), device="cuda")
+    pl = torch.full((R, 8, maxp), float("nan"), device="cuda")
+    ops.paged_multi_query_partials(po, pl, dev.q, dev.k_pool, dev.v_pool, dev.tables, dev.lens,
+                                   dev.qsl, inp.max_new_tokens, inp.softmax_scale, P,
+                                   dev.k_scales, dev.v_scales)
+    torch.cuda.synchronize()
+    got_l = pl.cpu().double().numpy()
+    got_o = po.cpu().double().numpy()
+    kp, vp = pa.kv_append_tokens(inp.k_pool, inp.v_pool, inp.k_new, inp.v_new, inp.block_tables,
+                                 inp.context_lens, inp.query_start_loc, inp.block_size)
+    tol_l = 1e-5 if kv == "f32" else 2e-3
+    tol_o = 1e-5 if kv == "f32" else (2e-2 if kv == "bf16" else 6e-2)
+    for b in range(inp.num_seqs):
+        ctx = int(inp.context_lens[b])
+        q0, q1 = int(inp.query_start_loc[b]), int(inp.query_start_loc[b + 1])
+        K = pa.gather_sequence(kp, inp.block_tables[b], ctx, 16, kv, inp.k_scales)
+        V = pa.gather_sequence(vp, inp.block_tables[b], ctx, 16, kv, inp.v_scales)
+        for j in range(q1 - q0):
+            r = q0 + j
+            n = pa.visible_tokens(ctx, q1 - q0, j)
+            seen = -(-n // P) if n > 0 else 0
+            assert np.all(np.isneginf(got_l[r, :, seen:])), (b, j)
+            if seen == 0:
+                continue
+            o_ref, l_ref = pa.partition_partials(pa.to_float64(inp.q[r], q), K[:, :n], V[:, :n],
+                                                 inp.softmax_scale, P)
+            assert np.abs(got_l[r, :, :seen] - l_ref).max() < tol_l, (b, j)
+            assert np.abs(got_o[r, :, :seen] - o_ref).max() < tol_o, (b, j)
+    merged = torch.empty_like(dev.q)
+    ops.merge_partials(merged, po, pl)
+    whole = dev.attend(P).clone()
+    torch.cuda.synchronize()
+    check_tolerance(kv, merged.float().cpu().double().numpy(), oracle_multi(inp, (kp, vp)),
+                    f"multi partials+merge {kv}", out_dtype=q)
+    assert torch.equal(merged, whole)

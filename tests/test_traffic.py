@@ -66,3 +66,21 @@ def test_attention_call_traffic_intensity():
                                        q_dtype="f32", kv_dtype="f32")
     # 2 blocks walked: table 8 B + length 4 B; q and out 2*4*64*4 B
     assert t["table_bytes"] == 12 and t["qo_bytes"] == 2048
+
+
+def test_multi_query_traffic_reduces_to_decode():
+    """One new token per sequence: the multi-token accounting is the decode
+    call's, plus the query offsets; t new tokens share one read of the cache."""
+    ctx = np.array([17, 512, 4000])
+    kw = dict(num_q_heads=32, num_kv_heads=8, head_dim=128, q_dtype="bf16", kv_dtype="bf16")
+    one = traffic.attention_call_traffic(ctx, **kw)
+    m1 = traffic.multi_query_traffic(ctx, np.ones(3, np.int64), **kw)
+    assert m1["kv_bytes"] == one["kv_bytes"] and m1["flops"] == one["flops"]
+    assert m1["total_bytes"] == one["total_bytes"] + 4 * 4
+    m4 = traffic.multi_query_traffic(ctx, np.full(3, 4), **kw)
+    assert m4["kv_bytes"] == one["kv_bytes"]
+    assert m4["qo_bytes"] == 4 * one["qo_bytes"]
+    # query j of 4 sees ctx - 3 + j tokens: 4 ctx - 6 pairs per sequence
+    assert m4["flops"] == 4 * 128 * 32 * int((4 * ctx - 6).sum())
+    # ctx < t: rows with no visible token add nothing
+    assert traffic.multi_query_traffic([2], [4], **kw)["flops"] == 4 * 128 * 32 * (1 + 2)
