@@ -1,4 +1,5 @@
-"""CPU float64 oracle for decode-step attention over a paged KV cache.
+"""CPU float64 oracle for decode-step attention over a paged KV cache, and
+(``oracle.kv_quant``) for appending to an fp8 cache with quantisation.
 
 TEST INFRASTRUCTURE ONLY: imported by the tests, by ``__graft_entry__.smoke()``
 and by the ``cpu_baseline`` leg of ``bench.py``; never by the library.
@@ -24,4 +25,11 @@ from .paged_attention import (  # noqa: F401
     slot_of,
     to_float64,
     visible_tokens,
+)
+from .kv_quant import (  # noqa: F401
+    SCALE_FIXED,
+    SCALE_RUNNING_AMAX,
+    encode_e4m3fn,
+    kv_append_quant,
+    quantize,
 )
