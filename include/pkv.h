@@ -69,6 +69,12 @@ typedef enum {
   PKV_FP8_E4M3 = 2   /* OCP float8 e4m3fn: bias 7, max 448, no inf, NaN=0x7F */
 } pkv_dtype_t;
 
+/* Scale policy of pkv_kv_append_quant. */
+typedef enum {
+  PKV_SCALE_FIXED = 0,        /* keep each (block, head) scale as allocated          */
+  PKV_SCALE_RUNNING_AMAX = 1  /* grow it to cover the new rows, requantising the block */
+} pkv_scale_mode_t;
+
 typedef enum {
   PKV_OK = 0,
   PKV_ERR_INVALID_ARG = 1,   /* null pointer, non-positive size, bad relation */
@@ -349,6 +355,48 @@ pkv_status_t pkv_paged_multi_query_partials(
     int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
     int32_t max_blocks_per_seq, float softmax_scale, int32_t partition_size,
     pkv_dtype_t q_dtype, pkv_dtype_t kv_dtype, void* stream);
+
+/*
+ * pkv_kv_append_quant - append new K/V rows given in bf16 or float32 to an
+ * e4m3 cache, quantising them with their (block, KV head) scale: the code of
+ * a value x is encode(f32(x / s)), one correctly rounded float32 division
+ * followed by rounding to the nearest e4m3fn value, ties to the even code,
+ * saturating at +-448 (NaN gives 0x7F).  Placement is that of
+ * pkv_kv_append_tokens (query_start_loc NULL: one row per sequence, row b
+ * to position ctx_b - 1, as pkv_kv_append).
+ *   KV-cache post, "The KV cache is big" (fewer bytes per number: an 8-bit
+ *   cache halves it); serving lesson, "Smaller caches: GQA, MQA, MLA and
+ *   quantized caches" (an fp8 cache halves e).
+ *
+ * mode PKV_SCALE_FIXED: every slice keeps the scale the caller gave its
+ * block at allocation (k_scales/v_scales are only read); values beyond
+ * 448 * s saturate.  mode PKV_SCALE_RUNNING_AMAX: for the new rows landing
+ * in one slice, amax = max |x| and the slice's scale becomes
+ * max(old, f32(amax / 448)), where old is ignored (taken as 0) if the first
+ * new row sits at slot 0 (a fresh block).  If the scale grew and the slice
+ * has earlier rows, each earlier code c is requantised to
+ * encode(f32(f32(decode(c) * old) / new)).  A scale of 0 (all values so far
+ * 0) stores code 0.  Scales never shrink.  The decode kernels read the
+ * result as any e4m3 cache (value = code * scale).
+ *
+ * k_pool, v_pool [device, read and written] e4m3 codes [num_blocks,
+ * num_kv_heads, block_size, head_dim]; k_scales, v_scales [device, read, and
+ * written in running mode] float32 [num_blocks, num_kv_heads]; k_new, v_new
+ * [device, read] [num_rows, num_kv_heads, head_dim] in new_dtype (F32 or
+ * BF16); block_tables, context_lens, query_start_loc [device, read].  One
+ * workgroup per (sequence, KV head) handles that sequence's slices in order,
+ * so no two sequences may append into the same physical block (copy a shared
+ * block first).  New rows must be finite.  num_seqs == 0 or num_rows == 0 is
+ * a no-op.  Supported: head_dim in {64, 128}, block_size == 16.
+ */
+pkv_status_t pkv_kv_append_quant(void* k_pool, void* v_pool, float* k_scales, float* v_scales,
+                                 const void* k_new, const void* v_new, pkv_dtype_t new_dtype,
+                                 const int32_t* block_tables, const int32_t* context_lens,
+                                 const int32_t* query_start_loc, int32_t num_seqs,
+                                 int32_t num_rows, int32_t num_kv_heads, int32_t head_dim,
+                                 int32_t block_size, int32_t num_blocks,
+                                 int32_t max_blocks_per_seq, pkv_scale_mode_t mode,
+                                 void* stream);
 
 #ifdef __cplusplus
 }

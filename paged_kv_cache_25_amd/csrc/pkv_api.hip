@@ -140,6 +140,50 @@ pkv_status_t pkv_kv_append_tokens(void* k_pool, void* v_pool, const void* k_new,
                      max_blocks_per_seq, kv_dtype, stream);
 }
 
+pkv_status_t pkv_kv_append_quant(void* k_pool, void* v_pool, float* k_scales, float* v_scales,
+                                 const void* k_new, const void* v_new, pkv_dtype_t new_dtype,
+                                 const int32_t* block_tables, const int32_t* context_lens,
+                                 const int32_t* query_start_loc, int32_t num_seqs,
+                                 int32_t num_rows, int32_t num_kv_heads, int32_t head_dim,
+                                 int32_t block_size, int32_t num_blocks,
+                                 int32_t max_blocks_per_seq, pkv_scale_mode_t mode,
+                                 void* stream) {
+  if (num_seqs < 0 || num_rows < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
+      num_blocks <= 0 || max_blocks_per_seq <= 0 ||
+      (new_dtype != PKV_F32 && new_dtype != PKV_BF16) ||
+      (mode != PKV_SCALE_FIXED && mode != PKV_SCALE_RUNNING_AMAX))
+    return PKV_ERR_INVALID_ARG;
+  if (!head_dim_ok(head_dim) || block_size != pkv::kBlockSizeBuilt) return PKV_ERR_UNSUPPORTED;
+  if (num_seqs == 0 || num_rows == 0) return PKV_OK;
+  if (!k_pool || !v_pool || !k_scales || !v_scales || !k_new || !v_new || !block_tables ||
+      !context_lens)
+    return PKV_ERR_INVALID_ARG;
+  if (!aligned16(k_pool) || !aligned16(v_pool) || !aligned16(k_new) || !aligned16(v_new) ||
+      !aligned4(k_scales) || !aligned4(v_scales) || !aligned4(block_tables) ||
+      !aligned4(context_lens) || !aligned4(query_start_loc))
+    return PKV_ERR_INVALID_ARG;
+  pkv::QuantAppendArgs a{};
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.k_scales = k_scales;
+  a.v_scales = v_scales;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.q_start = query_start_loc;
+  a.num_seqs = num_seqs;
+  a.num_kv_heads = num_kv_heads;
+  a.head_dim = head_dim;
+  a.num_blocks = num_blocks;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.new_bf16 = new_dtype == PKV_BF16;
+  a.mode = mode == PKV_SCALE_RUNNING_AMAX ? 1 : 0;
+  return pkv::launch_kv_append_quant(a, static_cast<hipStream_t>(stream)) == hipSuccess
+             ? PKV_OK
+             : PKV_ERR_HIP;
+}
+
 size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
                                   int32_t max_context_len, int32_t partition_size) {
   if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 || partition_size < 0) return 0;

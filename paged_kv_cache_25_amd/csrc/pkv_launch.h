@@ -27,6 +27,23 @@ struct AppendArgs {
   int num_rows;
 };
 
+// Quantise-on-append into an e4m3 cache (pools are codes, scales float32
+// [num_blocks, num_kv_heads]); k_new/v_new are bf16 (new_bf16) or float32.
+struct QuantAppendArgs {
+  void* k_pool;
+  void* v_pool;
+  float* k_scales;
+  float* v_scales;
+  const void* k_new;
+  const void* v_new;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  const int32_t* q_start;          // null: one new row per sequence
+  int num_seqs, num_kv_heads, head_dim, num_blocks, max_blocks_per_seq;
+  int new_bf16;
+  int mode;                        // 0: fixed scales, 1: running amax
+};
+
 struct DecodeArgs {
   void* out;               // final output (q dtype) when write_final
   float* part_o;           // [B, Hq, maxP, D] when !write_final
@@ -112,6 +129,7 @@ struct MergeArgs {
 };
 
 hipError_t launch_kv_append(const AppendArgs& a, hipStream_t stream);
+hipError_t launch_kv_append_quant(const QuantAppendArgs& a, hipStream_t stream);
 hipError_t launch_paged_decode(const DecodeArgs& a, int head_dim, int tile_heads, DType q_dtype,
                                DType kv_dtype, hipStream_t stream);
 // Matrix-core variant for bf16 queries over a bf16 cache; heads in tiles of 16.

@@ -17,6 +17,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpkv.so")
 
 PKV_F32, PKV_BF16, PKV_FP8_E4M3 = 0, 1, 2
+PKV_SCALE_FIXED, PKV_SCALE_RUNNING_AMAX = 0, 1
 STATUS = {0: "PKV_OK", 1: "PKV_ERR_INVALID_ARG", 2: "PKV_ERR_UNSUPPORTED",
           3: "PKV_ERR_WORKSPACE", 4: "PKV_ERR_HIP"}
 BLOCK_SIZE = 16
@@ -69,6 +70,9 @@ def load():
     L.pkv_paged_multi_query_partials.restype = ctypes.c_int
     L.pkv_paged_multi_query_partials.argtypes = [P, P, I, P, P, P, P, P, P, P, P, I, I, I, I, I,
                                                  I, I, I, I, F, I, ctypes.c_int, ctypes.c_int, P]
+    L.pkv_kv_append_quant.restype = ctypes.c_int
+    L.pkv_kv_append_quant.argtypes = [P, P, P, P, P, P, ctypes.c_int, P, P, P, I, I, I, I, I, I, I,
+                                      ctypes.c_int, P]
     _lib = L
     return L
 
@@ -266,3 +270,23 @@ def paged_multi_query_partials(partial_out, partial_lse, q, k_pool, v_pool, bloc
         block_tables.shape[1], float(softmax_scale), int(partition_size), dtype_code(q.dtype),
         dtype_code(k_pool.dtype), _stream(stream)))
     return partial_out, partial_lse
+
+
+def kv_append_quant(k_pool, v_pool, k_scales, v_scales, k_new, v_new, block_tables,
+                    context_lens, query_start_loc=None, mode=PKV_SCALE_FIXED, stream=None):
+    """Quantise bf16/fp32 rows [R, Hkv, D] into the e4m3 pools and append them
+    (pkv_kv_append_quant); ``mode`` PKV_SCALE_FIXED or PKV_SCALE_RUNNING_AMAX."""
+    _need_cuda(k_pool, v_pool, k_scales, v_scales, k_new, v_new, block_tables, context_lens,
+               query_start_loc)
+    if dtype_code(k_pool.dtype) != PKV_FP8_E4M3 or dtype_code(v_pool.dtype) != PKV_FP8_E4M3:
+        raise TypeError("pools must be e4m3")
+    if k_new.dtype != v_new.dtype or k_new.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("new rows must be float32 or bfloat16")
+    if k_scales.dtype != torch.float32 or v_scales.dtype != torch.float32:
+        raise TypeError("scales are float32")
+    nb, hkv, bs, d = k_pool.shape
+    B = block_tables.shape[0]
+    _check("pkv_kv_append_quant", load().pkv_kv_append_quant(
+        _ptr(k_pool), _ptr(v_pool), _ptr(k_scales), _ptr(v_scales), _ptr(k_new), _ptr(v_new),
+        dtype_code(k_new.dtype), _ptr(block_tables), _ptr(context_lens), _ptr(query_start_loc), B,
+        k_new.shape[0], hkv, d, bs, nb, block_tables.shape[1], int(mode), _stream(stream)))

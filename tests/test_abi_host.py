@@ -35,7 +35,8 @@ def test_header_declares_the_entry_points():
         "pkv_abi_version", "pkv_status_string", "pkv_kv_append", "pkv_decode_workspace_bytes",
         "pkv_paged_decode_attention", "pkv_paged_decode_step", "pkv_paged_decode_partials",
         "pkv_merge_partials", "pkv_kv_append_tokens", "pkv_multi_query_workspace_bytes",
-        "pkv_paged_multi_query_attention", "pkv_paged_multi_query_partials"])
+        "pkv_paged_multi_query_attention", "pkv_paged_multi_query_partials",
+        "pkv_kv_append_quant"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -251,6 +252,31 @@ def test_multi_query_partials_validation(lib):
     assert _multi_partials(lib, d=96) == UNSUPPORTED
     assert _multi_partials(lib, kvt=ops.PKV_FP8_E4M3) == INVALID
     assert _multi_partials(lib, T=0, po=None, qsl=None) == OK
+
+
+def _quant(lib, **over):
+    a = dict(kp=FAKE, vp=FAKE, ks=FAKE, vs=FAKE, kn=FAKE, vn=FAKE, nd=ops.PKV_BF16, tables=FAKE,
+             lens=FAKE, qsl=None, B=2, R=2, hkv=2, d=128, bs=16, nb=8, mbps=4,
+             mode=ops.PKV_SCALE_RUNNING_AMAX)
+    a.update(over)
+    return lib.pkv_kv_append_quant(a["kp"], a["vp"], a["ks"], a["vs"], a["kn"], a["vn"], a["nd"],
+                                   a["tables"], a["lens"], a["qsl"], a["B"], a["R"], a["hkv"],
+                                   a["d"], a["bs"], a["nb"], a["mbps"], a["mode"], None)
+
+
+def test_quant_append_validation(lib):
+    assert _quant(lib, ks=None) == INVALID
+    assert _quant(lib, vn=None) == INVALID
+    assert _quant(lib, nd=ops.PKV_FP8_E4M3) == INVALID       # new rows must be wider
+    assert _quant(lib, mode=2) == INVALID
+    assert _quant(lib, kn=ctypes.c_void_p(0x10008)) == INVALID
+    assert _quant(lib, ks=ctypes.c_void_p(0x10002)) == INVALID
+    assert _quant(lib, qsl=ctypes.c_void_p(0x10002)) == INVALID
+    assert _quant(lib, hkv=0) == INVALID
+    assert _quant(lib, d=96) == UNSUPPORTED
+    assert _quant(lib, bs=8) == UNSUPPORTED
+    assert _quant(lib, B=0, kp=None) == OK
+    assert _quant(lib, R=0, kp=None) == OK
 
 
 def test_binding_refuses_cpu_tensors():

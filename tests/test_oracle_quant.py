@@ -12,6 +12,7 @@ import torch
 
 import oracle.kv_quant as kq
 from oracle.paged_attention import decode_e4m3fn
+from workloads.fp8_append import fp8_append_state
 
 pytestmark = pytest.mark.filterwarnings("ignore::RuntimeWarning")
 
@@ -87,40 +88,8 @@ def test_encoder_saturates():
 
 # --- the append ------------------------------------------------------------------
 
-def _state(seed=0, B=5, hkv=3, D=64, bs=16, t=None):
-    """Synthetic fp8 pool state: random codes, random positive scales, a few
-    sequences with shuffled blocks; new rows as float32 values (bf16-exact)."""
-    rng = np.random.default_rng(seed)
-    ctx = rng.integers(1, 70, B)
-    if t is not None:
-        ctx = np.maximum(ctx, t)
-    nblk = -(-ctx // bs)
-    NB = int(nblk.sum()) + 3
-    perm = rng.permutation(NB)
-    tables = np.full((B, int(nblk.max()) + 1), -1, np.int32)
-    c = 0
-    for b in range(B):
-        tables[b, :nblk[b]] = perm[c:c + nblk[b]]
-        c += nblk[b]
-    pool_k = rng.integers(0, 256, (NB, hkv, bs, D)).astype(np.uint8)
-    pool_v = rng.integers(0, 256, (NB, hkv, bs, D)).astype(np.uint8)
-    pool_k[pool_k & 0x7F == 0x7F] = 0x11                   # no NaN codes in the state
-    pool_v[pool_v & 0x7F == 0x7F] = 0x22
-    ks = (rng.uniform(0.5, 2.0, (NB, hkv)) / 448).astype(np.float32)
-    vs = (rng.uniform(0.5, 2.0, (NB, hkv)) / 448).astype(np.float32)
-    if t is None:
-        qsl = None
-        rows = B
-    else:
-        tt = np.full(B, t)
-        qsl = np.concatenate([[0], np.cumsum(tt)]).astype(np.int32)
-        rows = int(qsl[-1])
-    bf = torch.from_numpy(rng.standard_normal((rows, hkv, D)).astype(np.float32) * 1.5)
-    k_new = bf.to(torch.bfloat16).float().numpy()
-    v_new = torch.from_numpy(rng.standard_normal((rows, hkv, D)).astype(np.float32)).to(
-        torch.bfloat16).float().numpy()
-    return dict(k_pool=pool_k, v_pool=pool_v, k_scales=ks, v_scales=vs, k_new=k_new, v_new=v_new,
-                block_tables=tables, context_lens=ctx.astype(np.int32), query_start_loc=qsl)
+def _state(seed=0, B=5, hkv=3, D=64, t=None):
+    return fp8_append_state(seed=seed, num_seqs=B, num_kv_heads=hkv, head_dim=D, new_tokens=t)
 
 
 def _placed(st, bs=16):
