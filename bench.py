@@ -55,6 +55,9 @@ def parse():
     ap.add_argument("--new-tokens", type=int, default=0,
                     help="time the multi-token path instead: every sequence of the workload "
                          "brings this many new tokens (append + shifted-causal attention)")
+    ap.add_argument("--quant-append", choices=["fixed", "running"], default=None,
+                    help="with an e4m3 workload: the step appends bf16 rows through "
+                         "pkv_kv_append_quant (scale policy fixed or running amax), then attends")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only time a plain device-to-device copy of this many MiB (the "
                          "reference kernel for scaling FETCH_SIZE / WRITE_SIZE counters)")
@@ -94,6 +97,9 @@ def main():
         return
     if args.new_tokens:
         main_multi(args)
+        return
+    if args.quant_append:
+        main_quant(args)
         return
 
     import torch
@@ -465,6 +471,115 @@ def main_multi(args):
                      "traffic": None, "algorithmic_bytes_per_launch": tr["kv_bytes"],
                      "flops_per_launch": tr["flops"]},
         "cpu_baseline": cpu,
+        "input_copies": n_copies,
+    }
+    print(json.dumps(result), flush=True)
+
+
+def main_quant(args):
+    """An e4m3 decode step whose new K/V rows arrive in bf16: one step is
+    pkv_kv_append_quant (quantise with the block's scale, fixed or running
+    amax) then pkv_paged_decode_attention."""
+    import torch
+
+    from paged_kv_cache_25_amd import ops, traffic
+    from workloads import named_config
+
+    lib = ops.load()
+    if not torch.cuda.is_available():
+        raise SystemExit("no GPU visible")
+    dev = torch.device("cuda:0")
+    cfg = 5 if args.config == 2 else args.config
+    inp = named_config(cfg, seed=args.seed)
+    if inp.kv_dtype != "fp8_e4m3":
+        raise SystemExit("--quant-append needs an e4m3 workload (e.g. --config 5)")
+    P = inp.partition_size if args.partition_size is None else args.partition_size
+    mode = ops.PKV_SCALE_RUNNING_AMAX if args.quant_append == "running" else ops.PKV_SCALE_FIXED
+    rng = np.random.default_rng(0)
+    new = [torch.from_numpy(rng.standard_normal(inp.k_new.shape).astype(np.float32)).to(
+        torch.bfloat16) for _ in range(2)]
+    base = dict(q=to_device(inp.q, inp.q_dtype, dev),
+                k_pool=to_device(inp.k_pool, inp.kv_dtype, dev),
+                v_pool=to_device(inp.v_pool, inp.kv_dtype, dev),
+                k_new=new[0].to(dev), v_new=new[1].to(dev),
+                tables=to_device(inp.block_tables, None, dev),
+                lens=to_device(inp.context_lens, None, dev),
+                k_scales=to_device(inp.k_scales, None, dev),
+                v_scales=to_device(inp.v_scales, None, dev))
+    copies, footprint = rotated_copies(base)
+    n_copies = len(copies)
+    B, Hq, Hkv, D = inp.num_seqs, inp.num_q_heads, inp.num_kv_heads, inp.head_dim
+    NB, MB, mcl = inp.num_blocks, inp.block_tables.shape[1], inp.max_context_len
+    qcode = ops.dtype_code(base["q"].dtype)
+    ws_bytes = ops.workspace_bytes(B, Hq, D, mcl, P)
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    V = ctypes.c_void_p
+
+    def ptr(t):
+        return None if t is None else V(t.data_ptr())
+
+    calls = []
+    for c in copies:
+        c["out"] = torch.empty(B, Hq, D, dtype=c["q"].dtype, device=dev)
+        c["ws"] = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+        qa = (ptr(c["k_pool"]), ptr(c["v_pool"]), ptr(c["k_scales"]), ptr(c["v_scales"]),
+              ptr(c["k_new"]), ptr(c["v_new"]), ops.PKV_BF16, ptr(c["tables"]), ptr(c["lens"]),
+              None, B, B, Hkv, D, 16, NB, MB, mode, sp)
+        att = (ptr(c["out"]), ptr(c["q"]), ptr(c["k_pool"]), ptr(c["v_pool"]),
+               ptr(c["k_scales"]), ptr(c["v_scales"]), ptr(c["tables"]), ptr(c["lens"]), B, Hq,
+               Hkv, D, 16, NB, MB, mcl, ctypes.c_float(inp.softmax_scale), P, ptr(c["ws"]),
+               ctypes.c_size_t(c["ws"].numel()), qcode, ops.PKV_FP8_E4M3, sp)
+        calls.append((qa, att))
+    f_q, f_att = lib.pkv_kv_append_quant, lib.pkv_paged_decode_attention
+
+    def step(i):
+        qa, att = calls[i % n_copies]
+        if f_q(*qa) != 0 or f_att(*att) != 0:
+            raise RuntimeError("libpkv call failed")
+
+    def quant_only(i):
+        if f_q(*calls[i % n_copies][0]) != 0:
+            raise RuntimeError("quant append failed")
+
+    def att_only(i):
+        if f_att(*calls[i % n_copies][1]) != 0:
+            raise RuntimeError("attention call failed")
+
+    print(f"[bench] {inp.name} + quantise-on-append ({args.quant_append}): {n_copies} input "
+          f"copies of {footprint / 1e6:.1f} MB; warmup {args.warmup}", file=sys.stderr, flush=True)
+    for i in range(args.warmup):
+        step(i)
+    timed = event_timer(stream)
+    step_ms = timed(step, args.steps)
+    quant_ms = timed(quant_only, args.kernel_reps)
+    att_ms = timed(att_only, args.kernel_reps)
+    tr = traffic.attention_call_traffic(inp.context_lens, num_q_heads=Hq, num_kv_heads=Hkv,
+                                        head_dim=D, q_dtype=inp.q_dtype, kv_dtype=inp.kv_dtype)
+    qb = traffic.quant_append_traffic(B, num_kv_heads=Hkv, head_dim=D, new_dtype="bf16")
+    value = (tr["total_bytes"] + qb["bytes"]) / (step_ms * 1e-3) / 1e9
+    result = {
+        "metric": "paged decode attention achieved HBM GB/s (% of peak) and decode tokens/s",
+        "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(step_ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None,
+        "dtype": f"fp8_e4m3 kv (quantised on append from bf16), {inp.q_dtype} q, f32 accumulate",
+        "data": "synthetic (seeded N(0,1) K/V/q, random block placement)",
+        "config": {"workload": f"{inp.name}_quant_{args.quant_append}", "batch": B,
+                   "q_heads": Hq, "kv_heads": Hkv, "head_dim": D, "block_size": 16,
+                   "partition_size": P, "context_tokens": int(inp.context_lens.sum()),
+                   "scale_policy": args.quant_append, "parallelism": "single GPU"},
+        "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
+        "tokens_per_s": round(B * 1e3 / step_ms, 1),
+        "kernel_us": {"quant_append": round(quant_ms * 1e3, 2),
+                      "attention_call": round(att_ms * 1e3, 2)},
+        "roofline": {"kernel": "kv_append_quant_kernel<bf16>", "bound": "hbm",
+                     "achieved": round(qb["bytes"] / (quant_ms * 1e-3) / 1e9, 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(qb["bytes"] / (quant_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 5),
+                     "traffic": None, "algorithmic_bytes_per_launch": qb["bytes"],
+                     "note": "launch-latency bound: a few hundred KB per launch"},
+        "cpu_baseline": None,
         "input_copies": n_copies,
     }
     print(json.dumps(result), flush=True)

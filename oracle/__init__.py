@@ -1,5 +1,6 @@
-"""CPU float64 oracle for decode-step attention over a paged KV cache, and
-(``oracle.kv_quant``) for appending to an fp8 cache with quantisation.
+"""CPU float64 oracle for decode-step attention over a paged KV cache,
+(``oracle.kv_quant``) for appending to an fp8 cache with quantisation, and
+(``oracle.block_manager``) for the block allocator with copy-on-write.
 
 TEST INFRASTRUCTURE ONLY: imported by the tests, by ``__graft_entry__.smoke()``
 and by the ``cpu_baseline`` leg of ``bench.py``; never by the library.
@@ -33,3 +34,4 @@ from .kv_quant import (  # noqa: F401
     kv_append_quant,
     quantize,
 )
+from .block_manager import BlockManager, OutOfBlocks, copy_blocks  # noqa: F401

@@ -110,3 +110,13 @@ def multi_query_traffic(context_lens, new_tokens, *, num_q_heads, num_kv_heads, 
                 scale_bytes=base["scale_bytes"], qo_bytes=qo, table_bytes=tables,
                 total_bytes=base["kv_bytes"] + base["scale_bytes"] + qo + tables,
                 flops=4 * head_dim * num_q_heads * pairs)
+
+
+def quant_append_traffic(num_rows, *, num_kv_heads, head_dim, new_dtype):
+    """Bytes quantise-on-append must move in fixed-scale mode: each new K and V
+    row read in its input dtype, its e4m3 codes written, and the slice's scale
+    read.  (A running-amax append that grows a scale also rewrites the slice's
+    earlier rows: up to 15 more code rows read and written.)"""
+    row = num_kv_heads * head_dim
+    per = 2 * (row * ELEM_BYTES[new_dtype] + row + num_kv_heads * 4)
+    return dict(bytes=num_rows * per)
