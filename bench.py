@@ -58,6 +58,9 @@ def parse():
     ap.add_argument("--quant-append", choices=["fixed", "running"], default=None,
                     help="with an e4m3 workload: the step appends bf16 rows through "
                          "pkv_kv_append_quant (scale policy fixed or running amax), then attends")
+    ap.add_argument("--copy-blocks", type=int, default=0,
+                    help="time pkv_copy_blocks alone: this many copy-on-write block copies "
+                         "of the workload's pools (bf16 Llama-3-8B blocks: 32 KiB each of K and V)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only time a plain device-to-device copy of this many MiB (the "
                          "reference kernel for scaling FETCH_SIZE / WRITE_SIZE counters)")
@@ -100,6 +103,9 @@ def main():
         return
     if args.quant_append:
         main_quant(args)
+        return
+    if args.copy_blocks:
+        main_copy_blocks(args)
         return
 
     import torch
@@ -583,6 +589,64 @@ def main_quant(args):
         "input_copies": n_copies,
     }
     print(json.dumps(result), flush=True)
+
+
+def main_copy_blocks(args):
+    """pkv_copy_blocks on its own: ``--copy-blocks`` (src, dst) pairs over the
+    workload's pools (distinct destinations, none a source), rotated over
+    several pair lists so the sources come from HBM."""
+    import torch
+
+    from paged_kv_cache_25_amd import ops
+    from workloads import named_config
+
+    lib = ops.load()
+    dev = torch.device("cuda:0")
+    inp = named_config(args.config, seed=args.seed)
+    NB, Hkv, D = inp.num_blocks, inp.num_kv_heads, inp.head_dim
+    n = args.copy_blocks
+    if 2 * n > NB:
+        raise SystemExit(f"--copy-blocks {n}: the pool has {NB} blocks; at most {NB // 2}")
+    kp = to_device(inp.k_pool, inp.kv_dtype, dev)
+    vp = to_device(inp.v_pool, inp.kv_dtype, dev)
+    ks = None if inp.k_scales is None else to_device(inp.k_scales, None, dev)
+    vs = None if inp.v_scales is None else to_device(inp.v_scales, None, dev)
+    rng = np.random.default_rng(0)
+    lists = []
+    for _ in range(4):
+        ids = rng.permutation(NB)
+        lists.append(torch.tensor(np.stack([ids[:n], ids[n:2 * n]], 1).astype(np.int32), device=dev))
+    code = ops.dtype_code(kp.dtype)
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    V = ctypes.c_void_p
+    f = lib.pkv_copy_blocks
+
+    def run(i):
+        pr = lists[i % len(lists)]
+        if f(V(kp.data_ptr()), V(vp.data_ptr()), None if ks is None else V(ks.data_ptr()),
+             None if vs is None else V(vs.data_ptr()), V(pr.data_ptr()), n, NB, Hkv, D, 16, code,
+             sp) != 0:
+            raise RuntimeError("pkv_copy_blocks failed")
+
+    for i in range(args.warmup):
+        run(i)
+    timed = event_timer(stream)
+    ms = timed(run, args.steps)
+    block = Hkv * 16 * D * {"f32": 4, "bf16": 2, "fp8_e4m3": 1}[inp.kv_dtype]
+    moved = n * 2 * block * 2 + (n * Hkv * 4 * 4 if ks is not None else 0)   # read + write
+    gbps = moved / (ms * 1e-3) / 1e9
+    print(json.dumps({
+        "metric": "copy-on-write block copies achieved HBM GB/s (read + write)",
+        "value": round(gbps, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": inp.kv_dtype, "data": "synthetic",
+        "config": {"workload": f"{inp.name}_copy_blocks_{n}", "pairs": n, "block_bytes": block,
+                   "kv_heads": Hkv, "head_dim": D},
+        "roofline": {"kernel": "copy_blocks_kernel", "bound": "hbm", "achieved": round(gbps, 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4),
+                     "traffic": None, "algorithmic_bytes_per_launch": moved},
+        "cpu_baseline": None}), flush=True)
 
 
 def cpu_baseline_multi(inp, budget_s):

@@ -80,7 +80,8 @@ typedef enum {
   PKV_ERR_INVALID_ARG = 1,   /* null pointer, non-positive size, bad relation */
   PKV_ERR_UNSUPPORTED = 2,   /* valid but not built: head_dim, block_size, dtypes */
   PKV_ERR_WORKSPACE = 3,     /* workspace missing or smaller than required */
-  PKV_ERR_HIP = 4            /* a HIP launch failed */
+  PKV_ERR_HIP = 4,           /* a HIP launch failed */
+  PKV_ERR_OUT_OF_BLOCKS = 5  /* the block allocator has too few free blocks; nothing changed */
 } pkv_status_t;
 
 /* The version of this header the library was built from (PKV_ABI_VERSION). */
@@ -397,6 +398,94 @@ pkv_status_t pkv_kv_append_quant(void* k_pool, void* v_pool, float* k_scales, fl
                                  int32_t block_size, int32_t num_blocks,
                                  int32_t max_blocks_per_seq, pkv_scale_mode_t mode,
                                  void* stream);
+
+/*
+ * Block allocator (host side) and copy-on-write copies (device side)
+ * ------------------------------------------------------------------
+ * The memory manager just above the kernels.  Blocks are handed out on
+ * demand: a sequence takes a new block only when its last one is full, so it
+ * wastes at most block_size - 1 slots; a finished sequence returns its blocks
+ * at once.  The free list starts as 0 .. num_blocks-1, allocation takes its
+ * last entry and freeing appends the sequence's table in order.  A physical
+ * block may be held by several sequences (forked samples of one prompt); a
+ * reference count says how many.  Before a sequence writes into a block whose
+ * count is above 1 it moves to a private copy: a fresh block, the old block's
+ * count minus 1, and a (src, dst) pair for pkv_copy_blocks.  The last sharer
+ * writes in place.  Only a partly filled last block is ever written, so one
+ * append needs at most one copy.
+ *   KV-cache post, "PagedAttention: the KV cache in blocks" (allocate on
+ *   demand, free immediately, sharing with copy-on-write); brunomaga post,
+ *   "PagedAttention: memory management for the KV cache" (PagedKVCache:
+ *   free-list order, out of blocks is the scheduler's problem); serving
+ *   lesson, "Sharing (section 4.4)" and exercise 3 (three samples of a
+ *   100-token prompt: 21 blocks unshared, 7 shared, 9 after each writes one
+ *   token).
+ * The allocator is plain host memory, not thread-safe (one scheduler thread
+ * owns it), and never touches the GPU.  Sequence ids are caller-chosen int64.
+ */
+typedef struct pkv_block_manager pkv_block_manager_t;
+
+/* A new allocator over num_blocks blocks of block_size tokens; NULL on bad sizes or no memory. */
+pkv_block_manager_t* pkv_bm_create(int32_t num_blocks, int32_t block_size);
+void pkv_bm_destroy(pkv_block_manager_t* bm);
+
+/* An empty sequence.  PKV_ERR_INVALID_ARG if the id is taken. */
+pkv_status_t pkv_bm_add_seq(pkv_block_manager_t* bm, int64_t seq_id);
+
+/* child shares all of parent's blocks (counts + 1) and its length.  The
+ * parent must exist and the child must not. */
+pkv_status_t pkv_bm_fork(pkv_block_manager_t* bm, int64_t parent, int64_t child);
+
+/* Drop a sequence: each of its blocks' counts - 1; blocks reaching 0 go back
+ * to the free list in table order. */
+pkv_status_t pkv_bm_free_seq(pkv_block_manager_t* bm, int64_t seq_id);
+
+/* Make room for num_tokens new tokens of seq_id (positions len .. len+n-1):
+ * new blocks as needed and, if the partly filled last block is shared, a
+ * private copy of it, returned as copy_src[0] -> copy_dst[0] with
+ * *num_copies = 1 (else 0).  copy_src/copy_dst [host, written] need room for
+ * max_copies >= 1 entries when a copy is needed (else PKV_ERR_INVALID_ARG).
+ * PKV_ERR_OUT_OF_BLOCKS, with nothing changed, when too few blocks are
+ * free.  The caller must run the copies (pkv_copy_blocks) before writing the
+ * new tokens. */
+pkv_status_t pkv_bm_append_slots(pkv_block_manager_t* bm, int64_t seq_id, int32_t num_tokens,
+                                 int32_t* copy_src, int32_t* copy_dst, int32_t max_copies,
+                                 int32_t* num_copies);
+
+/* Free blocks (-1 for a NULL allocator). */
+int32_t pkv_bm_num_free(const pkv_block_manager_t* bm);
+/* Reference count of a block (-1 if out of range). */
+int32_t pkv_bm_refcount(const pkv_block_manager_t* bm, int32_t block);
+/* Tokens of a sequence (-1 if unknown). */
+int64_t pkv_bm_seq_len(const pkv_block_manager_t* bm, int64_t seq_id);
+/* The free list, next allocation last: writes up to max_entries into out
+ * [host] (may be NULL) and returns its length. */
+int32_t pkv_bm_free_list(const pkv_block_manager_t* bm, int32_t* out, int32_t max_entries);
+
+/* The block tables and lengths of num_seqs sequences, in the layout the
+ * attention calls take: block_tables int32 [num_seqs, max_blocks_per_seq]
+ * (-1 past each table) and context_lens int32 [num_seqs] [host, written].
+ * PKV_ERR_INVALID_ARG (nothing written) for an unknown id or a table longer
+ * than max_blocks_per_seq. */
+pkv_status_t pkv_bm_block_tables(const pkv_block_manager_t* bm, const int64_t* seq_ids,
+                                 int32_t num_seqs, int32_t* block_tables,
+                                 int32_t max_blocks_per_seq, int32_t* context_lens);
+
+/*
+ * pkv_copy_blocks - run copy-on-write copies on the GPU: for each pair
+ * (src, dst) of pairs int32 [num_pairs][2] [device, read], block dst of
+ * k_pool and of v_pool (all num_kv_heads x block_size x head_dim elements)
+ * becomes a bitwise copy of block src; for an e4m3 cache k_scales/v_scales
+ * [device, read and written] rows dst become copies of rows src (the scales
+ * are ignored, and may be NULL, for other dtypes).  Every copy reads the
+ * state before the call: destinations must be distinct and none may be a
+ * source.  Pairs with an id outside [0, num_blocks) are skipped.
+ * Supported: head_dim in {64, 128}, block_size == 16, num_kv_heads <= 256.
+ */
+pkv_status_t pkv_copy_blocks(void* k_pool, void* v_pool, float* k_scales, float* v_scales,
+                             const int32_t* pairs, int32_t num_pairs, int32_t num_blocks,
+                             int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                             pkv_dtype_t kv_dtype, void* stream);
 
 #ifdef __cplusplus
 }

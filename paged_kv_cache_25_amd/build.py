@@ -1,8 +1,8 @@
 """Build libpkv.so (the HIP kernels and the C ABI) in-tree for gfx950.
 
 ``python -m paged_kv_cache_25_amd.build`` compiles every ``csrc/*.hip`` with
-hipcc into objects under ``_build/`` and links ``libpkv.so`` next to this
-file.  Packed-fp32 instructions are disabled for the device code.
+hipcc (and the host-only ``csrc/*.cpp`` with g++) into objects under
+``_build/`` and links ``libpkv.so`` next to this file.  Packed-fp32 instructions are disabled for the device code.
 """
 
 from __future__ import annotations
@@ -30,9 +30,16 @@ FLAGS = [
 ]
 
 
+CXX = shutil.which("g++") or "g++"
+CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", f"-I{INCLUDE}"]
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", src, "-o", obj]
+    if src.endswith(".cpp"):                  # host-only code (the block allocator)
+        cmd = [CXX, *CXX_FLAGS, "-c", src, "-o", obj]
+    else:
+        cmd = [HIPCC, *FLAGS, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")
@@ -41,7 +48,7 @@ def _compile(src: str) -> str:
 
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
-    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
     workers = min(len(srcs), int(os.environ.get("MAX_JOBS", "8")))
     with concurrent.futures.ThreadPoolExecutor(max_workers=workers) as ex:
         objs = list(ex.map(_compile, srcs))

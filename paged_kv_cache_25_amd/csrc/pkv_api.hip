@@ -70,6 +70,7 @@ const char* pkv_status_string(int status) {
     case PKV_ERR_UNSUPPORTED: return "PKV_ERR_UNSUPPORTED";
     case PKV_ERR_WORKSPACE: return "PKV_ERR_WORKSPACE";
     case PKV_ERR_HIP: return "PKV_ERR_HIP";
+    case PKV_ERR_OUT_OF_BLOCKS: return "PKV_ERR_OUT_OF_BLOCKS";
     default: return "PKV_UNKNOWN_STATUS";
   }
 }
@@ -180,6 +181,37 @@ pkv_status_t pkv_kv_append_quant(void* k_pool, void* v_pool, float* k_scales, fl
   a.new_bf16 = new_dtype == PKV_BF16;
   a.mode = mode == PKV_SCALE_RUNNING_AMAX ? 1 : 0;
   return pkv::launch_kv_append_quant(a, static_cast<hipStream_t>(stream)) == hipSuccess
+             ? PKV_OK
+             : PKV_ERR_HIP;
+}
+
+pkv_status_t pkv_copy_blocks(void* k_pool, void* v_pool, float* k_scales, float* v_scales,
+                             const int32_t* pairs, int32_t num_pairs, int32_t num_blocks,
+                             int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                             pkv_dtype_t kv_dtype, void* stream) {
+  if (num_pairs < 0 || num_blocks <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+      block_size <= 0 || !dtype_ok(kv_dtype))
+    return PKV_ERR_INVALID_ARG;
+  if (!head_dim_ok(head_dim) || block_size != pkv::kBlockSizeBuilt) return PKV_ERR_UNSUPPORTED;
+  if (num_kv_heads > 256) return PKV_ERR_UNSUPPORTED;
+  if (num_pairs == 0) return PKV_OK;
+  if (!k_pool || !v_pool || !pairs) return PKV_ERR_INVALID_ARG;
+  if (kv_dtype == PKV_FP8_E4M3 && (!k_scales || !v_scales)) return PKV_ERR_INVALID_ARG;
+  if (!aligned16(k_pool) || !aligned16(v_pool) || !aligned4(pairs) || !aligned4(k_scales) ||
+      !aligned4(v_scales))
+    return PKV_ERR_INVALID_ARG;
+  pkv::CopyBlocksArgs a{};
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.k_scales = kv_dtype == PKV_FP8_E4M3 ? k_scales : nullptr;
+  a.v_scales = kv_dtype == PKV_FP8_E4M3 ? v_scales : nullptr;
+  a.pairs = pairs;
+  a.num_pairs = num_pairs;
+  a.num_blocks = num_blocks;
+  a.num_kv_heads = num_kv_heads;
+  a.block_bytes = size_t(num_kv_heads) * size_t(block_size) * size_t(head_dim) *
+                  size_t(pkv::dtype_bytes(to_internal(kv_dtype)));
+  return pkv::launch_copy_blocks(a, static_cast<hipStream_t>(stream)) == hipSuccess
              ? PKV_OK
              : PKV_ERR_HIP;
 }

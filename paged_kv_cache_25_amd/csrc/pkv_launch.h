@@ -44,6 +44,17 @@ struct QuantAppendArgs {
   int mode;                        // 0: fixed scales, 1: running amax
 };
 
+// Copy-on-write block copies: pairs int32 [num_pairs][2] = (src, dst).
+struct CopyBlocksArgs {
+  void* k_pool;
+  void* v_pool;
+  float* k_scales;                 // null unless the cache is e4m3
+  float* v_scales;
+  const int32_t* pairs;
+  int num_pairs, num_blocks, num_kv_heads;
+  size_t block_bytes;              // one physical block of one pool, all KV heads
+};
+
 struct DecodeArgs {
   void* out;               // final output (q dtype) when write_final
   float* part_o;           // [B, Hq, maxP, D] when !write_final
@@ -130,6 +141,7 @@ struct MergeArgs {
 
 hipError_t launch_kv_append(const AppendArgs& a, hipStream_t stream);
 hipError_t launch_kv_append_quant(const QuantAppendArgs& a, hipStream_t stream);
+hipError_t launch_copy_blocks(const CopyBlocksArgs& a, hipStream_t stream);
 hipError_t launch_paged_decode(const DecodeArgs& a, int head_dim, int tile_heads, DType q_dtype,
                                DType kv_dtype, hipStream_t stream);
 // Matrix-core variant for bf16 queries over a bf16 cache; heads in tiles of 16.

@@ -19,7 +19,8 @@ LIB_PATH = os.path.join(_HERE, "libpkv.so")
 PKV_F32, PKV_BF16, PKV_FP8_E4M3 = 0, 1, 2
 PKV_SCALE_FIXED, PKV_SCALE_RUNNING_AMAX = 0, 1
 STATUS = {0: "PKV_OK", 1: "PKV_ERR_INVALID_ARG", 2: "PKV_ERR_UNSUPPORTED",
-          3: "PKV_ERR_WORKSPACE", 4: "PKV_ERR_HIP"}
+          3: "PKV_ERR_WORKSPACE", 4: "PKV_ERR_HIP", 5: "PKV_ERR_OUT_OF_BLOCKS"}
+PKV_ERR_OUT_OF_BLOCKS = 5
 BLOCK_SIZE = 16
 
 _lib = None
@@ -73,6 +74,31 @@ def load():
     L.pkv_kv_append_quant.restype = ctypes.c_int
     L.pkv_kv_append_quant.argtypes = [P, P, P, P, P, P, ctypes.c_int, P, P, P, I, I, I, I, I, I, I,
                                       ctypes.c_int, P]
+    I64 = ctypes.c_int64
+    L.pkv_bm_create.restype = P
+    L.pkv_bm_create.argtypes = [I, I]
+    L.pkv_bm_destroy.restype = None
+    L.pkv_bm_destroy.argtypes = [P]
+    L.pkv_bm_add_seq.restype = ctypes.c_int
+    L.pkv_bm_add_seq.argtypes = [P, I64]
+    L.pkv_bm_fork.restype = ctypes.c_int
+    L.pkv_bm_fork.argtypes = [P, I64, I64]
+    L.pkv_bm_free_seq.restype = ctypes.c_int
+    L.pkv_bm_free_seq.argtypes = [P, I64]
+    L.pkv_bm_append_slots.restype = ctypes.c_int
+    L.pkv_bm_append_slots.argtypes = [P, I64, I, P, P, I, P]
+    L.pkv_bm_num_free.restype = I
+    L.pkv_bm_num_free.argtypes = [P]
+    L.pkv_bm_refcount.restype = I
+    L.pkv_bm_refcount.argtypes = [P, I]
+    L.pkv_bm_seq_len.restype = I64
+    L.pkv_bm_seq_len.argtypes = [P, I64]
+    L.pkv_bm_free_list.restype = I
+    L.pkv_bm_free_list.argtypes = [P, P, I]
+    L.pkv_bm_block_tables.restype = ctypes.c_int
+    L.pkv_bm_block_tables.argtypes = [P, P, I, P, I, P]
+    L.pkv_copy_blocks.restype = ctypes.c_int
+    L.pkv_copy_blocks.argtypes = [P, P, P, P, P, I, I, I, I, I, ctypes.c_int, P]
     _lib = L
     return L
 
@@ -290,3 +316,79 @@ def kv_append_quant(k_pool, v_pool, k_scales, v_scales, k_new, v_new, block_tabl
         _ptr(k_pool), _ptr(v_pool), _ptr(k_scales), _ptr(v_scales), _ptr(k_new), _ptr(v_new),
         dtype_code(k_new.dtype), _ptr(block_tables), _ptr(context_lens), _ptr(query_start_loc), B,
         k_new.shape[0], hkv, d, bs, nb, block_tables.shape[1], int(mode), _stream(stream)))
+
+
+class BlockManager:
+    """The library's host-side block allocator (pkv_bm_*): on-demand blocks,
+    reference counts, forks and copy-on-write.  ``append_slots`` returns the
+    (src, dst) copies to run with ``copy_blocks`` before writing."""
+
+    def __init__(self, num_blocks: int, block_size: int = BLOCK_SIZE):
+        self._L = load()
+        self._h = self._L.pkv_bm_create(num_blocks, block_size)
+        if not self._h:
+            raise ValueError("pkv_bm_create failed")
+        self.num_blocks, self.block_size = num_blocks, block_size
+
+    def close(self):
+        if self._h:
+            self._L.pkv_bm_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def add(self, seq: int):
+        _check("pkv_bm_add_seq", self._L.pkv_bm_add_seq(self._h, seq))
+
+    def fork(self, parent: int, child: int):
+        _check("pkv_bm_fork", self._L.pkv_bm_fork(self._h, parent, child))
+
+    def free_seq(self, seq: int):
+        _check("pkv_bm_free_seq", self._L.pkv_bm_free_seq(self._h, seq))
+
+    def append_slots(self, seq: int, n: int):
+        src, dst, cnt = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+        _check("pkv_bm_append_slots", self._L.pkv_bm_append_slots(
+            self._h, seq, n, ctypes.byref(src), ctypes.byref(dst), 1, ctypes.byref(cnt)))
+        return [(src.value, dst.value)] if cnt.value else []
+
+    def num_free(self) -> int:
+        return self._L.pkv_bm_num_free(self._h)
+
+    def refcount(self, block: int) -> int:
+        return self._L.pkv_bm_refcount(self._h, block)
+
+    def seq_len(self, seq: int) -> int:
+        return self._L.pkv_bm_seq_len(self._h, seq)
+
+    def free_list(self):
+        n = self._L.pkv_bm_free_list(self._h, None, 0)
+        buf = (ctypes.c_int32 * max(n, 1))()
+        self._L.pkv_bm_free_list(self._h, buf, n)
+        return list(buf)[:n]
+
+    def block_tables(self, seqs, max_blocks: int):
+        """int32 numpy [len(seqs), max_blocks] tables (-1 padded) and lengths."""
+        import numpy as np
+        ids = np.ascontiguousarray(seqs, dtype=np.int64)
+        tables = np.empty((len(ids), max_blocks), np.int32)
+        lens = np.empty(len(ids), np.int32)
+        _check("pkv_bm_block_tables", self._L.pkv_bm_block_tables(
+            self._h, ids.ctypes.data_as(ctypes.c_void_p), len(ids),
+            tables.ctypes.data_as(ctypes.c_void_p), max_blocks,
+            lens.ctypes.data_as(ctypes.c_void_p)))
+        return tables, lens
+
+
+def copy_blocks(k_pool, v_pool, pairs, k_scales=None, v_scales=None, stream=None):
+    """Run copy-on-write copies: pairs int32 [n, 2] (src, dst) on the device."""
+    _need_cuda(k_pool, v_pool, pairs, k_scales, v_scales)
+    nb, hkv, bs, d = k_pool.shape
+    _check("pkv_copy_blocks", load().pkv_copy_blocks(
+        _ptr(k_pool), _ptr(v_pool), _ptr(k_scales), _ptr(v_scales), _ptr(pairs),
+        pairs.shape[0] if pairs.numel() else 0, nb, hkv, d, bs, dtype_code(k_pool.dtype),
+        _stream(stream)))

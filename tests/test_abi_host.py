@@ -36,7 +36,10 @@ def test_header_declares_the_entry_points():
         "pkv_paged_decode_attention", "pkv_paged_decode_step", "pkv_paged_decode_partials",
         "pkv_merge_partials", "pkv_kv_append_tokens", "pkv_multi_query_workspace_bytes",
         "pkv_paged_multi_query_attention", "pkv_paged_multi_query_partials",
-        "pkv_kv_append_quant"])
+        "pkv_kv_append_quant", "pkv_bm_create", "pkv_bm_destroy", "pkv_bm_add_seq",
+        "pkv_bm_fork", "pkv_bm_free_seq", "pkv_bm_append_slots", "pkv_bm_num_free",
+        "pkv_bm_refcount", "pkv_bm_seq_len", "pkv_bm_free_list", "pkv_bm_block_tables",
+        "pkv_copy_blocks"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -277,6 +280,26 @@ def test_quant_append_validation(lib):
     assert _quant(lib, bs=8) == UNSUPPORTED
     assert _quant(lib, B=0, kp=None) == OK
     assert _quant(lib, R=0, kp=None) == OK
+
+
+def _copy(lib, **over):
+    a = dict(kp=FAKE, vp=FAKE, ks=None, vs=None, pairs=FAKE, n=3, nb=8, hkv=2, d=128, bs=16,
+             kv=ops.PKV_BF16)
+    a.update(over)
+    return lib.pkv_copy_blocks(a["kp"], a["vp"], a["ks"], a["vs"], a["pairs"], a["n"], a["nb"],
+                               a["hkv"], a["d"], a["bs"], a["kv"], None)
+
+
+def test_copy_blocks_validation(lib):
+    assert _copy(lib, pairs=None) == INVALID
+    assert _copy(lib, kp=None) == INVALID
+    assert _copy(lib, n=-1) == INVALID
+    assert _copy(lib, kv=ops.PKV_FP8_E4M3) == INVALID          # e4m3 without scales
+    assert _copy(lib, kp=ctypes.c_void_p(0x10008)) == INVALID
+    assert _copy(lib, pairs=ctypes.c_void_p(0x10002)) == INVALID
+    assert _copy(lib, d=96) == UNSUPPORTED
+    assert _copy(lib, hkv=300) == UNSUPPORTED
+    assert _copy(lib, n=0, kp=None, pairs=None) == OK
 
 
 def test_binding_refuses_cpu_tensors():
