@@ -1,6 +1,7 @@
 """CPU float64 oracle for decode-step attention over a paged KV cache,
 (``oracle.kv_quant``) for appending to an fp8 cache with quantisation, and
-(``oracle.block_manager``) for the block allocator with copy-on-write.
+(``oracle.block_manager``) for the block allocator with copy-on-write, and
+(``oracle.mla``) for absorbed multi-head latent attention decode.
 
 TEST INFRASTRUCTURE ONLY: imported by the tests, by ``__graft_entry__.smoke()``
 and by the ``cpu_baseline`` leg of ``bench.py``; never by the library.
@@ -35,3 +36,4 @@ from .kv_quant import (  # noqa: F401
     quantize,
 )
 from .block_manager import BlockManager, OutOfBlocks, copy_blocks  # noqa: F401
+from .mla import absorb_query, mla_decode_absorbed, mla_decode_expanded, project_out  # noqa: F401

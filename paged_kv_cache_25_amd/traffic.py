@@ -120,3 +120,29 @@ def quant_append_traffic(num_rows, *, num_kv_heads, head_dim, new_dtype):
     row = num_kv_heads * head_dim
     per = 2 * (row * ELEM_BYTES[new_dtype] + row + num_kv_heads * 4)
     return dict(bytes=num_rows * per)
+
+
+def mla_numbers_per_token(kv_lora_rank: int, rope_dim: int) -> int:
+    """Numbers an MLA layer caches per token: the latent plus the shared rotary key."""
+    return kv_lora_rank + rope_dim
+
+
+def mla_attention_traffic(context_lens, *, num_heads, kv_lora_rank, rope_dim, dtype="bf16",
+                          block_size=16):
+    """Algorithmic bytes and FLOPs of one absorbed MLA decode-attention call.
+    Bytes: every attended token's one shared row (d_c + d_r numbers), the
+    absorbed queries, the latent outputs, table entries and lengths.  FLOPs:
+    per token and head, 2 (d_c + d_r) for the score and 2 d_c for the
+    weighted sum of latents."""
+    ctx = np.asarray(context_lens, dtype=np.int64)
+    tokens = int(ctx.sum())
+    e = ELEM_BYTES[dtype]
+    d = kv_lora_rank + rope_dim
+    B = len(ctx)
+    kv = tokens * d * e
+    nblk = int(blocks_needed(ctx, block_size).sum())
+    qo = B * num_heads * (d + kv_lora_rank) * e
+    tables = 4 * nblk + 4 * B
+    return dict(tokens=tokens, kv_bytes=kv, qo_bytes=qo, table_bytes=tables,
+                total_bytes=kv + qo + tables,
+                flops=tokens * num_heads * 2 * (d + kv_lora_rank))
