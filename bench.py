@@ -61,6 +61,9 @@ def parse():
     ap.add_argument("--copy-blocks", type=int, default=0,
                     help="time pkv_copy_blocks alone: this many copy-on-write block copies "
                          "of the workload's pools (bf16 Llama-3-8B blocks: 32 KiB each of K and V)")
+    ap.add_argument("--mla", default=None,
+                    help="time absorbed MLA decode on a named latent-cache workload instead "
+                         "(deepseek_mla_b64, deepseek_lite_mla_b8)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only time a plain device-to-device copy of this many MiB (the "
                          "reference kernel for scaling FETCH_SIZE / WRITE_SIZE counters)")
@@ -106,6 +109,9 @@ def main():
         return
     if args.copy_blocks:
         main_copy_blocks(args)
+        return
+    if args.mla:
+        main_mla(args)
         return
 
     import torch
@@ -647,6 +653,111 @@ def main_copy_blocks(args):
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4),
                      "traffic": None, "algorithmic_bytes_per_launch": moved},
         "cpu_baseline": None}), flush=True)
+
+
+def main_mla(args):
+    """Absorbed MLA decode: one step is pkv_mla_append (the new latent row)
+    then pkv_mla_decode_attention over the paged latent cache.  The decode
+    kernel alone is timed through pkv_mla_decode_partials."""
+    import torch
+
+    from paged_kv_cache_25_amd import ops, traffic
+    from workloads.mla import named_mla
+
+    lib = ops.load()
+    dev = torch.device("cuda:0")
+    t0 = time.time()
+    inp = named_mla(args.mla)
+    P = inp.partition_size if args.partition_size is None else args.partition_size
+    print(f"[bench] workload {inp.name}: generated in {time.time() - t0:.1f}s", file=sys.stderr,
+          flush=True)
+    base = dict(q=to_device(inp.q, inp.dtype, dev), pool=to_device(inp.latent_pool, inp.dtype, dev),
+                new=to_device(inp.latent_new, inp.dtype, dev),
+                tables=to_device(inp.block_tables, None, dev),
+                lens=to_device(inp.context_lens, None, dev))
+    copies, footprint = rotated_copies(base)
+    n_copies = len(copies)
+    B, H, dc, dr = inp.num_seqs, inp.num_heads, inp.kv_lora_rank, inp.rope_dim
+    NB, MB, mcl = inp.num_blocks, inp.block_tables.shape[1], inp.max_context_len
+    ws_bytes = int(lib.pkv_mla_workspace_bytes(B, H, dc, mcl, P))
+    maxp = max(1, -(-mcl // P)) if P else 1
+    lse_off = ((B * H * maxp * dc * 4 + 255) // 256) * 256
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    V = ctypes.c_void_p
+
+    def ptr(t):
+        return V(t.data_ptr())
+
+    calls = []
+    for c in copies:
+        c["out"] = torch.empty(B, H, dc, dtype=torch.bfloat16, device=dev)
+        c["ws"] = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+        c["parts"] = torch.empty(lse_off + B * H * maxp * 4, dtype=torch.uint8, device=dev)
+        app = (ptr(c["pool"]), ptr(c["new"]), ptr(c["tables"]), ptr(c["lens"]), B, dc + dr, 16, NB,
+               MB, sp)
+        att = (ptr(c["out"]), ptr(c["q"]), ptr(c["pool"]), ptr(c["tables"]), ptr(c["lens"]), B, H,
+               dc, dr, 16, NB, MB, mcl, ctypes.c_float(inp.softmax_scale), P, ptr(c["ws"]),
+               ctypes.c_size_t(c["ws"].numel()), sp)
+        prt = (V(c["parts"].data_ptr()), V(c["parts"].data_ptr() + lse_off), maxp, ptr(c["q"]),
+               ptr(c["pool"]), ptr(c["tables"]), ptr(c["lens"]), B, H, dc, dr, 16, NB, MB,
+               ctypes.c_float(inp.softmax_scale), P, sp)
+        calls.append((app, att, prt))
+    f_app, f_att, f_prt = lib.pkv_mla_append, lib.pkv_mla_decode_attention, lib.pkv_mla_decode_partials
+
+    def step(i):
+        app, att, _ = calls[i % n_copies]
+        if f_app(*app) != 0 or f_att(*att) != 0:
+            raise RuntimeError("libpkv call failed")
+
+    def att_only(i):
+        if f_att(*calls[i % n_copies][1]) != 0:
+            raise RuntimeError("attention call failed")
+
+    def decode_only(i):
+        if f_prt(*calls[i % n_copies][2]) != 0:
+            raise RuntimeError("partials call failed")
+
+    print(f"[bench] {n_copies} input copies of {footprint / 1e6:.1f} MB; warmup {args.warmup}",
+          file=sys.stderr, flush=True)
+    for i in range(args.warmup):
+        step(i)
+    timed = event_timer(stream)
+    step_ms = timed(step, args.steps)
+    att_ms = timed(att_only, args.kernel_reps)
+    decode_ms = timed(decode_only, args.kernel_reps)
+    merge_ms = max(att_ms - decode_ms, 0.0) if maxp > 1 else 0.0
+    tr = traffic.mla_attention_traffic(inp.context_lens, num_heads=H, kv_lora_rank=dc,
+                                       rope_dim=dr)
+    step_bytes = tr["total_bytes"] + 2 * B * (dc + dr) * 2
+    value = step_bytes / (step_ms * 1e-3) / 1e9
+    kernel_gbps = tr["kv_bytes"] / (decode_ms * 1e-3) / 1e9
+    tflops = tr["flops"] / (decode_ms * 1e-3) / 1e12
+    result = {
+        "metric": "paged decode attention achieved HBM GB/s (% of peak) and decode tokens/s",
+        "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(step_ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16 latent cache and queries, f32 accumulate",
+        "data": "synthetic (seeded N(0,1) latents and absorbed queries, random block placement)",
+        "config": {"workload": inp.name, "batch": B, "heads": H, "kv_lora_rank": dc,
+                   "rope_dim": dr, "block_size": 16, "partition_size": P,
+                   "context_tokens": int(inp.context_lens.sum()), "max_context": mcl,
+                   "parallelism": "single GPU"},
+        "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
+        "tokens_per_s": round(B * 1e3 / step_ms, 1),
+        "kernel_us": {"decode": round(decode_ms * 1e3, 2), "merge": round(merge_ms * 1e3, 2),
+                      "attention_call": round(att_ms * 1e3, 2)},
+        "roofline": {"kernel": "mla_decode_kernel", "bound": "hbm",
+                     "achieved": round(kernel_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(kernel_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "algorithmic_bytes_per_launch": tr["kv_bytes"],
+                     "mfma": {"achieved_tflops": round(tflops, 1), "peak_tflops": 2500.0,
+                              "frac": round(tflops / 2500.0, 4),
+                              "flops_per_launch": tr["flops"]}},
+        "cpu_baseline": None,
+        "input_copies": n_copies,
+    }
+    print(json.dumps(result), flush=True)
 
 
 def cpu_baseline_multi(inp, budget_s):

@@ -235,7 +235,7 @@ pkv_status_t pkv_paged_decode_partials(
  * (F32 or BF16); partial_out float32 [num_seqs, num_q_heads, max_partitions,
  * head_dim] and partial_lse float32 [num_seqs, num_q_heads, max_partitions]
  * [device, read]; num_partitions int32 [num_seqs] [device, read] or NULL.
- * Supported: head_dim in {64, 128}.
+ * Supported: head_dim in {64, 128, 512} (512: MLA latent rows).
  */
 pkv_status_t pkv_merge_partials(void* out, const float* partial_out, const float* partial_lse,
                                 const int32_t* num_partitions, int32_t num_seqs,
@@ -486,6 +486,74 @@ pkv_status_t pkv_copy_blocks(void* k_pool, void* v_pool, float* k_scales, float*
                              const int32_t* pairs, int32_t num_pairs, int32_t num_blocks,
                              int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                              pkv_dtype_t kv_dtype, void* stream);
+
+/*
+ * Multi-head latent attention (MLA), absorbed decode
+ * --------------------------------------------------
+ * An MLA layer caches one row per token: the latent c (kv_lora_rank = 512
+ * numbers) followed by the rotary key shared by all heads (rope_dim = 64):
+ * 576 numbers, against 2 x 128 x 128 for standard multi-head attention.
+ * In decode the up-projections are folded away: the caller forms each
+ * head's absorbed query [W_UK,i^T q_nope,i ; q_rope,i] (576 numbers), every
+ * head attends over the shared rows directly (key = the whole row, value =
+ * its latent), and the caller applies W_UV,i to the latent output.
+ *   KV-cache post, "MLA: how does decode get full-size keys and values
+ *   back?" (expand vs absorb; 512 + 64 numbers per token); serving lesson,
+ *   "Smaller caches: GQA, MQA, MLA and quantized caches".
+ * Layouts: latent_pool bf16 [num_blocks, block_size, 576]; block tables and
+ * context_lens as above (ctx counts the appended token); q bf16 [num_seqs,
+ * num_heads, 576]; out bf16 [num_seqs, num_heads, 512].
+ */
+
+/* pkv_mla_append - write each sequence's new 576-number row (latent_new bf16
+ * [num_seqs, 576] [device, read]) into slot ctx-1 of latent_pool [device,
+ * written], bit for bit; as pkv_kv_append with one shared head.  Supported:
+ * row_dim == 576, block_size == 16. */
+pkv_status_t pkv_mla_append(void* latent_pool, const void* latent_new,
+                            const int32_t* block_tables, const int32_t* context_lens,
+                            int32_t num_seqs, int32_t row_dim, int32_t block_size,
+                            int32_t num_blocks, int32_t max_blocks_per_seq, void* stream);
+
+/* Workspace of pkv_mla_decode_attention: float32 o [num_seqs, num_heads,
+ * maxP, kv_lora_rank] then, 256-byte aligned, float32 lse [num_seqs,
+ * num_heads, maxP]; 0 when maxP <= 1. */
+size_t pkv_mla_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t kv_lora_rank,
+                               int32_t max_context_len, int32_t partition_size);
+
+/*
+ * pkv_mla_decode_attention - out[b][i][:] = sum_t p_t row_t[:512] with
+ * p = softmax_t(softmax_scale * q[b][i] . row_t) over the ctx_b cached rows
+ * of sequence b (no other mask).  Scores, softmax and sums are float32 on the
+ * matrix cores with bf16 operands (the weights p rounded to bf16 for the
+ * weighted sum); out is rounded to bf16.  A sequence with ctx 0 gets zeros.
+ * Split-KV partitions of partition_size tokens are merged as in
+ * pkv_paged_decode_attention.  One workgroup serves up to 128 heads, so each
+ * cached row is read from HBM once per partition for all of them.
+ * out [device, written]; q, latent_pool, tables, lens [device, read];
+ * workspace [device, scratch] of pkv_mla_workspace_bytes(...) bytes.
+ * Supported: kv_lora_rank == 512, rope_dim == 64, num_heads a multiple of
+ * 16, block_size == 16, bf16.
+ */
+pkv_status_t pkv_mla_decode_attention(
+    void* out, const void* q, const void* latent_pool, const int32_t* block_tables,
+    const int32_t* context_lens, int32_t num_seqs, int32_t num_heads, int32_t kv_lora_rank,
+    int32_t rope_dim, int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
+    int32_t max_context_len, float softmax_scale, int32_t partition_size, void* workspace,
+    size_t workspace_bytes, void* stream);
+
+/* pkv_mla_decode_partials - the split-KV half of pkv_mla_decode_attention on
+ * its own, as pkv_paged_decode_partials is for standard attention:
+ * partial_out float32 [num_seqs, num_heads, max_partitions, 512] and
+ * partial_lse float32 [num_seqs, num_heads, max_partitions] [device,
+ * written]; partitions at or past ceil(ctx_b / P) get lse = -inf and leave
+ * partial_out untouched.  pkv_merge_partials (head_dim 512, out bf16) gives
+ * pkv_mla_decode_attention's output. */
+pkv_status_t pkv_mla_decode_partials(
+    float* partial_out, float* partial_lse, int32_t max_partitions, const void* q,
+    const void* latent_pool, const int32_t* block_tables, const int32_t* context_lens,
+    int32_t num_seqs, int32_t num_heads, int32_t kv_lora_rank, int32_t rope_dim,
+    int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq, float softmax_scale,
+    int32_t partition_size, void* stream);
 
 #ifdef __cplusplus
 }

@@ -141,7 +141,8 @@ hipError_t launch_d(const MergeArgs& a, DType out_dtype, hipStream_t stream) {
   // row group), or when there are enough (sequence, head) pairs to fill the
   // chip with single waves; four waves for few, long sequences.
   const bool one_batch = a.max_partitions * (D / 4) <= 8 * kWave;
-  const int threads = (one_batch || grid >= 4096) ? kWave : kThreads;
+  int threads = (one_batch || grid >= 4096) ? kWave : kThreads;
+  threads = threads < D / 4 ? D / 4 : threads;   // one row group reads a whole row
   if (out_dtype == DType::F32)
     hipLaunchKernelGGL((merge_kernel<D, OutF32>), dim3(unsigned(grid)), dim3(threads), 0, stream, a);
   else
@@ -153,6 +154,7 @@ hipError_t launch_d(const MergeArgs& a, DType out_dtype, hipStream_t stream) {
 
 hipError_t launch_merge(const MergeArgs& a, int head_dim, DType out_dtype, hipStream_t stream) {
   if (head_dim == 64) return launch_d<64>(a, out_dtype, stream);
+  if (head_dim == 512) return launch_d<512>(a, out_dtype, stream);   // MLA latent rows
   return launch_d<128>(a, out_dtype, stream);
 }
 

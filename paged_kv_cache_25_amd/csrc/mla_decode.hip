@@ -1,0 +1,301 @@
+// Absorbed multi-head latent attention (MLA) decode over a paged latent
+// cache, on the matrix cores of gfx950.
+//
+// Every token caches one row of d_c + d_r = 512 + 64 bf16 numbers (the latent
+// and the shared rotary key); in the absorbed form every head attends over
+// that row directly: the key is the whole row, the value its first 512
+// numbers (KV-cache post, "MLA: how does decode get full-size keys and values
+// back?": fold W_UK into the query and W_UV into the output).  The queries
+// arrive absorbed ([B, H, 576]); the kernel returns the latent outputs
+// [B, H, 512] (the caller applies W_UV).  All heads share one K/V row, so the
+// product is dense: per token and head 2 * (576 + 512) FLOP for 1,152 bytes.
+//
+// One workgroup of WAVES waves per (head chunk of 16*WAVES heads, sequence,
+// partition); wave w owns 16 heads.  The partition's blocks are walked in
+// pairs (32 tokens).  Each pair is copied once into LDS as 32 row-major rows
+// (576 numbers + 8 of padding, so that 16 rows read at one column hit 16
+// different bank groups), straight from HBM with 16-byte direct-to-LDS loads
+// (no registers; rows past the context, past the partition or of a block with
+// a bad table entry are loaded from a zero row instead).  Two buffers: the
+// next pair is in flight while this one is computed, one barrier per pair.
+// Per pair and wave:
+//   S^T[16 tok x 16 heads] = K . Q^T    2 x 18 mfma_f32_16x16x32_bf16
+//   online softmax in fp32 (log2 units, lazily raised maxima)
+//   O[16 heads x 512] += P[16 x 32 tok] . V[32 tok x 512]   32 mfma_f32_16x16x32_bf16
+// Lane l holds tokens 4*(l/16)+i of head l%16 after the score product; the
+// 32-token k index of the value product is ordered (block 0: 4g+i, block 1:
+// 16+4g+i) so that P is used in place as the A operand.  The B operand
+// (4 tokens x 1 latent column per lane and block) comes from the row-major
+// rows through gfx950's transposing LDS read: within a group of 16 lanes, lane
+// i receives element (i & 3) of the 8 bytes that lane 4k + (i >> 2) addresses,
+// for k = 0..3; lane (g, c) addresses row 4g + (c >> 2), columns 16t + 4(c & 3).
+#include "pkv_device.h"
+#include "pkv_launch.h"
+
+namespace pkv {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kDc = 512;                        // latent (value) width
+constexpr int kDk = 576;                        // row width: latent + rotary key
+constexpr int kRowBytes = kDk * 2;
+constexpr int kChunksPerRow = kRowBytes / 16;   // 72
+constexpr int kPairTokens = 32;
+constexpr int kKStride = kDk + 8;               // bf16 elements per staged row
+constexpr int kSlotsPerRow = kKStride * 2 / 16; // 73 16-byte slots, the last one padding
+constexpr int kPairSlots = kPairTokens * kSlotsPerRow;
+constexpr int kSlices = (kPairSlots + kWave - 1) / kWave;   // 64-slot direct loads per pair (37)
+constexpr int kBufElems = kSlices * kWave * 8;  // whole slices, so the last one stays inside
+constexpr int kSlabs = kDk / 32;                // 18 score products per block
+constexpr int kTiles = kDc / 16;                // 32 value products per pair
+constexpr float kRescaleThreshold = 8.0f;
+
+// 16 bytes of zeros in device memory: the source of rows that must read as 0.
+__device__ __attribute__((aligned(16))) uint32_t g_zero_row[4] = {0u, 0u, 0u, 0u};
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+
+template <int WAVES>
+__global__ __launch_bounds__(WAVES * kWave) void mla_decode_kernel(MlaArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t s_k[2][kBufElems];
+  constexpr int kSlicesPerWave = (kSlices + WAVES - 1) / WAVES;
+
+  int chunk, unit;
+  if (!decode_unit(blockIdx.x, a.head_chunks, a.num_seqs * a.max_partitions, chunk, unit)) return;
+  const int b = unit % a.num_seqs;
+  const int part = unit / a.num_seqs;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);   // uniform
+  const int lane = threadIdx.x % kWave;
+  const int g = lane >> 4, c = lane & 15;
+
+  const int raw_ctx = a.context_lens[b];
+  int ctx = raw_ctx < 0 ? 0 : raw_ctx;
+  const int cap = a.max_blocks_per_seq * kBlockSize;
+  ctx = ctx > cap ? cap : ctx;
+  const int n_blk_seq = (ctx + kBlockSize - 1) / kBlockSize;
+  const int blk_begin = part * a.blocks_per_partition;
+  int blk_end = blk_begin + a.blocks_per_partition;
+  blk_end = blk_end < n_blk_seq ? blk_end : n_blk_seq;
+  const int head_base = chunk * WAVES * 16;              // first head of the workgroup
+  const int h0 = head_base + wave * 16;                  // first head of this wave
+
+  if (blk_begin >= blk_end && !(a.write_final && part == 0)) {    // partition past the end
+    if (a.mark_empty && lane < 16 && h0 + lane < a.num_heads)
+      a.part_lse[(size_t(b) * a.num_heads + h0 + lane) * a.max_partitions + part] = -INFINITY;
+    return;
+  }
+  const bool final_out = a.write_final || (a.final_single && n_blk_seq <= a.blocks_per_partition);
+  const int limit = ctx < blk_end * kBlockSize ? ctx : blk_end * kBlockSize;   // tokens attended
+  const int32_t* table = a.block_tables + size_t(b) * a.max_blocks_per_seq;
+  const char* pool = static_cast<const char*>(a.pool);
+
+  // Absorbed query of head h0 + c as the B operand of the score product.
+  bf16x8 q[kSlabs];
+  {
+    const bool ok = h0 + c < a.num_heads;
+    const char* qrow = static_cast<const char*>(a.q) + (size_t(b) * a.num_heads + (ok ? h0 + c : 0)) * kRowBytes;
+#pragma unroll
+    for (int j = 0; j < kSlabs; ++j) {
+      const uint4 w = ok ? *reinterpret_cast<const uint4*>(qrow + 64 * j + 16 * g) : make_uint4(0, 0, 0, 0);
+      q[j] = __builtin_bit_cast(bf16x8, w);
+    }
+  }
+  f32x4 o[kTiles];
+#pragma unroll
+  for (int t = 0; t < kTiles; ++t) o[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  float m = -INFINITY, l = 0.0f;
+
+  const int n_pairs = (blk_end - blk_begin + 1) / 2;
+
+  // Block ids of the partition, 64 at a time in lane registers (lane i holds
+  // entry seg + i); a pair's two ids are broadcast with readlane, so the
+  // addresses and validity flags are wave-uniform scalars.
+  int seg = -kWave, my_id = 0;
+  uint64_t ok_mask = 0;
+  auto pair_ids = [&](int p, int& phys0, int& phys1, bool& ok0, bool& ok1) {
+    const int rel = 2 * p;                             // first block of the pair, from blk_begin
+    if (rel >= seg + kWave) {
+      seg = rel - rel % kWave;
+      const int blk = blk_begin + seg + lane;
+      my_id = blk < blk_end ? table[blk] : -1;
+      ok_mask = __ballot(unsigned(my_id) < unsigned(a.num_blocks));
+    }
+    const int k = rel - seg;
+    phys0 = __builtin_amdgcn_readlane(my_id, k);
+    phys1 = __builtin_amdgcn_readlane(my_id, k + 1);
+    ok0 = (ok_mask >> k) & 1;
+    ok1 = k + 1 < kWave && ((ok_mask >> (k + 1)) & 1);
+  };
+
+  // Pair p into buffer buf: slice s of the pair (64 consecutive 16-byte slots)
+  // is one direct-to-LDS load; slot 64s + lane is row (slot / 73), chunk
+  // (slot % 73) of the staged pair.  Padding slots and rows that must be zero
+  // read the zero row.
+  auto stage = [&](int p, int phys0, int phys1, bool ok0, bool ok1, int buf) {
+    const int pos0 = (blk_begin + 2 * p) * kBlockSize;
+#pragma unroll
+    for (int r = 0; r < kSlicesPerWave; ++r) {
+      const int sl = wave + r * WAVES;
+      if (sl >= kSlices) break;
+      const int slot = sl * kWave + lane;
+      const int row = slot / kSlotsPerRow;
+      const int ch = slot % kSlotsPerRow;
+      const bool blk_ok = row < 16 ? ok0 : ok1;
+      const bool live = row < kPairTokens && ch < kChunksPerRow && blk_ok && pos0 + row < limit;
+      const char* src = reinterpret_cast<const char*>(g_zero_row);
+      if (live) {
+        const int phys = row < 16 ? phys0 : phys1;
+        src = pool + (size_t(phys) * kBlockSize + (row & 15)) * kRowBytes + size_t(ch) * 16;
+      }
+      __builtin_amdgcn_global_load_lds(src, (lds_void*)&s_k[buf][sl * kWave * 8], 16, 0, 0);
+    }
+  };
+
+  int phys0 = 0, phys1 = 0;
+  bool ok0 = false, ok1 = false;
+  if (n_pairs > 0) {
+    pair_ids(0, phys0, phys1, ok0, ok1);
+    stage(0, phys0, phys1, ok0, ok1, 0);
+  }
+  __builtin_amdgcn_s_waitcnt(0);                      // this wave's copies have landed
+  __syncthreads();                                    // and everyone's
+  for (int p = 0; p < n_pairs; ++p) {
+    const int buf = p & 1;
+    // the next pair's copies, in flight while this pair is computed
+    int nphys0 = 0, nphys1 = 0;
+    bool nok0 = false, nok1 = false;
+    if (p + 1 < n_pairs) {
+      pair_ids(p + 1, nphys0, nphys1, nok0, nok1);
+      stage(p + 1, nphys0, nphys1, nok0, nok1, buf ^ 1);
+    }
+
+    // Scores of the pair's two blocks: lane holds tokens 16j + 4g + i of head h0 + c.
+    f32x4 s[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      s[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      const uint16_t* krow = &s_k[buf][(16 * j + c) * kKStride + 8 * g];
+#pragma unroll
+      for (int kc = 0; kc < kSlabs; ++kc) {
+        const bf16x8 kv = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(krow + 32 * kc));
+        s[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, q[kc], s[j], 0, 0, 0);
+      }
+    }
+    const int pos0 = (blk_begin + 2 * p) * kBlockSize;
+    float x[8];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int pos = pos0 + 16 * j + 4 * g + i;
+        const bool ok = (j ? ok1 : ok0) && pos < limit;
+        x[4 * j + i] = ok ? s[j][i] * a.scale_log2 : -INFINITY;
+      }
+    float bm = x[0];
+#pragma unroll
+    for (int k = 1; k < 8; ++k) bm = fmaxf(bm, x[k]);
+    bm = fmaxf(bm, __shfl_xor(bm, 16));
+    bm = fmaxf(bm, __shfl_xor(bm, 32));
+    if (__any(bm > m + kRescaleThreshold)) {              // rare: raise the reference maxima
+      const float mn = fmaxf(m, bm);
+      const float alpha = mn == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m - mn);
+      l *= alpha;
+      m = mn;
+      float ar[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ar[i] = __shfl(alpha, 4 * g + i);
+#pragma unroll
+      for (int t = 0; t < kTiles; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[t][i] *= ar[i];
+    }
+    const float m_eff = m == -INFINITY ? 0.0f : m;
+    uint32_t pw[4];
+#pragma unroll
+    for (int k = 0; k < 8; k += 2) {
+      const float p0 = __builtin_amdgcn_exp2f(x[k] - m_eff);
+      const float p1 = __builtin_amdgcn_exp2f(x[k + 1] - m_eff);
+      l += p0 + p1;
+      pw[k / 2] = uint32_t(f32_to_bf16_rne(p0)) | (uint32_t(f32_to_bf16_rne(p1)) << 16);
+    }
+    const bf16x8 pa = __builtin_bit_cast(bf16x8, make_uint4(pw[0], pw[1], pw[2], pw[3]));
+    // V operand of tile t: rows 4g + (c >> 2) (block 0) and 16 + 4g + (c >> 2)
+    // (block 1), columns 16t + 4(c & 3), read transposed.
+    const uint16_t* vrow = &s_k[buf][(4 * g + (c >> 2)) * kKStride + 4 * (c & 3)];
+#pragma unroll
+    for (int t = 0; t < kTiles; ++t) {
+      const v4i16 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vrow + 16 * t));
+      const v4i16 v1 =
+          __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vrow + 16 * kKStride + 16 * t));
+      const uint2 w0 = __builtin_bit_cast(uint2, v0);
+      const uint2 w1 = __builtin_bit_cast(uint2, v1);
+      const bf16x8 vb = __builtin_bit_cast(bf16x8, make_uint4(w0.x, w0.y, w1.x, w1.y));
+      o[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, vb, o[t], 0, 0, 0);
+    }
+    phys0 = nphys0;
+    phys1 = nphys1;
+    ok0 = nok0;
+    ok1 = nok1;
+    __builtin_amdgcn_s_waitcnt(0);                    // the next pair's copies have landed
+    __syncthreads();
+  }
+
+  // Denominator of head h0 + c over the four token groups; then of rows 4g+i.
+  float lt = l + __shfl_xor(l, 16);
+  lt += __shfl_xor(lt, 32);
+  float l_row[4], m_row[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    l_row[i] = __shfl(lt, 4 * g + i);
+    m_row[i] = __shfl(m, 4 * g + i);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int head = h0 + 4 * g + i;
+    if (head >= a.num_heads) continue;
+    const size_t row = size_t(b) * a.num_heads + head;
+    const bool empty = l_row[i] == 0.0f;
+    const float inv = empty ? 0.0f : 1.0f / l_row[i];
+    if (final_out) {
+      uint16_t* orow = static_cast<uint16_t*>(a.out) + row * kDc + c;
+#pragma unroll
+      for (int t = 0; t < kTiles; ++t) orow[16 * t] = f32_to_bf16_rne(o[t][i] * inv);
+    } else {
+      const size_t prow = row * a.max_partitions + part;
+      float* op = a.part_o + prow * kDc + c;
+#pragma unroll
+      for (int t = 0; t < kTiles; ++t) op[16 * t] = o[t][i] * inv;
+      if (c == 0)
+        a.part_lse[prow] = empty ? -INFINITY : (m_row[i] + __builtin_amdgcn_logf(l_row[i])) * kLn2;
+    }
+  }
+}
+
+}  // namespace
+
+int mla_heads_per_workgroup(int num_heads) {
+  int w = 1;
+  while (w < 8 && 16 * w < num_heads) w *= 2;
+  return 16 * w;
+}
+
+hipError_t launch_mla_decode(const MlaArgs& a, hipStream_t stream) {
+  const size_t units = size_t(a.num_seqs) * a.max_partitions;
+  if (units == 0) return hipSuccess;
+  if (units > 0x7fffffffu) return hipErrorInvalidConfiguration;
+  const size_t grid = decode_grid(units, a.head_chunks);
+  if (grid > 0x7fffffffu) return hipErrorInvalidConfiguration;
+  switch (mla_heads_per_workgroup(a.num_heads) / 16) {
+    case 1: hipLaunchKernelGGL(mla_decode_kernel<1>, dim3(unsigned(grid)), dim3(1 * kWave), 0, stream, a); break;
+    case 2: hipLaunchKernelGGL(mla_decode_kernel<2>, dim3(unsigned(grid)), dim3(2 * kWave), 0, stream, a); break;
+    case 4: hipLaunchKernelGGL(mla_decode_kernel<4>, dim3(unsigned(grid)), dim3(4 * kWave), 0, stream, a); break;
+    default: hipLaunchKernelGGL(mla_decode_kernel<8>, dim3(unsigned(grid)), dim3(8 * kWave), 0, stream, a); break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace pkv

@@ -216,6 +216,155 @@ pkv_status_t pkv_copy_blocks(void* k_pool, void* v_pool, float* k_scales, float*
              : PKV_ERR_HIP;
 }
 
+size_t pkv_mla_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t kv_lora_rank,
+                               int32_t max_context_len, int32_t partition_size) {
+  if (num_seqs <= 0 || num_heads <= 0 || kv_lora_rank <= 0 || partition_size < 0) return 0;
+  const int64_t maxp = max_partitions(max_context_len, partition_size);
+  if (maxp <= 1) return 0;
+  return part_layout(num_seqs, num_heads, kv_lora_rank, maxp).total;
+}
+
+pkv_status_t pkv_mla_append(void* latent_pool, const void* latent_new,
+                            const int32_t* block_tables, const int32_t* context_lens,
+                            int32_t num_seqs, int32_t row_dim, int32_t block_size,
+                            int32_t num_blocks, int32_t max_blocks_per_seq, void* stream) {
+  if (num_seqs < 0 || row_dim <= 0 || block_size <= 0 || num_blocks <= 0 ||
+      max_blocks_per_seq <= 0)
+    return PKV_ERR_INVALID_ARG;
+  if (row_dim != 576 || block_size != pkv::kBlockSizeBuilt) return PKV_ERR_UNSUPPORTED;
+  if (num_seqs == 0) return PKV_OK;
+  if (!latent_pool || !latent_new || !block_tables || !context_lens) return PKV_ERR_INVALID_ARG;
+  if (!aligned16(latent_pool) || !aligned16(latent_new) || !aligned4(block_tables) ||
+      !aligned4(context_lens))
+    return PKV_ERR_INVALID_ARG;
+  // The latent pool is a pool with one shared head of 576 bf16 numbers; the
+  // same bitwise scatter serves it (row ctx-1, the second pool is the same).
+  pkv::AppendArgs a{};
+  a.k_pool = latent_pool;
+  a.v_pool = latent_pool;
+  a.k_new = latent_new;
+  a.v_new = latent_new;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.num_seqs = num_seqs;
+  a.num_kv_heads = 1;
+  a.row_bytes = row_dim * 2;
+  a.num_blocks = num_blocks;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  return pkv::launch_kv_append(a, static_cast<hipStream_t>(stream)) == hipSuccess ? PKV_OK
+                                                                                  : PKV_ERR_HIP;
+}
+
+pkv_status_t pkv_mla_decode_attention(
+    void* out, const void* q, const void* latent_pool, const int32_t* block_tables,
+    const int32_t* context_lens, int32_t num_seqs, int32_t num_heads, int32_t kv_lora_rank,
+    int32_t rope_dim, int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
+    int32_t max_context_len, float softmax_scale, int32_t partition_size, void* workspace,
+    size_t workspace_bytes, void* stream) {
+  if (num_seqs < 0 || num_heads <= 0 || kv_lora_rank <= 0 || rope_dim < 0 || block_size <= 0 ||
+      num_blocks <= 0 || max_blocks_per_seq <= 0 || max_context_len < 0 || partition_size < 0 ||
+      !(softmax_scale == softmax_scale))
+    return PKV_ERR_INVALID_ARG;
+  if (partition_size % block_size != 0) return PKV_ERR_INVALID_ARG;
+  if (kv_lora_rank != 512 || rope_dim != 64 || block_size != pkv::kBlockSizeBuilt ||
+      num_heads % 16 != 0)
+    return PKV_ERR_UNSUPPORTED;
+  if (num_seqs == 0) return PKV_OK;
+  if (!out || !q || !latent_pool || !block_tables || !context_lens) return PKV_ERR_INVALID_ARG;
+  if (!aligned16(out) || !aligned16(q) || !aligned16(latent_pool) || !aligned4(block_tables) ||
+      !aligned4(context_lens) || !aligned16(workspace))
+    return PKV_ERR_INVALID_ARG;
+  const int64_t maxp = max_partitions(max_context_len, partition_size);
+  const bool single = maxp <= 1;
+  pkv::MlaArgs a{};
+  a.out = out;
+  a.q = q;
+  a.pool = latent_pool;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.num_seqs = num_seqs;
+  a.num_heads = num_heads;
+  const int per_wg = pkv::mla_heads_per_workgroup(num_heads);
+  a.head_chunks = (num_heads + per_wg - 1) / per_wg;
+  a.num_blocks = num_blocks;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.scale_log2 = softmax_scale * pkv::kLog2eHost;
+  if (!single) {
+    const PartLayout L = part_layout(num_seqs, num_heads, kv_lora_rank, maxp);
+    if (!workspace || workspace_bytes < L.total) return PKV_ERR_WORKSPACE;
+    a.part_o = static_cast<float*>(workspace);
+    a.part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + L.lse_offset);
+  }
+  a.blocks_per_partition =
+      single ? max_blocks_per_seq : partition_size / block_size;
+  a.max_partitions = int(maxp);
+  a.write_final = single ? 1 : 0;
+  a.final_single = 1;
+  a.mark_empty = 0;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (pkv::launch_mla_decode(a, st) != hipSuccess) return PKV_ERR_HIP;
+  if (single) return PKV_OK;
+  pkv::MergeArgs m{};
+  m.out = out;
+  m.part_o = a.part_o;
+  m.part_lse = a.part_lse;
+  m.num_partitions = nullptr;
+  m.context_lens = context_lens;
+  m.partition_size = partition_size;
+  m.num_seqs = num_seqs;
+  m.num_q_heads = num_heads;
+  m.max_partitions = int(maxp);
+  m.skip_single = 1;
+  m.q_start = nullptr;
+  m.num_batch = num_seqs;
+  return pkv::launch_merge(m, kv_lora_rank, DType::BF16, st) == hipSuccess ? PKV_OK
+                                                                            : PKV_ERR_HIP;
+}
+
+pkv_status_t pkv_mla_decode_partials(
+    float* partial_out, float* partial_lse, int32_t max_partitions_, const void* q,
+    const void* latent_pool, const int32_t* block_tables, const int32_t* context_lens,
+    int32_t num_seqs, int32_t num_heads, int32_t kv_lora_rank, int32_t rope_dim,
+    int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq, float softmax_scale,
+    int32_t partition_size, void* stream) {
+  if (num_seqs < 0 || num_heads <= 0 || kv_lora_rank <= 0 || rope_dim < 0 || block_size <= 0 ||
+      num_blocks <= 0 || max_blocks_per_seq <= 0 || partition_size < 0 || max_partitions_ <= 0 ||
+      !(softmax_scale == softmax_scale))
+    return PKV_ERR_INVALID_ARG;
+  if (partition_size % block_size != 0) return PKV_ERR_INVALID_ARG;
+  if (kv_lora_rank != 512 || rope_dim != 64 || block_size != pkv::kBlockSizeBuilt ||
+      num_heads % 16 != 0)
+    return PKV_ERR_UNSUPPORTED;
+  if (num_seqs == 0) return PKV_OK;
+  if (!partial_out || !partial_lse || !q || !latent_pool || !block_tables || !context_lens)
+    return PKV_ERR_INVALID_ARG;
+  if (!aligned16(partial_out) || !aligned4(partial_lse) || !aligned16(q) ||
+      !aligned16(latent_pool) || !aligned4(block_tables) || !aligned4(context_lens))
+    return PKV_ERR_INVALID_ARG;
+  pkv::MlaArgs a{};
+  a.part_o = partial_out;
+  a.part_lse = partial_lse;
+  a.q = q;
+  a.pool = latent_pool;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.num_seqs = num_seqs;
+  a.num_heads = num_heads;
+  const int per_wg = pkv::mla_heads_per_workgroup(num_heads);
+  a.head_chunks = (num_heads + per_wg - 1) / per_wg;
+  a.num_blocks = num_blocks;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.scale_log2 = softmax_scale * pkv::kLog2eHost;
+  a.blocks_per_partition =
+      partition_size == 0 ? max_blocks_per_seq : partition_size / block_size;
+  a.max_partitions = max_partitions_;
+  a.write_final = 0;
+  a.final_single = 0;
+  a.mark_empty = 1;
+  return pkv::launch_mla_decode(a, static_cast<hipStream_t>(stream)) == hipSuccess ? PKV_OK
+                                                                                   : PKV_ERR_HIP;
+}
+
 size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
                                   int32_t max_context_len, int32_t partition_size) {
   if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 || partition_size < 0) return 0;
@@ -584,7 +733,8 @@ pkv_status_t pkv_merge_partials(void* out, const float* partial_out, const float
   if (num_seqs < 0 || num_q_heads <= 0 || head_dim <= 0 || max_partitions <= 0 ||
       !dtype_ok(out_dtype))
     return PKV_ERR_INVALID_ARG;
-  if (!head_dim_ok(head_dim) || out_dtype == PKV_FP8_E4M3) return PKV_ERR_UNSUPPORTED;
+  if ((!head_dim_ok(head_dim) && head_dim != 512) || out_dtype == PKV_FP8_E4M3)
+    return PKV_ERR_UNSUPPORTED;
   if (num_seqs == 0) return PKV_OK;
   if (!out || !partial_out || !partial_lse) return PKV_ERR_INVALID_ARG;
   if (!aligned16(out) || !aligned16(partial_out) || !aligned4(partial_lse) ||

@@ -55,6 +55,22 @@ struct CopyBlocksArgs {
   size_t block_bytes;              // one physical block of one pool, all KV heads
 };
 
+// Absorbed MLA decode over a paged latent cache: pool [num_blocks, 16, 576]
+// bf16 rows (512 latent + 64 rotary key), q [B, H, 576], out [B, H, 512].
+struct MlaArgs {
+  void* out;                       // final latent output (bf16) when write_final
+  float* part_o;                   // [B, H, maxP, 512]
+  float* part_lse;                 // [B, H, maxP]
+  const void* q;
+  const void* pool;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  int num_seqs, num_heads, head_chunks, num_blocks, max_blocks_per_seq;
+  int blocks_per_partition, max_partitions;
+  float scale_log2;
+  int write_final, final_single, mark_empty;
+};
+
 struct DecodeArgs {
   void* out;               // final output (q dtype) when write_final
   float* part_o;           // [B, Hq, maxP, D] when !write_final
@@ -142,6 +158,8 @@ struct MergeArgs {
 hipError_t launch_kv_append(const AppendArgs& a, hipStream_t stream);
 hipError_t launch_kv_append_quant(const QuantAppendArgs& a, hipStream_t stream);
 hipError_t launch_copy_blocks(const CopyBlocksArgs& a, hipStream_t stream);
+int mla_heads_per_workgroup(int num_heads);
+hipError_t launch_mla_decode(const MlaArgs& a, hipStream_t stream);
 hipError_t launch_paged_decode(const DecodeArgs& a, int head_dim, int tile_heads, DType q_dtype,
                                DType kv_dtype, hipStream_t stream);
 // Matrix-core variant for bf16 queries over a bf16 cache; heads in tiles of 16.

@@ -99,6 +99,14 @@ def load():
     L.pkv_bm_block_tables.argtypes = [P, P, I, P, I, P]
     L.pkv_copy_blocks.restype = ctypes.c_int
     L.pkv_copy_blocks.argtypes = [P, P, P, P, P, I, I, I, I, I, ctypes.c_int, P]
+    L.pkv_mla_append.restype = ctypes.c_int
+    L.pkv_mla_append.argtypes = [P, P, P, P, I, I, I, I, I, P]
+    L.pkv_mla_workspace_bytes.restype = Z
+    L.pkv_mla_workspace_bytes.argtypes = [I, I, I, I, I]
+    L.pkv_mla_decode_attention.restype = ctypes.c_int
+    L.pkv_mla_decode_attention.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, I, F, I, P, Z, P]
+    L.pkv_mla_decode_partials.restype = ctypes.c_int
+    L.pkv_mla_decode_partials.argtypes = [P, P, I, P, P, P, P, I, I, I, I, I, I, I, F, I, P]
     _lib = L
     return L
 
@@ -392,3 +400,45 @@ def copy_blocks(k_pool, v_pool, pairs, k_scales=None, v_scales=None, stream=None
         _ptr(k_pool), _ptr(v_pool), _ptr(k_scales), _ptr(v_scales), _ptr(pairs),
         pairs.shape[0] if pairs.numel() else 0, nb, hkv, d, bs, dtype_code(k_pool.dtype),
         _stream(stream)))
+
+
+def mla_append(latent_pool, latent_new, block_tables, context_lens, stream=None):
+    """Write each sequence's new 576-number row into slot ctx-1 (pkv_mla_append)."""
+    _need_cuda(latent_pool, latent_new, block_tables, context_lens)
+    nb, bs, d = latent_pool.shape
+    _check("pkv_mla_append", load().pkv_mla_append(
+        _ptr(latent_pool), _ptr(latent_new), _ptr(block_tables), _ptr(context_lens),
+        block_tables.shape[0], d, bs, nb, block_tables.shape[1], _stream(stream)))
+
+
+def mla_decode_attention(out, q, latent_pool, block_tables, context_lens, max_context_len,
+                         softmax_scale, partition_size=512, kv_lora_rank=512, workspace=None,
+                         stream=None):
+    """out [B, H, 512] bf16: absorbed MLA decode of q [B, H, 576] over the paged
+    latent rows (pkv_mla_decode_attention)."""
+    _need_cuda(out, q, latent_pool, block_tables, context_lens, workspace)
+    B, H, d = q.shape
+    nb, bs, _ = latent_pool.shape
+    if workspace is None:
+        n = int(load().pkv_mla_workspace_bytes(B, H, kv_lora_rank, max_context_len,
+                                               partition_size))
+        workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=q.device)
+    _check("pkv_mla_decode_attention", load().pkv_mla_decode_attention(
+        _ptr(out), _ptr(q), _ptr(latent_pool), _ptr(block_tables), _ptr(context_lens), B, H,
+        kv_lora_rank, d - kv_lora_rank, bs, nb, block_tables.shape[1], int(max_context_len),
+        float(softmax_scale), int(partition_size), _ptr(workspace), workspace.numel(),
+        _stream(stream)))
+    return out
+
+
+def mla_decode_partials(partial_out, partial_lse, q, latent_pool, block_tables, context_lens,
+                        softmax_scale, partition_size=512, kv_lora_rank=512, stream=None):
+    """Unmerged MLA split-KV results: partial_out [B, H, P, 512], partial_lse [B, H, P]."""
+    _need_cuda(partial_out, partial_lse, q, latent_pool, block_tables, context_lens)
+    B, H, d = q.shape
+    nb, bs, _ = latent_pool.shape
+    _check("pkv_mla_decode_partials", load().pkv_mla_decode_partials(
+        _ptr(partial_out), _ptr(partial_lse), partial_out.shape[2], _ptr(q), _ptr(latent_pool),
+        _ptr(block_tables), _ptr(context_lens), B, H, kv_lora_rank, d - kv_lora_rank, bs, nb,
+        block_tables.shape[1], float(softmax_scale), int(partition_size), _stream(stream)))
+    return partial_out, partial_lse

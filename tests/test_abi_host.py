@@ -39,7 +39,8 @@ def test_header_declares_the_entry_points():
         "pkv_kv_append_quant", "pkv_bm_create", "pkv_bm_destroy", "pkv_bm_add_seq",
         "pkv_bm_fork", "pkv_bm_free_seq", "pkv_bm_append_slots", "pkv_bm_num_free",
         "pkv_bm_refcount", "pkv_bm_seq_len", "pkv_bm_free_list", "pkv_bm_block_tables",
-        "pkv_copy_blocks"])
+        "pkv_copy_blocks", "pkv_mla_append", "pkv_mla_workspace_bytes",
+        "pkv_mla_decode_attention", "pkv_mla_decode_partials"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -300,6 +301,47 @@ def test_copy_blocks_validation(lib):
     assert _copy(lib, d=96) == UNSUPPORTED
     assert _copy(lib, hkv=300) == UNSUPPORTED
     assert _copy(lib, n=0, kp=None, pairs=None) == OK
+
+
+def _mla(lib, **over):
+    a = dict(out=FAKE, q=FAKE, pool=FAKE, tables=FAKE, lens=FAKE, B=2, H=128, dc=512, dr=64,
+             bs=16, nb=8, mbps=4, maxctx=64, scale=0.07, P=32, ws=None, wsb=0)
+    a.update(over)
+    return lib.pkv_mla_decode_attention(a["out"], a["q"], a["pool"], a["tables"], a["lens"],
+                                        a["B"], a["H"], a["dc"], a["dr"], a["bs"], a["nb"],
+                                        a["mbps"], a["maxctx"], a["scale"], a["P"], a["ws"],
+                                        a["wsb"], None)
+
+
+def test_mla_validation(lib):
+    need = lib.pkv_mla_workspace_bytes(2, 128, 512, 64, 32)       # maxP = 2
+    assert need == 2 * 128 * 2 * 512 * 4 + 2 * 128 * 2 * 4
+    assert lib.pkv_mla_workspace_bytes(2, 128, 512, 32, 32) == 0
+    assert _mla(lib, q=None, ws=FAKE, wsb=need) == INVALID
+    assert _mla(lib, P=24) == INVALID
+    assert _mla(lib, maxctx=-1) == INVALID
+    assert _mla(lib, scale=float("nan")) == INVALID
+    assert _mla(lib, dc=256) == UNSUPPORTED
+    assert _mla(lib, dr=32) == UNSUPPORTED
+    assert _mla(lib, H=24) == UNSUPPORTED
+    assert _mla(lib, bs=32, P=32) == UNSUPPORTED
+    assert _mla(lib) == WORKSPACE
+    assert _mla(lib, ws=FAKE, wsb=need - 1) == WORKSPACE
+    assert _mla(lib, out=ctypes.c_void_p(0x10008), ws=FAKE, wsb=need) == INVALID
+    assert _mla(lib, B=0, q=None) == OK
+    f = lib.pkv_mla_append
+    assert f(None, FAKE, FAKE, FAKE, 2, 576, 16, 8, 4, None) == INVALID
+    assert f(FAKE, ctypes.c_void_p(0x10008), FAKE, FAKE, 2, 576, 16, 8, 4, None) == INVALID
+    assert f(FAKE, FAKE, FAKE, FAKE, 2, 512, 16, 8, 4, None) == UNSUPPORTED
+    assert f(None, None, None, None, 0, 576, 16, 8, 4, None) == OK
+    g = lib.pkv_mla_decode_partials
+    args = [FAKE, FAKE, 2, FAKE, FAKE, FAKE, FAKE, 2, 128, 512, 64, 16, 8, 4, 0.07, 32, None]
+    for i, bad in ((0, None), (2, 0), (3, None), (8, 24), (15, 24)):
+        a = list(args)
+        a[i] = bad
+        assert g(*a) in (INVALID, UNSUPPORTED), i
+    a = list(args); a[9] = 256
+    assert g(*a) == UNSUPPORTED
 
 
 def test_binding_refuses_cpu_tensors():

@@ -1,0 +1,155 @@
+"""GPU parity of the absorbed MLA decode (pkv_mla_append then
+pkv_mla_decode_attention) against oracle/mla.py: head counts 16..256 (one
+to eight waves per workgroup, and two head chunks), partition sizes that
+split pairs of blocks, edge context lengths, and the DeepSeek-shaped
+batch-64 layer at full size on sampled sequences."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.mla as mla
+from paged_kv_cache_25_amd import ops
+from tests.gpu_util import check_tolerance, dev_tensor, host_storage, log
+from workloads.mla import make_mla_inputs, named_mla
+
+pytestmark = pytest.mark.gpu
+
+
+class DevMLA:
+    def __init__(self, inp):
+        self.inp = inp
+        self.pool = dev_tensor(inp.latent_pool, inp.dtype)
+        self.new = dev_tensor(inp.latent_new, inp.dtype)
+        self.q = dev_tensor(inp.q, inp.dtype)
+        self.tables = dev_tensor(inp.block_tables, None)
+        self.lens = dev_tensor(inp.context_lens, None)
+        self.out = torch.empty(inp.num_seqs, inp.num_heads, inp.kv_lora_rank, dtype=torch.bfloat16,
+                               device="cuda")
+
+    def step(self, partition_size=None):
+        inp = self.inp
+        P = inp.partition_size if partition_size is None else partition_size
+        ops.mla_append(self.pool, self.new, self.tables, self.lens)
+        ops.mla_decode_attention(self.out, self.q, self.pool, self.tables, self.lens,
+                                 inp.max_context_len, inp.softmax_scale, P)
+        torch.cuda.synchronize()
+        return self.out.float().cpu().double().numpy()
+
+
+def _appended_pool(inp):
+    pool = inp.latent_pool.copy()
+    for b in range(inp.num_seqs):
+        ctx = int(inp.context_lens[b])
+        if ctx > 0:
+            pool[inp.block_tables[b, (ctx - 1) // 16], (ctx - 1) % 16] = inp.latent_new[b]
+    return pool
+
+
+def _oracle(inp, pool=None, seqs=None):
+    pool = _appended_pool(inp) if pool is None else pool
+    return mla.mla_decode_absorbed(inp.q, pool, inp.block_tables, inp.context_lens,
+                                   block_size=16, softmax_scale=inp.softmax_scale,
+                                   kv_lora_rank=inp.kv_lora_rank, dtype=inp.dtype, seqs=seqs)
+
+
+@pytest.mark.parametrize("heads", [16, 32, 64, 128, 256])
+@pytest.mark.parametrize("P", [512, 48, 32, 0])
+def test_heads_and_partitions(heads, P):
+    inp = make_mla_inputs(num_seqs=5, num_heads=heads, ctx=("fixed", [1, 33, 200, 517, 80]),
+                          seed=100 + heads, pool_used_fraction=0.8)
+    log(f"[case] mla H={heads} P={P}")
+    dev = DevMLA(inp)
+    gpu = dev.step(P)
+    pool = _appended_pool(inp)
+    assert np.array_equal(host_storage(dev.pool), pool)
+    check_tolerance("bf16", gpu, _oracle(inp, pool), f"mla H={heads} P={P}", out_dtype="bf16")
+
+
+def test_edge_context_lengths():
+    """Lengths at and around block and pair boundaries, and an empty sequence."""
+    lens = [0, 1, 15, 16, 17, 31, 32, 33, 63, 64, 65, 100]
+    inp = make_mla_inputs(num_seqs=len(lens), num_heads=128, ctx=("fixed", lens), seed=7)
+    for P in (0, 32, 64):
+        log(f"[case] mla edges P={P}")
+        gpu = DevMLA(inp).step(P)
+        assert np.all(gpu[0] == 0)                       # ctx 0: zeros
+        check_tolerance("bf16", gpu, _oracle(inp), f"mla edges P={P}", out_dtype="bf16")
+
+
+def test_lite_workload():
+    inp = named_mla("deepseek_lite_mla_b8")
+    log("[case] deepseek_lite_mla_b8")
+    check_tolerance("bf16", DevMLA(inp).step(), _oracle(inp), "deepseek lite b8", out_dtype="bf16")
+
+
+def test_deepseek_b64_sampled():
+    """The DeepSeek-shaped batch-64 layer (128 heads, lengths uniform in
+    [512, 4096]) at full size in the benchmark's launch configuration; the
+    oracle checks 6 sampled sequences."""
+    inp = named_mla("deepseek_mla_b64")
+    log("[case] deepseek_mla_b64 full size")
+    dev = DevMLA(inp)
+    gpu = dev.step()
+    pool = _appended_pool(inp)
+    seqs = sorted(np.random.default_rng(1).choice(inp.num_seqs, 6, replace=False).tolist())
+    ref = _oracle(inp, pool, seqs=seqs)
+    for b in seqs:
+        check_tolerance("bf16", gpu[b], ref[b], f"deepseek b64 seq {b} ctx {inp.context_lens[b]}",
+                        out_dtype="bf16")
+
+
+def _guard(inp, gpu, pool, seqs):
+    """The kernel's own arithmetic bound: fp32 products and softmax, each
+    weight rounded to bf16 for the latent sum (at most 2^-9 A, A = the
+    weights applied to |latent|) and the output rounded to bf16 (2^-9 |ref|);
+    margins of 2x."""
+    worst = 0.0
+    for b in seqs:
+        ctx = int(inp.context_lens[b])
+        if ctx == 0:
+            continue
+        nb = -(-ctx // 16)
+        rows = np.concatenate([pool[inp.block_tables[b, j]] for j in range(nb)])[:ctx]
+        rows = (rows.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        q = (inp.q[b].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        s = inp.softmax_scale * (q @ rows.T)
+        p = np.exp(s - s.max(axis=1, keepdims=True))
+        p /= p.sum(axis=1, keepdims=True)
+        ref = p @ rows[:, :512]
+        A = p @ np.abs(rows[:, :512])
+        bound = 2.0 ** -8 * np.abs(ref) + 2.0 ** -8 * A + 2e-5 * (1 + np.abs(ref))
+        err = np.abs(gpu[b] - ref)
+        worst = max(worst, float((err / bound).max()))
+        assert (err <= bound).all(), f"seq {b}: error exceeds the arithmetic bound"
+    log(f"[guard] mla: max err / bound = {worst:.3f}")
+
+
+def test_guard_bound():
+    inp = make_mla_inputs(num_seqs=6, num_heads=128, ctx=("fixed", [1, 17, 64, 300, 700, 1500]),
+                          seed=31)
+    dev = DevMLA(inp)
+    gpu = dev.step(64)
+    _guard(inp, gpu, _appended_pool(inp), range(inp.num_seqs))
+
+
+@pytest.mark.parametrize("P", [64, 160])
+def test_partials_and_merge(P):
+    """pkv_mla_decode_partials then pkv_merge_partials (512-wide rows) equals
+    pkv_mla_decode_attention bit for bit; partitions past a sequence's end
+    carry lse = -inf."""
+    inp = make_mla_inputs(num_seqs=4, num_heads=32, ctx=("fixed", [5, 64, 200, 333]), seed=41)
+    dev = DevMLA(inp)
+    whole = torch.from_numpy(dev.step(P))
+    maxp = -(-inp.max_context_len // P)
+    po = torch.full((4, 32, maxp, 512), float("nan"), device="cuda")
+    pl = torch.full((4, 32, maxp), float("nan"), device="cuda")
+    ops.mla_decode_partials(po, pl, dev.q, dev.pool, dev.tables, dev.lens, inp.softmax_scale, P)
+    merged = torch.empty_like(dev.out)
+    ops.merge_partials(merged, po, pl)
+    torch.cuda.synchronize()
+    lse = pl.cpu().numpy()
+    for b in range(4):
+        n = -(-int(inp.context_lens[b]) // P)
+        assert np.all(np.isfinite(lse[b, :, :n])) and np.all(np.isneginf(lse[b, :, n:]))
+    assert torch.equal(merged.float().cpu().double(), whole)
