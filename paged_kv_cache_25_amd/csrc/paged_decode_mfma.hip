@@ -151,6 +151,8 @@ struct MfmaDecode {
   // valid: tokens of the block inside the context (rows past it hold poison and
   // are zeroed in V); vis: tokens of the block this lane's column may see
   // (uniform need_mask says whether any column sees fewer than 16).
+  // With one new token vis == valid and need_mask == (valid < 16): one branch.
+  template <bool kMulti>
   __device__ __forceinline__ void block(BlockRegs<D>& br, int valid, int vis, bool need_mask,
                                         float k_mul, int lane) {
     const int r = lane >> 4;
@@ -162,14 +164,17 @@ struct MfmaDecode {
     float sc[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) sc[i] = s[i] * k_mul;
-    if (need_mask) {                        // wave-uniform: the sequence's last block(s)
+    if constexpr (kMulti) {
+      if (need_mask) {                      // wave-uniform: the sequence's last block(s)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sc[i] = 4 * r + i < vis ? sc[i] : -INFINITY;
+        for (int i = 0; i < 4; ++i) sc[i] = 4 * r + i < vis ? sc[i] : -INFINITY;
+      }
     }
-    if (valid < 16) {
+    if (valid < 16) {                       // wave-uniform: the sequence's last block
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const bool ok = 4 * r + i < valid;
+        if constexpr (!kMulti) sc[i] = ok ? sc[i] : -INFINITY;
 #pragma unroll
         for (int w = 0; w < T::kVWords; ++w) br.v[i][w] = ok ? br.v[i][w] : 0u;
       }
@@ -263,6 +268,11 @@ void paged_decode_mfma_kernel(DecodeArgs a) {
     cols.row0 = b;
     cols.t = 1;
   }
+  // Row of column n in q/out/partials; one new token needs no division.
+  auto row_of = [&](int n) -> size_t {
+    if constexpr (kMulti) return cols.row(n);
+    return size_t(b) * a.num_q_heads + size_t(h) * a.group + n;
+  };
   const int n0 = chunk * kHeadTile;
   if (!cols.valid(n0)) return;                        // no column of this tile exists
   const int my_n = n0 + c;
@@ -270,7 +280,7 @@ void paged_decode_mfma_kernel(DecodeArgs a) {
 
   if (blk_begin >= blk_end && !(a.write_final && part == 0)) {   // partition past the end
     if (a.mark_empty && lane < kHeadTile && my_col)
-      a.part_lse[cols.row(my_n) * a.max_partitions + part] = -INFINITY;
+      a.part_lse[row_of(my_n) * a.max_partitions + part] = -INFINITY;
     return;
   }
   const int my_vis = kMulti && my_col ? cols.visible(my_n, ctx) : ctx;   // tokens my column attends to
@@ -282,7 +292,7 @@ void paged_decode_mfma_kernel(DecodeArgs a) {
   MfmaDecode<D> dec;
   {
     const bool ok = my_col;
-    const char* qrow = reinterpret_cast<const char*>(a.q) + (ok ? cols.row(my_n) : 0) * T::kRowBytes;
+    const char* qrow = reinterpret_cast<const char*>(a.q) + (ok ? row_of(my_n) : 0) * T::kRowBytes;
 #pragma unroll
     for (int j = 0; j < T::kSlabs; ++j) {
       uint4 w = ok ? *reinterpret_cast<const uint4*>(qrow + 64 * j + 16 * r) : make_uint4(0, 0, 0, 0);
@@ -337,7 +347,7 @@ void paged_decode_mfma_kernel(DecodeArgs a) {
                            reinterpret_cast<char*>(a.v_pool_w) + off, t_new, lane);
         }
       }
-      dec.block(br, valid, vis, need_mask, k_mul, lane);
+      dec.template block<kMulti>(br, valid, vis, need_mask, k_mul, lane);
     };
 
     // Ring of kDepth register buffers: block k+kDepth-1 is requested before
@@ -369,7 +379,7 @@ void paged_decode_mfma_kernel(DecodeArgs a) {
   for (int i = 0; i < 4; ++i) {
     const int n = n0 + 4 * r + i;                      // output row 4r+i is column n
     if (!cols.valid(n)) continue;
-    const size_t qrow = cols.row(n);
+    const size_t qrow = row_of(n);
     const bool empty = l_row[i] == 0.0f;
     const float inv = empty ? 0.0f : 1.0f / l_row[i];
     if (final_out) {
