@@ -141,6 +141,19 @@ __device__ __forceinline__ void store_new_row(const BlockRegs<D>& br, char* ksli
   }
 }
 
+// V rows past `valid` hold poison: zero them (their weights are 0, and 0 * NaN
+// would not be).
+template <int D>
+__device__ __forceinline__ void zero_v_tail(BlockRegs<D>& br, int valid, int lane) {
+  const int r = lane >> 4;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const bool ok = 4 * r + i < valid;
+#pragma unroll
+    for (int w = 0; w < MfmaTile<D>::kVWords; ++w) br.v[i][w] = ok ? br.v[i][w] : 0u;
+  }
+}
+
 template <int D>
 struct MfmaDecode {
   using T = MfmaTile<D>;
@@ -152,7 +165,9 @@ struct MfmaDecode {
   // are zeroed in V); vis: tokens of the block this lane's column may see
   // (uniform need_mask says whether any column sees fewer than 16).
   // With one new token vis == valid and need_mask == (valid < 16): one branch.
-  template <bool kMulti>
+  // kZeroV: zero V past `valid` here (off when several tiles share the block
+  // and it was zeroed once before them).
+  template <bool kMulti, bool kZeroV = true>
   __device__ __forceinline__ void block(BlockRegs<D>& br, int valid, int vis, bool need_mask,
                                         float k_mul, int lane) {
     const int r = lane >> 4;
@@ -170,7 +185,7 @@ struct MfmaDecode {
         for (int i = 0; i < 4; ++i) sc[i] = 4 * r + i < vis ? sc[i] : -INFINITY;
       }
     }
-    if (valid < 16) {                       // wave-uniform: the sequence's last block
+    if (kZeroV && valid < 16) {             // wave-uniform: the sequence's last block
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const bool ok = 4 * r + i < valid;
@@ -219,10 +234,12 @@ struct MfmaDecode {
 // Three waves per SIMD: about 150 VGPRs for head dim 128 with two blocks in registers.
 // kMulti: several new tokens per sequence (per-column visibility); otherwise
 // one new token, whose column sees the whole context.  kNT: K/V loads carry the
-// nontemporal hint; off when several column tiles read the same blocks, so the
-// later tiles find them in L2.
-template <int D, bool kMulti, bool kNT>
-__global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(PKV_MFMA_WAVES_PER_EU)))
+// nontemporal hint; off when several workgroups read the same blocks, so the
+// later ones find them in L2.  NT: column tiles of 16 per wave, sharing each
+// block's K/V registers (2 for more than 16 columns: two waves per SIMD).
+template <int D, bool kMulti, bool kNT, int NT>
+__global__ __launch_bounds__(kWave)
+__attribute__((amdgpu_waves_per_eu(NT == 1 ? PKV_MFMA_WAVES_PER_EU : 2)))
 void paged_decode_mfma_kernel(DecodeArgs a) {
   using T = MfmaTile<D>;
   // blockIdx.x -> (column chunk, unit = (kv head, sequence, partition)).
@@ -273,35 +290,42 @@ void paged_decode_mfma_kernel(DecodeArgs a) {
     if constexpr (kMulti) return cols.row(n);
     return size_t(b) * a.num_q_heads + size_t(h) * a.group + n;
   };
-  const int n0 = chunk * kHeadTile;
-  if (!cols.valid(n0)) return;                        // no column of this tile exists
-  const int my_n = n0 + c;
-  const bool my_col = cols.valid(my_n);
+  const int n0 = chunk * kHeadTile * NT;
+  if (!cols.valid(n0)) return;                        // no column of this workgroup exists
 
   if (blk_begin >= blk_end && !(a.write_final && part == 0)) {   // partition past the end
-    if (a.mark_empty && lane < kHeadTile && my_col)
-      a.part_lse[row_of(my_n) * a.max_partitions + part] = -INFINITY;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+      if (a.mark_empty && lane < kHeadTile && cols.valid(n0 + 16 * nt + c))
+        a.part_lse[row_of(n0 + 16 * nt + c) * a.max_partitions + part] = -INFINITY;
     return;
   }
-  const int my_vis = kMulti && my_col ? cols.visible(my_n, ctx) : ctx;   // tokens my column attends to
-  const int min_vis = kMulti ? cols.visible(n0, ctx) : ctx;     // fewest: the tile's first column
+  int my_vis[NT];                                     // tokens my column of tile nt attends to
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int n = n0 + 16 * nt + c;
+    my_vis[nt] = kMulti && cols.valid(n) ? cols.visible(n, ctx) : ctx;
+  }
+  const int min_vis = kMulti ? cols.visible(n0, ctx) : ctx;     // fewest: the first column
   // A sequence whose blocks fit one partition is finished here: write the
   // final output instead of a partial (the merge skips it).
   const bool final_out = a.write_final || (a.final_single && n_blk_seq <= a.blocks_per_partition);
 
-  MfmaDecode<D> dec;
-  {
-    const bool ok = my_col;
-    const char* qrow = reinterpret_cast<const char*>(a.q) + (ok ? row_of(my_n) : 0) * T::kRowBytes;
+  MfmaDecode<D> dec[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int n = n0 + 16 * nt + c;
+    const bool ok = cols.valid(n);
+    const char* qrow = reinterpret_cast<const char*>(a.q) + (ok ? row_of(n) : 0) * T::kRowBytes;
 #pragma unroll
     for (int j = 0; j < T::kSlabs; ++j) {
       uint4 w = ok ? *reinterpret_cast<const uint4*>(qrow + 64 * j + 16 * r) : make_uint4(0, 0, 0, 0);
-      dec.q[j] = __builtin_bit_cast(bf16x8, w);
+      dec[nt].q[j] = __builtin_bit_cast(bf16x8, w);
     }
 #pragma unroll
-    for (int t = 0; t < T::kTiles; ++t) dec.o[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    dec.m = -INFINITY;
-    dec.l = 0.0f;
+    for (int t = 0; t < T::kTiles; ++t) dec[nt].o[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    dec[nt].m = -INFINITY;
+    dec[nt].l = 0.0f;
   }
 
   const char* kbase = reinterpret_cast<const char*>(a.k_pool);
@@ -330,12 +354,8 @@ void paged_decode_mfma_kernel(DecodeArgs a) {
       valid = valid < kBlockSize ? valid : kBlockSize;
       const bool ok = (ok_mask >> k) & 1;
       valid = ok ? valid : 0;
-      int vis = valid;
       bool need_mask = valid < kBlockSize;
-      if constexpr (kMulti) {
-        vis = ok ? my_vis - first : 0;
-        need_mask = !ok || first + kBlockSize > min_vis;
-      }
+      if constexpr (kMulti) need_mask = !ok || first + kBlockSize > min_vis;
       if (seg + k == append_blk && ok) {
         const size_t nrow = (size_t(b) * a.num_kv_heads + h) * T::kRowBytes;
         take_new_row<D>(br, reinterpret_cast<const char*>(a.k_new) + nrow,
@@ -347,7 +367,16 @@ void paged_decode_mfma_kernel(DecodeArgs a) {
                            reinterpret_cast<char*>(a.v_pool_w) + off, t_new, lane);
         }
       }
-      dec.template block<kMulti>(br, valid, vis, need_mask, k_mul, lane);
+      if constexpr (NT == 1) {
+        const int vis = kMulti ? (ok ? my_vis[0] - first : 0) : valid;
+        dec[0].template block<kMulti>(br, valid, vis, need_mask, k_mul, lane);
+      } else {
+        if (valid < kBlockSize) zero_v_tail<D>(br, valid, lane);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+          dec[nt].template block<kMulti, false>(br, valid, ok ? my_vis[nt] - first : 0, need_mask,
+                                                k_mul, lane);
+      }
     };
 
     // Ring of kDepth register buffers: block k+kDepth-1 is requested before
@@ -365,43 +394,47 @@ void paged_decode_mfma_kernel(DecodeArgs a) {
     }
   }
 
-  // Denominator of column l%16 over the 4 lane rows; then that of column 4r+i.
-  float lt = dec.l + __shfl_xor(dec.l, 16);
-  lt += __shfl_xor(lt, 32);
-  float l_row[4], m_row[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    l_row[i] = __shfl(lt, 4 * r + i);
-    m_row[i] = __shfl(dec.m, 4 * r + i);
-  }
   constexpr int kDimsPerLane = D / 16;       // dims dpl*c .. dpl*c + dpl-1 of each head row
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int n = n0 + 4 * r + i;                      // output row 4r+i is column n
-    if (!cols.valid(n)) continue;
-    const size_t qrow = row_of(n);
-    const bool empty = l_row[i] == 0.0f;
-    const float inv = empty ? 0.0f : 1.0f / l_row[i];
-    if (final_out) {
-      uint16_t* orow = reinterpret_cast<uint16_t*>(a.out) + qrow * D + kDimsPerLane * c;
-      uint32_t packed[kDimsPerLane / 2];
+  for (int nt = 0; nt < NT; ++nt) {
+    const MfmaDecode<D>& dt = dec[nt];
+    // Denominator of column l%16 over the 4 lane rows; then that of column 4r+i.
+    float lt = dt.l + __shfl_xor(dt.l, 16);
+    lt += __shfl_xor(lt, 32);
+    float l_row[4], m_row[4];
 #pragma unroll
-      for (int e = 0; e < kDimsPerLane; e += 2)
-        packed[e / 2] = uint32_t(f32_to_bf16_rne(dec.o[e][i] * inv)) |
-                        (uint32_t(f32_to_bf16_rne(dec.o[e + 1][i] * inv)) << 16);
-      if constexpr (kDimsPerLane == 8)
-        *reinterpret_cast<uint4*>(orow) = make_uint4(packed[0], packed[1], packed[2], packed[3]);
-      else
-        *reinterpret_cast<uint2*>(orow) = make_uint2(packed[0], packed[1]);
-    } else {
-      const size_t prow = qrow * a.max_partitions + part;
-      float* op = a.part_o + prow * D + kDimsPerLane * c;
+    for (int i = 0; i < 4; ++i) {
+      l_row[i] = __shfl(lt, 4 * r + i);
+      m_row[i] = __shfl(dt.m, 4 * r + i);
+    }
 #pragma unroll
-      for (int e = 0; e < kDimsPerLane; e += 4)
-        *reinterpret_cast<float4*>(op + e) = make_float4(dec.o[e][i] * inv, dec.o[e + 1][i] * inv,
-                                                         dec.o[e + 2][i] * inv, dec.o[e + 3][i] * inv);
-      if (c == 0)
-        a.part_lse[prow] = empty ? -INFINITY : (m_row[i] + __builtin_amdgcn_logf(l_row[i])) * kLn2;
+    for (int i = 0; i < 4; ++i) {
+      const int n = n0 + 16 * nt + 4 * r + i;          // output row 4r+i of tile nt is column n
+      if (!cols.valid(n)) continue;
+      const size_t qrow = row_of(n);
+      const bool empty = l_row[i] == 0.0f;
+      const float inv = empty ? 0.0f : 1.0f / l_row[i];
+      if (final_out) {
+        uint16_t* orow = reinterpret_cast<uint16_t*>(a.out) + qrow * D + kDimsPerLane * c;
+        uint32_t packed[kDimsPerLane / 2];
+#pragma unroll
+        for (int e = 0; e < kDimsPerLane; e += 2)
+          packed[e / 2] = uint32_t(f32_to_bf16_rne(dt.o[e][i] * inv)) |
+                          (uint32_t(f32_to_bf16_rne(dt.o[e + 1][i] * inv)) << 16);
+        if constexpr (kDimsPerLane == 8)
+          *reinterpret_cast<uint4*>(orow) = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+        else
+          *reinterpret_cast<uint2*>(orow) = make_uint2(packed[0], packed[1]);
+      } else {
+        const size_t prow = qrow * a.max_partitions + part;
+        float* op = a.part_o + prow * D + kDimsPerLane * c;
+#pragma unroll
+        for (int e = 0; e < kDimsPerLane; e += 4)
+          *reinterpret_cast<float4*>(op + e) = make_float4(dt.o[e][i] * inv, dt.o[e + 1][i] * inv,
+                                                           dt.o[e + 2][i] * inv, dt.o[e + 3][i] * inv);
+        if (c == 0)
+          a.part_lse[prow] = empty ? -INFINITY : (m_row[i] + __builtin_amdgcn_logf(l_row[i])) * kLn2;
+      }
     }
   }
 }
@@ -414,20 +447,18 @@ hipError_t launch_d(const DecodeArgs& a, hipStream_t stream) {
   const size_t grid = decode_grid(units, a.head_chunks);
   if (grid > 0x7fffffffu) return hipErrorInvalidConfiguration;
   const bool nt = a.head_chunks == 1 && PKV_NT_LOADS;
+  const dim3 g{unsigned(grid)}, blk{unsigned(kWave)};
   if (a.q_start) {
-    if (nt)
-      hipLaunchKernelGGL((paged_decode_mfma_kernel<D, true, true>), dim3(unsigned(grid)),
-                         dim3(kWave), 0, stream, a);
-    else
-      hipLaunchKernelGGL((paged_decode_mfma_kernel<D, true, false>), dim3(unsigned(grid)),
-                         dim3(kWave), 0, stream, a);
+    if (a.tiles_per_wave == 2) {
+      if (nt) hipLaunchKernelGGL((paged_decode_mfma_kernel<D, true, true, 2>), g, blk, 0, stream, a);
+      else hipLaunchKernelGGL((paged_decode_mfma_kernel<D, true, false, 2>), g, blk, 0, stream, a);
+    } else {
+      if (nt) hipLaunchKernelGGL((paged_decode_mfma_kernel<D, true, true, 1>), g, blk, 0, stream, a);
+      else hipLaunchKernelGGL((paged_decode_mfma_kernel<D, true, false, 1>), g, blk, 0, stream, a);
+    }
   } else {
-    if (nt)
-      hipLaunchKernelGGL((paged_decode_mfma_kernel<D, false, true>), dim3(unsigned(grid)),
-                         dim3(kWave), 0, stream, a);
-    else
-      hipLaunchKernelGGL((paged_decode_mfma_kernel<D, false, false>), dim3(unsigned(grid)),
-                         dim3(kWave), 0, stream, a);
+    if (nt) hipLaunchKernelGGL((paged_decode_mfma_kernel<D, false, true, 1>), g, blk, 0, stream, a);
+    else hipLaunchKernelGGL((paged_decode_mfma_kernel<D, false, false, 1>), g, blk, 0, stream, a);
   }
   return hipGetLastError();
 }

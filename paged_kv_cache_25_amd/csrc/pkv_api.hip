@@ -551,7 +551,10 @@ pkv_status_t multi_setup(MultiSetup& ms, const void* q, const void* k_pool, cons
   const int group = num_q_heads / num_kv_heads;
   const int64_t columns = int64_t(max_query_len) * group;     // queries per KV head
   ms.mfma = uses_mfma(q_dtype, kv_dtype, columns);
-  ms.tile = ms.mfma ? pkv::mfma_head_tile()
+  // More than 16 columns on the matrix cores: two 16-column tiles per wave
+  // share each block's K/V registers.
+  const int tiles_per_wave = ms.mfma && columns > pkv::mfma_head_tile() ? 2 : 1;
+  ms.tile = ms.mfma ? pkv::mfma_head_tile() * tiles_per_wave
                     : tile_heads(columns < (1 << 20) ? int(columns) : (1 << 20), head_dim);
   const int64_t chunks = (columns + ms.tile - 1) / ms.tile;
   if (chunks > 0x7fffffff) return PKV_ERR_INVALID_ARG;
@@ -560,6 +563,7 @@ pkv_status_t multi_setup(MultiSetup& ms, const void* q, const void* k_pool, cons
                      max_blocks_per_seq, softmax_scale, ms.tile);
   ms.a.q_start = query_start_loc;
   ms.a.max_q = max_query_len;
+  ms.a.tiles_per_wave = tiles_per_wave;
   ms.a.head_chunks = int(chunks);
   return PKV_OK;
 }

@@ -93,6 +93,7 @@ struct DecodeArgs {
   // Rows q_start[b] .. q_start[b+1]-1 of q/out are sequence b's newest tokens.
   const int32_t* q_start;
   int max_q;                  // most new tokens of any sequence (1 without q_start)
+  int tiles_per_wave;         // matrix-core kernel with q_start: 16-column tiles per wave (1 or 2)
   int num_seqs, num_q_heads, num_kv_heads, group, head_chunks;
   int num_blocks, max_blocks_per_seq;
   int blocks_per_partition;   // partition size / 16
