@@ -11,13 +11,27 @@
 // product is dense: per token and head 2 * (576 + 512) FLOP for 1,152 bytes.
 //
 // One workgroup of WAVES waves per (head chunk of 16*WAVES heads, sequence,
-// partition); wave w owns 16 heads.  The partition's blocks are walked in
-// pairs (32 tokens).  Each pair is copied once into LDS as 32 row-major rows
-// (576 numbers + 8 of padding, so that 16 rows read at one column hit 16
-// different bank groups), straight from HBM with 16-byte direct-to-LDS loads
-// (no registers; rows past the context, past the partition or of a block with
-// a bad table entry are loaded from a zero row instead).  Two buffers: the
-// next pair is in flight while this one is computed, one barrier per pair.
+// partition); wave w owns 16 heads.  128 heads are one workgroup of 8 waves,
+// so the copy of a pair of blocks into LDS (about 1,000 cycles of the CU's
+// direct-to-LDS path for 38 KB, the cost that splitting the heads over two
+// workgroups doubles) serves every head.  The 16 heads' absorbed queries (72
+// registers) and fp32 accumulators (128) stay in registers; two waves per
+// SIMD.
+//
+// The partition's blocks are walked in pairs (32 tokens).  Each pair is
+// copied once into LDS, straight from HBM with 16-byte direct-to-LDS loads:
+// block j of the pair occupies 19 whole 64-slot slices (16 rows of 74 slots,
+// then 32 unused), so that one load instruction never spans two blocks and
+// addresses a single block base plus a per-lane offset.  A row is 576 numbers
+// + 16 of padding: a stride of 296 dwords, 40 mod 64, puts both the 16-row
+// column reads of the score product and the transposed reads of the value
+// product on distinct LDS banks (a stride of 292 dwords measured half the
+// read rate).  Rows past the context, past the partition or of a block with a
+// bad table entry are not loaded: their slots keep zeros (both buffers are
+// cleared once) or a row of an earlier pair of this workgroup, and their
+// scores are masked, so their values get weight 0.  Two buffers: the next
+// pair is in flight while this one is computed.
+//
 // Per pair and wave:
 //   S^T[16 tok x 16 heads] = K . Q^T    2 x 18 mfma_f32_16x16x32_bf16
 //   online softmax in fp32 (log2 units, lazily raised maxima)
@@ -37,31 +51,49 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-
-constexpr int kDc = 512;                        // latent (value) width
-constexpr int kDk = 576;                        // row width: latent + rotary key
-constexpr int kRowBytes = kDk * 2;
-constexpr int kChunksPerRow = kRowBytes / 16;   // 72
-constexpr int kPairTokens = 32;
-constexpr int kKStride = kDk + 8;               // bf16 elements per staged row
-constexpr int kSlotsPerRow = kKStride * 2 / 16; // 73 16-byte slots, the last one padding
-constexpr int kPairSlots = kPairTokens * kSlotsPerRow;
-constexpr int kSlices = (kPairSlots + kWave - 1) / kWave;   // 64-slot direct loads per pair (37)
-constexpr int kBufElems = kSlices * kWave * 8;  // whole slices, so the last one stays inside
-constexpr int kSlabs = kDk / 32;                // 18 score products per block
-constexpr int kTiles = kDc / 16;                // 32 value products per pair
-constexpr float kRescaleThreshold = 8.0f;
-
-// 16 bytes of zeros in device memory: the source of rows that must read as 0.
-__device__ __attribute__((aligned(16))) uint32_t g_zero_row[4] = {0u, 0u, 0u, 0u};
-
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
+constexpr int kDc = 512;                        // latent (value) width
+constexpr int kDk = 576;                        // row width: latent + rotary key
+constexpr int kRowBytes = kDk * 2;
+constexpr int kBlockBytes = kBlockSize * kRowBytes;
+constexpr int kChunksPerRow = kRowBytes / 16;   // 72
+constexpr int kKStride = kDk + 16;              // bf16 elements per staged row
+constexpr int kSlotsPerRow = kKStride * 2 / 16; // 74 16-byte slots, the last two padding
+constexpr int kBlockSlices = (kBlockSize * kSlotsPerRow + kWave - 1) / kWave;   // 19
+constexpr int kSlices = 2 * kBlockSlices;       // 38 direct loads of 64 slots per pair
+constexpr int kBlockElems = kBlockSlices * kWave * 8;   // block 1 starts here (9,728)
+constexpr int kBufElems = 2 * kBlockElems;
+constexpr int kSlabs = kDk / 32;              // 18 score products per block and wave
+constexpr int kTiles = kDc / 16;              // 32 value products per pair and wave
+constexpr float kRescaleThreshold = 8.0f;
+static_assert(kBlockSlices * kWave >= kBlockSize * kSlotsPerRow, "a block's rows fit its slices");
+
+// Maximum over lanes l, l ^ 16, l ^ 32 and l ^ 48 (the four token groups of a
+// head): each lane swap returns the two halves it exchanged, whose larger
+// element is the pairwise maximum in every lane.
+__device__ __forceinline__ float max_over_groups(float v) {
+  const int x = __builtin_bit_cast(int, v);
+  const auto a = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  const float w = fmaxf(__builtin_bit_cast(float, a[0]), __builtin_bit_cast(float, a[1]));
+  const int y = __builtin_bit_cast(int, w);
+  const auto b = __builtin_amdgcn_permlane16_swap(y, y, false, false);
+  return fmaxf(__builtin_bit_cast(float, b[0]), __builtin_bit_cast(float, b[1]));
+}
+
+// Two floats to bf16 (round to nearest even), low one first.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return uint32_t(__builtin_bit_cast(uint16_t, __bf16(lo))) |
+         (uint32_t(__builtin_bit_cast(uint16_t, __bf16(hi))) << 16);
+}
+
 template <int WAVES>
 __global__ __launch_bounds__(WAVES * kWave) void mla_decode_kernel(MlaArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t s_k[2][kBufElems];
+  constexpr int kThreads = WAVES * kWave;
+  __shared__ __attribute__((aligned(16))) uint16_t s_k0[kBufElems];
+  __shared__ __attribute__((aligned(16))) uint16_t s_k1[kBufElems];
   constexpr int kSlicesPerWave = (kSlices + WAVES - 1) / WAVES;
 
   int chunk, unit;
@@ -80,9 +112,9 @@ __global__ __launch_bounds__(WAVES * kWave) void mla_decode_kernel(MlaArgs a) {
   const int blk_begin = part * a.blocks_per_partition;
   int blk_end = blk_begin + a.blocks_per_partition;
   blk_end = blk_end < n_blk_seq ? blk_end : n_blk_seq;
-  const int head_base = chunk * WAVES * 16;              // first head of the workgroup
-  const int h0 = head_base + wave * 16;                  // first head of this wave
+  const int h0 = (chunk * WAVES + wave) * 16;            // first head of this wave
 
+  // (b, part) is uniform over the workgroup: every wave returns here or none.
   if (blk_begin >= blk_end && !(a.write_final && part == 0)) {    // partition past the end
     if (a.mark_empty && lane < 16 && h0 + lane < a.num_heads)
       a.part_lse[(size_t(b) * a.num_heads + h0 + lane) * a.max_partitions + part] = -INFINITY;
@@ -93,11 +125,18 @@ __global__ __launch_bounds__(WAVES * kWave) void mla_decode_kernel(MlaArgs a) {
   const int32_t* table = a.block_tables + size_t(b) * a.max_blocks_per_seq;
   const char* pool = static_cast<const char*>(a.pool);
 
-  // Absorbed query of head h0 + c as the B operand of the score product.
+  // Clear both buffers, so that slots never loaded read as zeros.
+  for (int i = threadIdx.x; i < kBufElems / 8; i += kThreads) {
+    reinterpret_cast<uint4*>(s_k0)[i] = make_uint4(0, 0, 0, 0);
+    reinterpret_cast<uint4*>(s_k1)[i] = make_uint4(0, 0, 0, 0);
+  }
+
+  // The absorbed query of head h0 + c, as the B operand of the score product.
   bf16x8 q[kSlabs];
   {
     const bool ok = h0 + c < a.num_heads;
-    const char* qrow = static_cast<const char*>(a.q) + (size_t(b) * a.num_heads + (ok ? h0 + c : 0)) * kRowBytes;
+    const char* qrow = static_cast<const char*>(a.q) +
+                       (size_t(b) * a.num_heads + (ok ? h0 + c : 0)) * kRowBytes;
 #pragma unroll
     for (int j = 0; j < kSlabs; ++j) {
       const uint4 w = ok ? *reinterpret_cast<const uint4*>(qrow + 64 * j + 16 * g) : make_uint4(0, 0, 0, 0);
@@ -131,75 +170,68 @@ __global__ __launch_bounds__(WAVES * kWave) void mla_decode_kernel(MlaArgs a) {
     ok1 = k + 1 < kWave && ((ok_mask >> (k + 1)) & 1);
   };
 
-  // Pair p into buffer buf: slice s of the pair (64 consecutive 16-byte slots)
-  // is one direct-to-LDS load; slot 64s + lane is row (slot / 73), chunk
-  // (slot % 73) of the staged pair.  Padding slots and rows that must be zero
-  // read the zero row.
-  auto stage = [&](int p, int phys0, int phys1, bool ok0, bool ok1, int buf) {
-    const int pos0 = (blk_begin + 2 * p) * kBlockSize;
+  // Pair p into dst: slice sl is one direct-to-LDS load of 64 slots of block
+  // sl / 19; lanes whose row is padding, past the attended tokens or in a
+  // block with a bad table entry load nothing.
+  auto stage = [&](int p, uint16_t* dst, bool& ok0, bool& ok1) {
+    int phys0, phys1;
+    pair_ids(p, phys0, phys1, ok0, ok1);
+    const int rem0 = limit - (blk_begin + 2 * p) * kBlockSize;   // rows of block 0 attended
+    const char* base0 = pool + size_t(unsigned(phys0)) * kBlockBytes;
+    const char* base1 = pool + size_t(unsigned(phys1)) * kBlockBytes;
 #pragma unroll
     for (int r = 0; r < kSlicesPerWave; ++r) {
       const int sl = wave + r * WAVES;
       if (sl >= kSlices) break;
-      const int slot = sl * kWave + lane;
-      const int row = slot / kSlotsPerRow;
-      const int ch = slot % kSlotsPerRow;
-      const bool blk_ok = row < 16 ? ok0 : ok1;
-      const bool live = row < kPairTokens && ch < kChunksPerRow && blk_ok && pos0 + row < limit;
-      const char* src = reinterpret_cast<const char*>(g_zero_row);
-      if (live) {
-        const int phys = row < 16 ? phys0 : phys1;
-        src = pool + (size_t(phys) * kBlockSize + (row & 15)) * kRowBytes + size_t(ch) * 16;
+      const bool blk1 = sl >= kBlockSlices;
+      if (!(blk1 ? ok1 : ok0)) continue;
+      const int rem = blk1 ? rem0 - kBlockSize : rem0;
+      const int local = (sl - (blk1 ? kBlockSlices : 0)) * kWave + lane;
+      const int row = local / kSlotsPerRow, ch = local - row * kSlotsPerRow;
+      if (row < rem && row < kBlockSize && ch < kChunksPerRow) {
+        // (a named pointer: as a direct argument of the builtin this sum
+        // makes the host pass drop the kernel's launch stub)
+        const char* src = (blk1 ? base1 : base0) + (row * kRowBytes + ch * 16);
+        __builtin_amdgcn_global_load_lds(src, (lds_void*)(dst + sl * kWave * 8), 16, 0, 0);
       }
-      __builtin_amdgcn_global_load_lds(src, (lds_void*)&s_k[buf][sl * kWave * 8], 16, 0, 0);
     }
   };
 
-  int phys0 = 0, phys1 = 0;
-  bool ok0 = false, ok1 = false;
-  if (n_pairs > 0) {
-    pair_ids(0, phys0, phys1, ok0, ok1);
-    stage(0, phys0, phys1, ok0, ok1, 0);
-  }
-  __builtin_amdgcn_s_waitcnt(0);                      // this wave's copies have landed
-  __syncthreads();                                    // and everyone's
-  for (int p = 0; p < n_pairs; ++p) {
-    const int buf = p & 1;
-    // the next pair's copies, in flight while this pair is computed
-    int nphys0 = 0, nphys1 = 0;
-    bool nok0 = false, nok1 = false;
-    if (p + 1 < n_pairs) {
-      pair_ids(p + 1, nphys0, nphys1, nok0, nok1);
-      stage(p + 1, nphys0, nphys1, nok0, nok1, buf ^ 1);
-    }
-
-    // Scores of the pair's two blocks: lane holds tokens 16j + 4g + i of head h0 + c.
+  // Pair p, staged in kb, with its blocks' validity flags.
+  auto compute = [&](const uint16_t* kb, int p, bool ok0, bool ok1) {
+    // Scores of the pair's two blocks: lane holds tokens 16j + 4g + i of head
+    // h0 + c.
     f32x4 s[2];
 #pragma unroll
+    for (int j = 0; j < 2; ++j) s[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
     for (int j = 0; j < 2; ++j) {
-      s[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-      const uint16_t* krow = &s_k[buf][(16 * j + c) * kKStride + 8 * g];
+      const uint16_t* krow = kb + j * kBlockElems + c * kKStride + 8 * g;
 #pragma unroll
       for (int kc = 0; kc < kSlabs; ++kc) {
         const bf16x8 kv = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(krow + 32 * kc));
         s[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, q[kc], s[j], 0, 0, 0);
       }
     }
-    const int pos0 = (blk_begin + 2 * p) * kBlockSize;
+
+    const int rem = limit - (blk_begin + 2 * p) * kBlockSize;      // tokens of the pair attended
     float x[8];
+    if (ok0 && ok1 && rem >= 2 * kBlockSize) {           // uniform: the whole pair counts
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+      for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int pos = pos0 + 16 * j + 4 * g + i;
-        const bool ok = (j ? ok1 : ok0) && pos < limit;
-        x[4 * j + i] = ok ? s[j][i] * a.scale_log2 : -INFINITY;
-      }
-    float bm = x[0];
+        for (int i = 0; i < 4; ++i) x[4 * j + i] = s[j][i] * a.scale_log2;
+    } else {
 #pragma unroll
-    for (int k = 1; k < 8; ++k) bm = fmaxf(bm, x[k]);
-    bm = fmaxf(bm, __shfl_xor(bm, 16));
-    bm = fmaxf(bm, __shfl_xor(bm, 32));
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const bool ok = (j ? ok1 : ok0) && 16 * j + 4 * g + i < rem;
+          x[4 * j + i] = ok ? s[j][i] * a.scale_log2 : -INFINITY;
+        }
+    }
+    const float bm = max_over_groups(fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
+                                           fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7]))));
     if (__any(bm > m + kRescaleThreshold)) {              // rare: raise the reference maxima
       const float mn = fmaxf(m, bm);
       const float alpha = mn == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m - mn);
@@ -214,33 +246,49 @@ __global__ __launch_bounds__(WAVES * kWave) void mla_decode_kernel(MlaArgs a) {
         for (int i = 0; i < 4; ++i) o[t][i] *= ar[i];
     }
     const float m_eff = m == -INFINITY ? 0.0f : m;
-    uint32_t pw[4];
+    float pv[8];
 #pragma unroll
-    for (int k = 0; k < 8; k += 2) {
-      const float p0 = __builtin_amdgcn_exp2f(x[k] - m_eff);
-      const float p1 = __builtin_amdgcn_exp2f(x[k + 1] - m_eff);
-      l += p0 + p1;
-      pw[k / 2] = uint32_t(f32_to_bf16_rne(p0)) | (uint32_t(f32_to_bf16_rne(p1)) << 16);
+    for (int k = 0; k < 8; ++k) {
+      pv[k] = __builtin_amdgcn_exp2f(x[k] - m_eff);
+      l += pv[k];
     }
-    const bf16x8 pa = __builtin_bit_cast(bf16x8, make_uint4(pw[0], pw[1], pw[2], pw[3]));
-    // V operand of tile t: rows 4g + (c >> 2) (block 0) and 16 + 4g + (c >> 2)
-    // (block 1), columns 16t + 4(c & 3), read transposed.
-    const uint16_t* vrow = &s_k[buf][(4 * g + (c >> 2)) * kKStride + 4 * (c & 3)];
+    const bf16x8 pa = __builtin_bit_cast(
+        bf16x8, make_uint4(pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]),
+                           pack_bf16x2(pv[4], pv[5]), pack_bf16x2(pv[6], pv[7])));
+    // V operand of tile t: rows 4g + (c >> 2) of block 0 and of block 1,
+    // columns 16t + 4(c & 3), read transposed.
+    const uint16_t* vrow = kb + (4 * g + (c >> 2)) * kKStride + 4 * (c & 3);
 #pragma unroll
     for (int t = 0; t < kTiles; ++t) {
       const v4i16 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vrow + 16 * t));
       const v4i16 v1 =
-          __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vrow + 16 * kKStride + 16 * t));
+          __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vrow + kBlockElems + 16 * t));
       const uint2 w0 = __builtin_bit_cast(uint2, v0);
       const uint2 w1 = __builtin_bit_cast(uint2, v1);
       const bf16x8 vb = __builtin_bit_cast(bf16x8, make_uint4(w0.x, w0.y, w1.x, w1.y));
       o[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, vb, o[t], 0, 0, 0);
     }
-    phys0 = nphys0;
-    phys1 = nphys1;
-    ok0 = nok0;
-    ok1 = nok1;
-    __builtin_amdgcn_s_waitcnt(0);                    // the next pair's copies have landed
+  };
+
+  // Even pairs live in s_k0, odd pairs in s_k1.  Every wave runs the same
+  // number of iterations, so the barriers match.  (Unrolling the loop by two
+  // to name each buffer statically would let the compiler tell the copy of
+  // the next pair from the reads of this one, but the second copy of the
+  // body does not fit in the registers.)
+  __syncthreads();                                    // buffers cleared
+  bool ok0 = false, ok1 = false;
+  if (n_pairs > 0) stage(0, s_k0, ok0, ok1);
+  __builtin_amdgcn_s_waitcnt(0);                      // this wave's copies have landed
+  __syncthreads();                                    // and everyone's
+  for (int p = 0; p < n_pairs; ++p) {
+    bool nk0 = false, nk1 = false;
+    uint16_t* cur = (p & 1) ? s_k1 : s_k0;
+    uint16_t* nxt = (p & 1) ? s_k0 : s_k1;
+    if (p + 1 < n_pairs) stage(p + 1, nxt, nk0, nk1);
+    compute(cur, p, ok0, ok1);
+    ok0 = nk0;
+    ok1 = nk1;
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
 
@@ -289,11 +337,12 @@ hipError_t launch_mla_decode(const MlaArgs& a, hipStream_t stream) {
   if (units > 0x7fffffffu) return hipErrorInvalidConfiguration;
   const size_t grid = decode_grid(units, a.head_chunks);
   if (grid > 0x7fffffffu) return hipErrorInvalidConfiguration;
+  const dim3 g{unsigned(grid)};
   switch (mla_heads_per_workgroup(a.num_heads) / 16) {
-    case 1: hipLaunchKernelGGL(mla_decode_kernel<1>, dim3(unsigned(grid)), dim3(1 * kWave), 0, stream, a); break;
-    case 2: hipLaunchKernelGGL(mla_decode_kernel<2>, dim3(unsigned(grid)), dim3(2 * kWave), 0, stream, a); break;
-    case 4: hipLaunchKernelGGL(mla_decode_kernel<4>, dim3(unsigned(grid)), dim3(4 * kWave), 0, stream, a); break;
-    default: hipLaunchKernelGGL(mla_decode_kernel<8>, dim3(unsigned(grid)), dim3(8 * kWave), 0, stream, a); break;
+    case 1: hipLaunchKernelGGL(mla_decode_kernel<1>, g, dim3(1 * kWave), 0, stream, a); break;
+    case 2: hipLaunchKernelGGL(mla_decode_kernel<2>, g, dim3(2 * kWave), 0, stream, a); break;
+    case 4: hipLaunchKernelGGL(mla_decode_kernel<4>, g, dim3(4 * kWave), 0, stream, a); break;
+    default: hipLaunchKernelGGL(mla_decode_kernel<8>, g, dim3(8 * kWave), 0, stream, a); break;
   }
   return hipGetLastError();
 }

@@ -1,8 +1,9 @@
 """GPU parity of the absorbed MLA decode (pkv_mla_append then
-pkv_mla_decode_attention) against oracle/mla.py: head counts 16..256 (one
-to eight waves per workgroup, and two head chunks), partition sizes that
-split pairs of blocks, edge context lengths, and the DeepSeek-shaped
-batch-64 layer at full size on sampled sequences."""
+pkv_mla_decode_attention) against oracle/mla.py: head counts 16..256 (one to
+eight waves per workgroup, two head chunks, and workgroups whose last waves
+hold no heads), partition sizes that split pairs of blocks, edge context
+lengths, and the DeepSeek-shaped batch-64 layer at full size on sampled
+sequences."""
 
 import numpy as np
 import pytest
@@ -53,7 +54,7 @@ def _oracle(inp, pool=None, seqs=None):
                                    kv_lora_rank=inp.kv_lora_rank, dtype=inp.dtype, seqs=seqs)
 
 
-@pytest.mark.parametrize("heads", [16, 32, 64, 128, 256])
+@pytest.mark.parametrize("heads", [16, 32, 48, 64, 80, 128, 256])
 @pytest.mark.parametrize("P", [512, 48, 32, 0])
 def test_heads_and_partitions(heads, P):
     inp = make_mla_inputs(num_seqs=5, num_heads=heads, ctx=("fixed", [1, 33, 200, 517, 80]),
