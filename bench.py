@@ -769,7 +769,10 @@ def cpu_baseline_multi(inp, budget_s):
     qsl = inp.query_start_loc
     done, elapsed = [], 0.0
     with threadpool_limits(1):
-        for b in range(inp.num_seqs):
+        for k in range(-1, 1 << 30):      # k = -1 untimed; then around the batch until the budget
+            if inp.num_seqs == 0:
+                break
+            b = max(k, 0) % inp.num_seqs
             q0, q1 = int(qsl[b]), int(qsl[b + 1])
             tab = inp.block_tables[b:b + 1]
             lens = inp.context_lens[b:b + 1]
@@ -785,6 +788,8 @@ def cpu_baseline_multi(inp, budget_s):
                                      q_dtype=inp.q_dtype, kv_dtype=inp.kv_dtype,
                                      k_scales=None if inp.k_scales is None else inp.k_scales[ids],
                                      v_scales=None if inp.v_scales is None else inp.v_scales[ids])
+            if k < 0:
+                continue
             elapsed += time.perf_counter() - t
             done.append(b)
             if elapsed > budget_s:
@@ -797,7 +802,8 @@ def cpu_baseline_multi(inp, budget_s):
                                 head_dim=inp.head_dim, kv_dtype=inp.kv_dtype)
     return {"value": round((tr["total_bytes"] + ap["bytes"]) / elapsed / 1e9, 4), "unit": "GB/s",
             "cores": 1, "kind": "oracle",
-            "sample": f"{len(done)} of {inp.num_seqs} sequences ({tr['rows']} new tokens over "
+            "sample": f"{len(done)} sequences taken in order from the {inp.num_seqs}-sequence batch "
+                      f"({len(done) / max(inp.num_seqs, 1):.2f} passes, {tr['rows']} new tokens over "
                       f"{tr['tokens']} cached), append + attention, float64 NumPy, {elapsed:.1f} s",
             "new_tokens_per_s": round(int(t_new.sum()) / elapsed, 3)}
 
@@ -843,7 +849,13 @@ def _cpu_baseline(inp, budget_s, pa, traffic):
     t_start = time.time()
     done = []
     elapsed = 0.0
-    for b in range(inp.num_seqs):
+    # k = -1: one untimed pass over the first sequence (first-touch and
+    # library set-up costs stay out of the timed work); then the sequences in
+    # order, around the batch again until the budget is spent.
+    for k in range(-1, 1 << 30):
+        if inp.num_seqs == 0:
+            break
+        b = max(k, 0) % inp.num_seqs
         sub = inp.subset([b])
         t = time.perf_counter()
         kp, vp = pa.kv_append(sub.k_pool, sub.v_pool, sub.k_new, sub.v_new, sub.block_tables,
@@ -852,6 +864,8 @@ def _cpu_baseline(inp, budget_s, pa, traffic):
                             block_size=sub.block_size, softmax_scale=sub.softmax_scale,
                             q_dtype=sub.q_dtype, kv_dtype=sub.kv_dtype, k_scales=sub.k_scales,
                             v_scales=sub.v_scales)
+        if k < 0:
+            continue
         elapsed += time.perf_counter() - t
         done.append(b)
         if elapsed > budget_s:
@@ -863,7 +877,8 @@ def _cpu_baseline(inp, budget_s, pa, traffic):
                                 kv_dtype=inp.kv_dtype)
     gbps = (tr["total_bytes"] + ap["bytes"]) / elapsed / 1e9
     return {"value": round(gbps, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{len(done)} of {inp.num_seqs} sequences ({tr['tokens']} attended tokens), "
+            "sample": f"{len(done)} sequences taken in order from the {inp.num_seqs}-sequence batch "
+                      f"({len(done) / max(inp.num_seqs, 1):.2f} passes, {tr['tokens']} attended tokens), "
                       f"append + attention, float64 NumPy, {elapsed:.1f} s",
             "tokens_per_s": round(len(done) / elapsed, 3),
             "wall_s": round(time.time() - t_start, 1)}
