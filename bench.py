@@ -93,7 +93,7 @@ def copy_calibration(mib, reps):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only: the decode path "
+        print(json.dumps({"error": "bench.py runs on one GPU only: the decode path "
                           "shards by sequence or KV head with no exchange, so N GPUs run N "
                           "independent copies of this benchmark; --gpus must be 1"}))
         sys.exit(2)
