@@ -54,7 +54,10 @@ MLA_WORKLOADS = {
     "deepseek_mla_b64": dict(num_seqs=64, num_heads=128, ctx=("uniform", 512, 4096), seed=2,
                              partition_size=1024),
     # DeepSeek-V2-Lite's 16 heads, a small batch the oracle finishes quickly.
-    "deepseek_lite_mla_b8": dict(num_seqs=8, num_heads=16, ctx=("uniform", 1, 700), seed=12),
+    # Partitions of one pair of blocks: with one wave per workgroup the time
+    # grows with the pairs each wave walks.
+    "deepseek_lite_mla_b8": dict(num_seqs=8, num_heads=16, ctx=("uniform", 1, 700), seed=12,
+                                 partition_size=32),
 }
 
 
