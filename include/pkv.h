@@ -514,9 +514,25 @@ pkv_status_t pkv_mla_append(void* latent_pool, const void* latent_new,
                             int32_t num_seqs, int32_t row_dim, int32_t block_size,
                             int32_t num_blocks, int32_t max_blocks_per_seq, void* stream);
 
+/* partition_size of pkv_mla_workspace_bytes / pkv_mla_decode_attention
+ * asking for a balanced split: the library divides each sequence's pairs of
+ * blocks into chunks of nearly equal size, chosen from the context lengths on
+ * the device so that the whole batch takes at most max(S, num_seqs) chunks
+ * (S = 256 chunk slots for more than 64 heads, 512 otherwise: the workgroups
+ * MI355X runs at once), each within one sequence, and merges them.  The
+ * result equals a fixed-partition split's up to float rounding; only the
+ * grouping of the partial sums differs.  Intended for batches of uneven or
+ * long contexts, where a fixed partition size leaves the kernel waiting for
+ * the longest partitions. */
+#define PKV_PARTITION_BALANCED (-1)
+
 /* Workspace of pkv_mla_decode_attention: float32 o [num_seqs, num_heads,
  * maxP, kv_lora_rank] then, 256-byte aligned, float32 lse [num_seqs,
- * num_heads, maxP]; 0 when maxP <= 1. */
+ * num_heads, maxP]; 0 when maxP <= 1.  With PKV_PARTITION_BALANCED: float32
+ * o [R, num_heads, kv_lora_rank], float32 lse [R, num_heads] and int32
+ * chunk starts [num_seqs + 1], each 256-byte aligned, R = max(S, num_seqs)
+ * (see PKV_PARTITION_BALANCED); max_context_len is not used.  0 for invalid
+ * arguments. */
 size_t pkv_mla_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t kv_lora_rank,
                                int32_t max_context_len, int32_t partition_size);
 
@@ -527,8 +543,11 @@ size_t pkv_mla_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t kv_l
  * matrix cores with bf16 operands (the weights p rounded to bf16 for the
  * weighted sum); out is rounded to bf16.  A sequence with ctx 0 gets zeros.
  * Split-KV partitions of partition_size tokens are merged as in
- * pkv_paged_decode_attention.  One workgroup serves up to 128 heads, so each
- * cached row is read from HBM once per partition for all of them.
+ * pkv_paged_decode_attention; partition_size == PKV_PARTITION_BALANCED splits
+ * the work into balanced chunks instead (three kernels: the split schedule,
+ * the chunks, the merge; sequences that get one chunk are written directly).
+ * One workgroup serves up to 128 heads, so each cached row is read from HBM
+ * once per partition or chunk for all of them.
  * out [device, written]; q, latent_pool, tables, lens [device, read];
  * workspace [device, scratch] of pkv_mla_workspace_bytes(...) bytes.
  * Supported: kv_lora_rank == 512, rope_dim == 64, num_heads a multiple of
@@ -547,7 +566,8 @@ pkv_status_t pkv_mla_decode_attention(
  * partial_lse float32 [num_seqs, num_heads, max_partitions] [device,
  * written]; partitions at or past ceil(ctx_b / P) get lse = -inf and leave
  * partial_out untouched.  pkv_merge_partials (head_dim 512, out bf16) gives
- * pkv_mla_decode_attention's output. */
+ * pkv_mla_decode_attention's output.  partition_size >= 0 only (the balanced
+ * split's partials are grouped by chunk, not by partition). */
 pkv_status_t pkv_mla_decode_partials(
     float* partial_out, float* partial_lse, int32_t max_partitions, const void* q,
     const void* latent_pool, const int32_t* block_tables, const int32_t* context_lens,

@@ -37,7 +37,9 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(MergeArgs a) {
   const int g = t / kRowThreads, c = t % kRowThreads;
 
   int np = a.max_partitions;
-  if (a.num_partitions) {
+  if (a.chunk_first) {
+    np = a.chunk_first[b + 1] - a.chunk_first[b];
+  } else if (a.num_partitions) {
     np = a.num_partitions[b];
   } else if (a.context_lens) {
     int seq = b;
@@ -56,8 +58,15 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(MergeArgs a) {
   if (a.skip_single && np == 1) return;           // already final (uniform: whole block)
 
   const size_t row = size_t(b) * a.num_q_heads + qh;
-  const float* lse = a.part_lse + row * a.max_partitions;
-  const float* o = a.part_o + row * a.max_partitions * D + 4 * c;
+  // Partition p of this row: rows [b, H, max_partitions] (stride 1), or, for
+  // a balanced split, chunk slot chunk_first[b] + p of rows [slot, H] (stride H).
+  const size_t base = a.chunk_first ? size_t(a.chunk_first[b]) * a.num_q_heads + qh
+                                    : row * a.max_partitions;
+  const size_t stride = a.chunk_first ? size_t(a.num_q_heads) : 1;
+  const float* lse_base = a.part_lse + base;
+  const float* o_base = a.part_o + base * D + 4 * c;
+  auto lse_at = [&](int p) { return lse_base[size_t(p) * stride]; };
+  auto row_at = [&](int p) { return *reinterpret_cast<const float4*>(o_base + size_t(p) * stride * D); };
 
   // First batch of rows and their lse, issued together with the max pass.
   float4 rowv[kUnroll];
@@ -65,12 +74,11 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(MergeArgs a) {
 #pragma unroll
   for (int u = 0; u < kUnroll; ++u) {
     const int p = g + u * kGroups;
-    lp[u] = p < np ? lse[p] : -INFINITY;
-    rowv[u] = p < np ? *reinterpret_cast<const float4*>(o + size_t(p) * D)
-                     : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    lp[u] = p < np ? lse_at(p) : -INFINITY;
+    rowv[u] = p < np ? row_at(p) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
   }
   float M = -INFINITY;
-  for (int p = t; p < np; p += blockDim.x) M = fmaxf(M, lse[p]);
+  for (int p = t; p < np; p += blockDim.x) M = fmaxf(M, lse_at(p));
   M = wave_max(M);
   if ((t & (kWave - 1)) == 0) s_max[t / kWave] = M;
   __syncthreads();
@@ -97,9 +105,8 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(MergeArgs a) {
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
         const int p = p0 + u * kGroups;
-        lp[u] = p < np ? lse[p] : -INFINITY;
-        rowv[u] = p < np ? *reinterpret_cast<const float4*>(o + size_t(p) * D)
-                         : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        lp[u] = p < np ? lse_at(p) : -INFINITY;
+        rowv[u] = p < np ? row_at(p) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
       }
     }
   }

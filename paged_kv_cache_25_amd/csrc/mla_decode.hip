@@ -96,31 +96,65 @@ __global__ __launch_bounds__(WAVES * kWave) void mla_decode_kernel(MlaArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t s_k1[kBufElems];
   constexpr int kSlicesPerWave = (kSlices + WAVES - 1) / WAVES;
 
-  int chunk, unit;
-  if (!decode_unit(blockIdx.x, a.head_chunks, a.num_seqs * a.max_partitions, chunk, unit)) return;
-  const int b = unit % a.num_seqs;
-  const int part = unit / a.num_seqs;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);   // uniform
   const int lane = threadIdx.x % kWave;
   const int g = lane >> 4, c = lane & 15;
-
-  const int raw_ctx = a.context_lens[b];
-  int ctx = raw_ctx < 0 ? 0 : raw_ctx;
   const int cap = a.max_blocks_per_seq * kBlockSize;
-  ctx = ctx > cap ? cap : ctx;
-  const int n_blk_seq = (ctx + kBlockSize - 1) / kBlockSize;
-  const int blk_begin = part * a.blocks_per_partition;
-  int blk_end = blk_begin + a.blocks_per_partition;
-  blk_end = blk_end < n_blk_seq ? blk_end : n_blk_seq;
+
+  // The workgroup's head chunk, sequence and blocks [blk_begin, blk_end); its
+  // partial rows are slot * num_heads + head with slot = the partition of the
+  // sequence (fixed partitions: rows [b, H, max_partitions]) or the chunk
+  // slot (balanced split: rows [slot, H]).
+  int chunk, b, blk_begin, blk_end, n_blk_seq, ctx;
+  size_t slot_row, slot_stride;
+  bool final_out;
+  if (a.chunk_first) {
+    chunk = blockIdx.x % a.head_chunks;
+    const int cs = blockIdx.x / a.head_chunks;           // chunk slot (grid: every slot exists)
+    __shared__ int s_seq;
+    if (threadIdx.x == 0) s_seq = -1;
+    __syncthreads();
+    for (int s = threadIdx.x; s < a.num_seqs; s += kThreads)
+      if (a.chunk_first[s] <= cs && cs < a.chunk_first[s + 1]) s_seq = s;
+    __syncthreads();
+    b = s_seq;
+    if (b < 0) return;                                   // a slot past the last chunk: uniform
+    const int n_b = a.chunk_first[b + 1] - a.chunk_first[b];
+    const int k = cs - a.chunk_first[b];
+    const int raw_ctx = a.context_lens[b];
+    ctx = raw_ctx < 0 ? 0 : (raw_ctx > cap ? cap : raw_ctx);
+    n_blk_seq = (ctx + kBlockSize - 1) / kBlockSize;
+    const int pairs = (n_blk_seq + 1) / 2;                // chunk k: pairs [k u / n, (k+1) u / n)
+    blk_begin = 2 * int(int64_t(k) * pairs / n_b);
+    blk_end = 2 * int(int64_t(k + 1) * pairs / n_b);
+    blk_end = blk_end < n_blk_seq ? blk_end : n_blk_seq;
+    final_out = n_b == 1;                                // (also a sequence with nothing to attend)
+    slot_row = size_t(cs) * a.num_heads;
+    slot_stride = 1;
+  } else {
+    int unit;
+    if (!decode_unit(blockIdx.x, a.head_chunks, a.num_seqs * a.max_partitions, chunk, unit)) return;
+    b = unit % a.num_seqs;
+    const int part = unit / a.num_seqs;
+    const int raw_ctx = a.context_lens[b];
+    ctx = raw_ctx < 0 ? 0 : (raw_ctx > cap ? cap : raw_ctx);
+    n_blk_seq = (ctx + kBlockSize - 1) / kBlockSize;
+    blk_begin = part * a.blocks_per_partition;
+    blk_end = blk_begin + a.blocks_per_partition;
+    blk_end = blk_end < n_blk_seq ? blk_end : n_blk_seq;
+    final_out = a.write_final || (a.final_single && n_blk_seq <= a.blocks_per_partition);
+    slot_row = size_t(b) * a.num_heads * a.max_partitions + part;
+    slot_stride = a.max_partitions;
+    // (b, part) is uniform over the workgroup: every wave returns here or none.
+    if (blk_begin >= blk_end && !(a.write_final && part == 0)) {    // partition past the end
+      const int h = (chunk * WAVES + wave) * 16 + lane;
+      if (a.mark_empty && lane < 16 && h < a.num_heads)
+        a.part_lse[slot_row + size_t(h) * slot_stride] = -INFINITY;
+      return;
+    }
+  }
   const int h0 = (chunk * WAVES + wave) * 16;            // first head of this wave
 
-  // (b, part) is uniform over the workgroup: every wave returns here or none.
-  if (blk_begin >= blk_end && !(a.write_final && part == 0)) {    // partition past the end
-    if (a.mark_empty && lane < 16 && h0 + lane < a.num_heads)
-      a.part_lse[(size_t(b) * a.num_heads + h0 + lane) * a.max_partitions + part] = -INFINITY;
-    return;
-  }
-  const bool final_out = a.write_final || (a.final_single && n_blk_seq <= a.blocks_per_partition);
   const int limit = ctx < blk_end * kBlockSize ? ctx : blk_end * kBlockSize;   // tokens attended
   const int32_t* table = a.block_tables + size_t(b) * a.max_blocks_per_seq;
   const char* pool = static_cast<const char*>(a.pool);
@@ -313,7 +347,7 @@ __global__ __launch_bounds__(WAVES * kWave) void mla_decode_kernel(MlaArgs a) {
 #pragma unroll
       for (int t = 0; t < kTiles; ++t) orow[16 * t] = f32_to_bf16_rne(o[t][i] * inv);
     } else {
-      const size_t prow = row * a.max_partitions + part;
+      const size_t prow = slot_row + size_t(head) * slot_stride;
       float* op = a.part_o + prow * kDc + c;
 #pragma unroll
       for (int t = 0; t < kTiles; ++t) op[16 * t] = o[t][i] * inv;
@@ -335,7 +369,10 @@ hipError_t launch_mla_decode(const MlaArgs& a, hipStream_t stream) {
   const size_t units = size_t(a.num_seqs) * a.max_partitions;
   if (units == 0) return hipSuccess;
   if (units > 0x7fffffffu) return hipErrorInvalidConfiguration;
-  const size_t grid = decode_grid(units, a.head_chunks);
+  // Balanced split: one workgroup per (chunk slot, head chunk), max_partitions
+  // slots; fixed partitions: XCD-ordered (partition, sequence) units.
+  const size_t grid = a.chunk_first ? size_t(a.max_partitions) * a.head_chunks
+                                    : decode_grid(units, a.head_chunks);
   if (grid > 0x7fffffffu) return hipErrorInvalidConfiguration;
   const dim3 g{unsigned(grid)};
   switch (mla_heads_per_workgroup(a.num_heads) / 16) {

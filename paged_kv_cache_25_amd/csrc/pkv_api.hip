@@ -57,6 +57,30 @@ PartLayout part_layout(int64_t B, int64_t Hq, int64_t D, int64_t maxp) {
   return L;
 }
 
+// Balanced MLA split: chunk slots (one 8-wave workgroup per CU at a time, or
+// two smaller ones: their LDS halves fit one CU) and the workspace layout
+// o [R, H, D] | lse [R, H] | chunk starts [B + 1], each 256-byte aligned.
+int64_t mla_balanced_slots(int32_t num_seqs, int32_t num_heads) {
+  const int waves = pkv::mla_heads_per_workgroup(num_heads) / 16;
+  const int64_t budget = waves >= 8 ? 256 : 512;
+  return budget > num_seqs ? budget : num_seqs;
+}
+
+struct BalancedLayout {
+  PartLayout part;
+  int64_t slots;
+  size_t first_offset, total;
+};
+
+BalancedLayout balanced_layout(int32_t num_seqs, int32_t num_heads, int32_t d) {
+  BalancedLayout L;
+  L.slots = mla_balanced_slots(num_seqs, num_heads);
+  L.part = part_layout(L.slots, num_heads, d, 1);
+  L.first_offset = L.part.total;
+  L.total = L.first_offset + align_up((size_t(num_seqs) + 1) * sizeof(int32_t));
+  return L;
+}
+
 }  // namespace
 
 extern "C" {
@@ -218,7 +242,10 @@ pkv_status_t pkv_copy_blocks(void* k_pool, void* v_pool, float* k_scales, float*
 
 size_t pkv_mla_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t kv_lora_rank,
                                int32_t max_context_len, int32_t partition_size) {
-  if (num_seqs <= 0 || num_heads <= 0 || kv_lora_rank <= 0 || partition_size < 0) return 0;
+  if (num_seqs <= 0 || num_heads <= 0 || kv_lora_rank <= 0) return 0;
+  if (partition_size == PKV_PARTITION_BALANCED)
+    return balanced_layout(num_seqs, num_heads, kv_lora_rank).total;
+  if (partition_size < 0) return 0;
   const int64_t maxp = max_partitions(max_context_len, partition_size);
   if (maxp <= 1) return 0;
   return part_layout(num_seqs, num_heads, kv_lora_rank, maxp).total;
@@ -261,11 +288,12 @@ pkv_status_t pkv_mla_decode_attention(
     int32_t rope_dim, int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
     int32_t max_context_len, float softmax_scale, int32_t partition_size, void* workspace,
     size_t workspace_bytes, void* stream) {
+  const bool balanced = partition_size == PKV_PARTITION_BALANCED;
   if (num_seqs < 0 || num_heads <= 0 || kv_lora_rank <= 0 || rope_dim < 0 || block_size <= 0 ||
-      num_blocks <= 0 || max_blocks_per_seq <= 0 || max_context_len < 0 || partition_size < 0 ||
-      !(softmax_scale == softmax_scale))
+      num_blocks <= 0 || max_blocks_per_seq <= 0 || max_context_len < 0 ||
+      (partition_size < 0 && !balanced) || !(softmax_scale == softmax_scale))
     return PKV_ERR_INVALID_ARG;
-  if (partition_size % block_size != 0) return PKV_ERR_INVALID_ARG;
+  if (!balanced && partition_size % block_size != 0) return PKV_ERR_INVALID_ARG;
   if (kv_lora_rank != 512 || rope_dim != 64 || block_size != pkv::kBlockSizeBuilt ||
       num_heads % 16 != 0)
     return PKV_ERR_UNSUPPORTED;
@@ -274,6 +302,55 @@ pkv_status_t pkv_mla_decode_attention(
   if (!aligned16(out) || !aligned16(q) || !aligned16(latent_pool) || !aligned4(block_tables) ||
       !aligned4(context_lens) || !aligned16(workspace))
     return PKV_ERR_INVALID_ARG;
+  if (balanced) {
+    if (int64_t(max_blocks_per_seq) * block_size > 0x7fffffff) return PKV_ERR_INVALID_ARG;
+    const BalancedLayout L = balanced_layout(num_seqs, num_heads, kv_lora_rank);
+    if (!workspace || workspace_bytes < L.total) return PKV_ERR_WORKSPACE;
+    const int per_wg = pkv::mla_heads_per_workgroup(num_heads);
+    const int head_chunks = (num_heads + per_wg - 1) / per_wg;
+    if (L.slots * head_chunks > 0x7fffffff) return PKV_ERR_INVALID_ARG;
+    char* ws = static_cast<char*>(workspace);
+    int32_t* first = reinterpret_cast<int32_t*>(ws + L.first_offset);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    pkv::SplitArgs sp{};
+    sp.context_lens = context_lens;
+    sp.num_seqs = num_seqs;
+    sp.cap_tokens = max_blocks_per_seq * block_size;
+    sp.unit_tokens = 2 * block_size;                 // the kernel walks pairs of blocks
+    sp.budget = int(L.slots);
+    sp.chunk_first = first;
+    if (pkv::launch_balanced_split(sp, st) != hipSuccess) return PKV_ERR_HIP;
+    pkv::MlaArgs a{};
+    a.out = out;
+    a.part_o = reinterpret_cast<float*>(ws);
+    a.part_lse = reinterpret_cast<float*>(ws + L.part.lse_offset);
+    a.q = q;
+    a.pool = latent_pool;
+    a.block_tables = block_tables;
+    a.context_lens = context_lens;
+    a.num_seqs = num_seqs;
+    a.num_heads = num_heads;
+    a.head_chunks = head_chunks;
+    a.num_blocks = num_blocks;
+    a.max_blocks_per_seq = max_blocks_per_seq;
+    a.blocks_per_partition = max_blocks_per_seq;
+    a.max_partitions = int(L.slots);
+    a.scale_log2 = softmax_scale * pkv::kLog2eHost;
+    a.chunk_first = first;
+    if (pkv::launch_mla_decode(a, st) != hipSuccess) return PKV_ERR_HIP;
+    pkv::MergeArgs m{};
+    m.out = out;
+    m.part_o = a.part_o;
+    m.part_lse = a.part_lse;
+    m.num_seqs = num_seqs;
+    m.num_q_heads = num_heads;
+    m.max_partitions = int(L.slots);
+    m.skip_single = 1;                               // one-chunk sequences are already final
+    m.num_batch = num_seqs;
+    m.chunk_first = first;
+    return pkv::launch_merge(m, kv_lora_rank, DType::BF16, st) == hipSuccess ? PKV_OK
+                                                                              : PKV_ERR_HIP;
+  }
   const int64_t maxp = max_partitions(max_context_len, partition_size);
   const bool single = maxp <= 1;
   pkv::MlaArgs a{};
@@ -502,7 +579,7 @@ pkv_status_t attention_impl(
     return PKV_ERR_HIP;
   if (single) return PKV_OK;
 
-  pkv::MergeArgs m;
+  pkv::MergeArgs m{};
   m.out = out;
   m.part_o = a.part_o;
   m.part_lse = a.part_lse;
@@ -680,7 +757,7 @@ pkv_status_t pkv_paged_multi_query_attention(
     return PKV_ERR_HIP;
   if (single) return PKV_OK;
 
-  pkv::MergeArgs m;
+  pkv::MergeArgs m{};
   m.out = out;
   m.part_o = a.part_o;
   m.part_lse = a.part_lse;
@@ -744,7 +821,7 @@ pkv_status_t pkv_merge_partials(void* out, const float* partial_out, const float
   if (!aligned16(out) || !aligned16(partial_out) || !aligned4(partial_lse) ||
       !aligned4(num_partitions))
     return PKV_ERR_INVALID_ARG;
-  pkv::MergeArgs m;
+  pkv::MergeArgs m{};
   m.out = out;
   m.part_o = partial_out;
   m.part_lse = partial_lse;

@@ -69,6 +69,21 @@ struct MlaArgs {
   int blocks_per_partition, max_partitions;
   float scale_log2;
   int write_final, final_single, mark_empty;
+  // Balanced split (null otherwise): sequence b owns the chunk slots
+  // chunk_first[b] .. chunk_first[b+1]-1 and splits its pairs of blocks evenly
+  // over them; workgroup c takes slot c; partial rows are [slot, H].
+  const int32_t* chunk_first;
+};
+
+// The balanced split of a batch's work into at most max(budget, num_seqs)
+// chunks: each sequence's units (unit_tokens tokens each, the context
+// clamped to [0, cap_tokens]) go to n_b = max(1, ceil(units_b / t)) chunks,
+// t the smallest size that keeps the total within the budget; chunk_first
+// [num_seqs + 1] receives the exclusive prefix sums of n_b.
+struct SplitArgs {
+  const int32_t* context_lens;
+  int num_seqs, cap_tokens, unit_tokens, budget;
+  int32_t* chunk_first;
 };
 
 struct DecodeArgs {
@@ -154,6 +169,9 @@ struct MergeArgs {
   // entry sets its partition count.  Null: row r is sequence r.
   const int32_t* q_start;
   int num_batch;                   // sequences, when q_start is set
+  // Balanced split (MLA): partitions of sequence b are the chunk slots
+  // chunk_first[b] .. chunk_first[b+1]-1; rows [slot, num_q_heads].
+  const int32_t* chunk_first;
 };
 
 hipError_t launch_kv_append(const AppendArgs& a, hipStream_t stream);
@@ -161,6 +179,7 @@ hipError_t launch_kv_append_quant(const QuantAppendArgs& a, hipStream_t stream);
 hipError_t launch_copy_blocks(const CopyBlocksArgs& a, hipStream_t stream);
 int mla_heads_per_workgroup(int num_heads);
 hipError_t launch_mla_decode(const MlaArgs& a, hipStream_t stream);
+hipError_t launch_balanced_split(const SplitArgs& a, hipStream_t stream);
 hipError_t launch_paged_decode(const DecodeArgs& a, int head_dim, int tile_heads, DType q_dtype,
                                DType kv_dtype, hipStream_t stream);
 // Matrix-core variant for bf16 queries over a bf16 cache; heads in tiles of 16.

@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libpkv.so")
 
 PKV_F32, PKV_BF16, PKV_FP8_E4M3 = 0, 1, 2
 PKV_SCALE_FIXED, PKV_SCALE_RUNNING_AMAX = 0, 1
+PKV_PARTITION_BALANCED = -1        # MLA decode: balanced split of the batch's work
 STATUS = {0: "PKV_OK", 1: "PKV_ERR_INVALID_ARG", 2: "PKV_ERR_UNSUPPORTED",
           3: "PKV_ERR_WORKSPACE", 4: "PKV_ERR_HIP", 5: "PKV_ERR_OUT_OF_BLOCKS"}
 PKV_ERR_OUT_OF_BLOCKS = 5
@@ -415,7 +416,8 @@ def mla_decode_attention(out, q, latent_pool, block_tables, context_lens, max_co
                          softmax_scale, partition_size=512, kv_lora_rank=512, workspace=None,
                          stream=None):
     """out [B, H, 512] bf16: absorbed MLA decode of q [B, H, 576] over the paged
-    latent rows (pkv_mla_decode_attention)."""
+    latent rows (pkv_mla_decode_attention); partition_size PKV_PARTITION_BALANCED
+    splits the batch's work into balanced chunks."""
     _need_cuda(out, q, latent_pool, block_tables, context_lens, workspace)
     B, H, d = q.shape
     nb, bs, _ = latent_pool.shape

@@ -342,6 +342,34 @@ def test_mla_validation(lib):
         assert g(*a) in (INVALID, UNSUPPORTED), i
     a = list(args); a[9] = 256
     assert g(*a) == UNSUPPORTED
+    a = list(args); a[15] = -1                                     # balanced: attention only
+    assert g(*a) == INVALID
+
+
+def _align(n):
+    return (n + 255) // 256 * 256
+
+
+@pytest.mark.parametrize("B,H,slots", [(2, 128, 256), (2, 64, 512), (2, 16, 512), (300, 128, 300),
+                                       (700, 16, 700)])
+def test_mla_balanced_workspace(lib, B, H, slots):
+    """PKV_PARTITION_BALANCED: o [R, H, 512] f32 | lse [R, H] f32 | chunk starts
+    [B + 1] int32, each 256-byte aligned, R = max(256 for 8-wave workgroups
+    (more than 64 heads) or 512, B); max_context_len does not enter."""
+    want = _align(slots * H * 512 * 4) + _align(slots * H * 4) + _align((B + 1) * 4)
+    for maxctx in (0, 17, 100000):
+        assert lib.pkv_mla_workspace_bytes(B, H, 512, maxctx, -1) == want
+    assert lib.pkv_mla_workspace_bytes(B, H, 512, 64, -2) == 0
+
+
+def test_mla_balanced_validation(lib):
+    need = lib.pkv_mla_workspace_bytes(2, 128, 512, 64, -1)
+    assert _mla(lib, P=-1) == WORKSPACE                             # nothing launched
+    assert _mla(lib, P=-1, ws=FAKE, wsb=need - 1) == WORKSPACE
+    assert _mla(lib, P=-2, ws=FAKE, wsb=need) == INVALID
+    assert _mla(lib, P=-1, H=24, ws=FAKE, wsb=need) == UNSUPPORTED
+    assert _mla(lib, P=-1, ws=ctypes.c_void_p(0x10008), wsb=need) == INVALID
+    assert _mla(lib, P=-1, B=0, q=None) == OK
 
 
 def test_binding_refuses_cpu_tensors():

@@ -55,7 +55,7 @@ def _oracle(inp, pool=None, seqs=None):
 
 
 @pytest.mark.parametrize("heads", [16, 32, 48, 64, 80, 128, 256])
-@pytest.mark.parametrize("P", [512, 48, 32, 0])
+@pytest.mark.parametrize("P", [512, 48, 32, 0, ops.PKV_PARTITION_BALANCED])
 def test_heads_and_partitions(heads, P):
     inp = make_mla_inputs(num_seqs=5, num_heads=heads, ctx=("fixed", [1, 33, 200, 517, 80]),
                           seed=100 + heads, pool_used_fraction=0.8)
@@ -71,7 +71,7 @@ def test_edge_context_lengths():
     """Lengths at and around block and pair boundaries, and an empty sequence."""
     lens = [0, 1, 15, 16, 17, 31, 32, 33, 63, 64, 65, 100]
     inp = make_mla_inputs(num_seqs=len(lens), num_heads=128, ctx=("fixed", lens), seed=7)
-    for P in (0, 32, 64):
+    for P in (0, 32, 64, ops.PKV_PARTITION_BALANCED):
         log(f"[case] mla edges P={P}")
         gpu = DevMLA(inp).step(P)
         assert np.all(gpu[0] == 0)                       # ctx 0: zeros
@@ -86,8 +86,8 @@ def test_lite_workload():
 
 def test_deepseek_b64_sampled():
     """The DeepSeek-shaped batch-64 layer (128 heads, lengths uniform in
-    [512, 4096]) at full size in the benchmark's launch configuration; the
-    oracle checks 6 sampled sequences."""
+    [512, 4096]) at full size in the benchmark's launch configuration (the
+    balanced split); the oracle checks 6 sampled sequences."""
     inp = named_mla("deepseek_mla_b64")
     log("[case] deepseek_mla_b64 full size")
     dev = DevMLA(inp)
@@ -154,3 +154,41 @@ def test_partials_and_merge(P):
         n = -(-int(inp.context_lens[b]) // P)
         assert np.all(np.isfinite(lse[b, :, :n])) and np.all(np.isneginf(lse[b, :, n:]))
     assert torch.equal(merged.float().cpu().double(), whole)
+
+
+@pytest.mark.parametrize("case", ["long_and_short", "many_short", "all_empty", "one_long"])
+def test_balanced_split(case):
+    """The balanced split (PKV_PARTITION_BALANCED) on batches it treats
+    differently: one sequence far longer than the rest (many chunks for it,
+    one for the others), more sequences than chunk slots (one chunk each),
+    every context empty (zeros), and a single sequence of 6,000 tokens split
+    over up to 256 chunks of one pair of blocks or more."""
+    spec = {"long_and_short": dict(num_seqs=9, ctx=("fixed", [3000, 5, 17, 64, 1, 33, 100, 0, 48])),
+            "many_short": dict(num_seqs=600, ctx=("uniform", 0, 40)),
+            "all_empty": dict(num_seqs=4, ctx=("fixed", [0, 0, 0, 0])),
+            "one_long": dict(num_seqs=1, ctx=("fixed", [6000]))}[case]
+    heads = 16 if case == "many_short" else 128
+    seed = {"long_and_short": 51, "many_short": 52, "all_empty": 53, "one_long": 54}[case]
+    inp = make_mla_inputs(num_heads=heads, seed=seed, pool_used_fraction=0.9, **spec)
+    log(f"[case] mla balanced {case}")
+    dev = DevMLA(inp)
+    gpu = dev.step(ops.PKV_PARTITION_BALANCED)
+    pool = _appended_pool(inp)
+    assert np.array_equal(host_storage(dev.pool), pool)
+    ref = _oracle(inp, pool)
+    zero = inp.context_lens <= 0
+    assert np.all(gpu[zero] == 0)
+    check_tolerance("bf16", gpu, ref, f"mla balanced {case}", out_dtype="bf16")
+
+
+def test_deepseek_b64_fixed_partitions_sampled():
+    """The DeepSeek-shaped batch-64 layer at full size with fixed 1,024-token
+    partitions (its default is the balanced split)."""
+    inp = named_mla("deepseek_mla_b64")
+    log("[case] deepseek_mla_b64 P=1024")
+    gpu = DevMLA(inp).step(1024)
+    pool = _appended_pool(inp)
+    seqs = sorted(np.random.default_rng(2).choice(inp.num_seqs, 6, replace=False).tolist())
+    ref = _oracle(inp, pool, seqs=seqs)
+    for b in seqs:
+        check_tolerance("bf16", gpu[b], ref[b], f"deepseek b64 P=1024 seq {b}", out_dtype="bf16")

@@ -49,10 +49,10 @@ class MLAInputs:
 MLA_WORKLOADS = {
     # DeepSeek-V2/V3 attention shape (128 heads, 512 + 64 latent row, softmax
     # scale 1/sqrt(128 + 64)), the batch-64 decode layer with the same context
-    # lengths as the Llama-3-8B workload.  Partitions of 1,024 tokens: at most
-    # 4 x 64 = 256 workgroups, one round on the 256 CUs.
+    # lengths as the Llama-3-8B workload.  The balanced split (-1): at most 256
+    # chunks of nearly equal size, one round on the 256 CUs.
     "deepseek_mla_b64": dict(num_seqs=64, num_heads=128, ctx=("uniform", 512, 4096), seed=2,
-                             partition_size=1024),
+                             partition_size=-1),
     # DeepSeek-V2-Lite's 16 heads, a small batch the oracle finishes quickly.
     # Partitions of one pair of blocks: with one wave per workgroup the time
     # grows with the pairs each wave walks.
