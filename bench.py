@@ -15,8 +15,10 @@ Prints one JSON line.  ``value`` is the step's algorithmic bytes (K/V rows of
 every attended token, the appended rows, q, out, block-table entries and
 lengths) divided by the measured step time, in GB/s.  ``roofline`` reports the
 decode kernel alone, timed live with HIP events on the launch stream through
-``pkv_paged_decode_partials`` (the same kernel and grid without the merge),
-against the 8 TB/s HBM peak.
+``pkv_paged_decode_partials`` (the same kernel and grid without the merge), or,
+for the balanced split (partition size -1, the default of the batch-64, mix and
+fp8 workloads), ``pkv_paged_decode_partials_planned`` on a schedule made
+beforehand, against the 8 TB/s HBM peak.
 ``cpu_baseline`` times the float64 CPU oracle on a bounded sample of the same
 workload.
 """
@@ -166,6 +168,8 @@ def main():
     def ptr(t):
         return None if t is None else V(t.data_ptr())
 
+    balanced = P == ops.PKV_PARTITION_BALANCED
+    slots = lib.pkv_decode_plan_slots(B, Hq, Hkv, D, qcode, kvcode) if balanced else 0
     calls = []
     for c in copies:
         c["out"] = torch.empty(B, Hq, D, dtype=c["q"].dtype, device=dev)
@@ -176,23 +180,36 @@ def main():
                ptr(c["k_scales"]), ptr(c["v_scales"]), ptr(c["tables"]), ptr(c["lens"]), B, Hq,
                Hkv, D, 16, NB, MB, mcl, ctypes.c_float(inp.softmax_scale), P, ptr(c["ws"]),
                ctypes.c_size_t(c["ws"].numel()), qcode, kvcode, sp)
-        maxp = max(1, -(-mcl // P)) if P else 1
-        c["parts"] = torch.empty(max(ops.workspace_bytes(B, Hq, D, mcl, P),
-                                     B * Hq * maxp * (D + 1) * 4 + 256), dtype=torch.uint8,
-                                 device=dev)
-        lse_off = ((B * Hq * maxp * D * 4 + 255) // 256) * 256
-        # the decode kernel alone, same grid and work, partials into its own buffer
-        prt = (V(c["parts"].data_ptr()), V(c["parts"].data_ptr() + lse_off), maxp, ptr(c["q"]),
-               ptr(c["k_pool"]), ptr(c["v_pool"]), ptr(c["k_scales"]), ptr(c["v_scales"]),
-               ptr(c["tables"]), ptr(c["lens"]), B, Hq, Hkv, D, 16, NB, MB,
-               ctypes.c_float(inp.softmax_scale), P, qcode, kvcode, sp)
+        if balanced:
+            # the decode kernel alone on a schedule made beforehand (the plan
+            # kernel and the merge are in the attention call and the step)
+            c["plan"] = ops.decode_plan(c["lens"], slots, MB)
+            c["parts"] = torch.empty(slots * Hq * (D + 1) * 4 + 512, dtype=torch.uint8, device=dev)
+            lse_off = ((slots * Hq * D * 4 + 255) // 256) * 256
+            prt = (V(c["parts"].data_ptr()), V(c["parts"].data_ptr() + lse_off), ptr(c["plan"]),
+                   slots, ptr(c["q"]), ptr(c["k_pool"]), ptr(c["v_pool"]), ptr(c["k_scales"]),
+                   ptr(c["v_scales"]), ptr(c["tables"]), ptr(c["lens"]), B, Hq, Hkv, D, 16, NB, MB,
+                   ctypes.c_float(inp.softmax_scale), qcode, kvcode, sp)
+            maxp = slots
+        else:
+            maxp = max(1, -(-mcl // P)) if P else 1
+            c["parts"] = torch.empty(max(ops.workspace_bytes(B, Hq, D, mcl, P),
+                                         B * Hq * maxp * (D + 1) * 4 + 256), dtype=torch.uint8,
+                                     device=dev)
+            lse_off = ((B * Hq * maxp * D * 4 + 255) // 256) * 256
+            # the decode kernel alone, same grid and work, partials into its own buffer
+            prt = (V(c["parts"].data_ptr()), V(c["parts"].data_ptr() + lse_off), maxp, ptr(c["q"]),
+                   ptr(c["k_pool"]), ptr(c["v_pool"]), ptr(c["k_scales"]), ptr(c["v_scales"]),
+                   ptr(c["tables"]), ptr(c["lens"]), B, Hq, Hkv, D, 16, NB, MB,
+                   ctypes.c_float(inp.softmax_scale), P, qcode, kvcode, sp)
         stp = (ptr(c["out"]), ptr(c["q"]), ptr(c["k_pool"]), ptr(c["v_pool"]), ptr(c["k_new"]),
                ptr(c["v_new"]), ptr(c["k_scales"]), ptr(c["v_scales"]), ptr(c["tables"]),
                ptr(c["lens"]), B, Hq, Hkv, D, 16, NB, MB, mcl, ctypes.c_float(inp.softmax_scale),
                P, ptr(c["ws"]), ctypes.c_size_t(c["ws"].numel()), qcode, kvcode, sp)
         calls.append((app, att, prt, maxp > 1, stp))
 
-    f_app, f_att, f_prt = lib.pkv_kv_append, lib.pkv_paged_decode_attention, lib.pkv_paged_decode_partials
+    f_app, f_att = lib.pkv_kv_append, lib.pkv_paged_decode_attention
+    f_prt = lib.pkv_paged_decode_partials_planned if balanced else lib.pkv_paged_decode_partials
     f_stp = lib.pkv_paged_decode_step
 
     def step(i):
@@ -261,7 +278,7 @@ def main():
     value = step_bytes / (step_ms * 1e-3) / 1e9
     kernel_gbps = tr["kv_bytes"] / (decode_ms * 1e-3) / 1e9
 
-    traffic_bytes = measured_traffic(inp.name) if (P == 512 and args.seed is None) else None
+    traffic_bytes = measured_traffic(inp.name, P) if args.seed is None else None
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(inp, args.cpu_budget_s)
@@ -287,7 +304,8 @@ def main():
         "decode_steps_per_s": round(1e3 / step_ms, 1),
         "tokens_per_s": round(B * 1e3 / step_ms, 1),
         "kernel_us": {"append": round(append_ms * 1e3, 2), "decode": round(decode_ms * 1e3, 2),
-                      "merge": round(merge_ms * 1e3, 2), "attention_call": round(att_ms * 1e3, 2),
+                      ("plan_and_merge" if balanced else "merge"): round(merge_ms * 1e3, 2),
+                      "attention_call": round(att_ms * 1e3, 2),
                       "step_as_two_calls": round(two_call_ms * 1e3, 2)},
         "roofline": {"kernel": ("paged_decode_mfma_kernel" if (inp.q_dtype == "bf16" and
                                 inp.kv_dtype == "bf16" and Hq // Hkv >= 2)
@@ -361,6 +379,7 @@ def main_multi(args):
     inp = named_config(args.config, seed=args.seed, new_tokens=("const", T),
                        name=f"{CONFIG_NAMES[args.config]}_t{T}")
     P = inp.partition_size if args.partition_size is None else args.partition_size
+    P = 512 if P < 0 else P              # several new tokens: fixed partitions only
     print(f"[bench] workload {inp.name}: generated in {time.time() - t0:.1f}s", file=sys.stderr,
           flush=True)
     base = dict(q=to_device(inp.q, inp.q_dtype, dev),
@@ -820,9 +839,10 @@ KERNEL_SOURCES = ("paged_kv_cache_25_amd/csrc/paged_decode_mfma.hip",
                   "paged_kv_cache_25_amd/csrc/pkv_launch.h")
 
 
-def measured_traffic(workload):
+def measured_traffic(workload, partition_size):
     """HBM bytes per decode launch from the committed rocprofv3 counter summary,
-    or None when the workload differs or the kernel sources changed since."""
+    or None when the workload or partition differs or the kernel sources
+    changed since."""
     import hashlib
     if workload != "llama3_8b_b64" or not os.path.exists(TRAFFIC_FILE):
         return None
@@ -831,6 +851,8 @@ def measured_traffic(workload):
         if ":" in line and line.split(":", 1)[0].strip().replace("_", "").isalnum():
             k, v = line.split(":", 1)
             fields[k.strip()] = v.strip()
+    if fields.get("partition_size") != str(partition_size):
+        return None
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
         with open(os.path.join(ROOT, rel), "rb") as f:

@@ -115,12 +115,40 @@ pkv_status_t pkv_kv_append(void* k_pool, void* v_pool, const void* k_new, const 
                            int32_t max_blocks_per_seq, pkv_dtype_t kv_dtype, void* stream);
 
 /*
+ * partition_size asking for a balanced split (pkv_paged_decode_attention,
+ * pkv_paged_decode_step, pkv_mla_decode_attention and their workspace
+ * sizes).  Instead of fixed partitions, each sequence's blocks (pairs of
+ * blocks for MLA) are divided into n_b >= 1 chunks of nearly equal size,
+ * n_b = max(1, ceil(u_b / t)) for its u_b units, with t the smallest chunk
+ * size for which the batch needs at most R chunks.  S, the chunk slots of
+ * one wave of workgroups MI355X runs at once, sets R: one-token decode,
+ * S = 3072 / (num_kv_heads x column tiles) and R = S when 2 num_seqs <= S,
+ * else max(2 S, 2 num_seqs) (pkv_decode_plan_slots); MLA, S = 256 for more
+ * than 64 heads, 512 otherwise, and R = max(S, num_seqs).  The schedule is computed on the device from context_lens (no
+ * host copy, so a call stays capturable in a graph), the chunks are run and
+ * merged; a sequence with one chunk is written directly.  The result equals
+ * a fixed-partition split's up to float rounding: only the grouping of the
+ * partial sums changes (the log-sum-exp merge combines any split of the
+ * tokens).  Intended for batches of uneven or long contexts, where a fixed
+ * partition size leaves the kernel waiting for its longest partitions.
+ * max_context_len is not used to size anything in this mode.
+ *   serving lesson, "Where it shows up" (split-KV decoding spreads one
+ *   sequence over the whole GPU).
+ */
+#define PKV_PARTITION_BALANCED (-1)
+
+/*
  * pkv_decode_workspace_bytes - device workspace that
  * pkv_paged_decode_attention needs for its split-KV partial results:
  * float32 o [num_seqs, num_q_heads, maxP, head_dim] then, at the next
  * 256-byte boundary, float32 lse [num_seqs, num_q_heads, maxP], where
  * maxP = ceil(max_context_len / partition_size) (1 when partition_size == 0).
  * Returns 0 when maxP <= 1 (no workspace is needed) or on invalid sizes.
+ * With PKV_PARTITION_BALANCED: float32 o [R, num_q_heads, head_dim], float32
+ * lse [R, num_q_heads] and the plan of pkv_decode_plan for R slots, each
+ * 256-byte aligned, for R = max(2 x 3072 / ceil(num_q_heads / 16),
+ * 2 num_seqs), an upper bound of the slots a call uses (the call itself needs
+ * them for R = pkv_decode_plan_slots(...) only).
  */
 size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
                                   int32_t max_context_len, int32_t partition_size);
@@ -148,6 +176,7 @@ size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t
  * once for all the query heads of its group and writes a normalised partial
  * output plus its natural-log log-sum-exp to `workspace`; a second kernel
  * merges them (skipped when maxP == 1, where the first writes `out`).
+ * partition_size == PKV_PARTITION_BALANCED uses balanced chunks instead.
  *
  * out [device, written]; q, pools, scales, tables, lens [device, read];
  * workspace [device, scratch] of at least pkv_decode_workspace_bytes(...)
@@ -178,8 +207,9 @@ pkv_status_t pkv_paged_decode_attention(
  *
  * Arguments as for pkv_kv_append and pkv_paged_decode_attention; k_pool and
  * v_pool are [device, read and written].  The append of a sequence happens
- * only if 1 <= ctx <= max_blocks_per_seq * block_size and ctx <=
- * max_context_len (the launched partitions cover its last block).
+ * only if 1 <= ctx <= max_blocks_per_seq * block_size and (fixed
+ * partitions) ctx <= max_context_len (the launched partitions cover its last
+ * block; balanced chunks always cover it).
  */
 pkv_status_t pkv_paged_decode_step(
     void* out, const void* q, void* k_pool, void* v_pool, const void* k_new, const void* v_new,
@@ -241,6 +271,61 @@ pkv_status_t pkv_merge_partials(void* out, const float* partial_out, const float
                                 const int32_t* num_partitions, int32_t num_seqs,
                                 int32_t num_q_heads, int32_t head_dim, int32_t max_partitions,
                                 pkv_dtype_t out_dtype, void* stream);
+
+/*
+ * The balanced split in separate calls (the pieces of
+ * pkv_paged_decode_attention with PKV_PARTITION_BALANCED, for callers that
+ * reuse one schedule, time the pieces, or merge chunk results themselves).
+ *
+ * pkv_decode_plan_slots - R, the chunk slots of a balanced split for this
+ * shape and dtype pair (the value the attention call uses, see
+ * PKV_PARTITION_BALANCED); 0 for invalid arguments.
+ *
+ * pkv_decode_plan_bytes - bytes of a plan for num_seqs sequences and
+ * num_slots slots: int32 chunk_first [num_seqs + 1], then, 256-byte aligned,
+ * int32x4 slot_info [num_slots] = {sequence, first block, end block, chunks
+ * of that sequence}, or {-1, 0, 0, 0} past the last chunk.  0 when num_slots
+ * < max(1, num_seqs) or on invalid sizes.
+ *
+ * pkv_decode_plan - writes the plan [device, written, 16-byte aligned, at
+ * least pkv_decode_plan_bytes] from context_lens [device, read]: sequence b
+ * (its ctx clamped to [0, max_blocks_per_seq * block_size]) owns slots
+ * chunk_first[b] .. chunk_first[b+1]-1, chunk k of its n_b covering blocks
+ * [k u_b / n_b, (k+1) u_b / n_b) of its u_b = ceil(ctx / block_size); see
+ * PKV_PARTITION_BALANCED for n_b (here R = max(num_slots, num_seqs)).
+ *
+ * pkv_paged_decode_partials_planned - the chunks of a plan made by
+ * pkv_decode_plan with the same context_lens, num_seqs, num_slots,
+ * block_size and max_blocks_per_seq: for slot s of sequence b it writes the
+ * normalised partial output over the chunk's tokens to partial_out[s][i][:]
+ * and its natural-log log-sum-exp to partial_lse[s][i] (-inf for an empty
+ * sequence's one chunk); slots past the last chunk are not written.
+ * partial_out float32 [num_slots, num_q_heads, head_dim], partial_lse float32
+ * [num_slots, num_q_heads] [device, written]; the rest as for
+ * pkv_paged_decode_partials.
+ *
+ * pkv_merge_partials_planned - out[b][i][:] = the log-sum-exp merge (as
+ * pkv_merge_partials) of rows chunk_first[b] .. chunk_first[b+1]-1 of
+ * partial_out / partial_lse laid out as above; out in out_dtype (F32, BF16).
+ *   serving lesson, "Where it shows up" (split-KV partial results merged).
+ */
+int32_t pkv_decode_plan_slots(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                              int32_t head_dim, pkv_dtype_t q_dtype, pkv_dtype_t kv_dtype);
+size_t pkv_decode_plan_bytes(int32_t num_seqs, int32_t num_slots);
+pkv_status_t pkv_decode_plan(void* plan, size_t plan_bytes, const int32_t* context_lens,
+                             int32_t num_seqs, int32_t num_slots, int32_t block_size,
+                             int32_t max_blocks_per_seq, void* stream);
+pkv_status_t pkv_paged_decode_partials_planned(
+    float* partial_out, float* partial_lse, const void* plan, int32_t num_slots, const void* q,
+    const void* k_pool, const void* v_pool, const float* k_scales, const float* v_scales,
+    const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+    int32_t num_blocks, int32_t max_blocks_per_seq, float softmax_scale, pkv_dtype_t q_dtype,
+    pkv_dtype_t kv_dtype, void* stream);
+pkv_status_t pkv_merge_partials_planned(void* out, const float* partial_out,
+                                        const float* partial_lse, const void* plan,
+                                        int32_t num_slots, int32_t num_seqs, int32_t num_q_heads,
+                                        int32_t head_dim, pkv_dtype_t out_dtype, void* stream);
 
 /*
  * Several new tokens per sequence
@@ -513,18 +598,6 @@ pkv_status_t pkv_mla_append(void* latent_pool, const void* latent_new,
                             const int32_t* block_tables, const int32_t* context_lens,
                             int32_t num_seqs, int32_t row_dim, int32_t block_size,
                             int32_t num_blocks, int32_t max_blocks_per_seq, void* stream);
-
-/* partition_size of pkv_mla_workspace_bytes / pkv_mla_decode_attention
- * asking for a balanced split: the library divides each sequence's pairs of
- * blocks into chunks of nearly equal size, chosen from the context lengths on
- * the device so that the whole batch takes at most max(S, num_seqs) chunks
- * (S = 256 chunk slots for more than 64 heads, 512 otherwise: the workgroups
- * MI355X runs at once), each within one sequence, and merges them.  The
- * result equals a fixed-partition split's up to float rounding; only the
- * grouping of the partial sums differs.  Intended for batches of uneven or
- * long contexts, where a fixed partition size leaves the kernel waiting for
- * the longest partitions. */
-#define PKV_PARTITION_BALANCED (-1)
 
 /* Workspace of pkv_mla_decode_attention: float32 o [num_seqs, num_heads,
  * maxP, kv_lora_rank] then, 256-byte aligned, float32 lse [num_seqs,

@@ -8,7 +8,8 @@
 // (the budget is the number of workgroups that run at once); the kernel that
 // follows splits u_b evenly over the n_b chunks.  The output is the exclusive
 // prefix sum chunk_first[0..num_seqs] of n_b: sequence b owns chunk slots
-// chunk_first[b] .. chunk_first[b+1]-1.  This is scheduling only: the split
+// chunk_first[b] .. chunk_first[b+1]-1 (and, when asked, slot_info gives each
+// slot its sequence and units directly).  This is scheduling only: the split
 // does not change what is computed, only how partial results are grouped
 // (the log-sum-exp merge combines any split of the tokens).
 //
@@ -90,10 +91,18 @@ __global__ __launch_bounds__(kWave) void balanced_split_kernel(SplitArgs a) {
       const int y = __shfl_up(x, o);
       if (l >= o) x += y;
     }
-    if (b < a.num_seqs) a.chunk_first[b] = carry + x - n;
+    if (b < a.num_seqs) {
+      const int first = carry + x - n;
+      a.chunk_first[b] = first;
+      if (a.slot_info)                                   // chunk k: units [k u / n, (k+1) u / n)
+        for (int k = 0; k < n; ++k)
+          a.slot_info[first + k] = make_int4(b, int(int64_t(k) * u / n), int(int64_t(k + 1) * u / n), n);
+    }
     carry += __shfl(x, kWave - 1);
   }
   if (l == 0) a.chunk_first[a.num_seqs] = carry;
+  if (a.slot_info)
+    for (int slot = carry + l; slot < a.num_slots; slot += kWave) a.slot_info[slot] = make_int4(-1, 0, 0, 0);
 }
 
 }  // namespace

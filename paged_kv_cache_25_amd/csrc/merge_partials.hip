@@ -37,8 +37,10 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(MergeArgs a) {
   const int g = t / kRowThreads, c = t % kRowThreads;
 
   int np = a.max_partitions;
-  if (a.chunk_first) {
-    np = a.chunk_first[b + 1] - a.chunk_first[b];
+  int first = 0;
+  if (a.chunk_first) {                            // kept inside the max_partitions slots
+    first = min(max(a.chunk_first[b], 0), a.max_partitions);
+    np = min(max(a.chunk_first[b + 1], first), a.max_partitions) - first;
   } else if (a.num_partitions) {
     np = a.num_partitions[b];
   } else if (a.context_lens) {
@@ -60,7 +62,7 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(MergeArgs a) {
   const size_t row = size_t(b) * a.num_q_heads + qh;
   // Partition p of this row: rows [b, H, max_partitions] (stride 1), or, for
   // a balanced split, chunk slot chunk_first[b] + p of rows [slot, H] (stride H).
-  const size_t base = a.chunk_first ? size_t(a.chunk_first[b]) * a.num_q_heads + qh
+  const size_t base = a.chunk_first ? size_t(first) * a.num_q_heads + qh
                                     : row * a.max_partitions;
   const size_t stride = a.chunk_first ? size_t(a.num_q_heads) : 1;
   const float* lse_base = a.part_lse + base;

@@ -247,14 +247,11 @@ __global__ __launch_bounds__(kWave) void paged_decode_kernel(DecodeArgs a) {
   constexpr int W = TL::kWords;
   constexpr int KD = TL::kDims;
 
-  // blockIdx.x -> (column chunk, unit = (kv head, sequence, partition)).
-  int chunk, idx;
-  if (!decode_unit(blockIdx.x, a.head_chunks, a.num_seqs * a.num_kv_heads * a.max_partitions,
-                   chunk, idx))
-    return;
-  const int h = idx % a.num_kv_heads;      idx /= a.num_kv_heads;
-  const int b = idx % a.num_seqs;
-  const int part = idx / a.num_seqs;
+  // blockIdx.x -> (column chunk, unit = (kv head, sequence, partition)), or
+  // (column chunk, kv head, chunk slot) for a balanced split.
+  DecodeItem it;
+  if (!decode_item(a, it)) return;
+  const int chunk = it.chunk, h = it.h, b = it.b, part = it.part;
 
   const int lane = threadIdx.x;
   const int tg = lane / kLanesPerToken;
@@ -265,9 +262,8 @@ __global__ __launch_bounds__(kWave) void paged_decode_kernel(DecodeArgs a) {
   const int cap = a.max_blocks_per_seq * kBlockSize;
   ctx = ctx > cap ? cap : ctx;
   const int n_blk_seq = (ctx + kBlockSize - 1) / kBlockSize;
-  const int blk_begin = part * a.blocks_per_partition;
-  int blk_end = blk_begin + a.blocks_per_partition;
-  blk_end = blk_end < n_blk_seq ? blk_end : n_blk_seq;
+  const int blk_begin = it.blk_begin;
+  int blk_end = it.blk_end < n_blk_seq ? it.blk_end : n_blk_seq;
   // Fused append: the block of position ctx-1 takes its new row from k_new/v_new
   // (a sequence outside 1 <= ctx <= capacity appends nothing, as pkv_kv_append).
   const int append_blk = (a.k_new && raw_ctx >= 1 && raw_ctx <= cap) ? (raw_ctx - 1) / kBlockSize : -1;
@@ -289,9 +285,15 @@ __global__ __launch_bounds__(kWave) void paged_decode_kernel(DecodeArgs a) {
   const int n0 = chunk * G;
   if (!cols.valid(n0)) return;                          // no column of this tile exists
 
-  if (blk_begin >= blk_end && !(a.write_final && part == 0)) {   // partition past the end
-    if (a.mark_empty && lane < G && cols.valid(n0 + lane))
-      a.part_lse[cols.row(n0 + lane) * a.max_partitions + part] = -INFINITY;
+  // A sequence whose blocks fit one partition (or chunk) is finished here:
+  // write the final output instead of a partial (the merge skips it).
+  const bool final_out =
+      a.write_final ||
+      (a.final_single && (a.slot_info ? it.n_parts == 1 : n_blk_seq <= a.blocks_per_partition));
+  if (blk_begin >= blk_end && !(a.write_final && part == 0) &&
+      !(a.slot_info && final_out)) {                  // partition past the end, or an empty chunk
+    if ((a.mark_empty || a.slot_info) && lane < G && cols.valid(n0 + lane))
+      a.part_lse[partial_row(a, it, cols.row(n0 + lane))] = -INFINITY;
     return;
   }
   // Tokens each column attends to (all ctx for a single new token); the
@@ -300,9 +302,6 @@ __global__ __launch_bounds__(kWave) void paged_decode_kernel(DecodeArgs a) {
 #pragma unroll
   for (int i = 0; i < G; ++i) vis_all[i] = cols.valid(n0 + i) ? cols.visible(n0 + i, ctx) : ctx;
   const int min_vis = vis_all[0];
-  // A sequence whose blocks fit one partition is finished here: write the
-  // final output instead of a partial (the merge skips it).
-  const bool final_out = a.write_final || (a.final_single && n_blk_seq <= a.blocks_per_partition);
 
   Dec dec;
   dec.load_q(reinterpret_cast<const char*>(a.q), cols, n0, s);
@@ -414,7 +413,7 @@ __global__ __launch_bounds__(kWave) void paged_decode_kernel(DecodeArgs a) {
         else reinterpret_cast<uint16_t*>(orow)[TL::dim(s, k)] = f32_to_bf16_rne(v);
       }
     } else {
-      const size_t prow = qrow * a.max_partitions + part;
+      const size_t prow = partial_row(a, it, qrow);
       float* o = a.part_o + prow * D;
 #pragma unroll
       for (int k = 0; k < KD; ++k) o[TL::dim(s, k)] = dec.acc[i][k] * inv;
@@ -426,7 +425,7 @@ __global__ __launch_bounds__(kWave) void paged_decode_kernel(DecodeArgs a) {
 
 template <int D, int G, typename QT, typename KV>
 hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
-  const size_t units = size_t(a.num_seqs) * a.num_kv_heads * a.max_partitions;
+  const size_t units = (a.slot_info ? size_t(1) : size_t(a.num_seqs)) * a.num_kv_heads * a.max_partitions;
   if (units == 0 || a.head_chunks == 0) return hipSuccess;
   if (units > 0x7fffffffu) return hipErrorInvalidConfiguration;
   const size_t grid = decode_grid(units, a.head_chunks);

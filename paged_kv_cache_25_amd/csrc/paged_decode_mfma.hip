@@ -242,33 +242,29 @@ __global__ __launch_bounds__(kWave)
 __attribute__((amdgpu_waves_per_eu(NT == 1 ? PKV_MFMA_WAVES_PER_EU : 2)))
 void paged_decode_mfma_kernel(DecodeArgs a) {
   using T = MfmaTile<D>;
-  // blockIdx.x -> (column chunk, unit = (kv head, sequence, partition)).
-  int chunk, idx;
-  if (!decode_unit(blockIdx.x, a.head_chunks, a.num_seqs * a.num_kv_heads * a.max_partitions,
-                   chunk, idx))
-    return;
-  const int h = idx % a.num_kv_heads;      idx /= a.num_kv_heads;
-  const int b = idx % a.num_seqs;
-  const int part = idx / a.num_seqs;
+  // blockIdx.x -> (column chunk, unit = (kv head, sequence, partition)), or
+  // (column chunk, kv head, chunk slot) for a balanced split.
+  DecodeItem it;
+  if (!decode_item(a, it)) return;
+  const int chunk = it.chunk, h = it.h, b = it.b, part = it.part;
 
   const int lane = threadIdx.x;
   const int r = lane >> 4, c = lane & 15;
 
   const int32_t* table = a.block_tables + size_t(b) * a.max_blocks_per_seq;
-  const int blk_begin = part * a.blocks_per_partition;
+  const int blk_begin = it.blk_begin;
   // The first 64 table entries of the partition are fetched together with the
   // context length (both in bounds of the table row), so the first K/V loads
   // wait for one memory round trip, not two.
   const int first_n = a.max_blocks_per_seq - blk_begin;
-  int id0 = (lane < first_n && lane < a.blocks_per_partition) ? table[blk_begin + lane] : -1;
+  int id0 = (lane < first_n && lane < it.blk_end - blk_begin) ? table[blk_begin + lane] : -1;
 
   const int raw_ctx = a.context_lens[b];
   int ctx = raw_ctx < 0 ? 0 : raw_ctx;
   const int cap = a.max_blocks_per_seq * kBlockSize;
   ctx = ctx > cap ? cap : ctx;
   const int n_blk_seq = (ctx + kBlockSize - 1) / kBlockSize;
-  int blk_end = blk_begin + a.blocks_per_partition;
-  blk_end = blk_end < n_blk_seq ? blk_end : n_blk_seq;
+  int blk_end = it.blk_end < n_blk_seq ? it.blk_end : n_blk_seq;
   // Fused append: the block of position ctx-1 takes its new row from k_new/v_new
   // (a sequence outside 1 <= ctx <= capacity appends nothing, as pkv_kv_append).
   const int append_blk = (a.k_new && raw_ctx >= 1 && raw_ctx <= cap) ? (raw_ctx - 1) / kBlockSize : -1;
@@ -293,11 +289,17 @@ void paged_decode_mfma_kernel(DecodeArgs a) {
   const int n0 = chunk * kHeadTile * NT;
   if (!cols.valid(n0)) return;                        // no column of this workgroup exists
 
-  if (blk_begin >= blk_end && !(a.write_final && part == 0)) {   // partition past the end
+  // A sequence whose blocks fit one partition (or chunk) is finished here:
+  // write the final output instead of a partial (the merge skips it).
+  const bool final_out =
+      a.write_final ||
+      (a.final_single && (a.slot_info ? it.n_parts == 1 : n_blk_seq <= a.blocks_per_partition));
+  if (blk_begin >= blk_end && !(a.write_final && part == 0) &&
+      !(a.slot_info && final_out)) {                  // partition past the end, or an empty chunk
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
-      if (a.mark_empty && lane < kHeadTile && cols.valid(n0 + 16 * nt + c))
-        a.part_lse[row_of(n0 + 16 * nt + c) * a.max_partitions + part] = -INFINITY;
+      if ((a.mark_empty || a.slot_info) && lane < kHeadTile && cols.valid(n0 + 16 * nt + c))
+        a.part_lse[partial_row(a, it, row_of(n0 + 16 * nt + c))] = -INFINITY;
     return;
   }
   int my_vis[NT];                                     // tokens my column of tile nt attends to
@@ -307,9 +309,6 @@ void paged_decode_mfma_kernel(DecodeArgs a) {
     my_vis[nt] = kMulti && cols.valid(n) ? cols.visible(n, ctx) : ctx;
   }
   const int min_vis = kMulti ? cols.visible(n0, ctx) : ctx;     // fewest: the first column
-  // A sequence whose blocks fit one partition is finished here: write the
-  // final output instead of a partial (the merge skips it).
-  const bool final_out = a.write_final || (a.final_single && n_blk_seq <= a.blocks_per_partition);
 
   MfmaDecode<D> dec[NT];
 #pragma unroll
@@ -426,7 +425,7 @@ void paged_decode_mfma_kernel(DecodeArgs a) {
         else
           *reinterpret_cast<uint2*>(orow) = make_uint2(packed[0], packed[1]);
       } else {
-        const size_t prow = qrow * a.max_partitions + part;
+        const size_t prow = partial_row(a, it, qrow);
         float* op = a.part_o + prow * D + kDimsPerLane * c;
 #pragma unroll
         for (int e = 0; e < kDimsPerLane; e += 4)
@@ -441,7 +440,7 @@ void paged_decode_mfma_kernel(DecodeArgs a) {
 
 template <int D>
 hipError_t launch_d(const DecodeArgs& a, hipStream_t stream) {
-  const size_t units = size_t(a.num_seqs) * a.num_kv_heads * a.max_partitions;
+  const size_t units = (a.slot_info ? size_t(1) : size_t(a.num_seqs)) * a.num_kv_heads * a.max_partitions;
   if (units == 0 || a.head_chunks == 0) return hipSuccess;
   if (units > 0x7fffffffu) return hipErrorInvalidConfiguration;
   const size_t grid = decode_grid(units, a.head_chunks);

@@ -81,6 +81,55 @@ BalancedLayout balanced_layout(int32_t num_seqs, int32_t num_heads, int32_t d) {
   return L;
 }
 
+// Balanced split of the one-token decode: the grid runs slots x KV heads x
+// column chunks one-wave workgroups, and S, the slots of one wave of them, is
+// what the GPU holds at once: 256 CUs x 4 SIMDs x 3 waves of the decode
+// kernels.  With few sequences (2B <= S) one wave of slots is enough: each
+// chunk is about total / S blocks and every workgroup runs at once.  With
+// more, short sequences take slots while holding little work, and sequences
+// of equal length cannot split into fractions of a chunk, so two waves' worth
+// (and at least two slots per sequence) balances better.
+constexpr int64_t kDecodeResidentWaves = 3072;
+
+int64_t decode_balanced_slots(int32_t num_seqs, int64_t units_per_slot) {
+  const int64_t per = units_per_slot > 0 ? units_per_slot : 1;
+  const int64_t budget = kDecodeResidentWaves / per > 0 ? kDecodeResidentWaves / per : 1;
+  const int64_t two_b = 2 * int64_t(num_seqs);
+  if (two_b <= budget) return budget;
+  return 2 * budget > two_b ? 2 * budget : two_b;
+}
+
+// The plan: int32 chunk starts [num_seqs + 1], then, 256-byte aligned, one
+// int4 {sequence, first block, end block, chunks of the sequence} per slot.
+struct PlanLayout {
+  size_t info_offset, total;
+};
+
+PlanLayout plan_layout(int64_t num_seqs, int64_t slots) {
+  PlanLayout L;
+  L.info_offset = align_up(size_t(num_seqs + 1) * sizeof(int32_t));
+  L.total = L.info_offset + align_up(size_t(slots) * 4 * sizeof(int32_t));
+  return L;
+}
+
+// Workspace of a balanced decode call: partials o [R, Hq, D] | lse [R, Hq] |
+// the plan.
+struct DecodeBalancedLayout {
+  PartLayout part;
+  PlanLayout plan;
+  size_t plan_offset, total;
+};
+
+DecodeBalancedLayout decode_balanced_layout(int64_t num_seqs, int64_t Hq, int64_t D,
+                                            int64_t slots) {
+  DecodeBalancedLayout L;
+  L.part = part_layout(slots, Hq, D, 1);
+  L.plan = plan_layout(num_seqs, slots);
+  L.plan_offset = L.part.total;
+  L.total = L.plan_offset + L.plan.total;
+  return L;
+}
+
 }  // namespace
 
 extern "C" {
@@ -444,7 +493,16 @@ pkv_status_t pkv_mla_decode_partials(
 
 size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
                                   int32_t max_context_len, int32_t partition_size) {
-  if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 || partition_size < 0) return 0;
+  if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0) return 0;
+  if (partition_size == PKV_PARTITION_BALANCED) {
+    // KV heads x column chunks >= ceil(Hq / 16) (no workgroup serves more than
+    // 16 query heads), so S <= S_max = 3072 / ceil(Hq / 16) and the slots of
+    // a call, S or max(2 S, 2 B), are at most max(2 S_max, 2 B).
+    const int64_t s_max = kDecodeResidentWaves / ((int64_t(num_q_heads) + 15) / 16);
+    const int64_t slots = 2 * s_max > 2 * int64_t(num_seqs) ? 2 * s_max : 2 * int64_t(num_seqs);
+    return decode_balanced_layout(num_seqs, num_q_heads, head_dim, slots).total;
+  }
+  if (partition_size < 0) return 0;
   const int64_t maxp = max_partitions(max_context_len, partition_size);
   if (maxp <= 1) return 0;
   return part_layout(num_seqs, num_q_heads, head_dim, maxp).total;
@@ -454,7 +512,8 @@ size_t pkv_multi_query_workspace_bytes(int32_t num_tokens, int32_t num_q_heads,
                                        int32_t head_dim, int32_t max_context_len,
                                        int32_t partition_size) {
   // The partial results are laid out per query row, exactly as the
-  // one-token workspace is per sequence.
+  // one-token workspace is per sequence (no balanced split here).
+  if (partition_size < 0) return 0;
   return pkv_decode_workspace_bytes(num_tokens, num_q_heads, head_dim, max_context_len,
                                     partition_size);
 }
@@ -529,6 +588,56 @@ hipError_t launch_decode(const pkv::DecodeArgs& a, int head_dim, int tile, bool 
                                          to_internal(kv_dtype), st);
 }
 
+// Kernel choice shared by the one-token decode entry points.
+struct DecodeKind {
+  bool mfma;
+  int tile;
+};
+
+DecodeKind decode_kind(int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                       pkv_dtype_t q_dtype, pkv_dtype_t kv_dtype) {
+  const int group = num_q_heads / num_kv_heads;
+  DecodeKind k;
+  k.mfma = uses_mfma(q_dtype, kv_dtype, group);
+  k.tile = k.mfma ? pkv::mfma_head_tile() : tile_heads(group, head_dim);
+  return k;
+}
+
+// Chunk slots of a balanced one-token decode (ignoring the cap of the grid).
+int64_t decode_slots_for(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                         int32_t head_dim, pkv_dtype_t q_dtype, pkv_dtype_t kv_dtype) {
+  const DecodeKind k = decode_kind(num_q_heads, num_kv_heads, head_dim, q_dtype, kv_dtype);
+  const int64_t chunks = (num_q_heads / num_kv_heads + k.tile - 1) / k.tile;
+  return decode_balanced_slots(num_seqs, int64_t(num_kv_heads) * chunks);
+}
+
+// Writes the plan of a balanced split of the one-token decode: chunk_first
+// and slot_info (see PlanLayout) from the context lengths.
+hipError_t launch_plan(void* plan, const int32_t* context_lens, int32_t num_seqs, int64_t slots,
+                       int32_t block_size, int32_t max_blocks_per_seq, hipStream_t st) {
+  const PlanLayout L = plan_layout(num_seqs, slots);
+  pkv::SplitArgs sp{};
+  sp.context_lens = context_lens;
+  sp.num_seqs = num_seqs;
+  sp.cap_tokens = max_blocks_per_seq * block_size;
+  sp.unit_tokens = block_size;                     // chunks are runs of whole blocks
+  sp.budget = int(slots);
+  sp.chunk_first = static_cast<int32_t*>(plan);
+  sp.slot_info = reinterpret_cast<int4*>(static_cast<char*>(plan) + L.info_offset);
+  sp.num_slots = int(slots);
+  return pkv::launch_balanced_split(sp, st);
+}
+
+// The balanced one-token decode: plan, chunks, merge (sequences with one
+// chunk are written by the decode kernel and skipped by the merge).
+pkv_status_t balanced_impl(
+    void* out, const void* q, const void* k_pool, const void* v_pool, const float* k_scales,
+    const float* v_scales, const int32_t* block_tables, const int32_t* context_lens,
+    int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq, float softmax_scale,
+    void* workspace, size_t workspace_bytes, pkv_dtype_t q_dtype, pkv_dtype_t kv_dtype,
+    hipStream_t st, const void* k_new, const void* v_new, void* k_pool_w, void* v_pool_w);
+
 pkv_status_t attention_impl(
     void* out, const void* q, const void* k_pool, const void* v_pool, const float* k_scales,
     const float* v_scales, const int32_t* block_tables, const int32_t* context_lens,
@@ -538,12 +647,20 @@ pkv_status_t attention_impl(
     pkv_dtype_t q_dtype, pkv_dtype_t kv_dtype, void* stream, const void* k_new,
     const void* v_new, void* k_pool_w, void* v_pool_w) {
   if (max_context_len < 0) return PKV_ERR_INVALID_ARG;
+  const bool balanced = partition_size == PKV_PARTITION_BALANCED;
   const pkv_status_t st0 = check_decode(q, k_pool, v_pool, k_scales, v_scales, block_tables,
                                         context_lens, num_seqs, num_q_heads, num_kv_heads,
                                         head_dim, block_size, num_blocks, max_blocks_per_seq,
-                                        softmax_scale, partition_size, q_dtype, kv_dtype);
+                                        softmax_scale, balanced ? 0 : partition_size, q_dtype,
+                                        kv_dtype);
   if (st0 != PKV_OK || num_seqs == 0) return st0;
   if (!out || !aligned16(out) || !aligned16(workspace)) return PKV_ERR_INVALID_ARG;
+  if (balanced)
+    return balanced_impl(out, q, k_pool, v_pool, k_scales, v_scales, block_tables, context_lens,
+                         num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                         max_blocks_per_seq, softmax_scale, workspace, workspace_bytes, q_dtype,
+                         kv_dtype, static_cast<hipStream_t>(stream), k_new, v_new, k_pool_w,
+                         v_pool_w);
 
   const int64_t maxp = max_partitions(max_context_len, partition_size);
   const int64_t blocks_per_part =
@@ -592,6 +709,57 @@ pkv_status_t attention_impl(
   m.skip_single = 1;
   m.q_start = nullptr;
   m.num_batch = num_seqs;
+  return pkv::launch_merge(m, head_dim, to_internal(q_dtype), st) == hipSuccess ? PKV_OK
+                                                                                : PKV_ERR_HIP;
+}
+
+pkv_status_t balanced_impl(
+    void* out, const void* q, const void* k_pool, const void* v_pool, const float* k_scales,
+    const float* v_scales, const int32_t* block_tables, const int32_t* context_lens,
+    int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq, float softmax_scale,
+    void* workspace, size_t workspace_bytes, pkv_dtype_t q_dtype, pkv_dtype_t kv_dtype,
+    hipStream_t st, const void* k_new, const void* v_new, void* k_pool_w, void* v_pool_w) {
+  if (int64_t(max_blocks_per_seq) * block_size > 0x7fffffff) return PKV_ERR_INVALID_ARG;
+  const DecodeKind k = decode_kind(num_q_heads, num_kv_heads, head_dim, q_dtype, kv_dtype);
+  const int64_t slots =
+      decode_slots_for(num_seqs, num_q_heads, num_kv_heads, head_dim, q_dtype, kv_dtype);
+  pkv::DecodeArgs a = decode_args(q, k_pool, v_pool, k_scales, v_scales, block_tables,
+                                  context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                  num_blocks, max_blocks_per_seq, softmax_scale, k.tile);
+  if (slots * num_kv_heads * a.head_chunks > 0x7fffffff) return PKV_ERR_INVALID_ARG;
+  const DecodeBalancedLayout L = decode_balanced_layout(num_seqs, num_q_heads, head_dim, slots);
+  if (!workspace || workspace_bytes < L.total) return PKV_ERR_WORKSPACE;
+  char* ws = static_cast<char*>(workspace);
+  char* plan = ws + L.plan_offset;
+  if (launch_plan(plan, context_lens, num_seqs, slots, block_size, max_blocks_per_seq, st) !=
+      hipSuccess)
+    return PKV_ERR_HIP;
+  a.out = out;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.k_pool_w = k_pool_w;
+  a.v_pool_w = v_pool_w;
+  a.part_o = reinterpret_cast<float*>(ws);
+  a.part_lse = reinterpret_cast<float*>(ws + L.part.lse_offset);
+  a.blocks_per_partition = max_blocks_per_seq;
+  a.max_partitions = int(slots);
+  a.write_final = 0;
+  a.final_single = 1;
+  a.mark_empty = 0;
+  a.slot_info = reinterpret_cast<const int4*>(plan + L.plan.info_offset);
+  if (launch_decode(a, head_dim, k.tile, k.mfma, q_dtype, kv_dtype, st) != hipSuccess)
+    return PKV_ERR_HIP;
+  pkv::MergeArgs m{};
+  m.out = out;
+  m.part_o = a.part_o;
+  m.part_lse = a.part_lse;
+  m.num_seqs = num_seqs;
+  m.num_q_heads = num_q_heads;
+  m.max_partitions = int(slots);
+  m.skip_single = 1;
+  m.num_batch = num_seqs;
+  m.chunk_first = reinterpret_cast<const int32_t*>(plan);
   return pkv::launch_merge(m, head_dim, to_internal(q_dtype), st) == hipSuccess ? PKV_OK
                                                                                 : PKV_ERR_HIP;
 }
@@ -711,6 +879,104 @@ pkv_status_t pkv_paged_decode_partials(
   a.mark_empty = 1;
   return launch_decode(a, head_dim, tile, mfma, q_dtype, kv_dtype,
                        static_cast<hipStream_t>(stream)) == hipSuccess
+             ? PKV_OK
+             : PKV_ERR_HIP;
+}
+
+int32_t pkv_decode_plan_slots(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                              int32_t head_dim, pkv_dtype_t q_dtype, pkv_dtype_t kv_dtype) {
+  if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0 ||
+      !head_dim_ok(head_dim) || !dtype_ok(q_dtype) || !dtype_ok(kv_dtype))
+    return 0;
+  const int64_t slots =
+      decode_slots_for(num_seqs, num_q_heads, num_kv_heads, head_dim, q_dtype, kv_dtype);
+  return slots > 0x7fffffff ? 0 : int32_t(slots);
+}
+
+size_t pkv_decode_plan_bytes(int32_t num_seqs, int32_t num_slots) {
+  if (num_seqs < 0 || num_slots <= 0 || num_slots < num_seqs) return 0;
+  return plan_layout(num_seqs, num_slots).total;
+}
+
+pkv_status_t pkv_decode_plan(void* plan, size_t plan_bytes, const int32_t* context_lens,
+                             int32_t num_seqs, int32_t num_slots, int32_t block_size,
+                             int32_t max_blocks_per_seq, void* stream) {
+  if (num_seqs < 0 || num_slots <= 0 || num_slots < num_seqs || block_size <= 0 ||
+      max_blocks_per_seq <= 0)
+    return PKV_ERR_INVALID_ARG;
+  if (int64_t(max_blocks_per_seq) * block_size > 0x7fffffff) return PKV_ERR_INVALID_ARG;
+  if (!plan || !aligned16(plan)) return PKV_ERR_INVALID_ARG;
+  if (plan_bytes < plan_layout(num_seqs, num_slots).total) return PKV_ERR_WORKSPACE;
+  if (num_seqs == 0) return PKV_OK;
+  if (!context_lens || !aligned4(context_lens)) return PKV_ERR_INVALID_ARG;
+  return launch_plan(plan, context_lens, num_seqs, num_slots, block_size, max_blocks_per_seq,
+                     static_cast<hipStream_t>(stream)) == hipSuccess
+             ? PKV_OK
+             : PKV_ERR_HIP;
+}
+
+pkv_status_t pkv_paged_decode_partials_planned(
+    float* partial_out, float* partial_lse, const void* plan, int32_t num_slots, const void* q,
+    const void* k_pool, const void* v_pool, const float* k_scales, const float* v_scales,
+    const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+    int32_t num_blocks, int32_t max_blocks_per_seq, float softmax_scale, pkv_dtype_t q_dtype,
+    pkv_dtype_t kv_dtype, void* stream) {
+  if (num_slots <= 0 || num_slots < num_seqs) return PKV_ERR_INVALID_ARG;
+  const pkv_status_t st0 = check_decode(q, k_pool, v_pool, k_scales, v_scales, block_tables,
+                                        context_lens, num_seqs, num_q_heads, num_kv_heads,
+                                        head_dim, block_size, num_blocks, max_blocks_per_seq,
+                                        softmax_scale, 0, q_dtype, kv_dtype);
+  if (st0 != PKV_OK || num_seqs == 0) return st0;
+  if (!plan || !aligned16(plan) || !partial_out || !partial_lse || !aligned16(partial_out) ||
+      !aligned4(partial_lse))
+    return PKV_ERR_INVALID_ARG;
+  const DecodeKind k = decode_kind(num_q_heads, num_kv_heads, head_dim, q_dtype, kv_dtype);
+  pkv::DecodeArgs a = decode_args(q, k_pool, v_pool, k_scales, v_scales, block_tables,
+                                  context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                  num_blocks, max_blocks_per_seq, softmax_scale, k.tile);
+  if (int64_t(num_slots) * num_kv_heads * a.head_chunks > 0x7fffffff) return PKV_ERR_INVALID_ARG;
+  a.out = nullptr;
+  a.part_o = partial_out;
+  a.part_lse = partial_lse;
+  a.blocks_per_partition = max_blocks_per_seq;
+  a.max_partitions = num_slots;
+  a.write_final = 0;
+  a.final_single = 0;
+  a.mark_empty = 1;
+  a.slot_info = reinterpret_cast<const int4*>(static_cast<const char*>(plan) +
+                                              plan_layout(num_seqs, num_slots).info_offset);
+  return launch_decode(a, head_dim, k.tile, k.mfma, q_dtype, kv_dtype,
+                       static_cast<hipStream_t>(stream)) == hipSuccess
+             ? PKV_OK
+             : PKV_ERR_HIP;
+}
+
+pkv_status_t pkv_merge_partials_planned(void* out, const float* partial_out,
+                                        const float* partial_lse, const void* plan,
+                                        int32_t num_slots, int32_t num_seqs, int32_t num_q_heads,
+                                        int32_t head_dim, pkv_dtype_t out_dtype, void* stream) {
+  if (num_seqs < 0 || num_q_heads <= 0 || head_dim <= 0 || num_slots <= 0 ||
+      num_slots < num_seqs || !dtype_ok(out_dtype))
+    return PKV_ERR_INVALID_ARG;
+  if ((!head_dim_ok(head_dim) && head_dim != 512) || out_dtype == PKV_FP8_E4M3)
+    return PKV_ERR_UNSUPPORTED;
+  if (num_seqs == 0) return PKV_OK;
+  if (!out || !partial_out || !partial_lse || !plan) return PKV_ERR_INVALID_ARG;
+  if (!aligned16(out) || !aligned16(partial_out) || !aligned4(partial_lse) || !aligned16(plan))
+    return PKV_ERR_INVALID_ARG;
+  pkv::MergeArgs m{};
+  m.out = out;
+  m.part_o = partial_out;
+  m.part_lse = partial_lse;
+  m.num_seqs = num_seqs;
+  m.num_q_heads = num_q_heads;
+  m.max_partitions = num_slots;
+  m.skip_single = 0;
+  m.num_batch = num_seqs;
+  m.chunk_first = static_cast<const int32_t*>(plan);
+  return pkv::launch_merge(m, head_dim, to_internal(out_dtype), static_cast<hipStream_t>(stream)) ==
+                 hipSuccess
              ? PKV_OK
              : PKV_ERR_HIP;
 }

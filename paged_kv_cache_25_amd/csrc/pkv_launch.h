@@ -84,6 +84,11 @@ struct SplitArgs {
   const int32_t* context_lens;
   int num_seqs, cap_tokens, unit_tokens, budget;
   int32_t* chunk_first;
+  // Optional (null: not written): per chunk slot s < num_slots, {sequence,
+  // first unit, end unit, chunks of that sequence}; slots past the last chunk
+  // get sequence -1.  num_slots >= max(budget, num_seqs).
+  int4* slot_info;
+  int num_slots;
 };
 
 struct DecodeArgs {
@@ -117,6 +122,11 @@ struct DecodeArgs {
   int write_final;            // every sequence has one partition: write `out`
   int final_single;           // a sequence with one partition writes `out` (the merge skips it)
   int mark_empty;             // partitions past a sequence's end write lse = -inf
+  // Balanced split (null: fixed partitions): the plan's slot_info[slot] =
+  // {sequence, first block, end block, chunks of the sequence}; the grid runs
+  // max_partitions slots; partial rows are [slot, Hq] and an empty chunk
+  // writes lse = -inf.  One new token per sequence only.
+  const int4* slot_info;
 };
 
 // The columns of one (sequence, KV head) work item: column n is new token
@@ -153,6 +163,45 @@ __device__ inline bool decode_unit(int id, int chunks, int units, int& chunk, in
   chunk = r % chunks;
   unit = (r / chunks) * kXcds + xcd;
   return unit < units;
+}
+
+// The work of one decode workgroup: column chunk, KV head, sequence and the
+// blocks [blk_begin, blk_end) it walks (not yet clipped to the sequence);
+// part is the partition (fixed split) or the chunk slot (balanced split), and
+// n_parts the sequence's chunk count (balanced only).  False: no work.
+struct DecodeItem {
+  int chunk, h, b, part, blk_begin, blk_end, n_parts;
+};
+
+__device__ inline bool decode_item(const DecodeArgs& a, DecodeItem& it) {
+  const int per_head = a.slot_info ? a.max_partitions : a.num_seqs * a.max_partitions;
+  int idx;
+  if (!decode_unit(blockIdx.x, a.head_chunks, per_head * a.num_kv_heads, it.chunk, idx)) return false;
+  it.h = idx % a.num_kv_heads;
+  idx /= a.num_kv_heads;
+  if (a.slot_info) {
+    const int4 si = a.slot_info[idx];
+    if (si.x < 0 || si.x >= a.num_seqs) return false;  // slot past the last chunk
+    it.b = si.x;
+    it.part = idx;
+    it.blk_begin = si.y;
+    it.blk_end = si.z;
+    it.n_parts = si.w;
+  } else {
+    it.b = idx % a.num_seqs;
+    it.part = idx / a.num_seqs;
+    it.blk_begin = it.part * a.blocks_per_partition;
+    it.blk_end = it.blk_begin + a.blocks_per_partition;
+    it.n_parts = 0;
+  }
+  return true;
+}
+
+// Row of the partial arrays for query row qrow: [rows, max_partitions] for a
+// fixed split, [slot, Hq] for a balanced one (qrow = b * Hq + head).
+__device__ inline size_t partial_row(const DecodeArgs& a, const DecodeItem& it, size_t qrow) {
+  return a.slot_info ? qrow + (size_t(it.part) - size_t(it.b)) * a.num_q_heads
+                     : qrow * a.max_partitions + it.part;
 }
 
 struct MergeArgs {

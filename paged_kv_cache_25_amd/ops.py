@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libpkv.so")
 
 PKV_F32, PKV_BF16, PKV_FP8_E4M3 = 0, 1, 2
 PKV_SCALE_FIXED, PKV_SCALE_RUNNING_AMAX = 0, 1
-PKV_PARTITION_BALANCED = -1        # MLA decode: balanced split of the batch's work
+PKV_PARTITION_BALANCED = -1        # decode / MLA decode: balanced split of the batch's work
 STATUS = {0: "PKV_OK", 1: "PKV_ERR_INVALID_ARG", 2: "PKV_ERR_UNSUPPORTED",
           3: "PKV_ERR_WORKSPACE", 4: "PKV_ERR_HIP", 5: "PKV_ERR_OUT_OF_BLOCKS"}
 PKV_ERR_OUT_OF_BLOCKS = 5
@@ -61,6 +61,17 @@ def load():
                                             ctypes.c_int, ctypes.c_int, P]
     L.pkv_merge_partials.restype = ctypes.c_int
     L.pkv_merge_partials.argtypes = [P, P, P, P, I, I, I, I, ctypes.c_int, P]
+    L.pkv_decode_plan_slots.restype = I
+    L.pkv_decode_plan_slots.argtypes = [I, I, I, I, ctypes.c_int, ctypes.c_int]
+    L.pkv_decode_plan_bytes.restype = Z
+    L.pkv_decode_plan_bytes.argtypes = [I, I]
+    L.pkv_decode_plan.restype = ctypes.c_int
+    L.pkv_decode_plan.argtypes = [P, Z, P, I, I, I, I, P]
+    L.pkv_paged_decode_partials_planned.restype = ctypes.c_int
+    L.pkv_paged_decode_partials_planned.argtypes = [P, P, P, I, P, P, P, P, P, P, P, I, I, I, I,
+                                                    I, I, I, F, ctypes.c_int, ctypes.c_int, P]
+    L.pkv_merge_partials_planned.restype = ctypes.c_int
+    L.pkv_merge_partials_planned.argtypes = [P, P, P, P, I, I, I, I, ctypes.c_int, P]
     L.pkv_kv_append_tokens.restype = ctypes.c_int
     L.pkv_kv_append_tokens.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, ctypes.c_int, P]
     L.pkv_multi_query_workspace_bytes.restype = Z
@@ -207,6 +218,65 @@ def merge_partials(out, partial_out, partial_lse, num_partitions=None, stream=No
     _check("pkv_merge_partials", load().pkv_merge_partials(
         _ptr(out), _ptr(partial_out), _ptr(partial_lse), _ptr(num_partitions), B, hq, d, maxp,
         dtype_code(out.dtype), _stream(stream)))
+    return out
+
+
+def decode_plan_slots(num_seqs, num_q_heads, num_kv_heads, head_dim, q_dtype, kv_dtype):
+    """Chunk slots of a balanced split for this shape (pkv_decode_plan_slots)."""
+    n = int(load().pkv_decode_plan_slots(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                         dtype_code(q_dtype), dtype_code(kv_dtype)))
+    if n <= 0:
+        raise PkvError("pkv_decode_plan_slots", 1)
+    return n
+
+
+def decode_plan(context_lens, num_slots, max_blocks_per_seq, plan=None, stream=None):
+    """The balanced split's schedule (pkv_decode_plan) in a uint8 device
+    buffer: chunk_first int32 [B + 1], then slot_info int32x4 [num_slots] at
+    the offset plan_info_offset(B)."""
+    _need_cuda(context_lens, plan)
+    B = context_lens.shape[0]
+    n = int(load().pkv_decode_plan_bytes(B, num_slots))
+    if n == 0:
+        raise PkvError("pkv_decode_plan_bytes", 1)
+    if plan is None:
+        plan = torch.empty(n, dtype=torch.uint8, device=context_lens.device)
+    _check("pkv_decode_plan", load().pkv_decode_plan(
+        _ptr(plan), plan.numel(), _ptr(context_lens), B, int(num_slots), BLOCK_SIZE,
+        int(max_blocks_per_seq), _stream(stream)))
+    return plan
+
+
+def plan_info_offset(num_seqs):
+    """Byte offset of slot_info in a plan: chunk_first rounded up to 256 bytes."""
+    return (4 * (num_seqs + 1) + 255) // 256 * 256
+
+
+def paged_decode_partials_planned(partial_out, partial_lse, plan, q, k_pool, v_pool,
+                                  block_tables, context_lens, softmax_scale, k_scales=None,
+                                  v_scales=None, stream=None):
+    """Chunk results of a plan: partial_out [R, Hq, D] fp32, partial_lse [R, Hq] fp32."""
+    _need_cuda(partial_out, partial_lse, plan, q, k_pool, v_pool, block_tables, context_lens,
+               k_scales, v_scales)
+    if partial_out.dtype != torch.float32 or partial_lse.dtype != torch.float32:
+        raise TypeError("partials are float32")
+    B, hq, d = q.shape
+    nb, hkv, bs, _ = k_pool.shape
+    _check("pkv_paged_decode_partials_planned", load().pkv_paged_decode_partials_planned(
+        _ptr(partial_out), _ptr(partial_lse), _ptr(plan), partial_out.shape[0], _ptr(q),
+        _ptr(k_pool), _ptr(v_pool), _ptr(k_scales), _ptr(v_scales), _ptr(block_tables),
+        _ptr(context_lens), B, hq, hkv, d, bs, nb, block_tables.shape[1], float(softmax_scale),
+        dtype_code(q.dtype), dtype_code(k_pool.dtype), _stream(stream)))
+    return partial_out, partial_lse
+
+
+def merge_partials_planned(out, partial_out, partial_lse, plan, stream=None):
+    """out[B, Hq, D] = LSE merge of each sequence's chunk rows of partial_out [R, Hq, D]."""
+    _need_cuda(out, partial_out, partial_lse, plan)
+    B, hq, d = out.shape
+    _check("pkv_merge_partials_planned", load().pkv_merge_partials_planned(
+        _ptr(out), _ptr(partial_out), _ptr(partial_lse), _ptr(plan), partial_out.shape[0], B, hq,
+        d, dtype_code(out.dtype), _stream(stream)))
     return out
 
 

@@ -40,7 +40,9 @@ def test_header_declares_the_entry_points():
         "pkv_bm_fork", "pkv_bm_free_seq", "pkv_bm_append_slots", "pkv_bm_num_free",
         "pkv_bm_refcount", "pkv_bm_seq_len", "pkv_bm_free_list", "pkv_bm_block_tables",
         "pkv_copy_blocks", "pkv_mla_append", "pkv_mla_workspace_bytes",
-        "pkv_mla_decode_attention", "pkv_mla_decode_partials"])
+        "pkv_mla_decode_attention", "pkv_mla_decode_partials", "pkv_decode_plan_slots",
+        "pkv_decode_plan_bytes", "pkv_decode_plan", "pkv_paged_decode_partials_planned",
+        "pkv_merge_partials_planned"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -160,6 +162,7 @@ def test_partials_validation(lib):
     assert _partials(lib, po=ctypes.c_void_p(0x10008)) == INVALID
     assert _partials(lib, hq=6, hkv=4) == INVALID
     assert _partials(lib, P=24) == INVALID
+    assert _partials(lib, P=-1) == INVALID                # balanced: the planned call
     assert _partials(lib, d=96) == UNSUPPORTED
     assert _partials(lib, kvt=ops.PKV_FP8_E4M3) == INVALID
     assert _partials(lib, B=0, po=None) == OK
@@ -370,6 +373,99 @@ def test_mla_balanced_validation(lib):
     assert _mla(lib, P=-1, H=24, ws=FAKE, wsb=need) == UNSUPPORTED
     assert _mla(lib, P=-1, ws=ctypes.c_void_p(0x10008), wsb=need) == INVALID
     assert _mla(lib, P=-1, B=0, q=None) == OK
+
+
+@pytest.mark.parametrize("B,hq,hkv,kind,slots", [
+    (64, 32, 8, "mfma", 384),       # 8 KV heads x 1 tile of 16 columns: S = 3072 / 8
+    (256, 32, 8, "mfma", 768),      # 2B > S: two waves' worth
+    (128, 32, 32, "vector", 256),   # S = 3072 / 32 = 96: 2B
+    (192, 32, 8, "mfma", 384),      # 2B = S: one wave
+    (193, 32, 8, "mfma", 768),
+    (3, 4, 4, "f32", 768),          # vector tiles of one column: 3072 / 4
+    (2, 64, 1, "mfma", 768),        # 64 columns = 4 tiles of 16
+    (5000, 8, 1, "mfma", 10000)])
+def test_decode_plan_slots(lib, B, hq, hkv, kind, slots):
+    """R = S if 2B <= S else max(2S, 2B), S = 3072 // (KV heads x column
+    tiles): the one-wave decode workgroups MI355X holds at once (256 CUs x 4
+    SIMDs x 3 waves)."""
+    qt, kvt = {"mfma": (ops.PKV_BF16, ops.PKV_BF16), "vector": (ops.PKV_BF16, ops.PKV_FP8_E4M3),
+               "f32": (ops.PKV_F32, ops.PKV_F32)}[kind]
+    assert lib.pkv_decode_plan_slots(B, hq, hkv, 128, qt, kvt) == slots
+    # The workspace function, which does not know num_kv_heads, bounds it.
+    ws = lib.pkv_decode_workspace_bytes(B, hq, 128, 0, -1)
+    used = _align(slots * hq * 128 * 4) + _align(slots * hq * 4) + lib.pkv_decode_plan_bytes(B, slots)
+    assert ws >= used
+
+
+def test_decode_plan_layout(lib):
+    """chunk_first int32 [B + 1] then slot_info int32x4 [R], each 256-aligned;
+    the balanced workspace is o | lse | plan at the bound
+    R = max(2 x 3072 // ceil(Hq/16), 2B)."""
+    assert lib.pkv_decode_plan_bytes(64, 384) == 512 + 384 * 16
+    assert lib.pkv_decode_plan_bytes(0, 1) == 256 + 256
+    assert lib.pkv_decode_plan_bytes(10, 9) == 0                   # fewer slots than sequences
+    assert lib.pkv_decode_plan_bytes(1, 0) == 0
+    r = 2 * (3072 // 2)
+    assert lib.pkv_decode_workspace_bytes(64, 32, 128, 4096, -1) == (
+        _align(r * 32 * 128 * 4) + _align(r * 32 * 4) + lib.pkv_decode_plan_bytes(64, r))
+    assert lib.pkv_decode_workspace_bytes(64, 32, 128, 0, -1) == lib.pkv_decode_workspace_bytes(
+        64, 32, 128, 100000, -1)                                  # max_context_len does not enter
+    assert lib.pkv_decode_workspace_bytes(64, 32, 128, 4096, -2) == 0
+    assert lib.pkv_multi_query_workspace_bytes(64, 32, 128, 4096, -1) == 0
+    assert ops.plan_info_offset(64) == 512 and ops.plan_info_offset(63) == 256
+
+
+def test_decode_balanced_validation(lib):
+    # What a call with these sizes uses (the workspace function bounds it from above).
+    r = lib.pkv_decode_plan_slots(2, 8, 2, 128, ops.PKV_BF16, ops.PKV_BF16)
+    assert r == 3072 // 2
+    used = _align(r * 8 * 128 * 4) + _align(r * 8 * 4) + lib.pkv_decode_plan_bytes(2, r)
+    need = lib.pkv_decode_workspace_bytes(2, 8, 128, 64, -1)
+    assert need >= used
+    assert _decode(lib, P=-1) == WORKSPACE                          # nothing launched
+    assert _decode(lib, P=-1, ws=FAKE, wsb=used - 1) == WORKSPACE
+    assert _decode(lib, P=-2, ws=FAKE, wsb=need) == INVALID
+    assert _decode(lib, P=-1, d=96, ws=FAKE, wsb=need) == UNSUPPORTED
+    assert _decode(lib, P=-1, ws=ctypes.c_void_p(0x10008), wsb=need) == INVALID
+    assert _decode(lib, P=-1, mbps=1 << 28, ws=FAKE, wsb=need) == INVALID   # tokens overflow int32
+    assert _step(lib, P=-1) == WORKSPACE
+    assert _step(lib, P=-1, kn=None) == INVALID
+    assert _decode(lib, P=-1, B=0, q=None) == OK
+
+
+def test_decode_plan_validation(lib):
+    f = lib.pkv_decode_plan
+    need = lib.pkv_decode_plan_bytes(2, 384)
+    assert f(FAKE, need, FAKE, 2, 1, 16, 4, None) == INVALID         # fewer slots than sequences
+    assert f(FAKE, need, FAKE, 2, 384, 0, 4, None) == INVALID
+    assert f(FAKE, need, FAKE, 2, 384, 16, 0, None) == INVALID
+    assert f(FAKE, need, FAKE, 2, 384, 16, 1 << 28, None) == INVALID
+    assert f(None, need, FAKE, 2, 384, 16, 4, None) == INVALID
+    assert f(ctypes.c_void_p(0x10008), need, FAKE, 2, 384, 16, 4, None) == INVALID
+    assert f(FAKE, need - 1, FAKE, 2, 384, 16, 4, None) == WORKSPACE
+    assert f(FAKE, need, None, 2, 384, 16, 4, None) == INVALID
+    assert f(FAKE, need, ctypes.c_void_p(0x10002), 2, 384, 16, 4, None) == INVALID
+    assert f(FAKE, lib.pkv_decode_plan_bytes(0, 384), None, 0, 384, 16, 4, None) == OK
+    g = lib.pkv_paged_decode_partials_planned
+    args = [FAKE, FAKE, FAKE, 384, FAKE, FAKE, FAKE, None, None, FAKE, FAKE, 2, 8, 2, 128, 16, 8,
+            4, 0.088, ops.PKV_BF16, ops.PKV_BF16, None]
+    for i, bad in [(0, None), (1, None), (2, None), (2, ctypes.c_void_p(0x10008)), (3, 1),
+                   (3, 0), (4, None), (12, 7), (14, 96), (15, 32), (18, float("nan")),
+                   (20, ops.PKV_FP8_E4M3)]:
+        a = list(args)
+        a[i] = bad
+        assert g(*a) in (INVALID, UNSUPPORTED), i
+    a = list(args); a[11] = 0; a[4] = None
+    assert g(*a) == OK
+    m = lib.pkv_merge_partials_planned
+    margs = [FAKE, FAKE, FAKE, FAKE, 384, 2, 8, 128, ops.PKV_BF16, None]
+    for i, bad in [(0, None), (3, None), (3, ctypes.c_void_p(0x10008)), (4, 1), (7, 96),
+                   (8, ops.PKV_FP8_E4M3)]:
+        a = list(margs)
+        a[i] = bad
+        assert m(*a) in (INVALID, UNSUPPORTED), i
+    a = list(margs); a[5] = 0; a[0] = None
+    assert m(*a) == OK
 
 
 def test_binding_refuses_cpu_tensors():

@@ -1,0 +1,261 @@
+"""GPU parity of the balanced split of the one-token decode
+(partition_size = PKV_PARTITION_BALANCED), through the C ABI.
+
+The split only regroups the partial sums: each sequence's blocks are cut into
+n_b >= 1 runs of nearly equal length, each run is attended on its own and the
+runs are merged by their log-sum-exps, which combine any split of the tokens.
+So the attention output is checked against the oracle at the usual bars, and
+each run's partial result against the oracle restricted to that run's tokens.
+
+The schedule itself is integer work, checked bit for bit against its
+definition written out below: u_b = ceil(min(max(ctx_b, 0), cap) / 16)
+blocks, n_b = max(1, ceil(u_b / t)) with t the smallest positive integer for
+which sum_b n_b <= R = max(num_slots, num_seqs), chunk k of n_b covering
+blocks [k u_b // n_b, (k+1) u_b // n_b).
+"""
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import oracle.paged_attention as pa  # noqa: E402
+from paged_kv_cache_25_amd import ops  # noqa: E402
+from tests.gpu_util import (DeviceStep, check_guard, check_tolerance,  # noqa: E402
+                            host_storage, log, oracle_out)
+from workloads import make_inputs, named_config  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+BAL = ops.PKV_PARTITION_BALANCED
+TORCH_DT = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8_e4m3": torch.float8_e4m3fn}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    ops.load()
+
+
+def expected_plan(lens, num_slots, max_blocks, block_size=16):
+    """(chunk_first [B + 1], slot_info [num_slots, 4]) from the definition."""
+    B = len(lens)
+    cap = max_blocks * block_size
+    u = [-(-min(max(int(c), 0), cap) // block_size) for c in lens]
+    R = max(num_slots, B)
+
+    def count(t):
+        return sum(max(1, -(-x // t)) for x in u)
+
+    lo, hi = 1, max(max(u, default=1), 1)          # count(hi) = B <= R
+    while lo < hi:
+        mid = (lo + hi) // 2
+        if count(mid) <= R:
+            hi = mid
+        else:
+            lo = mid + 1
+    n = [max(1, -(-x // lo)) for x in u]
+    first = np.zeros(B + 1, np.int32)
+    first[1:] = np.cumsum(n)
+    info = np.tile(np.array([-1, 0, 0, 0], np.int32), (num_slots, 1))
+    for b in range(B):
+        for k in range(n[b]):
+            info[first[b] + k] = (b, k * u[b] // n[b], (k + 1) * u[b] // n[b], n[b])
+    return first, info
+
+
+def device_plan(lens, num_slots, max_blocks):
+    lens_d = torch.from_numpy(np.asarray(lens, np.int32)).cuda()
+    plan = ops.decode_plan(lens_d, num_slots, max_blocks)
+    torch.cuda.synchronize()
+    raw = host_storage(plan).view(np.uint8)
+    B = len(lens)
+    first = raw[:4 * (B + 1)].view(np.int32)
+    off = ops.plan_info_offset(B)
+    info = raw[off:off + 16 * num_slots].view(np.int32).reshape(num_slots, 4)
+    return first, info, plan
+
+
+# --- the schedule --------------------------------------------------------------
+
+def plan_case(case):
+    """(context lengths, slots, max_blocks_per_seq) of a schedule test."""
+    if case.startswith("config"):
+        inp = named_config(int(case[6]))
+        return inp.context_lens, 384, inp.max_blocks_per_seq
+    return {
+        "long_and_short": (np.array([3000, 5, 17, 64, 1, 33, 100, 0, 48]), 384, 200),
+        "many_short": (np.random.default_rng(61).integers(0, 41, 600), 600, 3),
+        "all_empty": (np.zeros(4, np.int64), 384, 4),
+        "one_long": (np.array([6000]), 384, 375),
+        "clamped": (np.array([-5, 10 ** 6, 129, 128]), 384, 8),   # past the table / negative
+        "few_slots": (np.array([100, 200, 300]), 7, 19),
+        "as_many_slots_as_seqs": (np.array([5000, 16, 17, 0]), 4, 313),
+    }[case]
+
+
+@pytest.mark.parametrize("case", ["long_and_short", "many_short", "all_empty", "one_long",
+                                  "clamped", "few_slots", "as_many_slots_as_seqs",
+                                  "config2_lens", "config4_lens"])
+def test_plan_matches_definition(case):
+    lens, slots, mb = plan_case(case)
+    log(f"[case] plan {case}: B={len(lens)} slots={slots} max_blocks={mb}")
+    first, info, _ = device_plan(lens, slots, mb)
+    want_first, want_info = expected_plan(lens, slots, mb)
+    assert np.array_equal(first, want_first)
+    assert np.array_equal(info, want_info)
+
+
+def test_plan_slots_of_the_workloads():
+    """R for the five workloads' shapes: one wave of resident decode
+    workgroups (S), or max(2S, 2B) when 2B > S."""
+    assert ops.decode_plan_slots(64, 32, 8, 128, torch.bfloat16, torch.bfloat16) == 384
+    assert ops.decode_plan_slots(256, 32, 8, 128, torch.bfloat16, torch.bfloat16) == 768
+    assert ops.decode_plan_slots(128, 32, 32, 128, torch.bfloat16, torch.float8_e4m3fn) == 256
+    assert ops.decode_plan_slots(4, 4, 4, 64, torch.float32, torch.float32) == 768
+
+
+# --- attention and the fused step -------------------------------------------------
+
+def run_balanced(inp, label, seqs=None, fused=False):
+    label = f"{label} balanced" + (" [fused step]" if fused else "")
+    log(f"[case] {label}: B={inp.num_seqs} Hq={inp.num_q_heads} Hkv={inp.num_kv_heads} "
+        f"D={inp.head_dim} kv={inp.kv_dtype} q={inp.q_dtype} max_ctx={inp.max_context_len}")
+    d = DeviceStep(inp)
+    d.step(BAL, fused=fused)
+    kp, vp = pa.kv_append(inp.k_pool, inp.v_pool, inp.k_new, inp.v_new, inp.block_tables,
+                          inp.context_lens, inp.block_size)
+    assert np.array_equal(host_storage(d.k_pool).view(np.uint8), kp.view(np.uint8)), "K pool"
+    assert np.array_equal(host_storage(d.v_pool).view(np.uint8), vp.view(np.uint8)), "V pool"
+    ref = oracle_out(inp, seqs=seqs, pools=(kp, vp))
+    gpu = d.out_f64() if seqs is None else d.out_f64()[list(seqs)]
+    check_tolerance(inp.kv_dtype, gpu, ref, label, out_dtype=inp.q_dtype)
+    check_guard(inp, gpu, ref, label, seqs=seqs, pools=(kp, vp))
+    return d
+
+
+FUSED = pytest.mark.parametrize("fused", [False, True], ids=["two_calls", "fused_step"])
+
+
+@FUSED
+def test_config1_tiny_fp32(fused):
+    run_balanced(named_config(1), "config1 tiny fp32", fused=fused)
+
+
+@FUSED
+def test_config2_llama3_8b_b64(fused):
+    run_balanced(named_config(2), "config2 llama3-8b b64", fused=fused)
+
+
+@FUSED
+def test_config3_long_context_sampled(fused):
+    run_balanced(named_config(3), "config3 131072 ctx (seqs 0,3)", seqs=[0, 3], fused=fused)
+
+
+@FUSED
+def test_config4_continuous_batching(fused):
+    run_balanced(named_config(4), "config4 lognormal mix b256", fused=fused)
+
+
+@FUSED
+def test_config5_fp8_sampled(fused):
+    run_balanced(named_config(5), "config5 fp8 b128 (8 seqs)",
+                 seqs=[0, 1, 17, 40, 63, 64, 100, 127], fused=fused)
+
+
+EDGE_CTX = [0, 1, 15, 16, 17, 300, 2500, 33]
+
+
+@FUSED
+@pytest.mark.parametrize("q,kv", [("f32", "f32"), ("f32", "bf16"), ("f32", "fp8_e4m3"),
+                                  ("bf16", "f32"), ("bf16", "bf16"), ("bf16", "fp8_e4m3")])
+@pytest.mark.parametrize("d", [64, 128])
+def test_dtypes_and_edge_lengths(q, kv, d, fused):
+    """Every kernel family, with empty, one-token, one-block, block-edge and
+    long contexts in one batch (the long one is cut into many chunks)."""
+    inp = make_inputs(num_seqs=len(EDGE_CTX), num_q_heads=8, num_kv_heads=2, head_dim=d,
+                      ctx=("fixed", EDGE_CTX), pool=("used_fraction", 0.85), q_dtype=q,
+                      kv_dtype=kv, seed=91)
+    dev = run_balanced(inp, f"edges q={q} kv={kv} d={d}", fused=fused)
+    assert np.all(dev.out_f64()[0] == 0)                    # ctx 0: zeros
+
+
+@pytest.mark.parametrize("hq,hkv,d", [(48, 2, 128), (32, 1, 64), (6, 2, 128), (16, 16, 64)])
+def test_group_shapes(hq, hkv, d):
+    """Several column tiles per KV head (48 and 32 heads per group on the
+    matrix cores), a vector tile of 3, and no grouping."""
+    inp = make_inputs(num_seqs=5, num_q_heads=hq, num_kv_heads=hkv, head_dim=d,
+                      ctx=("fixed", [4000, 7, 160, 0, 1234]), pool=("used_fraction", 0.9),
+                      q_dtype="bf16", kv_dtype="bf16", seed=92)
+    run_balanced(inp, f"groups Hq={hq} Hkv={hkv} d={d}")
+
+
+def test_deterministic_and_equal_to_split_math():
+    """Two calls give the same bits; the result agrees with the fixed
+    512-token split within float rounding (only the grouping differs)."""
+    inp = named_config(2, num_seqs=16)
+    log("[case] balanced determinism")
+    d = DeviceStep(inp)
+    d.append()
+    a = d.decode(BAL).clone()
+    b = d.decode(BAL).clone()
+    c = d.decode(512).clone()
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    diff = (a.float() - c.float()).abs().max().item()
+    assert diff <= 2.0 ** -7 * max(1.0, c.float().abs().max().item()), diff
+
+
+# --- the planned pieces -------------------------------------------------------------
+
+@pytest.mark.parametrize("kv,q", [("bf16", "bf16"), ("f32", "f32"), ("fp8_e4m3", "bf16")])
+def test_planned_partials_and_merge(kv, q):
+    """pkv_paged_decode_partials_planned: each chunk's normalised output and
+    natural-log lse against the oracle over that chunk's tokens; an empty
+    sequence's chunk has lse = -inf; unused slots are not written; merging
+    with pkv_merge_partials_planned gives the attention output."""
+    lens = [1, 700, 63, 1500, 0, 2900]
+    inp = make_inputs(num_seqs=len(lens), num_q_heads=8, num_kv_heads=2, head_dim=128,
+                      ctx=("fixed", lens), pool=("used_fraction", 0.8), q_dtype=q, kv_dtype=kv,
+                      seed=93)
+    d = DeviceStep(inp)
+    d.append()
+    slots = ops.decode_plan_slots(len(lens), 8, 2, 128, TORCH_DT[q], TORCH_DT[kv])
+    log(f"[case] planned partials kv={kv} q={q} slots={slots}")
+    first, info, plan = device_plan(inp.context_lens, slots, inp.max_blocks_per_seq)
+    po = torch.full((slots, 8, 128), float("nan"), device="cuda")
+    pl = torch.full((slots, 8), float("nan"), device="cuda")
+    ops.paged_decode_partials_planned(po, pl, plan, d.q, d.k_pool, d.v_pool, d.tables, d.lens,
+                                      inp.softmax_scale, d.k_scales, d.v_scales)
+    torch.cuda.synchronize()
+    got_o = po.cpu().double().numpy()
+    got_l = pl.cpu().double().numpy()
+    kp, vp = pa.kv_append(inp.k_pool, inp.v_pool, inp.k_new, inp.v_new, inp.block_tables,
+                          inp.context_lens, inp.block_size)
+    used = int(first[-1])
+    assert np.isnan(got_l[used:]).all() and np.isnan(got_o[used:]).all()
+    tol_l = 1e-5 if kv == "f32" else 2e-3
+    tol_o = 1e-5 if kv == "f32" else (2e-2 if kv == "bf16" else 6e-2)
+    for s in range(used):
+        b, k0, k1, _ = (int(x) for x in info[s])
+        ctx = int(inp.context_lens[b])
+        if ctx <= 0:
+            assert np.isneginf(got_l[s]).all()
+            continue
+        K = pa.gather_sequence(kp, inp.block_tables[b], ctx, 16, kv, inp.k_scales)
+        V = pa.gather_sequence(vp, inp.block_tables[b], ctx, 16, kv, inp.v_scales)
+        lo, hi = 16 * k0, min(16 * k1, ctx)
+        o_ref, l_ref = pa.partition_partials(pa.to_float64(inp.q[b], q), K[:, lo:hi],
+                                             V[:, lo:hi], inp.softmax_scale, hi - lo)
+        assert np.abs(got_l[s] - l_ref[:, 0]).max() < tol_l, s
+        assert np.abs(got_o[s] - o_ref[:, 0]).max() < tol_o, s
+    merged = torch.empty_like(d.q)
+    ops.merge_partials_planned(merged, po, pl, plan)
+    whole = d.decode(BAL)
+    torch.cuda.synchronize()
+    ref = oracle_out(inp, pools=(kp, vp))
+    check_tolerance(kv, merged.float().cpu().double().numpy(), ref, f"planned merge {kv}",
+                    out_dtype=q)
+    # Sequences of two or more chunks go through the same kernels either way.
+    multi = [b for b in range(len(lens)) if first[b + 1] - first[b] >= 2]
+    assert multi and torch.equal(merged[multi], whole[multi])

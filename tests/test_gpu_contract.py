@@ -37,7 +37,7 @@ def _without_block(tables, lens, b, j, block_size=16):
 
 @pytest.mark.parametrize("q_dtype,kv_dtype,heads", [("bf16", "bf16", (16, 4)), ("f32", "f32", (4, 4)),
                                                      ("bf16", "fp8_e4m3", (4, 4))])
-@pytest.mark.parametrize("P", [0, 32, 512])
+@pytest.mark.parametrize("P", [0, 32, 512, -1])
 def test_decode_bad_table_entry_is_an_empty_block(q_dtype, kv_dtype, heads, P):
     hq, hkv = heads
     inp = make_inputs(num_seqs=3, num_q_heads=hq, num_kv_heads=hkv, head_dim=128,
@@ -62,7 +62,7 @@ def test_decode_bad_table_entry_is_an_empty_block(q_dtype, kv_dtype, heads, P):
     check_tolerance(kv_dtype, gpu, ref, label, out_dtype=q_dtype)
 
 
-@pytest.mark.parametrize("P", [0, 32, 64])
+@pytest.mark.parametrize("P", [0, 32, 64, -1])
 def test_mla_bad_table_entry_is_an_empty_block(P):
     inp = make_mla_inputs(num_seqs=3, num_heads=128, ctx=("fixed", CTX), seed=78,
                           pool_used_fraction=0.8)

@@ -51,7 +51,8 @@ def run_and_check(inp, label, seqs=None, partition_size=None, check_pools=True, 
     return err
 
 
-# --- the five workloads at their full sizes -------------------------------
+# --- the five workloads at their full sizes, fixed 512-token partitions ----
+# (their balanced-split defaults are covered in test_gpu_balanced.py)
 
 FUSED = pytest.mark.parametrize("fused", [False, True], ids=["two_calls", "fused_step"])
 
@@ -63,7 +64,8 @@ def test_config1_tiny_fp32_full(fused):
 
 @FUSED
 def test_config2_llama3_8b_b64_full(fused):
-    run_and_check(named_config(2), "config2 llama3-8b b64", fused=fused)
+    run_and_check(named_config(2), "config2 llama3-8b b64 P=512", partition_size=512,
+                  fused=fused)
 
 
 @FUSED
@@ -74,14 +76,15 @@ def test_config3_long_context_sampled(fused):
 
 @FUSED
 def test_config4_continuous_batching_full(fused):
-    run_and_check(named_config(4), "config4 lognormal mix b256", fused=fused)
+    run_and_check(named_config(4), "config4 lognormal mix b256 P=512", partition_size=512,
+                  fused=fused)
 
 
 @FUSED
 def test_config5_fp8_sampled(fused):
     inp = named_config(5)
-    run_and_check(inp, "config5 fp8 b128 (8 seqs)", seqs=[0, 1, 17, 40, 63, 64, 100, 127],
-                  fused=fused)
+    run_and_check(inp, "config5 fp8 b128 (8 seqs) P=512", seqs=[0, 1, 17, 40, 63, 64, 100, 127],
+                  partition_size=512, fused=fused)
 
 
 # --- float32 twins: the same shapes at the 1e-5 bar ------------------------
@@ -182,7 +185,7 @@ def test_group_sizes_bf16(hq, hkv, d):
     run_and_check(inp, f"bf16 g={hq // hkv} D={d}", fused=hq // hkv >= 16)
 
 
-@pytest.mark.parametrize("config,P", [(2, 512), (2, 0), (4, 512), (3, 512)])
+@pytest.mark.parametrize("config,P", [(2, 512), (2, 0), (4, 512), (3, 512), (2, -1), (4, -1)])
 def test_peaky_softmax_bf16(config, P):
     """Scores with a standard deviation near 6 (softmax scale 0.5): a few
     tokens carry each output, so a wrong token, dim or head mapping moves it by

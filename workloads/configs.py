@@ -61,22 +61,27 @@ CONFIG_NAMES = {
 #                                            clipped to [lo, hi]
 # ``pool`` is ("blocks", n) for a pool of n blocks, or ("used_fraction", f) for
 # ceil(blocks needed / f) blocks (f = 1: exactly the blocks needed).
+# ``partition_size`` is the one-token decode's default split: 512 tokens where
+# the workload names it (the long-context one) or where one partition holds
+# every sequence, else -1, the balanced split (chunks of nearly equal size
+# chosen from the context lengths); calls with several new tokens per
+# sequence take 512 in its place.
 _RECIPES = {
     1: dict(num_seqs=4, num_q_heads=4, num_kv_heads=4, head_dim=64,
             ctx=("fixed", [17, 33, 64, 100]), pool=("blocks", 64),
             q_dtype="f32", kv_dtype="f32", partition_size=512),
     2: dict(num_seqs=64, num_q_heads=32, num_kv_heads=8, head_dim=128,
             ctx=("uniform", 512, 4096), pool=("used_fraction", 1.0),
-            q_dtype="bf16", kv_dtype="bf16", partition_size=512),
+            q_dtype="bf16", kv_dtype="bf16", partition_size=-1),
     3: dict(num_seqs=4, num_q_heads=32, num_kv_heads=8, head_dim=128,
             ctx=("const", 131072), pool=("used_fraction", 1.0),
             q_dtype="bf16", kv_dtype="bf16", partition_size=512),
     4: dict(num_seqs=256, num_q_heads=32, num_kv_heads=8, head_dim=128,
             ctx=("lognormal", 1024, 1.0, 1, 32768), pool=("used_fraction", 0.7),
-            q_dtype="bf16", kv_dtype="bf16", partition_size=512),
+            q_dtype="bf16", kv_dtype="bf16", partition_size=-1),
     5: dict(num_seqs=128, num_q_heads=32, num_kv_heads=32, head_dim=128,
             ctx=("const", 2048), pool=("used_fraction", 1.0),
-            q_dtype="bf16", kv_dtype="fp8_e4m3", partition_size=512),
+            q_dtype="bf16", kv_dtype="fp8_e4m3", partition_size=-1),
 }
 
 
@@ -130,6 +135,8 @@ class PagedDecodeInputs:
 
     def num_partitions(self, partition_size: int | None = None) -> np.ndarray:
         p = self.partition_size if partition_size is None else partition_size
+        if p < 0:
+            raise ValueError("the balanced split has no fixed partition count")
         if p == 0:
             return np.minimum(self.context_lens, 1).astype(np.int64)
         return -(-self.context_lens.astype(np.int64) // p)
