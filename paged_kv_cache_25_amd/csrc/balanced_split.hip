@@ -94,9 +94,22 @@ __global__ __launch_bounds__(kWave) void balanced_split_kernel(SplitArgs a) {
     if (b < a.num_seqs) {
       const int first = carry + x - n;
       a.chunk_first[b] = first;
-      if (a.slot_info)                                   // chunk k: units [k u / n, (k+1) u / n)
-        for (int k = 0; k < n; ++k)
-          a.slot_info[first + k] = make_int4(b, int(int64_t(k) * u / n), int(int64_t(k + 1) * u / n), n);
+      if (a.slot_info) {
+        // Chunk k covers units [floor(k u / n), floor((k+1) u / n)).  With
+        // u = q n + r that bound is k q + floor(k r / n); k r mod n grows by
+        // r < n per chunk, so one compare keeps the floor exact (no division
+        // per chunk).
+        const int q = u / n, r = u - q * n;
+        int lo = 0, frac = 0;
+        for (int k = 0; k < n; ++k) {
+          frac += r;
+          const int carry_unit = frac >= n ? 1 : 0;
+          frac -= carry_unit * n;
+          const int hi = lo + q + carry_unit;
+          a.slot_info[first + k] = make_int4(b, lo, hi, n);
+          lo = hi;
+        }
+      }
     }
     carry += __shfl(x, kWave - 1);
   }
