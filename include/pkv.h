@@ -124,13 +124,16 @@ pkv_status_t pkv_kv_append(void* k_pool, void* v_pool, const void* k_new, const 
  * one wave of workgroups MI355X runs at once, sets R: one-token decode,
  * S = 3072 / (num_kv_heads x column tiles) and R = S when 2 num_seqs <= S,
  * else max(2 S, 2 num_seqs) (pkv_decode_plan_slots); MLA, S = 256 for more
- * than 64 heads, 512 otherwise, and R = max(S, num_seqs).  The schedule is computed on the device from context_lens (no
- * host copy, so a call stays capturable in a graph), the chunks are run and
- * merged; a sequence with one chunk is written directly.  The result equals
- * a fixed-partition split's up to float rounding: only the grouping of the
- * partial sums changes (the log-sum-exp merge combines any split of the
- * tokens).  Intended for batches of uneven or long contexts, where a fixed
- * partition size leaves the kernel waiting for its longest partitions.
+ * than 64 heads, 512 otherwise, and R = max(S, num_seqs).  The schedule is
+ * computed on the device from context_lens (no host copy, so a call stays
+ * capturable in a graph): for the one-token decode of up to 256 sequences
+ * each decode workgroup derives it itself, otherwise a one-wave kernel runs
+ * first.  The chunks are run and merged; a sequence with one chunk is written
+ * directly.  The result equals a fixed-partition split's up to float
+ * rounding: only the grouping of the partial sums changes (the log-sum-exp
+ * merge combines any split of the tokens).  Intended for batches of uneven or
+ * long contexts, where a fixed partition size leaves the kernel waiting for
+ * its longest partitions.
  * max_context_len is not used to size anything in this mode.
  *   serving lesson, "Where it shows up" (split-KV decoding spreads one
  *   sequence over the whole GPU).
@@ -294,15 +297,18 @@ pkv_status_t pkv_merge_partials(void* out, const float* partial_out, const float
  * [k u_b / n_b, (k+1) u_b / n_b) of its u_b = ceil(ctx / block_size); see
  * PKV_PARTITION_BALANCED for n_b (here R = max(num_slots, num_seqs)).
  *
- * pkv_paged_decode_partials_planned - the chunks of a plan made by
- * pkv_decode_plan with the same context_lens, num_seqs, num_slots,
- * block_size and max_blocks_per_seq: for slot s of sequence b it writes the
- * normalised partial output over the chunk's tokens to partial_out[s][i][:]
- * and its natural-log log-sum-exp to partial_lse[s][i] (-inf for an empty
- * sequence's one chunk); slots past the last chunk are not written.
- * partial_out float32 [num_slots, num_q_heads, head_dim], partial_lse float32
- * [num_slots, num_q_heads] [device, written]; the rest as for
- * pkv_paged_decode_partials.
+ * pkv_paged_decode_partials_planned - the decode half of a balanced
+ * attention call: it schedules the batch over num_slots slots (as
+ * pkv_decode_plan does) and runs the chunks.  For slot s of sequence b it
+ * writes the normalised partial output over the chunk's tokens to
+ * partial_out[s][i][:] and its natural-log log-sum-exp to partial_lse[s][i]
+ * (-inf for an empty sequence's one chunk); slots past the last chunk are not
+ * written.  plan [device, written, pkv_decode_plan_bytes bytes] receives
+ * chunk_first (and, for more than 256 sequences, slot_info: batches up to
+ * that size are scheduled inside the decode kernel itself, larger ones by a
+ * separate plan kernel first).  partial_out float32 [num_slots, num_q_heads,
+ * head_dim], partial_lse float32 [num_slots, num_q_heads] [device, written];
+ * the rest as for pkv_paged_decode_partials.
  *
  * pkv_merge_partials_planned - out[b][i][:] = the log-sum-exp merge (as
  * pkv_merge_partials) of rows chunk_first[b] .. chunk_first[b+1]-1 of
@@ -316,7 +322,7 @@ pkv_status_t pkv_decode_plan(void* plan, size_t plan_bytes, const int32_t* conte
                              int32_t num_seqs, int32_t num_slots, int32_t block_size,
                              int32_t max_blocks_per_seq, void* stream);
 pkv_status_t pkv_paged_decode_partials_planned(
-    float* partial_out, float* partial_lse, const void* plan, int32_t num_slots, const void* q,
+    float* partial_out, float* partial_lse, void* plan, int32_t num_slots, const void* q,
     const void* k_pool, const void* v_pool, const float* k_scales, const float* v_scales,
     const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
     int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,

@@ -293,12 +293,12 @@ void paged_decode_mfma_kernel(DecodeArgs a) {
   // write the final output instead of a partial (the merge skips it).
   const bool final_out =
       a.write_final ||
-      (a.final_single && (a.slot_info ? it.n_parts == 1 : n_blk_seq <= a.blocks_per_partition));
+      (a.final_single && (a.balanced() ? it.n_parts == 1 : n_blk_seq <= a.blocks_per_partition));
   if (blk_begin >= blk_end && !(a.write_final && part == 0) &&
-      !(a.slot_info && final_out)) {                  // partition past the end, or an empty chunk
+      !(a.balanced() && final_out)) {                  // partition past the end, or an empty chunk
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
-      if ((a.mark_empty || a.slot_info) && lane < kHeadTile && cols.valid(n0 + 16 * nt + c))
+      if ((a.mark_empty || a.balanced()) && lane < kHeadTile && cols.valid(n0 + 16 * nt + c))
         a.part_lse[partial_row(a, it, row_of(n0 + 16 * nt + c))] = -INFINITY;
     return;
   }
@@ -440,7 +440,7 @@ void paged_decode_mfma_kernel(DecodeArgs a) {
 
 template <int D>
 hipError_t launch_d(const DecodeArgs& a, hipStream_t stream) {
-  const size_t units = (a.slot_info ? size_t(1) : size_t(a.num_seqs)) * a.num_kv_heads * a.max_partitions;
+  const size_t units = (a.balanced() ? size_t(1) : size_t(a.num_seqs)) * a.num_kv_heads * a.max_partitions;
   if (units == 0 || a.head_chunks == 0) return hipSuccess;
   if (units > 0x7fffffffu) return hipErrorInvalidConfiguration;
   const size_t grid = decode_grid(units, a.head_chunks);

@@ -628,6 +628,23 @@ hipError_t launch_plan(void* plan, const int32_t* context_lens, int32_t num_seqs
   return pkv::launch_balanced_split(sp, st);
 }
 
+// Sets up the schedule of a balanced decode in `plan` (PlanLayout): batches
+// of up to kPlanMaxSeqs sequences are planned inside the decode kernel, which
+// writes chunk_first; larger ones by the plan kernel first, whose slot_info the
+// decode kernel reads.
+bool plan_decode(pkv::DecodeArgs& a, char* plan, int64_t slots, int32_t block_size,
+                 hipStream_t st) {
+  if (a.num_seqs <= pkv::kPlanMaxSeqs && slots < 46341) {   // chunk bounds in 32 bits
+    a.plan_first = reinterpret_cast<int32_t*>(plan);
+    a.slot_info = nullptr;
+    return true;
+  }
+  a.plan_first = nullptr;
+  a.slot_info = reinterpret_cast<const int4*>(plan + plan_layout(a.num_seqs, slots).info_offset);
+  return launch_plan(plan, a.context_lens, a.num_seqs, slots, block_size, a.max_blocks_per_seq,
+                     st) == hipSuccess;
+}
+
 // The balanced one-token decode: plan, chunks, merge (sequences with one
 // chunk are written by the decode kernel and skipped by the merge).
 pkv_status_t balanced_impl(
@@ -732,9 +749,7 @@ pkv_status_t balanced_impl(
   if (!workspace || workspace_bytes < L.total) return PKV_ERR_WORKSPACE;
   char* ws = static_cast<char*>(workspace);
   char* plan = ws + L.plan_offset;
-  if (launch_plan(plan, context_lens, num_seqs, slots, block_size, max_blocks_per_seq, st) !=
-      hipSuccess)
-    return PKV_ERR_HIP;
+  if (!plan_decode(a, plan, slots, block_size, st)) return PKV_ERR_HIP;
   a.out = out;
   a.k_new = k_new;
   a.v_new = v_new;
@@ -747,7 +762,6 @@ pkv_status_t balanced_impl(
   a.write_final = 0;
   a.final_single = 1;
   a.mark_empty = 0;
-  a.slot_info = reinterpret_cast<const int4*>(plan + L.plan.info_offset);
   if (launch_decode(a, head_dim, k.tile, k.mfma, q_dtype, kv_dtype, st) != hipSuccess)
     return PKV_ERR_HIP;
   pkv::MergeArgs m{};
@@ -916,7 +930,7 @@ pkv_status_t pkv_decode_plan(void* plan, size_t plan_bytes, const int32_t* conte
 }
 
 pkv_status_t pkv_paged_decode_partials_planned(
-    float* partial_out, float* partial_lse, const void* plan, int32_t num_slots, const void* q,
+    float* partial_out, float* partial_lse, void* plan, int32_t num_slots, const void* q,
     const void* k_pool, const void* v_pool, const float* k_scales, const float* v_scales,
     const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
     int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
@@ -931,6 +945,7 @@ pkv_status_t pkv_paged_decode_partials_planned(
   if (!plan || !aligned16(plan) || !partial_out || !partial_lse || !aligned16(partial_out) ||
       !aligned4(partial_lse))
     return PKV_ERR_INVALID_ARG;
+  if (int64_t(max_blocks_per_seq) * block_size > 0x7fffffff) return PKV_ERR_INVALID_ARG;
   const DecodeKind k = decode_kind(num_q_heads, num_kv_heads, head_dim, q_dtype, kv_dtype);
   pkv::DecodeArgs a = decode_args(q, k_pool, v_pool, k_scales, v_scales, block_tables,
                                   context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim,
@@ -944,10 +959,9 @@ pkv_status_t pkv_paged_decode_partials_planned(
   a.write_final = 0;
   a.final_single = 0;
   a.mark_empty = 1;
-  a.slot_info = reinterpret_cast<const int4*>(static_cast<const char*>(plan) +
-                                              plan_layout(num_seqs, num_slots).info_offset);
-  return launch_decode(a, head_dim, k.tile, k.mfma, q_dtype, kv_dtype,
-                       static_cast<hipStream_t>(stream)) == hipSuccess
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (!plan_decode(a, static_cast<char*>(plan), num_slots, block_size, st)) return PKV_ERR_HIP;
+  return launch_decode(a, head_dim, k.tile, k.mfma, q_dtype, kv_dtype, st) == hipSuccess
              ? PKV_OK
              : PKV_ERR_HIP;
 }

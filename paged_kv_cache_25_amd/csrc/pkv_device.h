@@ -78,6 +78,42 @@ __device__ __forceinline__ float max_over_groups8(float x) {
   return x;
 }
 
+// Integer sum over the wave, returned uniform: rows of 16 lanes by DPP, then
+// the four row totals read as scalars.
+template <int Ctrl>
+__device__ __forceinline__ int dpp_i(int x) {
+  return __builtin_amdgcn_update_dpp(0, x, Ctrl, 0xF, 0xF, false);
+}
+__device__ __forceinline__ int wave_sum_uniform(int x) {
+  x += dpp_i<kDppQuadXor1>(x);
+  x += dpp_i<kDppQuadXor2>(x);
+  x += dpp_i<kDppHalfMirror>(x);
+  x += dpp_i<kDppRowRor8>(x);
+  return __builtin_amdgcn_readlane(x, 0) + __builtin_amdgcn_readlane(x, 16) +
+         __builtin_amdgcn_readlane(x, 32) + __builtin_amdgcn_readlane(x, 48);
+}
+__device__ __forceinline__ int wave_max_uniform(int x) {
+  x = max(x, dpp_i<kDppQuadXor1>(x));
+  x = max(x, dpp_i<kDppQuadXor2>(x));
+  x = max(x, dpp_i<kDppHalfMirror>(x));
+  x = max(x, dpp_i<kDppRowRor8>(x));
+  return max(max(__builtin_amdgcn_readlane(x, 0), __builtin_amdgcn_readlane(x, 16)),
+             max(__builtin_amdgcn_readlane(x, 32), __builtin_amdgcn_readlane(x, 48)));
+}
+
+// Inclusive prefix sum over the wave's 64 lanes: DPP shifts within rows of
+// 16 lanes, then the totals of the earlier rows read as scalars.
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  x += dpp_i<0x111>(x);                  // row_shr:1 (lanes shifted in from outside the row read 0)
+  x += dpp_i<0x112>(x);                  // row_shr:2
+  x += dpp_i<0x114>(x);                  // row_shr:4
+  x += dpp_i<0x118>(x);                  // row_shr:8
+  const int r0 = __builtin_amdgcn_readlane(x, 15), r1 = __builtin_amdgcn_readlane(x, 31),
+            r2 = __builtin_amdgcn_readlane(x, 47);
+  const int row = (threadIdx.x & 63) >> 4;
+  return x + (row >= 1 ? r0 : 0) + (row >= 2 ? r1 : 0) + (row >= 3 ? r2 : 0);
+}
+
 __device__ __forceinline__ float wave_max(float x) {
   for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
   return x;

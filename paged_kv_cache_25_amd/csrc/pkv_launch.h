@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "pkv_device.h"
+
 namespace pkv {
 
 enum class DType : int { F32 = 0, BF16 = 1, FP8 = 2 };
@@ -127,7 +129,19 @@ struct DecodeArgs {
   // max_partitions slots; partial rows are [slot, Hq] and an empty chunk
   // writes lse = -inf.  One new token per sequence only.
   const int4* slot_info;
+  // Balanced split planned inside the decode kernel (null: not): every
+  // workgroup derives the schedule from context_lens itself (at most
+  // kPlanMaxSeqs sequences) and the workgroup of a sequence's first chunk
+  // writes plan_first[b] (and plan_first[B] for the last sequence) for the
+  // merge.  The grid runs max_partitions slots.
+  int32_t* plan_first;
+  // Chunk slots of a balanced split instead of fixed partitions.
+  __host__ __device__ bool balanced() const { return slot_info != nullptr || plan_first != nullptr; }
 };
+
+// Sequences a decode workgroup plans for itself: four per lane, in registers.
+constexpr int kPlanSeqsPerLane = 4;
+constexpr int kPlanMaxSeqs = kPlanSeqsPerLane * 64;
 
 // The columns of one (sequence, KV head) work item: column n is new token
 // j = n / group of the sequence (of t) and query head i = n % group of the KV
@@ -173,12 +187,121 @@ struct DecodeItem {
   int chunk, h, b, part, blk_begin, blk_end, n_parts;
 };
 
+// The balanced schedule of chunk slot `slot`, computed by the whole wave from
+// context_lens (uniform result).  Sequence l + 64 g is held by lane l.  Its
+// u_b = ceil(min(max(ctx, 0), capacity) / 16) blocks go to n_b = max(1,
+// ceil(u_b / t)) chunks, t the smallest size with sum n_b <= R =
+// max_partitions; the bisection for t is bracketed by [total / R,
+// total / (R - B)] (the count lies in [total / t, total / t + B]), so no
+// count it evaluates exceeds R + B.  The slot's sequence is the one whose
+// run of slots [first_b, first_b + n_b) holds it (a prefix sum over the
+// lanes, then a ballot), and chunk k of it covers blocks
+// [k u / n, (k+1) u / n).  False: the slot is past the last chunk.
+// Every decode workgroup runs this at once, so it is written for few VALU
+// instructions: groups of 64 sequences past the batch are skipped, and
+// quotients by the uniform chunk size come from a float reciprocal, exact
+// after one correction each way (u < 2^22 blocks; longer tables take the
+// integer division).
+__device__ __forceinline__ int ceil_div_uniform(int u, int t, float rt, bool fast) {
+  if (!fast) return (u + t - 1) / t;
+  int q = int(float(u) * rt);             // within one of floor(u / t)
+  q -= q * t > u ? 1 : 0;
+  q += (q + 1) * t <= u ? 1 : 0;
+  return q + (q * t < u ? 1 : 0);
+}
+
+__device__ inline bool plan_slot(const DecodeArgs& a, int slot, DecodeItem& it, int& total_chunks) {
+  constexpr int G = kPlanSeqsPerLane;
+  const int l = threadIdx.x & 63;
+  const int B = a.num_seqs;
+  const int groups = (B + 63) >> 6;        // uniform, at most G
+  const int cap = a.max_blocks_per_seq * kBlockSize;
+  int u[G];
+  int mx = 0, lo16 = 0, hi16 = 0;
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    u[g] = 0;
+    if (g < groups) {
+      const int b = l + 64 * g;
+      int ctx = b < B ? a.context_lens[b] : 0;
+      ctx = ctx < 0 ? 0 : (ctx > cap ? cap : ctx);
+      u[g] = (ctx + kBlockSize - 1) / kBlockSize;
+      mx = max(mx, u[g]);
+      lo16 += u[g] & 0xFFFF;              // total = hi16 * 65536 + lo16, each sum < 2^24
+      hi16 += u[g] >> 16;
+    }
+  }
+  mx = wave_max_uniform(mx);
+  const int64_t total = int64_t(wave_sum_uniform(hi16)) * 65536 + wave_sum_uniform(lo16);
+  const int64_t R = a.max_partitions > B ? a.max_partitions : B;
+  const int top = mx > 1 ? mx : 1;
+  const int64_t lo_l = (total + R - 1) / R;
+  const int64_t hi_l = R > B ? (total + (R - B) - 1) / (R - B) : top;
+  int lo = int(lo_l < 1 ? 1 : (lo_l > top ? top : lo_l));
+  int hi = int(hi_l < lo ? lo : (hi_l > top ? top : hi_l));
+  const bool fast = mx < (1 << 22);
+  // Chunks of one lane's sequences for chunk size t (0 for sequences past B).
+  auto lane_chunks = [&](int g, int t, float rt) {
+    const int b = l + 64 * g;
+    return b >= B ? 0 : (u[g] <= t ? 1 : ceil_div_uniform(u[g], t, rt, fast));
+  };
+  while (lo < hi) {
+    const int mid = lo + (hi - lo) / 2;
+    const float rt = 1.0f / float(mid);
+    int c = 0;
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+      if (g < groups) c += lane_chunks(g, mid, rt);
+    if (wave_sum_uniform(c) <= R) hi = mid; else lo = mid + 1;
+  }
+  const float rt = 1.0f / float(lo);
+  int carry = 0;
+  bool found = false;
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    if (g < groups) {
+      const int n = lane_chunks(g, lo, rt);
+      const int incl = wave_incl_scan(n);
+      const int first = carry + incl - n;
+      const uint64_t owner = __ballot(n > 0 && first <= slot && slot < first + n);
+      if (!found && owner != 0) {
+        const int lane = __builtin_ctzll(owner);
+        const int nb = __builtin_amdgcn_readlane(n, lane);
+        const int ub = __builtin_amdgcn_readlane(u[g], lane);
+        const int k = slot - __builtin_amdgcn_readlane(first, lane);
+        // k u / n = k q + k r / n with u = q n + r; k r < n^2 fits 32 bits
+        // (the host keeps R below 46341 slots for this path).
+        const int q = ub / nb, r = ub - q * nb;
+        it.b = lane + 64 * g;
+        it.part = slot;
+        it.blk_begin = k * q + (k * r) / nb;
+        it.blk_end = (k + 1) * q + ((k + 1) * r) / nb;
+        it.n_parts = nb;
+        found = true;
+      }
+      carry += __builtin_amdgcn_readlane(incl, 63);
+    }
+  }
+  total_chunks = carry;
+  return found;
+}
+
 __device__ inline bool decode_item(const DecodeArgs& a, DecodeItem& it) {
-  const int per_head = a.slot_info ? a.max_partitions : a.num_seqs * a.max_partitions;
+  const int per_head = a.balanced() ? a.max_partitions : a.num_seqs * a.max_partitions;
   int idx;
   if (!decode_unit(blockIdx.x, a.head_chunks, per_head * a.num_kv_heads, it.chunk, idx)) return false;
   it.h = idx % a.num_kv_heads;
   idx /= a.num_kv_heads;
+  if (a.plan_first) {
+    int total_chunks;
+    if (!plan_slot(a, idx, it, total_chunks)) return false;
+    // The first chunk's workgroup publishes the sequence's first slot.
+    if (it.chunk == 0 && it.h == 0 && it.blk_begin == 0 && (threadIdx.x & 63) == 0) {
+      a.plan_first[it.b] = idx;
+      if (it.b == a.num_seqs - 1) a.plan_first[a.num_seqs] = total_chunks;
+    }
+    return true;
+  }
   if (a.slot_info) {
     const int4 si = a.slot_info[idx];
     if (si.x < 0 || si.x >= a.num_seqs) return false;  // slot past the last chunk
@@ -200,8 +323,8 @@ __device__ inline bool decode_item(const DecodeArgs& a, DecodeItem& it) {
 // Row of the partial arrays for query row qrow: [rows, max_partitions] for a
 // fixed split, [slot, Hq] for a balanced one (qrow = b * Hq + head).
 __device__ inline size_t partial_row(const DecodeArgs& a, const DecodeItem& it, size_t qrow) {
-  return a.slot_info ? qrow + (size_t(it.part) - size_t(it.b)) * a.num_q_heads
-                     : qrow * a.max_partitions + it.part;
+  return a.balanced() ? qrow + (size_t(it.part) - size_t(it.b)) * a.num_q_heads
+                      : qrow * a.max_partitions + it.part;
 }
 
 struct MergeArgs {

@@ -255,7 +255,9 @@ def plan_info_offset(num_seqs):
 def paged_decode_partials_planned(partial_out, partial_lse, plan, q, k_pool, v_pool,
                                   block_tables, context_lens, softmax_scale, k_scales=None,
                                   v_scales=None, stream=None):
-    """Chunk results of a plan: partial_out [R, Hq, D] fp32, partial_lse [R, Hq] fp32."""
+    """Chunk results of a balanced split over R = partial_out.shape[0] slots:
+    partial_out [R, Hq, D] fp32, partial_lse [R, Hq] fp32; the schedule is
+    written into ``plan`` (uint8, pkv_decode_plan_bytes(B, R) bytes)."""
     _need_cuda(partial_out, partial_lse, plan, q, k_pool, v_pool, block_tables, context_lens,
                k_scales, v_scales)
     if partial_out.dtype != torch.float32 or partial_lse.dtype != torch.float32:

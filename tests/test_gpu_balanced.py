@@ -190,6 +190,19 @@ def test_group_shapes(hq, hkv, d):
     run_balanced(inp, f"groups Hq={hq} Hkv={hkv} d={d}")
 
 
+@FUSED
+def test_more_sequences_than_planned_in_kernel(fused):
+    """Batches of more than 256 sequences are scheduled by the one-wave plan
+    kernel before the decode kernel (smaller ones plan inside it): 300
+    sequences, mostly short, three long."""
+    lens = np.random.default_rng(94).integers(0, 200, 300)
+    lens[[7, 150, 299]] = [3000, 2200, 1700]
+    inp = make_inputs(num_seqs=300, num_q_heads=8, num_kv_heads=2, head_dim=64,
+                      ctx=("fixed", lens.tolist()), pool=("used_fraction", 0.9), q_dtype="bf16",
+                      kv_dtype="bf16", seed=94)
+    run_balanced(inp, "300 sequences", fused=fused)
+
+
 def test_deterministic_and_equal_to_split_math():
     """Two calls give the same bits; the result agrees with the fixed
     512-token split within float rounding (only the grouping differs)."""
@@ -210,10 +223,13 @@ def test_deterministic_and_equal_to_split_math():
 
 @pytest.mark.parametrize("kv,q", [("bf16", "bf16"), ("f32", "f32"), ("fp8_e4m3", "bf16")])
 def test_planned_partials_and_merge(kv, q):
-    """pkv_paged_decode_partials_planned: each chunk's normalised output and
-    natural-log lse against the oracle over that chunk's tokens; an empty
-    sequence's chunk has lse = -inf; unused slots are not written; merging
-    with pkv_merge_partials_planned gives the attention output."""
+    """pkv_paged_decode_partials_planned: it writes the schedule's chunk
+    starts (planned inside the decode kernel at this batch size) equal to
+    pkv_decode_plan's; each chunk's normalised output and natural-log lse
+    against the oracle over the chunk's tokens as pkv_decode_plan's slot
+    records give them; an empty sequence's chunk has lse = -inf; unused slots
+    are not written; merging with pkv_merge_partials_planned gives the
+    attention output."""
     lens = [1, 700, 63, 1500, 0, 2900]
     inp = make_inputs(num_seqs=len(lens), num_q_heads=8, num_kv_heads=2, head_dim=128,
                       ctx=("fixed", lens), pool=("used_fraction", 0.8), q_dtype=q, kv_dtype=kv,
@@ -225,9 +241,11 @@ def test_planned_partials_and_merge(kv, q):
     first, info, plan = device_plan(inp.context_lens, slots, inp.max_blocks_per_seq)
     po = torch.full((slots, 8, 128), float("nan"), device="cuda")
     pl = torch.full((slots, 8), float("nan"), device="cuda")
+    plan[:4 * (len(lens) + 1)] = 0xFF                     # chunk_first is rewritten by the call
     ops.paged_decode_partials_planned(po, pl, plan, d.q, d.k_pool, d.v_pool, d.tables, d.lens,
                                       inp.softmax_scale, d.k_scales, d.v_scales)
     torch.cuda.synchronize()
+    assert np.array_equal(host_storage(plan)[:4 * (len(lens) + 1)].view(np.int32), first)
     got_o = po.cpu().double().numpy()
     got_l = pl.cpu().double().numpy()
     kp, vp = pa.kv_append(inp.k_pool, inp.v_pool, inp.k_new, inp.v_new, inp.block_tables,
