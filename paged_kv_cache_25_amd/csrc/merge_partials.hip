@@ -148,8 +148,11 @@ hipError_t launch_d(const MergeArgs& a, DType out_dtype, hipStream_t stream) {
   if (grid > 0x7fffffffu) return hipErrorInvalidConfiguration;
   // One wave per (sequence, head) when its rows fit one batch (8 rows per
   // row group), or when there are enough (sequence, head) pairs to fill the
-  // chip with single waves; four waves for few, long sequences.
-  const bool one_batch = a.max_partitions * (D / 4) <= 8 * kWave;
+  // chip with single waves; four waves for few, long sequences.  Chunk slots
+  // of a balanced split are spread over the sequences: judge by their mean.
+  const int rows = a.chunk_first ? (a.max_partitions + a.num_batch - 1) / a.num_batch
+                                 : a.max_partitions;
+  const bool one_batch = rows * (D / 4) <= 8 * kWave;
   int threads = (one_batch || grid >= 4096) ? kWave : kThreads;
   threads = threads < D / 4 ? D / 4 : threads;   // one row group reads a whole row
   if (out_dtype == DType::F32)
