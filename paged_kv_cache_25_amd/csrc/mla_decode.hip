@@ -69,6 +69,9 @@ constexpr int kBufElems = 2 * kBlockElems;
 constexpr int kSlabs = kDk / 32;              // 18 score products per block and wave
 constexpr int kTiles = kDc / 16;              // 32 value products per pair and wave
 constexpr float kRescaleThreshold = 8.0f;
+// LDS operand reads in flight ahead of their MFMAs (more spills at 8 waves).
+constexpr int kKAhead = 4;                    // K slabs of the score product
+constexpr int kVAhead = 3;                    // V tiles of the latent sum
 static_assert(kBlockSlices * kWave >= kBlockSize * kSlotsPerRow, "a block's rows fit its slices");
 
 // Maximum over lanes l, l ^ 16, l ^ 32 and l ^ 48 (the four token groups of a
@@ -235,16 +238,31 @@ __global__ __launch_bounds__(WAVES * kWave) void mla_decode_kernel(MlaArgs a) {
   auto compute = [&](const uint16_t* kb, int p, bool ok0, bool ok1) {
     // Scores of the pair's two blocks: lane holds tokens 16j + 4g + i of head
     // h0 + c.
+    // The 36 products alternate between the blocks (two independent
+    // accumulation chains) and read their K slab kKAhead products ahead from
+    // a rotating set of registers; the scheduling fences keep that order (left
+    // alone, the compiler waits on every LDS read before its MFMA, short of
+    // registers).
     f32x4 s[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j) s[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    {
+      constexpr int kN = 2 * kSlabs;                 // product i: slab i / 2 of block i % 2
+      const uint16_t* krow = kb + c * kKStride + 8 * g;
+      auto kload = [&](int i) {
+        return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(
+                                              krow + (i & 1) * kBlockElems + 32 * (i >> 1)));
+      };
+      bf16x8 kbuf[kKAhead];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const uint16_t* krow = kb + j * kBlockElems + c * kKStride + 8 * g;
+      for (int i = 0; i < kKAhead; ++i) kbuf[i] = kload(i);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int kc = 0; kc < kSlabs; ++kc) {
-        const bf16x8 kv = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(krow + 32 * kc));
-        s[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, q[kc], s[j], 0, 0, 0);
+      for (int i = 0; i < kN; ++i) {
+        s[i & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kbuf[i % kKAhead], q[i >> 1], s[i & 1],
+                                                          0, 0, 0);
+        if (i + kKAhead < kN) kbuf[i % kKAhead] = kload(i + kKAhead);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
 
@@ -291,16 +309,25 @@ __global__ __launch_bounds__(WAVES * kWave) void mla_decode_kernel(MlaArgs a) {
                            pack_bf16x2(pv[4], pv[5]), pack_bf16x2(pv[6], pv[7])));
     // V operand of tile t: rows 4g + (c >> 2) of block 0 and of block 1,
     // columns 16t + 4(c & 3), read transposed.
+    // Read kVAhead tiles ahead, as for the scores.
     const uint16_t* vrow = kb + (4 * g + (c >> 2)) * kKStride + 4 * (c & 3);
-#pragma unroll
-    for (int t = 0; t < kTiles; ++t) {
+    auto vload = [&](int t) {
       const v4i16 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vrow + 16 * t));
       const v4i16 v1 =
           __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vrow + kBlockElems + 16 * t));
       const uint2 w0 = __builtin_bit_cast(uint2, v0);
       const uint2 w1 = __builtin_bit_cast(uint2, v1);
-      const bf16x8 vb = __builtin_bit_cast(bf16x8, make_uint4(w0.x, w0.y, w1.x, w1.y));
-      o[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, vb, o[t], 0, 0, 0);
+      return __builtin_bit_cast(bf16x8, make_uint4(w0.x, w0.y, w1.x, w1.y));
+    };
+    bf16x8 vbuf[kVAhead];
+#pragma unroll
+    for (int t = 0; t < kVAhead; ++t) vbuf[t] = vload(t);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int t = 0; t < kTiles; ++t) {
+      o[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, vbuf[t % kVAhead], o[t], 0, 0, 0);
+      if (t + kVAhead < kTiles) vbuf[t % kVAhead] = vload(t + kVAhead);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
