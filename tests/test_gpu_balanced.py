@@ -203,6 +203,39 @@ def test_more_sequences_than_planned_in_kernel(fused):
     run_balanced(inp, "300 sequences", fused=fused)
 
 
+def test_planned_partials_with_many_slots():
+    """50,000 slots (more than the decode kernel plans for itself, whose chunk
+    bounds stay in 32 bits below 46,341 slots): the planned pieces take the
+    plan kernel, and merging them still gives the oracle's attention."""
+    lens = [0, 5, 900, 3100]
+    inp = make_inputs(num_seqs=4, num_q_heads=2, num_kv_heads=1, head_dim=64,
+                      ctx=("fixed", lens), pool=("used_fraction", 0.9), q_dtype="bf16",
+                      kv_dtype="bf16", seed=95)
+    d = DeviceStep(inp)
+    d.append()
+    slots = 50000
+    log(f"[case] planned partials, {slots} slots")
+    lens_d = torch.from_numpy(inp.context_lens.astype(np.int32)).cuda()
+    plan = torch.empty(ops.load().pkv_decode_plan_bytes(4, slots), dtype=torch.uint8, device="cuda")
+    po = torch.empty((slots, 2, 64), device="cuda")
+    pl = torch.empty((slots, 2), device="cuda")
+    ops.paged_decode_partials_planned(po, pl, plan, d.q, d.k_pool, d.v_pool, d.tables, lens_d,
+                                      inp.softmax_scale)
+    torch.cuda.synchronize()
+    first, info = expected_plan(inp.context_lens, slots, inp.max_blocks_per_seq)
+    raw = host_storage(plan).view(np.uint8)
+    assert np.array_equal(raw[:20].view(np.int32), first)
+    off = ops.plan_info_offset(4)
+    assert np.array_equal(raw[off:off + 16 * slots].view(np.int32).reshape(slots, 4), info)
+    merged = torch.empty_like(d.q)
+    ops.merge_partials_planned(merged, po, pl, plan)
+    torch.cuda.synchronize()
+    kp, vp = pa.kv_append(inp.k_pool, inp.v_pool, inp.k_new, inp.v_new, inp.block_tables,
+                          inp.context_lens, inp.block_size)
+    check_tolerance("bf16", merged.float().cpu().double().numpy(), oracle_out(inp, pools=(kp, vp)),
+                    "planned, 50000 slots", out_dtype="bf16")
+
+
 def test_deterministic_and_equal_to_split_math():
     """Two calls give the same bits; the result agrees with the fixed
     512-token split within float rounding (only the grouping differs)."""
