@@ -126,9 +126,8 @@ pkv_status_t pkv_kv_append(void* k_pool, void* v_pool, const void* k_new, const 
  * else max(2 S, 2 num_seqs) (pkv_decode_plan_slots); MLA, S = 256 for more
  * than 64 heads, 512 otherwise, and R = max(S, num_seqs).  The schedule is
  * computed on the device from context_lens (no host copy, so a call stays
- * capturable in a graph): for the one-token decode of up to 256 sequences
- * each decode workgroup derives it itself, otherwise a one-wave kernel runs
- * first.  The chunks are run and merged; a sequence with one chunk is written
+ * capturable in a graph): for up to 256 sequences each decode workgroup
+ * derives it itself, otherwise a one-wave kernel runs first.  The chunks are run and merged; a sequence with one chunk is written
  * directly.  The result equals a fixed-partition split's up to float
  * rounding: only the grouping of the partial sums changes (the log-sum-exp
  * merge combines any split of the tokens).  Intended for batches of uneven or

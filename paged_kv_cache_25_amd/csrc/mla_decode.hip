@@ -111,7 +111,41 @@ __global__ __launch_bounds__(WAVES * kWave) void mla_decode_kernel(MlaArgs a) {
   int chunk, b, blk_begin, blk_end, n_blk_seq, ctx;
   size_t slot_row, slot_stride;
   bool final_out;
-  if (a.chunk_first) {
+  if (a.plan_first) {
+    // Wave 0 plans the workgroup's chunk (pairs of blocks) and shares it.
+    chunk = blockIdx.x % a.head_chunks;
+    const int cs = blockIdx.x / a.head_chunks;           // chunk slot
+    const int cap_tok = a.max_blocks_per_seq * kBlockSize;
+    __shared__ int s_plan[4];                            // sequence (-1: none), first pair, end pair, chunks
+    if (wave == 0) {
+      PlanChunk pc;
+      int total_chunks;
+      const bool any = plan_slot(a.context_lens, a.num_seqs, cap_tok, 2 * kBlockSize,
+                                 a.max_partitions, cs, pc, total_chunks);
+      if (lane == 0) {
+        s_plan[0] = any ? pc.b : -1;
+        s_plan[1] = pc.u_begin;
+        s_plan[2] = pc.u_end;
+        s_plan[3] = pc.n;
+        if (any && pc.u_begin == 0 && chunk == 0) {      // the sequence's first chunk
+          a.plan_first[pc.b] = cs;
+          if (pc.b == a.num_seqs - 1) a.plan_first[a.num_seqs] = total_chunks;
+        }
+      }
+    }
+    __syncthreads();
+    b = s_plan[0];
+    if (b < 0) return;                                   // a slot past the last chunk: uniform
+    const int raw_ctx = a.context_lens[b];
+    ctx = raw_ctx < 0 ? 0 : (raw_ctx > cap_tok ? cap_tok : raw_ctx);
+    n_blk_seq = (ctx + kBlockSize - 1) / kBlockSize;
+    blk_begin = 2 * s_plan[1];
+    blk_end = 2 * s_plan[2];
+    blk_end = blk_end < n_blk_seq ? blk_end : n_blk_seq;
+    final_out = s_plan[3] == 1;                          // (also a sequence with nothing to attend)
+    slot_row = size_t(cs) * a.num_heads;
+    slot_stride = 1;
+  } else if (a.chunk_first) {
     chunk = blockIdx.x % a.head_chunks;
     const int cs = blockIdx.x / a.head_chunks;           // chunk slot (grid: every slot exists)
     __shared__ int s_seq;
@@ -396,10 +430,11 @@ hipError_t launch_mla_decode(const MlaArgs& a, hipStream_t stream) {
   const size_t units = size_t(a.num_seqs) * a.max_partitions;
   if (units == 0) return hipSuccess;
   if (units > 0x7fffffffu) return hipErrorInvalidConfiguration;
-  // Balanced split: one workgroup per (chunk slot, head chunk), max_partitions
-  // slots; fixed partitions: XCD-ordered (partition, sequence) units.
-  const size_t grid = a.chunk_first ? size_t(a.max_partitions) * a.head_chunks
-                                    : decode_grid(units, a.head_chunks);
+  // Balanced split (planned before or inside): one workgroup per (chunk slot,
+  // head chunk), max_partitions slots; fixed partitions: XCD-ordered
+  // (partition, sequence) units.
+  const size_t grid = (a.chunk_first || a.plan_first) ? size_t(a.max_partitions) * a.head_chunks
+                                                      : decode_grid(units, a.head_chunks);
   if (grid > 0x7fffffffu) return hipErrorInvalidConfiguration;
   const dim3 g{unsigned(grid)};
   switch (mla_heads_per_workgroup(a.num_heads) / 16) {

@@ -361,14 +361,19 @@ pkv_status_t pkv_mla_decode_attention(
     char* ws = static_cast<char*>(workspace);
     int32_t* first = reinterpret_cast<int32_t*>(ws + L.first_offset);
     hipStream_t st = static_cast<hipStream_t>(stream);
-    pkv::SplitArgs sp{};
-    sp.context_lens = context_lens;
-    sp.num_seqs = num_seqs;
-    sp.cap_tokens = max_blocks_per_seq * block_size;
-    sp.unit_tokens = 2 * block_size;                 // the kernel walks pairs of blocks
-    sp.budget = int(L.slots);
-    sp.chunk_first = first;
-    if (pkv::launch_balanced_split(sp, st) != hipSuccess) return PKV_ERR_HIP;
+    // Up to kPlanMaxSeqs sequences each workgroup plans its own chunk (and the
+    // first chunks publish chunk_first); larger batches run the plan kernel.
+    const bool plan_inside = num_seqs <= pkv::kPlanMaxSeqs && L.slots < 46341;
+    if (!plan_inside) {
+      pkv::SplitArgs sp{};
+      sp.context_lens = context_lens;
+      sp.num_seqs = num_seqs;
+      sp.cap_tokens = max_blocks_per_seq * block_size;
+      sp.unit_tokens = 2 * block_size;               // the kernel walks pairs of blocks
+      sp.budget = int(L.slots);
+      sp.chunk_first = first;
+      if (pkv::launch_balanced_split(sp, st) != hipSuccess) return PKV_ERR_HIP;
+    }
     pkv::MlaArgs a{};
     a.out = out;
     a.part_o = reinterpret_cast<float*>(ws);
@@ -385,7 +390,7 @@ pkv_status_t pkv_mla_decode_attention(
     a.blocks_per_partition = max_blocks_per_seq;
     a.max_partitions = int(L.slots);
     a.scale_log2 = softmax_scale * pkv::kLog2eHost;
-    a.chunk_first = first;
+    if (plan_inside) a.plan_first = first; else a.chunk_first = first;
     if (pkv::launch_mla_decode(a, st) != hipSuccess) return PKV_ERR_HIP;
     pkv::MergeArgs m{};
     m.out = out;

@@ -75,6 +75,11 @@ struct MlaArgs {
   // chunk_first[b] .. chunk_first[b+1]-1 and splits its pairs of blocks evenly
   // over them; workgroup c takes slot c; partial rows are [slot, H].
   const int32_t* chunk_first;
+  // Balanced split planned inside the kernel (null: not): wave 0 of every
+  // workgroup derives its slot's chunk from context_lens (at most
+  // kPlanMaxSeqs sequences) and the first chunk's workgroup writes
+  // plan_first[b] (and plan_first[B]) for the merge.
+  int32_t* plan_first;
 };
 
 // The balanced split of a batch's work into at most max(budget, num_seqs)
@@ -210,12 +215,18 @@ __device__ __forceinline__ int ceil_div_uniform(int u, int t, float rt, bool fas
   return q + (q * t < u ? 1 : 0);
 }
 
-__device__ inline bool plan_slot(const DecodeArgs& a, int slot, DecodeItem& it, int& total_chunks) {
+// The chunk of slot `slot`: sequence b, units [u_begin, u_end) of it and its
+// chunk count n (unit_tokens tokens per unit; contexts clamped to
+// [0, cap_tokens]; R = max(slots, B)).
+struct PlanChunk {
+  int b, u_begin, u_end, n;
+};
+
+__device__ inline bool plan_slot(const int32_t* context_lens, int B, int cap, int unit_tokens,
+                                 int slots, int slot, PlanChunk& pc, int& total_chunks) {
   constexpr int G = kPlanSeqsPerLane;
   const int l = threadIdx.x & 63;
-  const int B = a.num_seqs;
   const int groups = (B + 63) >> 6;        // uniform, at most G
-  const int cap = a.max_blocks_per_seq * kBlockSize;
   int u[G];
   int mx = 0, lo16 = 0, hi16 = 0;
 #pragma unroll
@@ -223,9 +234,9 @@ __device__ inline bool plan_slot(const DecodeArgs& a, int slot, DecodeItem& it, 
     u[g] = 0;
     if (g < groups) {
       const int b = l + 64 * g;
-      int ctx = b < B ? a.context_lens[b] : 0;
+      int ctx = b < B ? context_lens[b] : 0;
       ctx = ctx < 0 ? 0 : (ctx > cap ? cap : ctx);
-      u[g] = (ctx + kBlockSize - 1) / kBlockSize;
+      u[g] = (ctx + unit_tokens - 1) / unit_tokens;
       mx = max(mx, u[g]);
       lo16 += u[g] & 0xFFFF;              // total = hi16 * 65536 + lo16, each sum < 2^24
       hi16 += u[g] >> 16;
@@ -233,7 +244,7 @@ __device__ inline bool plan_slot(const DecodeArgs& a, int slot, DecodeItem& it, 
   }
   mx = wave_max_uniform(mx);
   const int64_t total = int64_t(wave_sum_uniform(hi16)) * 65536 + wave_sum_uniform(lo16);
-  const int64_t R = a.max_partitions > B ? a.max_partitions : B;
+  const int64_t R = slots > B ? slots : B;
   const int top = mx > 1 ? mx : 1;
   const int64_t lo_l = (total + R - 1) / R;
   const int64_t hi_l = R > B ? (total + (R - B) - 1) / (R - B) : top;
@@ -272,11 +283,10 @@ __device__ inline bool plan_slot(const DecodeArgs& a, int slot, DecodeItem& it, 
         // k u / n = k q + k r / n with u = q n + r; k r < n^2 fits 32 bits
         // (the host keeps R below 46341 slots for this path).
         const int q = ub / nb, r = ub - q * nb;
-        it.b = lane + 64 * g;
-        it.part = slot;
-        it.blk_begin = k * q + (k * r) / nb;
-        it.blk_end = (k + 1) * q + ((k + 1) * r) / nb;
-        it.n_parts = nb;
+        pc.b = lane + 64 * g;
+        pc.u_begin = k * q + (k * r) / nb;
+        pc.u_end = (k + 1) * q + ((k + 1) * r) / nb;
+        pc.n = nb;
         found = true;
       }
       carry += __builtin_amdgcn_readlane(incl, 63);
@@ -294,7 +304,15 @@ __device__ inline bool decode_item(const DecodeArgs& a, DecodeItem& it) {
   idx /= a.num_kv_heads;
   if (a.plan_first) {
     int total_chunks;
-    if (!plan_slot(a, idx, it, total_chunks)) return false;
+    PlanChunk pc;
+    if (!plan_slot(a.context_lens, a.num_seqs, a.max_blocks_per_seq * kBlockSize, kBlockSize,
+                   a.max_partitions, idx, pc, total_chunks))
+      return false;
+    it.b = pc.b;
+    it.part = idx;
+    it.blk_begin = pc.u_begin;
+    it.blk_end = pc.u_end;
+    it.n_parts = pc.n;
     // The first chunk's workgroup publishes the sequence's first slot.
     if (it.chunk == 0 && it.h == 0 && it.blk_begin == 0 && (threadIdx.x & 63) == 0) {
       a.plan_first[it.b] = idx;
