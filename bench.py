@@ -746,8 +746,9 @@ def main_mla(args):
     step_ms = timed(step, args.steps)
     att_ms = timed(att_only, args.kernel_reps)
     # The balanced split's kernels run inside one call: the roofline is then
-    # taken over the whole call (split, chunks and merge), a lower bound on
-    # the chunk kernel's own rate (rocprofv3 gives the kernels apart).
+    # taken over the whole call (chunks, each planning its own, and merge; a
+    # plan kernel first for more than 256 sequences), a lower bound on the
+    # chunk kernel's own rate (rocprofv3 gives the kernels apart).
     decode_ms = att_ms if balanced else timed(decode_only, args.kernel_reps)
     merge_ms = max(att_ms - decode_ms, 0.0) if maxp > 1 else 0.0
     tr = traffic.mla_attention_traffic(inp.context_lens, num_heads=H, kv_lora_rank=dc,
@@ -771,7 +772,8 @@ def main_mla(args):
         "kernel_us": ({"attention_call": round(att_ms * 1e3, 2)} if balanced else
                       {"decode": round(decode_ms * 1e3, 2), "merge": round(merge_ms * 1e3, 2),
                        "attention_call": round(att_ms * 1e3, 2)}),
-        "roofline": {"kernel": ("balanced_split_kernel + mla_decode_kernel + merge_kernel"
+        "roofline": {"kernel": (("balanced_split_kernel + " if B > 256 else "")
+                                + "mla_decode_kernel + merge_kernel"
                                 if balanced else "mla_decode_kernel"), "bound": "hbm",
                      "achieved": round(kernel_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(kernel_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
