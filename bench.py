@@ -379,7 +379,7 @@ def main_multi(args):
     inp = named_config(args.config, seed=args.seed, new_tokens=("const", T),
                        name=f"{CONFIG_NAMES[args.config]}_t{T}")
     P = inp.partition_size if args.partition_size is None else args.partition_size
-    P = 512 if P < 0 else P              # several new tokens: fixed partitions only
+    balanced = P == ops.PKV_PARTITION_BALANCED
     print(f"[bench] workload {inp.name}: generated in {time.time() - t0:.1f}s", file=sys.stderr,
           flush=True)
     base = dict(q=to_device(inp.q, inp.q_dtype, dev),
@@ -400,8 +400,13 @@ def main_multi(args):
     R = inp.total_queries
     mcl, mq = inp.max_context_len, inp.max_new_tokens
     qcode, kvcode = ops.dtype_code(base["q"].dtype), ops.dtype_code(base["k_pool"].dtype)
-    ws_bytes = ops.multi_query_workspace_bytes(R, Hq, D, mcl, P)
-    maxp = max(1, -(-mcl // P)) if P else 1
+    if balanced:
+        ws_bytes = int(lib.pkv_multi_query_balanced_workspace_bytes(B, mq, Hq, Hkv, D, qcode,
+                                                                    kvcode))
+        maxp = 1                         # (no partials call: the balanced call is timed whole)
+    else:
+        ws_bytes = ops.multi_query_workspace_bytes(R, Hq, D, mcl, P)
+        maxp = max(1, -(-mcl // P)) if P else 1
     lse_off = ((R * Hq * maxp * D * 4 + 255) // 256) * 256
     stream = torch.cuda.current_stream()
     sp = ctypes.c_void_p(stream.cuda_stream)
@@ -460,7 +465,10 @@ def main_multi(args):
 
     reps = args.kernel_reps
     att_ms = timed(att_only, reps)
-    decode_ms = timed(decode_only, reps)
+    # The balanced split has no partials entry point for several tokens: its
+    # roofline is taken over the whole call (decode kernel planning its
+    # chunks, then the merge), a lower bound on the decode kernel's own rate.
+    decode_ms = att_ms if balanced else timed(decode_only, reps)
     append_ms = timed(append_only, reps)
     merge_ms = max(att_ms - decode_ms, 0.0) if maxp > 1 else 0.0
 
@@ -493,10 +501,13 @@ def main_multi(args):
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "steps_per_s": round(1e3 / step_ms, 1),
         "new_tokens_per_s": round(R * 1e3 / step_ms, 1),
-        "kernel_us": {"append": round(append_ms * 1e3, 2), "decode": round(decode_ms * 1e3, 2),
-                      "merge": round(merge_ms * 1e3, 2), "attention_call": round(att_ms * 1e3, 2)},
+        "kernel_us": ({"append": round(append_ms * 1e3, 2),
+                       "attention_call": round(att_ms * 1e3, 2)} if balanced else
+                      {"append": round(append_ms * 1e3, 2), "decode": round(decode_ms * 1e3, 2),
+                       "merge": round(merge_ms * 1e3, 2), "attention_call": round(att_ms * 1e3, 2)}),
         "roofline": {"kernel": ("paged_decode_mfma_kernel" if mfma else "paged_decode_kernel")
-                               + f"<{D}> (several new tokens)",
+                               + f"<{D}> (several new tokens)"
+                               + (" + merge_kernel" if balanced else ""),
                      "bound": "hbm", "achieved": round(kernel_gbps, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(kernel_gbps / HBM_PEAK_GBPS, 4),
                      "traffic": None, "algorithmic_bytes_per_launch": tr["kv_bytes"],

@@ -385,6 +385,22 @@ size_t pkv_multi_query_workspace_bytes(int32_t num_tokens, int32_t num_q_heads,
                                        int32_t partition_size);
 
 /*
+ * pkv_multi_query_balanced_workspace_bytes - device workspace of
+ * pkv_paged_multi_query_attention with PKV_PARTITION_BALANCED (which
+ * pkv_multi_query_workspace_bytes cannot size: it depends on the KV heads and
+ * the longest query): float32 o [R, max_query_len, num_q_heads, head_dim],
+ * float32 lse [R, max_query_len, num_q_heads] and a plan of
+ * pkv_decode_plan_bytes(num_seqs, R) bytes, each 256-byte aligned, R the
+ * chunk slots for num_kv_heads x ceil(max_query_len x group / tile) units
+ * (as pkv_decode_plan_slots counts them for one new token).  0 on invalid
+ * arguments.
+ */
+size_t pkv_multi_query_balanced_workspace_bytes(int32_t num_seqs, int32_t max_query_len,
+                                                int32_t num_q_heads, int32_t num_kv_heads,
+                                                int32_t head_dim, pkv_dtype_t q_dtype,
+                                                pkv_dtype_t kv_dtype);
+
+/*
  * pkv_paged_multi_query_attention - every new token attends over the cached
  * tokens up to and including its own position (call pkv_kv_append_tokens
  * first, on the same stream): the causal mask shifted by the cache length.
@@ -405,12 +421,16 @@ size_t pkv_multi_query_workspace_bytes(int32_t num_tokens, int32_t num_q_heads,
  * column n of sequence b is new token n / g and head n % g of the KV head's
  * group (g = num_q_heads / num_kv_heads), so the g*t_b queries that share a
  * KV head read each cached block once per partition.  Partitions are merged
- * as in pkv_paged_decode_attention.
+ * as in pkv_paged_decode_attention.  partition_size == PKV_PARTITION_BALANCED
+ * splits each sequence's blocks into balanced chunks as for one new token
+ * (every query of a chunk's sequence attends over the chunk; partial rows
+ * [slot, max_query_len, num_q_heads]).
  *
  * out [device, written] in q_dtype; q, pools, scales, tables, lens,
  * query_start_loc [device, read]; workspace [device, scratch] of at least
  * pkv_multi_query_workspace_bytes(num_tokens, ...) bytes (may be NULL when
- * that is 0).  max_query_len: a host-side upper bound of every t_b (>= 1),
+ * that is 0), or pkv_multi_query_balanced_workspace_bytes(...) bytes for the
+ * balanced split.  max_query_len: a host-side upper bound of every t_b (>= 1),
  * used to size the grid; max_context_len as for pkv_paged_decode_attention.
  * Supported as for pkv_paged_decode_attention.
  */

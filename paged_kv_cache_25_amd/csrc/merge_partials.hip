@@ -36,23 +36,28 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(MergeArgs a) {
   const int t = threadIdx.x;
   const int g = t / kRowThreads, c = t % kRowThreads;
 
+  // Row b's sequence (several new tokens per sequence: the last s with
+  // q_start[s] <= b) and its new token j there.
+  int seq = b, j = 0;
+  if (a.q_start && (a.chunk_first || a.context_lens)) {
+    int lo = 0, hi = a.num_batch - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (a.q_start[mid] <= b) lo = mid; else hi = mid - 1;
+    }
+    seq = lo;
+    j = b - a.q_start[seq];
+  }
+  const int slot_rows = a.slot_rows > 1 ? a.slot_rows : 1;
   int np = a.max_partitions;
   int first = 0;
   if (a.chunk_first) {                            // kept inside the max_partitions slots
-    first = min(max(a.chunk_first[b], 0), a.max_partitions);
-    np = min(max(a.chunk_first[b + 1], first), a.max_partitions) - first;
+    first = min(max(a.chunk_first[seq], 0), a.max_partitions);
+    np = min(max(a.chunk_first[seq + 1], first), a.max_partitions) - first;
+    if (j < 0 || j >= slot_rows) np = 0;          // no slot row for this token
   } else if (a.num_partitions) {
     np = a.num_partitions[b];
   } else if (a.context_lens) {
-    int seq = b;
-    if (a.q_start) {                              // last s with q_start[s] <= b
-      int lo = 0, hi = a.num_batch - 1;
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (a.q_start[mid] <= b) lo = mid; else hi = mid - 1;
-      }
-      seq = lo;
-    }
     const int ctx = a.context_lens[seq];
     np = ctx <= 0 ? 0 : (ctx + a.partition_size - 1) / a.partition_size;
   }
@@ -61,10 +66,11 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(MergeArgs a) {
 
   const size_t row = size_t(b) * a.num_q_heads + qh;
   // Partition p of this row: rows [b, H, max_partitions] (stride 1), or, for
-  // a balanced split, chunk slot chunk_first[b] + p of rows [slot, H] (stride H).
-  const size_t base = a.chunk_first ? size_t(first) * a.num_q_heads + qh
+  // a balanced split, chunk slot chunk_first[seq] + p of rows [slot,
+  // slot_rows, H] (stride slot_rows * H).
+  const size_t base = a.chunk_first ? (size_t(first) * slot_rows + j) * a.num_q_heads + qh
                                     : row * a.max_partitions;
-  const size_t stride = a.chunk_first ? size_t(a.num_q_heads) : 1;
+  const size_t stride = a.chunk_first ? size_t(slot_rows) * a.num_q_heads : 1;
   const float* lse_base = a.part_lse + base;
   const float* o_base = a.part_o + base * D + 4 * c;
   auto lse_at = [&](int p) { return lse_base[size_t(p) * stride]; };
@@ -151,7 +157,7 @@ hipError_t launch_d(const MergeArgs& a, DType out_dtype, hipStream_t stream) {
   // chip with single waves; four waves for few, long sequences.  Chunk slots
   // of a balanced split are spread over the sequences: judge by their mean.
   const int rows = a.chunk_first ? (a.max_partitions + a.num_batch - 1) / a.num_batch
-                                 : a.max_partitions;
+                                 : a.max_partitions;     // partial rows per merged row
   const bool one_batch = rows * (D / 4) <= 8 * kWave;
   int threads = (one_batch || grid >= 4096) ? kWave : kThreads;
   threads = threads < D / 4 ? D / 4 : threads;   // one row group reads a whole row

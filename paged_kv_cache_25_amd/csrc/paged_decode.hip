@@ -292,8 +292,9 @@ __global__ __launch_bounds__(kWave) void paged_decode_kernel(DecodeArgs a) {
       (a.final_single && (a.balanced() ? it.n_parts == 1 : n_blk_seq <= a.blocks_per_partition));
   if (blk_begin >= blk_end && !(a.write_final && part == 0) &&
       !(a.balanced() && final_out)) {                  // partition past the end, or an empty chunk
-    if ((a.mark_empty || a.balanced()) && lane < G && cols.valid(n0 + lane))
-      a.part_lse[partial_row(a, it, cols.row(n0 + lane))] = -INFINITY;
+    if ((a.mark_empty || a.balanced()) && lane < G && cols.valid(n0 + lane) &&
+        partial_row_ok(a, cols.row(n0 + lane), cols.row0))
+      a.part_lse[partial_row(a, it, cols.row(n0 + lane), cols.row0)] = -INFINITY;
     return;
   }
   // Tokens each column attends to (all ctx for a single new token); the
@@ -413,7 +414,8 @@ __global__ __launch_bounds__(kWave) void paged_decode_kernel(DecodeArgs a) {
         else reinterpret_cast<uint16_t*>(orow)[TL::dim(s, k)] = f32_to_bf16_rne(v);
       }
     } else {
-      const size_t prow = partial_row(a, it, qrow);
+      if (!partial_row_ok(a, qrow, cols.row0)) continue;
+      const size_t prow = partial_row(a, it, qrow, cols.row0);
       float* o = a.part_o + prow * D;
 #pragma unroll
       for (int k = 0; k < KD; ++k) o[TL::dim(s, k)] = dec.acc[i][k] * inv;

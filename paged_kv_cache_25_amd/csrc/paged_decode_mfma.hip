@@ -298,8 +298,9 @@ void paged_decode_mfma_kernel(DecodeArgs a) {
       !(a.balanced() && final_out)) {                  // partition past the end, or an empty chunk
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
-      if ((a.mark_empty || a.balanced()) && lane < kHeadTile && cols.valid(n0 + 16 * nt + c))
-        a.part_lse[partial_row(a, it, row_of(n0 + 16 * nt + c))] = -INFINITY;
+      if ((a.mark_empty || a.balanced()) && lane < kHeadTile && cols.valid(n0 + 16 * nt + c) &&
+          partial_row_ok(a, row_of(n0 + 16 * nt + c), cols.row0))
+        a.part_lse[partial_row(a, it, row_of(n0 + 16 * nt + c), cols.row0)] = -INFINITY;
     return;
   }
   int my_vis[NT];                                     // tokens my column of tile nt attends to
@@ -425,7 +426,8 @@ void paged_decode_mfma_kernel(DecodeArgs a) {
         else
           *reinterpret_cast<uint2*>(orow) = make_uint2(packed[0], packed[1]);
       } else {
-        const size_t prow = partial_row(a, it, qrow);
+        if (!partial_row_ok(a, qrow, cols.row0)) continue;
+        const size_t prow = partial_row(a, it, qrow, cols.row0);
         float* op = a.part_o + prow * D + kDimsPerLane * c;
 #pragma unroll
         for (int e = 0; e < kDimsPerLane; e += 4)

@@ -91,9 +91,10 @@ BalancedLayout balanced_layout(int32_t num_seqs, int32_t num_heads, int32_t d) {
 // (and at least two slots per sequence) balances better.
 constexpr int64_t kDecodeResidentWaves = 3072;
 
-int64_t decode_balanced_slots(int32_t num_seqs, int64_t units_per_slot) {
+int64_t decode_balanced_slots(int32_t num_seqs, int64_t units_per_slot,
+                              int64_t resident = kDecodeResidentWaves) {
   const int64_t per = units_per_slot > 0 ? units_per_slot : 1;
-  const int64_t budget = kDecodeResidentWaves / per > 0 ? kDecodeResidentWaves / per : 1;
+  const int64_t budget = resident / per > 0 ? resident / per : 1;
   const int64_t two_b = 2 * int64_t(num_seqs);
   if (two_b <= budget) return budget;
   return 2 * budget > two_b ? 2 * budget : two_b;
@@ -783,6 +784,46 @@ pkv_status_t balanced_impl(
                                                                                 : PKV_ERR_HIP;
 }
 
+// Kernel choice for several new tokens per sequence: query columns per KV
+// head = max_query_len x group, on the matrix cores in tiles of 16 (two tiles
+// per wave past 16 columns) or on the vector kernel.
+struct MultiKind {
+  bool mfma;
+  int tile, tiles_per_wave;
+  int64_t chunks;
+};
+
+MultiKind multi_kind(int32_t max_query_len, int32_t num_q_heads, int32_t num_kv_heads,
+                     int32_t head_dim, pkv_dtype_t q_dtype, pkv_dtype_t kv_dtype) {
+  MultiKind k;
+  const int group = num_q_heads / num_kv_heads;
+  const int64_t columns = int64_t(max_query_len) * group;     // queries per KV head
+  k.mfma = uses_mfma(q_dtype, kv_dtype, columns);
+  k.tiles_per_wave = k.mfma && columns > pkv::mfma_head_tile() ? 2 : 1;
+  k.tile = k.mfma ? pkv::mfma_head_tile() * k.tiles_per_wave
+                  : tile_heads(columns < (1 << 20) ? int(columns) : (1 << 20), head_dim);
+  k.chunks = (columns + k.tile - 1) / k.tile;
+  return k;
+}
+
+// Resident waves of the decode kernel for several new tokens: two tiles per
+// wave take more registers (two waves per SIMD instead of three).
+int64_t multi_resident_waves(const MultiKind& k) {
+  return k.tiles_per_wave == 2 ? 2048 : kDecodeResidentWaves;
+}
+
+// Workspace of a balanced call with several new tokens: partials o
+// [R, max_q, Hq, D] | lse [R, max_q, Hq] | the plan.
+DecodeBalancedLayout multi_balanced_layout(int64_t num_seqs, int64_t max_q, int64_t Hq, int64_t D,
+                                           int64_t slots) {
+  DecodeBalancedLayout L;
+  L.part = part_layout(slots * max_q, Hq, D, 1);
+  L.plan = plan_layout(num_seqs, slots);
+  L.plan_offset = L.part.total;
+  L.total = L.plan_offset + L.plan.total;
+  return L;
+}
+
 // Checks and kernel set-up shared by the two multi-token entry points.
 struct MultiSetup {
   pkv::DecodeArgs a;
@@ -812,15 +853,14 @@ pkv_status_t multi_setup(MultiSetup& ms, const void* q, const void* k_pool, cons
   }
   if (max_query_len < 1 || !query_start_loc || !aligned4(query_start_loc))
     return PKV_ERR_INVALID_ARG;
-  const int group = num_q_heads / num_kv_heads;
-  const int64_t columns = int64_t(max_query_len) * group;     // queries per KV head
-  ms.mfma = uses_mfma(q_dtype, kv_dtype, columns);
   // More than 16 columns on the matrix cores: two 16-column tiles per wave
   // share each block's K/V registers.
-  const int tiles_per_wave = ms.mfma && columns > pkv::mfma_head_tile() ? 2 : 1;
-  ms.tile = ms.mfma ? pkv::mfma_head_tile() * tiles_per_wave
-                    : tile_heads(columns < (1 << 20) ? int(columns) : (1 << 20), head_dim);
-  const int64_t chunks = (columns + ms.tile - 1) / ms.tile;
+  const MultiKind k = multi_kind(max_query_len, num_q_heads, num_kv_heads, head_dim, q_dtype,
+                                 kv_dtype);
+  ms.mfma = k.mfma;
+  ms.tile = k.tile;
+  const int tiles_per_wave = k.tiles_per_wave;
+  const int64_t chunks = k.chunks;
   if (chunks > 0x7fffffff) return PKV_ERR_INVALID_ARG;
   ms.a = decode_args(q, k_pool, v_pool, k_scales, v_scales, block_tables, context_lens,
                      num_seqs, num_q_heads, num_kv_heads, head_dim, num_blocks,
@@ -1000,6 +1040,21 @@ pkv_status_t pkv_merge_partials_planned(void* out, const float* partial_out,
              : PKV_ERR_HIP;
 }
 
+size_t pkv_multi_query_balanced_workspace_bytes(int32_t num_seqs, int32_t max_query_len,
+                                                int32_t num_q_heads, int32_t num_kv_heads,
+                                                int32_t head_dim, pkv_dtype_t q_dtype,
+                                                pkv_dtype_t kv_dtype) {
+  if (num_seqs <= 0 || max_query_len <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
+      num_q_heads % num_kv_heads != 0 || !head_dim_ok(head_dim) || !dtype_ok(q_dtype) ||
+      !dtype_ok(kv_dtype))
+    return 0;
+  const MultiKind k =
+      multi_kind(max_query_len, num_q_heads, num_kv_heads, head_dim, q_dtype, kv_dtype);
+  const int64_t slots = decode_balanced_slots(num_seqs, int64_t(num_kv_heads) * k.chunks,
+                                              multi_resident_waves(k));
+  return multi_balanced_layout(num_seqs, max_query_len, num_q_heads, head_dim, slots).total;
+}
+
 pkv_status_t pkv_paged_multi_query_attention(
     void* out, const void* q, const void* k_pool, const void* v_pool, const float* k_scales,
     const float* v_scales, const int32_t* block_tables, const int32_t* context_lens,
@@ -1009,13 +1064,59 @@ pkv_status_t pkv_paged_multi_query_attention(
     float softmax_scale, int32_t partition_size, void* workspace, size_t workspace_bytes,
     pkv_dtype_t q_dtype, pkv_dtype_t kv_dtype, void* stream) {
   if (max_context_len < 0) return PKV_ERR_INVALID_ARG;
+  const bool balanced = partition_size == PKV_PARTITION_BALANCED;
   MultiSetup ms;
   const pkv_status_t st0 = multi_setup(
       ms, q, k_pool, v_pool, k_scales, v_scales, block_tables, context_lens, query_start_loc,
       num_seqs, num_tokens, max_query_len, num_q_heads, num_kv_heads, head_dim, block_size,
-      num_blocks, max_blocks_per_seq, softmax_scale, partition_size, q_dtype, kv_dtype);
+      num_blocks, max_blocks_per_seq, softmax_scale, balanced ? 0 : partition_size, q_dtype,
+      kv_dtype);
   if (st0 != PKV_OK || ms.nothing) return st0;
   if (!out || !aligned16(out) || !aligned16(workspace)) return PKV_ERR_INVALID_ARG;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+
+  if (balanced) {
+    // Chunk slots as for one new token (the units are KV heads x column tiles);
+    // partial rows [slot, max_query_len, Hq]; the merge finds each row's
+    // sequence and new token from query_start_loc.
+    if (int64_t(max_blocks_per_seq) * block_size > 0x7fffffff) return PKV_ERR_INVALID_ARG;
+    pkv::DecodeArgs& a = ms.a;
+    const MultiKind k =
+        multi_kind(max_query_len, num_q_heads, num_kv_heads, head_dim, q_dtype, kv_dtype);
+    const int64_t slots = decode_balanced_slots(num_seqs, int64_t(num_kv_heads) * a.head_chunks,
+                                                multi_resident_waves(k));
+    if (slots * num_kv_heads * a.head_chunks > 0x7fffffff) return PKV_ERR_INVALID_ARG;
+    const DecodeBalancedLayout L =
+        multi_balanced_layout(num_seqs, max_query_len, num_q_heads, head_dim, slots);
+    if (!workspace || workspace_bytes < L.total) return PKV_ERR_WORKSPACE;
+    char* ws = static_cast<char*>(workspace);
+    char* plan = ws + L.plan_offset;
+    a.out = out;
+    a.part_o = reinterpret_cast<float*>(ws);
+    a.part_lse = reinterpret_cast<float*>(ws + L.part.lse_offset);
+    a.blocks_per_partition = max_blocks_per_seq;
+    a.max_partitions = int(slots);
+    a.write_final = 0;
+    a.final_single = 1;
+    a.mark_empty = 0;
+    if (!plan_decode(a, plan, slots, block_size, st)) return PKV_ERR_HIP;
+    if (launch_decode(a, head_dim, ms.tile, ms.mfma, q_dtype, kv_dtype, st) != hipSuccess)
+      return PKV_ERR_HIP;
+    pkv::MergeArgs m{};
+    m.out = out;
+    m.part_o = a.part_o;
+    m.part_lse = a.part_lse;
+    m.num_seqs = num_tokens;
+    m.num_q_heads = num_q_heads;
+    m.max_partitions = int(slots);
+    m.skip_single = 1;
+    m.q_start = query_start_loc;
+    m.num_batch = num_seqs;
+    m.chunk_first = reinterpret_cast<const int32_t*>(plan);
+    m.slot_rows = max_query_len;
+    return pkv::launch_merge(m, head_dim, to_internal(q_dtype), st) == hipSuccess ? PKV_OK
+                                                                                  : PKV_ERR_HIP;
+  }
 
   const int64_t maxp = max_partitions(max_context_len, partition_size);
   const bool single = maxp <= 1;
@@ -1037,7 +1138,6 @@ pkv_status_t pkv_paged_multi_query_attention(
   a.final_single = 1;
   a.mark_empty = 0;
 
-  hipStream_t st = static_cast<hipStream_t>(stream);
   if (launch_decode(a, head_dim, ms.tile, ms.mfma, q_dtype, kv_dtype, st) != hipSuccess)
     return PKV_ERR_HIP;
   if (single) return PKV_OK;

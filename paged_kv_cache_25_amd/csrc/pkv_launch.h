@@ -338,11 +338,21 @@ __device__ inline bool decode_item(const DecodeArgs& a, DecodeItem& it) {
   return true;
 }
 
-// Row of the partial arrays for query row qrow: [rows, max_partitions] for a
-// fixed split, [slot, Hq] for a balanced one (qrow = b * Hq + head).
-__device__ inline size_t partial_row(const DecodeArgs& a, const DecodeItem& it, size_t qrow) {
-  return a.balanced() ? qrow + (size_t(it.part) - size_t(it.b)) * a.num_q_heads
-                      : qrow * a.max_partitions + it.part;
+// Row of the partial arrays for query row qrow = (row0 + j) * Hq + head (row0
+// the sequence's first query row, j its new token): [rows, max_partitions]
+// for a fixed split; [slot, Hq] for a balanced one, or [slot, max_q, Hq] with
+// several new tokens per sequence.
+__device__ inline size_t partial_row(const DecodeArgs& a, const DecodeItem& it, size_t qrow,
+                                     int row0) {
+  if (!a.balanced()) return qrow * a.max_partitions + it.part;
+  if (!a.q_start) return qrow + (size_t(it.part) - size_t(it.b)) * a.num_q_heads;
+  const size_t j = qrow / a.num_q_heads - size_t(row0);
+  return (size_t(it.part) * a.max_q + j) * a.num_q_heads + qrow % a.num_q_heads;
+}
+// False for a new token past max_q (a violated contract): a balanced split
+// with several tokens has no partial row for it.
+__device__ inline bool partial_row_ok(const DecodeArgs& a, size_t qrow, int row0) {
+  return !(a.balanced() && a.q_start) || qrow / a.num_q_heads - size_t(row0) < size_t(a.max_q);
 }
 
 struct MergeArgs {
@@ -359,9 +369,11 @@ struct MergeArgs {
   // entry sets its partition count.  Null: row r is sequence r.
   const int32_t* q_start;
   int num_batch;                   // sequences, when q_start is set
-  // Balanced split (MLA): partitions of sequence b are the chunk slots
-  // chunk_first[b] .. chunk_first[b+1]-1; rows [slot, num_q_heads].
+  // Balanced split: partitions of sequence b are the chunk slots
+  // chunk_first[b] .. chunk_first[b+1]-1; rows [slot, slot_rows, num_q_heads]
+  // (slot_rows: the most new tokens of a sequence; 0 or 1 for one each).
   const int32_t* chunk_first;
+  int slot_rows;
 };
 
 hipError_t launch_kv_append(const AppendArgs& a, hipStream_t stream);

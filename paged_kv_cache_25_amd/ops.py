@@ -76,6 +76,9 @@ def load():
     L.pkv_kv_append_tokens.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, ctypes.c_int, P]
     L.pkv_multi_query_workspace_bytes.restype = Z
     L.pkv_multi_query_workspace_bytes.argtypes = [I, I, I, I, I]
+    L.pkv_multi_query_balanced_workspace_bytes.restype = Z
+    L.pkv_multi_query_balanced_workspace_bytes.argtypes = [I, I, I, I, I, ctypes.c_int,
+                                                           ctypes.c_int]
     L.pkv_paged_multi_query_attention.restype = ctypes.c_int
     L.pkv_paged_multi_query_attention.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I,
                                                   I, I, I, F, I, P, Z, ctypes.c_int,
@@ -347,7 +350,11 @@ def paged_multi_query_attention(out, q, k_pool, v_pool, block_tables, context_le
     if query_start_loc.shape[0] != B + 1:
         raise ValueError("query_start_loc must have num_seqs + 1 entries")
     if workspace is None:
-        n = multi_query_workspace_bytes(T, hq, d, max_context_len, partition_size)
+        if partition_size == PKV_PARTITION_BALANCED:
+            n = int(load().pkv_multi_query_balanced_workspace_bytes(
+                B, int(max_query_len), hq, hkv, d, dtype_code(q.dtype), dtype_code(k_pool.dtype)))
+        else:
+            n = multi_query_workspace_bytes(T, hq, d, max_context_len, partition_size)
         workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=q.device)
     _check("pkv_paged_multi_query_attention", load().pkv_paged_multi_query_attention(
         _ptr(out), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(k_scales), _ptr(v_scales),

@@ -181,7 +181,6 @@ class DeviceMultiStep:
     def attend(self, partition_size=None, max_query_len=None):
         inp = self.inp
         P = inp.partition_size if partition_size is None else partition_size
-        P = 512 if P < 0 else P                   # several tokens: fixed partitions only
         mq = max(inp.max_new_tokens, 1) if max_query_len is None else max_query_len
         ops.paged_multi_query_attention(self.out, self.q, self.k_pool, self.v_pool, self.tables,
                                         self.lens, self.qsl, mq, inp.max_context_len,

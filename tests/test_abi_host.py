@@ -42,7 +42,7 @@ def test_header_declares_the_entry_points():
         "pkv_copy_blocks", "pkv_mla_append", "pkv_mla_workspace_bytes",
         "pkv_mla_decode_attention", "pkv_mla_decode_partials", "pkv_decode_plan_slots",
         "pkv_decode_plan_bytes", "pkv_decode_plan", "pkv_paged_decode_partials_planned",
-        "pkv_merge_partials_planned"])
+        "pkv_merge_partials_planned", "pkv_multi_query_balanced_workspace_bytes"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -235,6 +235,14 @@ def test_multi_query_validation(lib):
     assert _multi(lib, ws=FAKE, wsb=need - 1) == WORKSPACE
     assert _multi(lib, B=0, q=None, qsl=None) == OK
     assert _multi(lib, T=0, q=None, qsl=None) == OK
+    # the balanced split: sized by its own function, checked before any launch
+    bal = lib.pkv_multi_query_balanced_workspace_bytes(2, 4, 8, 2, 128, ops.PKV_BF16, ops.PKV_BF16)
+    assert bal > 0
+    assert _multi(lib, P=-1) == WORKSPACE
+    assert _multi(lib, P=-1, ws=FAKE, wsb=bal - 1) == WORKSPACE
+    assert _multi(lib, P=-2, ws=FAKE, wsb=bal) == INVALID
+    assert _multi(lib, P=-1, qsl=None, ws=FAKE, wsb=bal) == INVALID
+    assert _multi_partials(lib, P=-1) == INVALID                 # no balanced partials call
 
 
 def _multi_partials(lib, **over):
@@ -412,6 +420,19 @@ def test_decode_plan_layout(lib):
         64, 32, 128, 100000, -1)                                  # max_context_len does not enter
     assert lib.pkv_decode_workspace_bytes(64, 32, 128, 4096, -2) == 0
     assert lib.pkv_multi_query_workspace_bytes(64, 32, 128, 4096, -1) == 0
+    # several new tokens: [R, max_q, Hq, D] | [R, max_q, Hq] | plan; t = 4, g = 4: one
+    # 16-column tile per KV head, so R = 384 as for one token
+    t = 4
+    assert lib.pkv_multi_query_balanced_workspace_bytes(64, t, 32, 8, 128, ops.PKV_BF16,
+                                                        ops.PKV_BF16) == (
+        _align(384 * t * 32 * 128 * 4) + _align(384 * t * 32 * 4) + lib.pkv_decode_plan_bytes(64, 384))
+    # t = 16: 64 columns = 2 waves of two tiles each (two waves per SIMD resident, 2048 in
+    # all): units 8 x 2 = 16, S = 128, 2B = 128 <= S
+    assert lib.pkv_multi_query_balanced_workspace_bytes(64, 16, 32, 8, 128, ops.PKV_BF16,
+                                                        ops.PKV_BF16) == (
+        _align(128 * 16 * 32 * 128 * 4) + _align(128 * 16 * 32 * 4) + lib.pkv_decode_plan_bytes(64, 128))
+    assert lib.pkv_multi_query_balanced_workspace_bytes(64, 0, 32, 8, 128, ops.PKV_BF16,
+                                                        ops.PKV_BF16) == 0
     assert ops.plan_info_offset(64) == 512 and ops.plan_info_offset(63) == 256
 
 

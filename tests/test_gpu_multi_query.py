@@ -6,7 +6,9 @@ Covers both kernels (matrix cores for bf16 over bf16 with 2+ queries per KV
 head, the vector kernel otherwise), column tiles that span several new tokens
 and a ragged last tile, partition boundaries inside the new tokens,
 sequences with no new token, rows that see nothing, a prompt prefilled in
-chunks, and the one-token case against the decode entry point bit for bit."""
+chunks, the one-token case against the decode entry point bit for bit, and
+the balanced split (partial rows [slot, max_query_len, Hq]) on the same
+cases."""
 
 import numpy as np
 import pytest
@@ -18,6 +20,7 @@ from tests.gpu_util import (DeviceMultiStep, DeviceStep, check_tolerance, host_s
 from workloads import make_inputs, named_config
 
 pytestmark = pytest.mark.gpu
+BAL = -1                             # PKV_PARTITION_BALANCED
 
 
 def _shape(config, **over):
@@ -58,6 +61,7 @@ def test_fixed_new_tokens_f32(t):
     inp = make_inputs(seed=10 + t, name=f"tiny_f32_t{t}", new_tokens=("const", t), **r)
     _check(inp, f"f32 t={t}")
     _check(inp, f"f32 t={t} P=32", partition_size=32)
+    _check(inp, f"f32 t={t} balanced", partition_size=BAL)
 
 
 @pytest.mark.parametrize("t", [1, 2, 4, 5, 8, 16])
@@ -66,7 +70,7 @@ def test_fixed_new_tokens_gqa_bf16(t):
     hold 4 new tokens, so t=5 leaves a ragged tile."""
     inp = named_config(2, seed=20 + t, num_seqs=6, ctx=("uniform", 16, 1400),
                        new_tokens=("const", t), name=f"gqa_bf16_t{t}")
-    _check(inp, f"gqa bf16 t={t}")
+    _check(inp, f"gqa bf16 t={t} balanced (the workload's default)")
     _check(inp, f"gqa bf16 t={t} P=64", partition_size=64)
 
 
@@ -86,6 +90,7 @@ def test_group_and_dtype_mix(group, head_dim, dtypes):
                       kv_dtype=kd, partition_size=128, seed=30 + group,
                       new_tokens=("uniform", 1, 9), name=f"g{group}_d{head_dim}_{qd}_{kd}")
     _check(inp, inp.name)
+    _check(inp, inp.name + " balanced", partition_size=BAL)
 
 
 def test_ragged_new_tokens_and_empty_sequences():
@@ -97,6 +102,7 @@ def test_ragged_new_tokens_and_empty_sequences():
     assert inp.total_queries == 60
     _check(inp, "ragged bf16 P=512")
     _check(inp, "ragged bf16 P=32", partition_size=32)
+    _check(inp, "ragged bf16 balanced", partition_size=BAL)
     r.update(q_dtype="f32", kv_dtype="f32")
     _check(make_inputs(seed=41, name="ragged_f32", **r), "ragged f32", partition_size=48)
 
@@ -120,6 +126,8 @@ def test_rows_that_see_nothing():
     inp.context_lens[2] = 5
     _, gpu, ref = _check(inp, "ctx < t")
     assert np.all(gpu[0:3] == 0) and np.all(ref[0:3] == 0)
+    _, gpu, ref = _check(inp, "ctx < t balanced", partition_size=BAL)
+    assert np.all(gpu[0:3] == 0)
 
 
 def test_one_token_matches_decode_entry_point():

@@ -64,8 +64,8 @@ CONFIG_NAMES = {
 # ``partition_size`` is the one-token decode's default split: 512 tokens where
 # the workload names it (the long-context one) or where one partition holds
 # every sequence, else -1, the balanced split (chunks of nearly equal size
-# chosen from the context lengths); calls with several new tokens per
-# sequence take 512 in its place.
+# chosen from the context lengths), for one new token per sequence or
+# several.
 _RECIPES = {
     1: dict(num_seqs=4, num_q_heads=4, num_kv_heads=4, head_dim=64,
             ctx=("fixed", [17, 33, 64, 100]), pool=("blocks", 64),
