@@ -187,9 +187,10 @@ def main():
             c["parts"] = torch.empty(slots * Hq * (D + 1) * 4 + 512, dtype=torch.uint8, device=dev)
             lse_off = ((slots * Hq * D * 4 + 255) // 256) * 256
             prt = (V(c["parts"].data_ptr()), V(c["parts"].data_ptr() + lse_off), ptr(c["plan"]),
-                   slots, ptr(c["q"]), ptr(c["k_pool"]), ptr(c["v_pool"]), ptr(c["k_scales"]),
-                   ptr(c["v_scales"]), ptr(c["tables"]), ptr(c["lens"]), B, Hq, Hkv, D, 16, NB, MB,
-                   ctypes.c_float(inp.softmax_scale), qcode, kvcode, sp)
+                   ctypes.c_size_t(c["plan"].numel()), slots, ptr(c["q"]), ptr(c["k_pool"]),
+                   ptr(c["v_pool"]), ptr(c["k_scales"]), ptr(c["v_scales"]), ptr(c["tables"]),
+                   ptr(c["lens"]), B, Hq, Hkv, D, 16, NB, MB, ctypes.c_float(inp.softmax_scale),
+                   qcode, kvcode, sp)
             maxp = slots
         else:
             maxp = max(1, -(-mcl // P)) if P else 1

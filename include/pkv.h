@@ -302,8 +302,8 @@ pkv_status_t pkv_merge_partials(void* out, const float* partial_out, const float
  * writes the normalised partial output over the chunk's tokens to
  * partial_out[s][i][:] and its natural-log log-sum-exp to partial_lse[s][i]
  * (-inf for an empty sequence's one chunk); slots past the last chunk are not
- * written.  plan [device, written, pkv_decode_plan_bytes bytes] receives
- * chunk_first (and, for more than 256 sequences, slot_info: batches up to
+ * written.  plan [device, written; plan_bytes >= pkv_decode_plan_bytes(
+ * num_seqs, num_slots), else PKV_ERR_WORKSPACE] receives chunk_first (and, for more than 256 sequences, slot_info: batches up to
  * that size are scheduled inside the decode kernel itself, larger ones by a
  * separate plan kernel first).  partial_out float32 [num_slots, num_q_heads,
  * head_dim], partial_lse float32 [num_slots, num_q_heads] [device, written];
@@ -321,7 +321,8 @@ pkv_status_t pkv_decode_plan(void* plan, size_t plan_bytes, const int32_t* conte
                              int32_t num_seqs, int32_t num_slots, int32_t block_size,
                              int32_t max_blocks_per_seq, void* stream);
 pkv_status_t pkv_paged_decode_partials_planned(
-    float* partial_out, float* partial_lse, void* plan, int32_t num_slots, const void* q,
+    float* partial_out, float* partial_lse, void* plan, size_t plan_bytes, int32_t num_slots,
+    const void* q,
     const void* k_pool, const void* v_pool, const float* k_scales, const float* v_scales,
     const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
     int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,

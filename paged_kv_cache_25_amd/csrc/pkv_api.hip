@@ -975,7 +975,8 @@ pkv_status_t pkv_decode_plan(void* plan, size_t plan_bytes, const int32_t* conte
 }
 
 pkv_status_t pkv_paged_decode_partials_planned(
-    float* partial_out, float* partial_lse, void* plan, int32_t num_slots, const void* q,
+    float* partial_out, float* partial_lse, void* plan, size_t plan_bytes, int32_t num_slots,
+    const void* q,
     const void* k_pool, const void* v_pool, const float* k_scales, const float* v_scales,
     const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
     int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
@@ -991,6 +992,7 @@ pkv_status_t pkv_paged_decode_partials_planned(
       !aligned4(partial_lse))
     return PKV_ERR_INVALID_ARG;
   if (int64_t(max_blocks_per_seq) * block_size > 0x7fffffff) return PKV_ERR_INVALID_ARG;
+  if (plan_bytes < plan_layout(num_seqs, num_slots).total) return PKV_ERR_WORKSPACE;
   const DecodeKind k = decode_kind(num_q_heads, num_kv_heads, head_dim, q_dtype, kv_dtype);
   pkv::DecodeArgs a = decode_args(q, k_pool, v_pool, k_scales, v_scales, block_tables,
                                   context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim,

@@ -68,8 +68,8 @@ def load():
     L.pkv_decode_plan.restype = ctypes.c_int
     L.pkv_decode_plan.argtypes = [P, Z, P, I, I, I, I, P]
     L.pkv_paged_decode_partials_planned.restype = ctypes.c_int
-    L.pkv_paged_decode_partials_planned.argtypes = [P, P, P, I, P, P, P, P, P, P, P, I, I, I, I,
-                                                    I, I, I, F, ctypes.c_int, ctypes.c_int, P]
+    L.pkv_paged_decode_partials_planned.argtypes = [P, P, P, Z, I, P, P, P, P, P, P, P, I, I, I,
+                                                    I, I, I, I, F, ctypes.c_int, ctypes.c_int, P]
     L.pkv_merge_partials_planned.restype = ctypes.c_int
     L.pkv_merge_partials_planned.argtypes = [P, P, P, P, I, I, I, I, ctypes.c_int, P]
     L.pkv_kv_append_tokens.restype = ctypes.c_int
@@ -268,7 +268,8 @@ def paged_decode_partials_planned(partial_out, partial_lse, plan, q, k_pool, v_p
     B, hq, d = q.shape
     nb, hkv, bs, _ = k_pool.shape
     _check("pkv_paged_decode_partials_planned", load().pkv_paged_decode_partials_planned(
-        _ptr(partial_out), _ptr(partial_lse), _ptr(plan), partial_out.shape[0], _ptr(q),
+        _ptr(partial_out), _ptr(partial_lse), _ptr(plan), plan.numel() * plan.element_size(),
+        partial_out.shape[0], _ptr(q),
         _ptr(k_pool), _ptr(v_pool), _ptr(k_scales), _ptr(v_scales), _ptr(block_tables),
         _ptr(context_lens), B, hq, hkv, d, bs, nb, block_tables.shape[1], float(softmax_scale),
         dtype_code(q.dtype), dtype_code(k_pool.dtype), _stream(stream)))

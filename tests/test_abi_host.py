@@ -468,15 +468,17 @@ def test_decode_plan_validation(lib):
     assert f(FAKE, need, ctypes.c_void_p(0x10002), 2, 384, 16, 4, None) == INVALID
     assert f(FAKE, lib.pkv_decode_plan_bytes(0, 384), None, 0, 384, 16, 4, None) == OK
     g = lib.pkv_paged_decode_partials_planned
-    args = [FAKE, FAKE, FAKE, 384, FAKE, FAKE, FAKE, None, None, FAKE, FAKE, 2, 8, 2, 128, 16, 8,
-            4, 0.088, ops.PKV_BF16, ops.PKV_BF16, None]
-    for i, bad in [(0, None), (1, None), (2, None), (2, ctypes.c_void_p(0x10008)), (3, 1),
-                   (3, 0), (4, None), (12, 7), (14, 96), (15, 32), (18, float("nan")),
-                   (20, ops.PKV_FP8_E4M3)]:
+    args = [FAKE, FAKE, FAKE, need, 384, FAKE, FAKE, FAKE, None, None, FAKE, FAKE, 2, 8, 2, 128, 16,
+            8, 4, 0.088, ops.PKV_BF16, ops.PKV_BF16, None]
+    for i, bad in [(0, None), (1, None), (2, None), (2, ctypes.c_void_p(0x10008)), (4, 1),
+                   (4, 0), (5, None), (13, 7), (15, 96), (16, 32), (19, float("nan")),
+                   (21, ops.PKV_FP8_E4M3)]:
         a = list(args)
         a[i] = bad
         assert g(*a) in (INVALID, UNSUPPORTED), i
-    a = list(args); a[11] = 0; a[4] = None
+    a = list(args); a[3] = need - 1
+    assert g(*a) == WORKSPACE                                     # plan buffer too small
+    a = list(args); a[12] = 0; a[5] = None
     assert g(*a) == OK
     m = lib.pkv_merge_partials_planned
     margs = [FAKE, FAKE, FAKE, FAKE, 384, 2, 8, 128, ops.PKV_BF16, None]
