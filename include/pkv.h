@@ -45,8 +45,10 @@
  * each sequence are in [0, num_blocks).  The kernels never read or write
  * outside the buffers described here even when it is violated: a table entry
  * outside [0, num_blocks) is treated as an empty block, ctx is clamped to
- * the table's capacity, and tokens past max_context_len are ignored.  Results
- * are then unspecified, but no fault follows.
+ * the table's capacity, and tokens past max_context_len are ignored (fixed
+ * partitions; the balanced split sizes nothing by max_context_len and attends
+ * up to the clamped ctx).  Results are then unspecified, but no fault
+ * follows.
  *
  * Errors are returned as pkv_status_t; nothing is launched when a call
  * returns anything but PKV_OK, except PKV_ERR_HIP (a launch failed).
@@ -303,11 +305,12 @@ pkv_status_t pkv_merge_partials(void* out, const float* partial_out, const float
  * partial_out[s][i][:] and its natural-log log-sum-exp to partial_lse[s][i]
  * (-inf for an empty sequence's one chunk); slots past the last chunk are not
  * written.  plan [device, written; plan_bytes >= pkv_decode_plan_bytes(
- * num_seqs, num_slots), else PKV_ERR_WORKSPACE] receives chunk_first (and, for more than 256 sequences, slot_info: batches up to
- * that size are scheduled inside the decode kernel itself, larger ones by a
- * separate plan kernel first).  partial_out float32 [num_slots, num_q_heads,
- * head_dim], partial_lse float32 [num_slots, num_q_heads] [device, written];
- * the rest as for pkv_paged_decode_partials.
+ * num_seqs, num_slots), else PKV_ERR_WORKSPACE] receives chunk_first (and,
+ * for more than 256 sequences or 46,340 slots, slot_info: smaller batches are
+ * scheduled inside the decode kernel itself, larger ones by a separate plan
+ * kernel first).  partial_out float32 [num_slots, num_q_heads, head_dim],
+ * partial_lse float32 [num_slots, num_q_heads] [device, written]; the rest as
+ * for pkv_paged_decode_partials.
  *
  * pkv_merge_partials_planned - out[b][i][:] = the log-sum-exp merge (as
  * pkv_merge_partials) of rows chunk_first[b] .. chunk_first[b+1]-1 of
@@ -322,8 +325,8 @@ pkv_status_t pkv_decode_plan(void* plan, size_t plan_bytes, const int32_t* conte
                              int32_t max_blocks_per_seq, void* stream);
 pkv_status_t pkv_paged_decode_partials_planned(
     float* partial_out, float* partial_lse, void* plan, size_t plan_bytes, int32_t num_slots,
-    const void* q,
-    const void* k_pool, const void* v_pool, const float* k_scales, const float* v_scales,
+    const void* q, const void* k_pool, const void* v_pool, const float* k_scales,
+    const float* v_scales,
     const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
     int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
     int32_t num_blocks, int32_t max_blocks_per_seq, float softmax_scale, pkv_dtype_t q_dtype,
