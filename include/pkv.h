@@ -129,8 +129,9 @@ pkv_status_t pkv_kv_append(void* k_pool, void* v_pool, const void* k_new, const 
  * than 64 heads, 512 otherwise, and R = max(S, num_seqs).  The schedule is
  * computed on the device from context_lens (no host copy, so a call stays
  * capturable in a graph): for up to 256 sequences each decode workgroup
- * derives it itself, otherwise a one-wave kernel runs first.  The chunks are run and merged; a sequence with one chunk is written
- * directly.  The result equals a fixed-partition split's up to float
+ * derives it itself, otherwise a one-wave kernel runs first.  The chunks are
+ * run and merged; a sequence with one chunk is written directly.  The result
+ * equals a fixed-partition split's up to float
  * rounding: only the grouping of the partial sums changes (the log-sum-exp
  * merge combines any split of the tokens).  Intended for batches of uneven or
  * long contexts, where a fixed partition size leaves the kernel waiting for
