@@ -236,6 +236,47 @@ def test_planned_partials_with_many_slots():
                     "planned, 50000 slots", out_dtype="bf16")
 
 
+@pytest.mark.parametrize("B,kind,slot_mult,q,kv", [
+    (1, "uniform", 1, "bf16", "bf16"), (7, "mixed", 3, "f32", "f32"),
+    (64, "lognormal", 1, "bf16", "bf16"), (100, "short", 2, "bf16", "bf16"),
+    (255, "uniform", 1, "f32", "bf16"), (256, "lognormal", 4, "bf16", "bf16")])
+def test_in_kernel_plan_random_batches(B, kind, slot_mult, q, kv):
+    """The schedule each decode workgroup derives for itself (up to 256
+    sequences), on random batches and slot counts: the chunk starts it
+    publishes equal the definition bit for bit, and merging its chunks gives
+    the oracle's attention (a wrong chunk range would drop or repeat tokens)."""
+    rng = np.random.default_rng(1000 + B)
+    lens = {"uniform": lambda: rng.integers(1, 3000, B),
+            "mixed": lambda: np.where(rng.random(B) < 0.5, rng.integers(0, 20, B),
+                                      rng.integers(500, 4000, B)),
+            "lognormal": lambda: np.clip(np.exp(rng.normal(np.log(400), 1.2, B)), 0, 6000),
+            "short": lambda: rng.integers(0, 40, B)}[kind]().astype(np.int64)
+    inp = make_inputs(num_seqs=B, num_q_heads=2, num_kv_heads=1, head_dim=64,
+                      ctx=("fixed", lens.tolist()), pool=("used_fraction", 0.95), q_dtype=q,
+                      kv_dtype=kv, seed=2000 + B)
+    slots = max(1, slot_mult * ops.decode_plan_slots(B, 2, 1, 64, TORCH_DT[q], TORCH_DT[kv]) // 2)
+    slots = max(slots, B)
+    log(f"[case] in-kernel plan: B={B} {kind} slots={slots} {q}/{kv}")
+    d = DeviceStep(inp)
+    d.append()
+    plan = torch.full((ops.load().pkv_decode_plan_bytes(B, slots),), 0xFF, dtype=torch.uint8,
+                      device="cuda")
+    po = torch.empty((slots, 2, 64), device="cuda")
+    pl = torch.empty((slots, 2), device="cuda")
+    ops.paged_decode_partials_planned(po, pl, plan, d.q, d.k_pool, d.v_pool, d.tables, d.lens,
+                                      inp.softmax_scale)
+    merged = torch.empty_like(d.q)
+    ops.merge_partials_planned(merged, po, pl, plan)
+    torch.cuda.synchronize()
+    first, _ = expected_plan(inp.context_lens, slots, inp.max_blocks_per_seq)
+    got_first = host_storage(plan)[:4 * (B + 1)].view(np.int32)
+    assert np.array_equal(got_first, first)
+    kp, vp = pa.kv_append(inp.k_pool, inp.v_pool, inp.k_new, inp.v_new, inp.block_tables,
+                          inp.context_lens, inp.block_size)
+    check_tolerance(kv, merged.float().cpu().double().numpy(), oracle_out(inp, pools=(kp, vp)),
+                    f"in-kernel plan B={B}", out_dtype=q)
+
+
 def test_deterministic_and_equal_to_split_math():
     """Two calls give the same bits; the result agrees with the fixed
     512-token split within float rounding (only the grouping differs)."""
