@@ -277,6 +277,33 @@ def test_in_kernel_plan_random_batches(B, kind, slot_mult, q, kv):
                     f"in-kernel plan B={B}", out_dtype=q)
 
 
+def test_huge_table_takes_the_integer_division():
+    """A table row of 2^22 + 5 entries whose context fills it (67M tokens)
+    makes the in-kernel planner divide in integers (its float-reciprocal
+    quotient is exact only below 2^22 blocks) and sum block counts past 16
+    bits.  Only the first three entries are valid; the rest are outside the
+    pool, i.e. empty blocks, so the result is attention over 48 tokens."""
+    inp = make_inputs(num_seqs=1, num_q_heads=2, num_kv_heads=1, head_dim=64,
+                      ctx=("fixed", [48]), pool=("used_fraction", 1.0), q_dtype="bf16",
+                      kv_dtype="bf16", seed=98)
+    d = DeviceStep(inp)
+    d.append()                                              # position 47 gets its row
+    mb = (1 << 22) + 5
+    table = np.full((1, mb), -1, np.int32)
+    table[0, :3] = inp.block_tables[0, :3]
+    d.tables = torch.from_numpy(table).cuda()
+    d.lens = torch.tensor([mb * 16], dtype=torch.int32, device="cuda")
+    log(f"[case] huge table: {mb} entries, ctx {mb * 16}")
+    ws = ops.alloc_workspace(1, 2, 64, mb * 16, BAL, "cuda")
+    ops.paged_decode_attention(d.out, d.q, d.k_pool, d.v_pool, d.tables, d.lens, mb * 16,
+                               inp.softmax_scale, BAL, workspace=ws)
+    torch.cuda.synchronize()
+    kp, vp = pa.kv_append(inp.k_pool, inp.v_pool, inp.k_new, inp.v_new, inp.block_tables,
+                          inp.context_lens, inp.block_size)
+    check_tolerance("bf16", d.out_f64(), oracle_out(inp, pools=(kp, vp)), "huge table",
+                    out_dtype="bf16")
+
+
 def test_deterministic_and_equal_to_split_math():
     """Two calls give the same bits; the result agrees with the fixed
     512-token split within float rounding (only the grouping differs)."""
