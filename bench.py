@@ -20,7 +20,10 @@ for the balanced split (partition size -1, the default of the batch-64, mix and
 fp8 workloads), ``pkv_paged_decode_partials_planned`` on a schedule made
 beforehand, against the 8 TB/s HBM peak.
 ``cpu_baseline`` times the float64 CPU oracle on a bounded sample of the same
-workload.
+workload.  ``attainable`` is the read rate measured live by
+``pkv_stream_read`` (a kernel that only reads a 2 GiB buffer) and the
+roofline kernel's rate as a fraction of it: the practical ceiling, below the
+data-sheet peak.
 """
 
 from __future__ import annotations
@@ -318,6 +321,7 @@ def main():
                                      "copy-calibrated)",
                      "algorithmic_bytes_per_launch": tr["kv_bytes"]},
         "cpu_baseline": cpu,
+        "attainable": attainable_entry(ops, stream, kernel_gbps),
         "input_copies": n_copies,
     }
     print(json.dumps(result), flush=True)
@@ -359,6 +363,41 @@ def event_timer(stream):
         torch.cuda.synchronize()
         return a.elapsed_time(b) / reps
     return timed
+
+
+STREAM_READ_BYTES = 2 * 2 ** 30
+STREAM_READ_GRIDS = (1024, 2048, 4096, 8192, 16384)
+
+
+def attainable_read(ops, stream, reps=20):
+    """The measured read ceiling: pkv_stream_read over a 2 GiB buffer (8x the
+    last-level cache), the best of a few grid sizes, timed with HIP events on
+    ``stream``; returns (GB/s, workgroups)."""
+    import torch
+    buf = torch.arange(STREAM_READ_BYTES // 4, dtype=torch.int32, device="cuda")
+    out = torch.empty(int(ops.load().pkv_stream_read_out_words(max(STREAM_READ_GRIDS))),
+                      dtype=torch.int32, device="cuda")
+    timed = event_timer(stream)
+    best = (0.0, 0)
+    for g in STREAM_READ_GRIDS:
+        run = lambda i, g=g: ops.stream_read(buf, g, out=out, stream=stream)
+        for i in range(3):
+            run(i)
+        ms = min(timed(run, reps) for _ in range(2))
+        best = max(best, (STREAM_READ_BYTES / (ms * 1e-3) / 1e9, g))
+    del buf, out
+    torch.cuda.empty_cache()
+    return best
+
+
+def attainable_entry(ops, stream, kernel_gbps):
+    """The ``attainable`` object of the JSON line: the read ceiling and the
+    roofline kernel's rate as a fraction of it."""
+    gbps, grid = attainable_read(ops, stream)
+    print(f"[bench] stream read: {gbps:.1f} GB/s ({grid} workgroups)", file=sys.stderr, flush=True)
+    return {"kernel": "stream_read_kernel", "bytes": STREAM_READ_BYTES, "workgroups": grid,
+            "read_gbps": round(gbps, 1), "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4),
+            "roofline_kernel_frac_of_attainable": round(kernel_gbps / gbps, 4)}
 
 
 def main_multi(args):
@@ -514,6 +553,7 @@ def main_multi(args):
                      "traffic": None, "algorithmic_bytes_per_launch": tr["kv_bytes"],
                      "flops_per_launch": tr["flops"]},
         "cpu_baseline": cpu,
+        "attainable": attainable_entry(ops, stream, kernel_gbps),
         "input_copies": n_copies,
     }
     print(json.dumps(result), flush=True)

@@ -603,6 +603,32 @@ pkv_status_t pkv_copy_blocks(void* k_pool, void* v_pool, float* k_scales, float*
                              pkv_dtype_t kv_dtype, void* stream);
 
 /*
+ * Measurement: attainable read bandwidth
+ * --------------------------------------
+ * A decode step is left of the ridge point, where memory bandwidth is the
+ * only roof (brunomaga inference post, "Roofline model"); what a kernel can
+ * reach in practice is below the data-sheet peak.  pkv_stream_read does
+ * nothing but read, so its rate over a buffer far larger than the last-level
+ * cache is the practical read ceiling against which a decode kernel's rate
+ * is judged.  Not part of the attention path.
+ */
+#define PKV_STREAM_READ_MAX_WORKGROUPS (1 << 20)
+
+/* pkv_stream_read - read bytes of src [device, read; 16-byte aligned; bytes
+ * a multiple of 16, may be 0] once, with 16-byte nontemporal loads, in
+ * num_workgroups workgroups of 256 threads (1 .. PKV_STREAM_READ_MAX_WORKGROUPS)
+ * striding over the buffer, and fold every 32-bit word read with XOR: out
+ * uint32 [pkv_stream_read_out_words(num_workgroups)] [device, written] gets
+ * one fold per wave, and the XOR of all of out is the XOR of all 32-bit
+ * words of src.  PKV_ERR_INVALID_ARG for a bad count, size or pointer. */
+pkv_status_t pkv_stream_read(uint32_t* out, const void* src, size_t bytes,
+                             int32_t num_workgroups, void* stream);
+
+/* Words pkv_stream_read writes for num_workgroups workgroups (one per wave);
+ * 0 for a count outside 1 .. PKV_STREAM_READ_MAX_WORKGROUPS. */
+int32_t pkv_stream_read_out_words(int32_t num_workgroups);
+
+/*
  * Multi-head latent attention (MLA), absorbed decode
  * --------------------------------------------------
  * An MLA layer caches one row per token: the latent c (kv_lora_rank = 512

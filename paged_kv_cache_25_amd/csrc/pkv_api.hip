@@ -7,6 +7,7 @@
 #include <stdint.h>
 
 #include "pkv_launch.h"
+#include "stream_read.h"
 
 namespace {
 
@@ -288,6 +289,23 @@ pkv_status_t pkv_copy_blocks(void* k_pool, void* v_pool, float* k_scales, float*
   return pkv::launch_copy_blocks(a, static_cast<hipStream_t>(stream)) == hipSuccess
              ? PKV_OK
              : PKV_ERR_HIP;
+}
+
+pkv_status_t pkv_stream_read(uint32_t* out, const void* src, size_t bytes,
+                             int32_t num_workgroups, void* stream) {
+  if (num_workgroups <= 0 || num_workgroups > PKV_STREAM_READ_MAX_WORKGROUPS || bytes % 16 != 0)
+    return PKV_ERR_INVALID_ARG;
+  if (!out || !aligned4(out) || (bytes > 0 && (!src || !aligned16(src))))
+    return PKV_ERR_INVALID_ARG;
+  return pkv::launch_stream_read(out, src, bytes, num_workgroups,
+                                 static_cast<hipStream_t>(stream)) == hipSuccess
+             ? PKV_OK
+             : PKV_ERR_HIP;
+}
+
+int32_t pkv_stream_read_out_words(int32_t num_workgroups) {
+  if (num_workgroups <= 0 || num_workgroups > PKV_STREAM_READ_MAX_WORKGROUPS) return 0;
+  return num_workgroups * pkv::stream_read_waves_per_workgroup();
 }
 
 size_t pkv_mla_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t kv_lora_rank,

@@ -114,6 +114,10 @@ def load():
     L.pkv_bm_block_tables.argtypes = [P, P, I, P, I, P]
     L.pkv_copy_blocks.restype = ctypes.c_int
     L.pkv_copy_blocks.argtypes = [P, P, P, P, P, I, I, I, I, I, ctypes.c_int, P]
+    L.pkv_stream_read.restype = ctypes.c_int
+    L.pkv_stream_read.argtypes = [P, P, Z, I, P]
+    L.pkv_stream_read_out_words.restype = I
+    L.pkv_stream_read_out_words.argtypes = [I]
     L.pkv_mla_append.restype = ctypes.c_int
     L.pkv_mla_append.argtypes = [P, P, P, P, I, I, I, I, I, P]
     L.pkv_mla_workspace_bytes.restype = Z
@@ -481,6 +485,23 @@ def copy_blocks(k_pool, v_pool, pairs, k_scales=None, v_scales=None, stream=None
         _ptr(k_pool), _ptr(v_pool), _ptr(k_scales), _ptr(v_scales), _ptr(pairs),
         pairs.shape[0] if pairs.numel() else 0, nb, hkv, d, bs, dtype_code(k_pool.dtype),
         _stream(stream)))
+
+
+def stream_read(src, num_workgroups, out=None, stream=None):
+    """Read every byte of src once (pkv_stream_read, a bandwidth measurement);
+    returns out, int32 [pkv_stream_read_out_words(num_workgroups)], whose XOR
+    is the XOR of src's 32-bit words."""
+    _need_cuda(src, out)
+    words = int(load().pkv_stream_read_out_words(num_workgroups))
+    if words == 0:
+        raise ValueError(f"num_workgroups {num_workgroups} out of range")
+    if out is None:
+        out = torch.empty(words, dtype=torch.int32, device=src.device)
+    elif out.numel() < words:
+        raise ValueError(f"out holds {out.numel()} words, {words} needed")
+    _check("pkv_stream_read", load().pkv_stream_read(
+        _ptr(out), _ptr(src), src.numel() * src.element_size(), num_workgroups, _stream(stream)))
+    return out
 
 
 def mla_append(latent_pool, latent_new, block_tables, context_lens, stream=None):

@@ -42,7 +42,8 @@ def test_header_declares_the_entry_points():
         "pkv_copy_blocks", "pkv_mla_append", "pkv_mla_workspace_bytes",
         "pkv_mla_decode_attention", "pkv_mla_decode_partials", "pkv_decode_plan_slots",
         "pkv_decode_plan_bytes", "pkv_decode_plan", "pkv_paged_decode_partials_planned",
-        "pkv_merge_partials_planned", "pkv_multi_query_balanced_workspace_bytes"])
+        "pkv_merge_partials_planned", "pkv_multi_query_balanced_workspace_bytes",
+        "pkv_stream_read", "pkv_stream_read_out_words"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -312,6 +313,22 @@ def test_copy_blocks_validation(lib):
     assert _copy(lib, d=96) == UNSUPPORTED
     assert _copy(lib, hkv=300) == UNSUPPORTED
     assert _copy(lib, n=0, kp=None, pairs=None) == OK
+
+
+def test_stream_read_validation(lib):
+    big = 1 << 20                                                   # the header's maximum
+    assert lib.pkv_stream_read_out_words(1) == 4                    # one word per wave
+    assert lib.pkv_stream_read_out_words(big) == 4 * big
+    assert lib.pkv_stream_read_out_words(0) == 0
+    assert lib.pkv_stream_read_out_words(big + 1) == 0
+    read = lambda out, src, n, g: lib.pkv_stream_read(out, src, n, g, None)
+    assert read(FAKE, FAKE, 1024, 0) == INVALID
+    assert read(FAKE, FAKE, 1024, big + 1) == INVALID
+    assert read(FAKE, FAKE, 1000, 8) == INVALID                     # not a multiple of 16
+    assert read(None, FAKE, 1024, 8) == INVALID
+    assert read(ctypes.c_void_p(0x10002), FAKE, 1024, 8) == INVALID
+    assert read(FAKE, None, 1024, 8) == INVALID
+    assert read(FAKE, ctypes.c_void_p(0x10008), 1024, 8) == INVALID
 
 
 def _mla(lib, **over):

@@ -1,0 +1,43 @@
+"""pkv_stream_read, the read-bandwidth measurement kernel: it must read every
+byte of its buffer exactly once, whatever the size and grid.  The XOR of its
+per-wave folds has to equal the XOR of the buffer's 32-bit words (computed
+here with NumPy): a skipped, repeated or out-of-range load changes it, for
+these random buffers, with overwhelming probability.  Words past the ones it
+reports are left untouched."""
+
+import numpy as np
+import pytest
+import torch
+
+from paged_kv_cache_25_amd import ops
+from tests.gpu_util import log
+
+pytestmark = pytest.mark.gpu
+PASS = 256 * 8 * 16        # bytes one workgroup reads per pass
+SENTINEL = 0x5A5A5A5A
+
+
+@pytest.mark.parametrize("nbytes,grid", [
+    (0, 4), (16, 1), (48, 8), (PASS, 1), (PASS + 16, 1), (PASS - 16, 3),
+    (5 * PASS + 1232, 2), (5 * PASS + 1232, 64), (64 * 2 ** 20 + 208, 1000),
+    (256 * 2 ** 20, 4096)])
+def test_stream_read_folds_every_word(nbytes, grid):
+    log(f"[case] stream_read bytes={nbytes} grid={grid}")
+    rng = np.random.default_rng(nbytes % 9973 + grid)
+    host = rng.integers(0, 2 ** 32, size=nbytes // 4, dtype=np.uint32)
+    src = torch.from_numpy(host.view(np.int32)).cuda()
+    words = int(ops.load().pkv_stream_read_out_words(grid))
+    out = torch.full((words + 64,), SENTINEL, dtype=torch.int32, device="cuda")
+    ops.stream_read(src, grid, out=out)
+    got = out.cpu().numpy().view(np.uint32)
+    want = np.bitwise_xor.reduce(host) if host.size else np.uint32(0)
+    assert np.bitwise_xor.reduce(got[:words]) == want
+    assert (got[words:] == SENTINEL).all()
+
+
+def test_stream_read_rejects_bad_arguments():
+    src = torch.zeros(1024, dtype=torch.int32, device="cuda")
+    with pytest.raises(ops.PkvError):
+        ops.stream_read(src[:-1], 8)                      # 4092 bytes: not a multiple of 16
+    with pytest.raises(ValueError):
+        ops.stream_read(src, 0)
