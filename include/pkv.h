@@ -657,9 +657,10 @@ pkv_status_t pkv_mla_append(void* latent_pool, const void* latent_new,
 
 /* Workspace of pkv_mla_decode_attention: float32 o [num_seqs, num_heads,
  * maxP, kv_lora_rank] then, 256-byte aligned, float32 lse [num_seqs,
- * num_heads, maxP]; 0 when maxP <= 1.  With PKV_PARTITION_BALANCED: float32
- * o [R, num_heads, kv_lora_rank], float32 lse [R, num_heads] and int32
- * chunk starts [num_seqs + 1], each 256-byte aligned, R = max(S, num_seqs)
+ * num_heads, maxP]; 0 when maxP <= 1.  With PKV_PARTITION_BALANCED: o [R,
+ * num_heads, kv_lora_rank] as bf16 (round to nearest even, in a region sized
+ * for float32), float32 lse [R, num_heads] and int32 chunk starts
+ * [num_seqs + 1], each 256-byte aligned, R = max(S, num_seqs)
  * (see PKV_PARTITION_BALANCED); max_context_len is not used.  0 for invalid
  * arguments. */
 size_t pkv_mla_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t kv_lora_rank,

@@ -20,7 +20,7 @@ namespace {
 
 constexpr int kThreads = 256;
 
-template <int D, typename OT>
+template <int D, typename OT, bool kBf16Part>
 __global__ __launch_bounds__(kThreads) void merge_kernel(MergeArgs a) {
   constexpr int kRowThreads = D / 4;              // float4 per thread covers one partition row
   constexpr int kMaxGroups = kThreads / kRowThreads;
@@ -72,9 +72,18 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(MergeArgs a) {
                                     : row * a.max_partitions;
   const size_t stride = a.chunk_first ? size_t(slot_rows) * a.num_q_heads : 1;
   const float* lse_base = a.part_lse + base;
-  const float* o_base = a.part_o + base * D + 4 * c;
+  const size_t o_off = base * D + 4 * c;                  // elements, float32 or bf16
   auto lse_at = [&](int p) { return lse_base[size_t(p) * stride]; };
-  auto row_at = [&](int p) { return *reinterpret_cast<const float4*>(o_base + size_t(p) * stride * D); };
+  auto row_at = [&](int p) {
+    if constexpr (kBf16Part) {
+      const uint2 w = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(a.part_o) +
+                                                      o_off + size_t(p) * stride * D);
+      return make_float4(__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u),
+                         __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xffff0000u));
+    } else {
+      return *reinterpret_cast<const float4*>(a.part_o + o_off + size_t(p) * stride * D);
+    }
+  };
 
   // First batch of rows and their lse, issued together with the max pass.
   float4 rowv[kUnroll];
@@ -147,7 +156,7 @@ struct OutBF16 {
   }
 };
 
-template <int D>
+template <int D, bool kBf16Part = false>
 hipError_t launch_d(const MergeArgs& a, DType out_dtype, hipStream_t stream) {
   const size_t grid = size_t(a.num_seqs) * a.num_q_heads;
   if (grid == 0) return hipSuccess;
@@ -162,15 +171,21 @@ hipError_t launch_d(const MergeArgs& a, DType out_dtype, hipStream_t stream) {
   int threads = (one_batch || grid >= 4096) ? kWave : kThreads;
   threads = threads < D / 4 ? D / 4 : threads;   // one row group reads a whole row
   if (out_dtype == DType::F32)
-    hipLaunchKernelGGL((merge_kernel<D, OutF32>), dim3(unsigned(grid)), dim3(threads), 0, stream, a);
+    hipLaunchKernelGGL((merge_kernel<D, OutF32, kBf16Part>), dim3(unsigned(grid)), dim3(threads), 0,
+                       stream, a);
   else
-    hipLaunchKernelGGL((merge_kernel<D, OutBF16>), dim3(unsigned(grid)), dim3(threads), 0, stream, a);
+    hipLaunchKernelGGL((merge_kernel<D, OutBF16, kBf16Part>), dim3(unsigned(grid)), dim3(threads), 0,
+                       stream, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_merge(const MergeArgs& a, int head_dim, DType out_dtype, hipStream_t stream) {
+  if (a.part_bf16) {                              // bf16 partial rows: MLA latent rows only
+    if (head_dim != 512) return hipErrorInvalidValue;
+    return launch_d<512, true>(a, out_dtype, stream);
+  }
   if (head_dim == 64) return launch_d<64>(a, out_dtype, stream);
   if (head_dim == 512) return launch_d<512>(a, out_dtype, stream);   // MLA latent rows
   return launch_d<128>(a, out_dtype, stream);

@@ -409,9 +409,15 @@ __global__ __launch_bounds__(WAVES * kWave) void mla_decode_kernel(MlaArgs a) {
       for (int t = 0; t < kTiles; ++t) orow[16 * t] = f32_to_bf16_rne(o[t][i] * inv);
     } else {
       const size_t prow = slot_row + size_t(head) * slot_stride;
-      float* op = a.part_o + prow * kDc + c;
+      if (a.part_bf16) {                                 // uniform
+        uint16_t* op = reinterpret_cast<uint16_t*>(a.part_o) + prow * kDc + c;
 #pragma unroll
-      for (int t = 0; t < kTiles; ++t) op[16 * t] = o[t][i] * inv;
+        for (int t = 0; t < kTiles; ++t) op[16 * t] = f32_to_bf16_rne(o[t][i] * inv);
+      } else {
+        float* op = a.part_o + prow * kDc + c;
+#pragma unroll
+        for (int t = 0; t < kTiles; ++t) op[16 * t] = o[t][i] * inv;
+      }
       if (c == 0)
         a.part_lse[prow] = empty ? -INFINITY : (m_row[i] + __builtin_amdgcn_logf(l_row[i])) * kLn2;
     }

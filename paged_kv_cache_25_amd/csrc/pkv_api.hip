@@ -410,11 +410,16 @@ pkv_status_t pkv_mla_decode_attention(
     a.max_partitions = int(L.slots);
     a.scale_log2 = softmax_scale * pkv::kLog2eHost;
     if (plan_inside) a.plan_first = first; else a.chunk_first = first;
+    // The chunks' partial rows go through the workspace as bf16: the merge
+    // reads half the bytes (they are as large as a sizeable share of the
+    // latent rows read), at the cost of one more rounding of each partial.
+    a.part_bf16 = 1;
     if (pkv::launch_mla_decode(a, st) != hipSuccess) return PKV_ERR_HIP;
     pkv::MergeArgs m{};
     m.out = out;
     m.part_o = a.part_o;
     m.part_lse = a.part_lse;
+    m.part_bf16 = 1;
     m.num_seqs = num_seqs;
     m.num_q_heads = num_heads;
     m.max_partitions = int(L.slots);

@@ -80,6 +80,8 @@ struct MlaArgs {
   // kPlanMaxSeqs sequences) and the first chunk's workgroup writes
   // plan_first[b] (and plan_first[B]) for the merge.
   int32_t* plan_first;
+  // Partial rows of part_o stored as bf16 (RNE) instead of float32.
+  int part_bf16;
 };
 
 // The balanced split of a batch's work into at most max(budget, num_seqs)
@@ -374,6 +376,8 @@ struct MergeArgs {
   // (slot_rows: the most new tokens of a sequence; 0 or 1 for one each).
   const int32_t* chunk_first;
   int slot_rows;
+  // part_o holds bf16 rows (head_dim 512 only) instead of float32.
+  int part_bf16;
 };
 
 hipError_t launch_kv_append(const AppendArgs& a, hipStream_t stream);
