@@ -1,9 +1,10 @@
 // Log-sum-exp merge of split-KV partial results, for gfx950.
 //
 // One workgroup per (sequence, query head): one wave when every sequence's
-// partition rows fit in one batch or the batch is large, else 256 threads.  A row group of D/4
-// threads reads one partition row with float4 loads and keeps eight rows in
-// flight (64 rows per 256 threads for D=128); the
+// partition rows fit in one batch or the batch is large, else 256 threads.  A row group reads one
+// partition row with 16-byte loads (D/4 threads for float32 rows, D/8 for
+// the bf16 rows of the balanced MLA split) and keeps eight rows in flight
+// (four for bf16 rows; 64 rows per 256 threads for D=128); the
 // first batch is issued together with the pass that finds M = max lse over the
 // partitions that count.  Each group accumulates sum_p exp(lse_p - M) o_p over
 // its partitions, and the groups are summed in LDS and divided by the summed
@@ -20,12 +21,19 @@ namespace {
 
 constexpr int kThreads = 256;
 
+template <int N>
+struct VecF {
+  float v[N];
+};
+
 template <int D, typename OT, bool kBf16Part>
 __global__ __launch_bounds__(kThreads) void merge_kernel(MergeArgs a) {
-  constexpr int kRowThreads = D / 4;              // float4 per thread covers one partition row
+  constexpr int kVec = kBf16Part ? 8 : 4;         // 16 bytes of a row per thread and load
+  constexpr int kRowThreads = D / kVec;           // threads covering one partition row
   constexpr int kMaxGroups = kThreads / kRowThreads;
-  constexpr int kUnroll = 8;                      // rows in flight per row group
-  __shared__ float4 s_acc[kMaxGroups][kRowThreads];
+  constexpr int kUnroll = kBf16Part ? 4 : 8;      // rows in flight per row group
+  using Vec = VecF<kVec>;
+  __shared__ Vec s_acc[kMaxGroups][kRowThreads];
   __shared__ float s_w[kMaxGroups];
   __shared__ float s_max[kThreads / kWave];
   const int kGroups = blockDim.x / kRowThreads;   // row groups in this launch
@@ -72,27 +80,35 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(MergeArgs a) {
                                     : row * a.max_partitions;
   const size_t stride = a.chunk_first ? size_t(slot_rows) * a.num_q_heads : 1;
   const float* lse_base = a.part_lse + base;
-  const size_t o_off = base * D + 4 * c;                  // elements, float32 or bf16
+  const size_t o_off = base * D + size_t(kVec) * c;        // elements, float32 or bf16
   auto lse_at = [&](int p) { return lse_base[size_t(p) * stride]; };
   auto row_at = [&](int p) {
+    Vec r;
     if constexpr (kBf16Part) {
-      const uint2 w = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(a.part_o) +
+      const uint4 w = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.part_o) +
                                                       o_off + size_t(p) * stride * D);
-      return make_float4(__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u),
-                         __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xffff0000u));
+      const uint32_t x[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        r.v[2 * e] = __uint_as_float(x[e] << 16);
+        r.v[2 * e + 1] = __uint_as_float(x[e] & 0xffff0000u);
+      }
     } else {
-      return *reinterpret_cast<const float4*>(a.part_o + o_off + size_t(p) * stride * D);
+      const float4 f = *reinterpret_cast<const float4*>(a.part_o + o_off + size_t(p) * stride * D);
+      r.v[0] = f.x; r.v[1] = f.y; r.v[2] = f.z; r.v[3] = f.w;
     }
+    return r;
   };
+  const Vec zero = {};
 
   // First batch of rows and their lse, issued together with the max pass.
-  float4 rowv[kUnroll];
+  Vec rowv[kUnroll];
   float lp[kUnroll];
 #pragma unroll
   for (int u = 0; u < kUnroll; ++u) {
     const int p = g + u * kGroups;
     lp[u] = p < np ? lse_at(p) : -INFINITY;
-    rowv[u] = p < np ? row_at(p) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    rowv[u] = p < np ? row_at(p) : zero;
   }
   float M = -INFINITY;
   for (int p = t; p < np; p += blockDim.x) M = fmaxf(M, lse_at(p));
@@ -103,7 +119,7 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(MergeArgs a) {
   for (int w = 1; w < n_waves; ++w) M = fmaxf(M, s_max[w]);
 
   // Row group g takes partitions g, g + kGroups, ...; -inf partitions never count.
-  float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  Vec acc = zero;
   float wsum = 0.0f;
   if (M > -INFINITY) {
     for (int p0 = g;; ) {
@@ -112,10 +128,8 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(MergeArgs a) {
         if (lp[u] == -INFINITY) continue;
         const float w = __expf(lp[u] - M);
         wsum += w;
-        acc.x = fmaf(w, rowv[u].x, acc.x);
-        acc.y = fmaf(w, rowv[u].y, acc.y);
-        acc.z = fmaf(w, rowv[u].z, acc.z);
-        acc.w = fmaf(w, rowv[u].w, acc.w);
+#pragma unroll
+        for (int e = 0; e < kVec; ++e) acc.v[e] = fmaf(w, rowv[u].v[e], acc.v[e]);
       }
       p0 += kGroups * kUnroll;
       if (p0 >= np) break;
@@ -123,7 +137,7 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(MergeArgs a) {
       for (int u = 0; u < kUnroll; ++u) {
         const int p = p0 + u * kGroups;
         lp[u] = p < np ? lse_at(p) : -INFINITY;
-        rowv[u] = p < np ? row_at(p) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        rowv[u] = p < np ? row_at(p) : zero;
       }
     }
   }
@@ -133,16 +147,15 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(MergeArgs a) {
   if (g != 0) return;
   float W = 0.0f;
   for (int k = 0; k < kGroups; ++k) {
-    const float4 v = s_acc[k][c];
-    acc = k == 0 ? v : make_float4(acc.x + v.x, acc.y + v.y, acc.z + v.z, acc.w + v.w);
+    const Vec v = s_acc[k][c];
+#pragma unroll
+    for (int e = 0; e < kVec; ++e) acc.v[e] = k == 0 ? v.v[e] : acc.v[e] + v.v[e];
     W += s_w[k];
   }
   const float inv = W > 0.0f ? 1.0f / W : 0.0f;
   char* orow = reinterpret_cast<char*>(a.out) + row * D * sizeof(typename OT::Storage);
-  OT::store(orow, 4 * c + 0, acc.x * inv);
-  OT::store(orow, 4 * c + 1, acc.y * inv);
-  OT::store(orow, 4 * c + 2, acc.z * inv);
-  OT::store(orow, 4 * c + 3, acc.w * inv);
+#pragma unroll
+  for (int e = 0; e < kVec; ++e) OT::store(orow, kVec * c + e, acc.v[e] * inv);
 }
 
 struct OutF32 {
@@ -161,15 +174,17 @@ hipError_t launch_d(const MergeArgs& a, DType out_dtype, hipStream_t stream) {
   const size_t grid = size_t(a.num_seqs) * a.num_q_heads;
   if (grid == 0) return hipSuccess;
   if (grid > 0x7fffffffu) return hipErrorInvalidConfiguration;
-  // One wave per (sequence, head) when its rows fit one batch (8 rows per
-  // row group), or when there are enough (sequence, head) pairs to fill the
+  // One wave per (sequence, head) when its rows fit one batch (kUnroll rows
+  // per row group), or when there are enough (sequence, head) pairs to fill the
   // chip with single waves; four waves for few, long sequences.  Chunk slots
   // of a balanced split are spread over the sequences: judge by their mean.
   const int rows = a.chunk_first ? (a.max_partitions + a.num_batch - 1) / a.num_batch
                                  : a.max_partitions;     // partial rows per merged row
-  const bool one_batch = rows * (D / 4) <= 8 * kWave;
+  constexpr int kRowThreads = D / (kBf16Part ? 8 : 4);   // 16 bytes of a row per thread
+  constexpr int kUnroll = kBf16Part ? 4 : 8;              // rows in flight per row group
+  const bool one_batch = rows * kRowThreads <= kUnroll * kWave;
   int threads = (one_batch || grid >= 4096) ? kWave : kThreads;
-  threads = threads < D / 4 ? D / 4 : threads;   // one row group reads a whole row
+  threads = threads < kRowThreads ? kRowThreads : threads;   // one row group reads a whole row
   if (out_dtype == DType::F32)
     hipLaunchKernelGGL((merge_kernel<D, OutF32, kBf16Part>), dim3(unsigned(grid)), dim3(threads), 0,
                        stream, a);
