@@ -98,7 +98,11 @@ def to_float64(storage: np.ndarray, dtype: str) -> np.ndarray:
     if dtype == "bf16":
         return decode_bf16(storage)
     if dtype == "fp8_e4m3":
-        return decode_e4m3fn(storage)
+        # An e4m3 value depends on its 8-bit code alone: decode all 256 codes
+        # from their bits, then look every stored code up (same values as
+        # decoding each element, far faster on a whole cache).
+        table = decode_e4m3fn(np.arange(256, dtype=np.uint8))
+        return table[np.asarray(storage, dtype=np.uint8)]
     raise ValueError(dtype)
 
 

@@ -160,13 +160,73 @@ def _need_cuda(*ts):
             raise ValueError("tensors must be contiguous and on the GPU")
 
 
+_KV_DTYPES = (torch.float32, torch.bfloat16, torch.float8_e4m3fn, torch.uint8)
+_Q_DTYPES = (torch.float32, torch.bfloat16)
+_I32 = (torch.int32,)
+_F32 = (torch.float32,)
+
+
+def _want(name, t, dtypes, shape, optional=False):
+    """Check one tensor argument before anything is launched: the C ABI takes
+    raw pointers, so a wrong dtype or shape here would make a kernel read or
+    write past the caller's buffers.  ``dtypes``: allowed torch dtypes (None:
+    any); ``shape``: expected sizes, None for a size not fixed by the others.
+    Raises TypeError (dtype) or ValueError (missing tensor, rank or size)."""
+    if t is None:
+        if optional:
+            return
+        raise ValueError(f"{name} is required")
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if dtypes is not None and t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {list(dtypes)}")
+    if t.dim() != len(shape) or any(e is not None and e != g for e, g in zip(shape, t.shape)):
+        want = "[" + ", ".join("*" if e is None else str(e) for e in shape) + "]"
+        raise ValueError(f"{name} has shape {list(t.shape)}, expected {want}")
+
+
+def _want_pools(k_pool, v_pool, dtypes=_KV_DTYPES):
+    """Pools [NB, Hkv, 16, D] of one dtype; returns (NB, Hkv, block_size, D)."""
+    _want("k_pool", k_pool, dtypes, (None, None, None, None))
+    nb, hkv, bs, d = k_pool.shape
+    _want("v_pool", v_pool, (k_pool.dtype,), (nb, hkv, bs, d))
+    return nb, hkv, bs, d
+
+
+def _want_tables(block_tables, context_lens, num_seqs=None):
+    """Tables int32 [B, max_blocks], lengths int32 [B]; returns B."""
+    _want("block_tables", block_tables, _I32, (num_seqs, None))
+    B = block_tables.shape[0]
+    _want("context_lens", context_lens, _I32, (B,))
+    return B
+
+
+def _want_scales(k_scales, v_scales, nb, hkv):
+    _want("k_scales", k_scales, _F32, (nb, hkv), optional=True)
+    _want("v_scales", v_scales, _F32, (nb, hkv), optional=True)
+
+
+def _want_query(q, out, num_rows=None):
+    """q [rows, Hq, D] float32/bfloat16 and out of the same dtype and shape."""
+    _want("q", q, _Q_DTYPES, (num_rows, None, None))
+    _want("out", out, (q.dtype,), tuple(q.shape))
+
+
+def _want_workspace(workspace):
+    _want("workspace", workspace, None, (None,), optional=True)
+
+
+def _nbytes(t):
+    return t.numel() * t.element_size()
+
+
 def kv_append(k_pool, v_pool, k_new, v_new, block_tables, context_lens, stream=None):
     """Write every sequence's new K/V rows [B, Hkv, D] into slot ctx-1 (pkv_kv_append)."""
+    nb, hkv, bs, d = _want_pools(k_pool, v_pool)
+    B = _want_tables(block_tables, context_lens)
+    _want("k_new", k_new, (k_pool.dtype,), (B, hkv, d))
+    _want("v_new", v_new, (k_pool.dtype,), (B, hkv, d))
     _need_cuda(k_pool, v_pool, k_new, v_new, block_tables, context_lens)
-    nb, hkv, bs, d = k_pool.shape
-    B = block_tables.shape[0]
-    if k_new.dtype != k_pool.dtype or v_new.dtype != v_pool.dtype or k_pool.dtype != v_pool.dtype:
-        raise TypeError("k_new/v_new must have the pool's dtype")
     _check("pkv_kv_append", load().pkv_kv_append(
         _ptr(k_pool), _ptr(v_pool), _ptr(k_new), _ptr(v_new), _ptr(block_tables),
         _ptr(context_lens), B, hkv, d, bs, nb, block_tables.shape[1], dtype_code(k_pool.dtype),
@@ -187,16 +247,21 @@ def paged_decode_attention(out, q, k_pool, v_pool, block_tables, context_lens, m
                            softmax_scale, partition_size=512, k_scales=None, v_scales=None,
                            workspace=None, stream=None):
     """out[B, Hq, D] (q's dtype) = attention of q over each sequence's paged cache."""
+    nb, hkv, bs, d = _want_pools(k_pool, v_pool)
+    B = _want_tables(block_tables, context_lens)
+    _want_query(q, out, B)
+    _want("q", q, None, (B, None, d))
+    _want_scales(k_scales, v_scales, nb, hkv)
+    _want_workspace(workspace)
     _need_cuda(out, q, k_pool, v_pool, block_tables, context_lens, k_scales, v_scales, workspace)
-    B, hq, d = q.shape
-    nb, hkv, bs, _ = k_pool.shape
+    hq = q.shape[1]
     if workspace is None:
         workspace = alloc_workspace(B, hq, d, max_context_len, partition_size, q.device)
     _check("pkv_paged_decode_attention", load().pkv_paged_decode_attention(
         _ptr(out), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(k_scales), _ptr(v_scales),
         _ptr(block_tables), _ptr(context_lens), B, hq, hkv, d, bs, nb, block_tables.shape[1],
         int(max_context_len), float(softmax_scale), int(partition_size), _ptr(workspace),
-        workspace.numel(), dtype_code(q.dtype), dtype_code(k_pool.dtype), _stream(stream)))
+        _nbytes(workspace), dtype_code(q.dtype), dtype_code(k_pool.dtype), _stream(stream)))
     return out
 
 
@@ -204,12 +269,15 @@ def paged_decode_partials(partial_out, partial_lse, q, k_pool, v_pool, block_tab
                           context_lens, softmax_scale, partition_size=512, k_scales=None,
                           v_scales=None, stream=None):
     """Unmerged split-KV results: partial_out [B, Hq, P, D] fp32, partial_lse [B, Hq, P] fp32."""
+    nb, hkv, bs, d = _want_pools(k_pool, v_pool)
+    B = _want_tables(block_tables, context_lens)
+    _want("q", q, _Q_DTYPES, (B, None, d))
+    hq = q.shape[1]
+    _want("partial_out", partial_out, _F32, (B, hq, None, d))
+    _want("partial_lse", partial_lse, _F32, (B, hq, partial_out.shape[2]))
+    _want_scales(k_scales, v_scales, nb, hkv)
     _need_cuda(partial_out, partial_lse, q, k_pool, v_pool, block_tables, context_lens,
                k_scales, v_scales)
-    if partial_out.dtype != torch.float32 or partial_lse.dtype != torch.float32:
-        raise TypeError("partials are float32")
-    B, hq, d = q.shape
-    nb, hkv, bs, _ = k_pool.shape
     _check("pkv_paged_decode_partials", load().pkv_paged_decode_partials(
         _ptr(partial_out), _ptr(partial_lse), partial_out.shape[2], _ptr(q), _ptr(k_pool),
         _ptr(v_pool), _ptr(k_scales), _ptr(v_scales), _ptr(block_tables), _ptr(context_lens), B,
@@ -220,8 +288,12 @@ def paged_decode_partials(partial_out, partial_lse, q, k_pool, v_pool, block_tab
 
 def merge_partials(out, partial_out, partial_lse, num_partitions=None, stream=None):
     """out[B, Hq, D] = LSE merge of partial_out [B, Hq, P, D] with partial_lse [B, Hq, P]."""
-    _need_cuda(out, partial_out, partial_lse, num_partitions)
+    _want("partial_out", partial_out, _F32, (None, None, None, None))
     B, hq, maxp, d = partial_out.shape
+    _want("partial_lse", partial_lse, _F32, (B, hq, maxp))
+    _want("out", out, _Q_DTYPES, (B, hq, d))
+    _want("num_partitions", num_partitions, _I32, (B,), optional=True)
+    _need_cuda(out, partial_out, partial_lse, num_partitions)
     _check("pkv_merge_partials", load().pkv_merge_partials(
         _ptr(out), _ptr(partial_out), _ptr(partial_lse), _ptr(num_partitions), B, hq, d, maxp,
         dtype_code(out.dtype), _stream(stream)))
@@ -241,6 +313,8 @@ def decode_plan(context_lens, num_slots, max_blocks_per_seq, plan=None, stream=N
     """The balanced split's schedule (pkv_decode_plan) in a uint8 device
     buffer: chunk_first int32 [B + 1], then slot_info int32x4 [num_slots] at
     the offset plan_info_offset(B)."""
+    _want("context_lens", context_lens, _I32, (None,))
+    _want("plan", plan, (torch.uint8,), (None,), optional=True)
     _need_cuda(context_lens, plan)
     B = context_lens.shape[0]
     n = int(load().pkv_decode_plan_bytes(B, num_slots))
@@ -265,14 +339,18 @@ def paged_decode_partials_planned(partial_out, partial_lse, plan, q, k_pool, v_p
     """Chunk results of a balanced split over R = partial_out.shape[0] slots:
     partial_out [R, Hq, D] fp32, partial_lse [R, Hq] fp32; the schedule is
     written into ``plan`` (uint8, pkv_decode_plan_bytes(B, R) bytes)."""
+    nb, hkv, bs, d = _want_pools(k_pool, v_pool)
+    B = _want_tables(block_tables, context_lens)
+    _want("q", q, _Q_DTYPES, (B, None, d))
+    hq = q.shape[1]
+    _want("partial_out", partial_out, _F32, (None, hq, d))
+    _want("partial_lse", partial_lse, _F32, (partial_out.shape[0], hq))
+    _want("plan", plan, (torch.uint8,), (None,))
+    _want_scales(k_scales, v_scales, nb, hkv)
     _need_cuda(partial_out, partial_lse, plan, q, k_pool, v_pool, block_tables, context_lens,
                k_scales, v_scales)
-    if partial_out.dtype != torch.float32 or partial_lse.dtype != torch.float32:
-        raise TypeError("partials are float32")
-    B, hq, d = q.shape
-    nb, hkv, bs, _ = k_pool.shape
     _check("pkv_paged_decode_partials_planned", load().pkv_paged_decode_partials_planned(
-        _ptr(partial_out), _ptr(partial_lse), _ptr(plan), plan.numel() * plan.element_size(),
+        _ptr(partial_out), _ptr(partial_lse), _ptr(plan), _nbytes(plan),
         partial_out.shape[0], _ptr(q),
         _ptr(k_pool), _ptr(v_pool), _ptr(k_scales), _ptr(v_scales), _ptr(block_tables),
         _ptr(context_lens), B, hq, hkv, d, bs, nb, block_tables.shape[1], float(softmax_scale),
@@ -282,8 +360,12 @@ def paged_decode_partials_planned(partial_out, partial_lse, plan, q, k_pool, v_p
 
 def merge_partials_planned(out, partial_out, partial_lse, plan, stream=None):
     """out[B, Hq, D] = LSE merge of each sequence's chunk rows of partial_out [R, Hq, D]."""
-    _need_cuda(out, partial_out, partial_lse, plan)
+    _want("out", out, _Q_DTYPES, (None, None, None))
     B, hq, d = out.shape
+    _want("partial_out", partial_out, _F32, (None, hq, d))
+    _want("partial_lse", partial_lse, _F32, (partial_out.shape[0], hq))
+    _want("plan", plan, (torch.uint8,), (None,))
+    _need_cuda(out, partial_out, partial_lse, plan)
     _check("pkv_merge_partials_planned", load().pkv_merge_partials_planned(
         _ptr(out), _ptr(partial_out), _ptr(partial_lse), _ptr(plan), partial_out.shape[0], B, hq,
         d, dtype_code(out.dtype), _stream(stream)))
@@ -301,19 +383,24 @@ def decode_step(out, q, k_pool, v_pool, k_new, v_new, block_tables, context_lens
         return paged_decode_attention(out, q, k_pool, v_pool, block_tables, context_lens,
                                       max_context_len, softmax_scale, partition_size, k_scales,
                                       v_scales, workspace, stream)
+    nb, hkv, bs, d = _want_pools(k_pool, v_pool)
+    B = _want_tables(block_tables, context_lens)
+    _want_query(q, out, B)
+    _want("q", q, None, (B, None, d))
+    _want("k_new", k_new, (k_pool.dtype,), (B, hkv, d))
+    _want("v_new", v_new, (k_pool.dtype,), (B, hkv, d))
+    _want_scales(k_scales, v_scales, nb, hkv)
+    _want_workspace(workspace)
     _need_cuda(out, q, k_pool, v_pool, k_new, v_new, block_tables, context_lens, k_scales,
                v_scales, workspace)
-    if k_new.dtype != k_pool.dtype or v_new.dtype != v_pool.dtype:
-        raise TypeError("k_new/v_new must have the pool's dtype")
-    B, hq, d = q.shape
-    nb, hkv, bs, _ = k_pool.shape
+    hq = q.shape[1]
     if workspace is None:
         workspace = alloc_workspace(B, hq, d, max_context_len, partition_size, q.device)
     _check("pkv_paged_decode_step", load().pkv_paged_decode_step(
         _ptr(out), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(k_new), _ptr(v_new), _ptr(k_scales),
         _ptr(v_scales), _ptr(block_tables), _ptr(context_lens), B, hq, hkv, d, bs, nb,
         block_tables.shape[1], int(max_context_len), float(softmax_scale), int(partition_size),
-        _ptr(workspace), workspace.numel(), dtype_code(q.dtype), dtype_code(k_pool.dtype),
+        _ptr(workspace), _nbytes(workspace), dtype_code(q.dtype), dtype_code(k_pool.dtype),
         _stream(stream)))
     return out
 
@@ -322,13 +409,12 @@ def kv_append_tokens(k_pool, v_pool, k_new, v_new, block_tables, context_lens, q
                      stream=None):
     """Write rows qsl[b] .. qsl[b+1]-1 of k_new/v_new [T, Hkv, D] into positions
     ctx_b - t_b .. ctx_b - 1 of sequence b (pkv_kv_append_tokens)."""
+    nb, hkv, bs, d = _want_pools(k_pool, v_pool)
+    B = _want_tables(block_tables, context_lens)
+    _want("query_start_loc", query_start_loc, _I32, (B + 1,))
+    _want("k_new", k_new, (k_pool.dtype,), (None, hkv, d))
+    _want("v_new", v_new, (k_pool.dtype,), (k_new.shape[0], hkv, d))
     _need_cuda(k_pool, v_pool, k_new, v_new, block_tables, context_lens, query_start_loc)
-    nb, hkv, bs, d = k_pool.shape
-    B = block_tables.shape[0]
-    if k_new.dtype != k_pool.dtype or v_new.dtype != v_pool.dtype or k_pool.dtype != v_pool.dtype:
-        raise TypeError("k_new/v_new must have the pool's dtype")
-    if query_start_loc.shape[0] != B + 1 or k_new.shape[0] != v_new.shape[0]:
-        raise ValueError("query_start_loc must have num_seqs + 1 entries")
     _check("pkv_kv_append_tokens", load().pkv_kv_append_tokens(
         _ptr(k_pool), _ptr(v_pool), _ptr(k_new), _ptr(v_new), _ptr(block_tables),
         _ptr(context_lens), _ptr(query_start_loc), B, k_new.shape[0], hkv, d, bs, nb,
@@ -347,13 +433,16 @@ def paged_multi_query_attention(out, q, k_pool, v_pool, block_tables, context_le
                                 stream=None):
     """out[T, Hq, D] (q's dtype): row qsl[b] + j attends over the first
     ctx_b - t_b + j + 1 cached tokens of sequence b (pkv_paged_multi_query_attention)."""
+    nb, hkv, bs, d = _want_pools(k_pool, v_pool)
+    B = _want_tables(block_tables, context_lens)
+    _want("query_start_loc", query_start_loc, _I32, (B + 1,))
+    _want_query(q, out)
+    _want("q", q, None, (None, None, d))
+    _want_scales(k_scales, v_scales, nb, hkv)
+    _want_workspace(workspace)
     _need_cuda(out, q, k_pool, v_pool, block_tables, context_lens, query_start_loc, k_scales,
                v_scales, workspace)
-    T, hq, d = q.shape
-    nb, hkv, bs, _ = k_pool.shape
-    B = block_tables.shape[0]
-    if query_start_loc.shape[0] != B + 1:
-        raise ValueError("query_start_loc must have num_seqs + 1 entries")
+    T, hq, _ = q.shape
     if workspace is None:
         if partition_size == PKV_PARTITION_BALANCED:
             n = int(load().pkv_multi_query_balanced_workspace_bytes(
@@ -365,7 +454,7 @@ def paged_multi_query_attention(out, q, k_pool, v_pool, block_tables, context_le
         _ptr(out), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(k_scales), _ptr(v_scales),
         _ptr(block_tables), _ptr(context_lens), _ptr(query_start_loc), B, T, int(max_query_len),
         hq, hkv, d, bs, nb, block_tables.shape[1], int(max_context_len), float(softmax_scale),
-        int(partition_size), _ptr(workspace), workspace.numel(), dtype_code(q.dtype),
+        int(partition_size), _ptr(workspace), _nbytes(workspace), dtype_code(q.dtype),
         dtype_code(k_pool.dtype), _stream(stream)))
     return out
 
@@ -375,13 +464,16 @@ def paged_multi_query_partials(partial_out, partial_lse, q, k_pool, v_pool, bloc
                                partition_size=512, k_scales=None, v_scales=None, stream=None):
     """Unmerged split-KV results of the multi-token attention: partial_out
     [T, Hq, P, D] fp32, partial_lse [T, Hq, P] fp32 (pkv_paged_multi_query_partials)."""
+    nb, hkv, bs, d = _want_pools(k_pool, v_pool)
+    B = _want_tables(block_tables, context_lens)
+    _want("query_start_loc", query_start_loc, _I32, (B + 1,))
+    _want("q", q, _Q_DTYPES, (None, None, d))
+    T, hq, _ = q.shape
+    _want("partial_out", partial_out, _F32, (T, hq, None, d))
+    _want("partial_lse", partial_lse, _F32, (T, hq, partial_out.shape[2]))
+    _want_scales(k_scales, v_scales, nb, hkv)
     _need_cuda(partial_out, partial_lse, q, k_pool, v_pool, block_tables, context_lens,
                query_start_loc, k_scales, v_scales)
-    if partial_out.dtype != torch.float32 or partial_lse.dtype != torch.float32:
-        raise TypeError("partials are float32")
-    T, hq, d = q.shape
-    nb, hkv, bs, _ = k_pool.shape
-    B = block_tables.shape[0]
     _check("pkv_paged_multi_query_partials", load().pkv_paged_multi_query_partials(
         _ptr(partial_out), _ptr(partial_lse), partial_out.shape[2], _ptr(q), _ptr(k_pool),
         _ptr(v_pool), _ptr(k_scales), _ptr(v_scales), _ptr(block_tables), _ptr(context_lens),
@@ -395,16 +487,15 @@ def kv_append_quant(k_pool, v_pool, k_scales, v_scales, k_new, v_new, block_tabl
                     context_lens, query_start_loc=None, mode=PKV_SCALE_FIXED, stream=None):
     """Quantise bf16/fp32 rows [R, Hkv, D] into the e4m3 pools and append them
     (pkv_kv_append_quant); ``mode`` PKV_SCALE_FIXED or PKV_SCALE_RUNNING_AMAX."""
+    nb, hkv, bs, d = _want_pools(k_pool, v_pool, (torch.float8_e4m3fn, torch.uint8))
+    B = _want_tables(block_tables, context_lens)
+    _want("k_scales", k_scales, _F32, (nb, hkv))
+    _want("v_scales", v_scales, _F32, (nb, hkv))
+    _want("query_start_loc", query_start_loc, _I32, (B + 1,), optional=True)
+    _want("k_new", k_new, _Q_DTYPES, (B if query_start_loc is None else None, hkv, d))
+    _want("v_new", v_new, (k_new.dtype,), (k_new.shape[0], hkv, d))
     _need_cuda(k_pool, v_pool, k_scales, v_scales, k_new, v_new, block_tables, context_lens,
                query_start_loc)
-    if dtype_code(k_pool.dtype) != PKV_FP8_E4M3 or dtype_code(v_pool.dtype) != PKV_FP8_E4M3:
-        raise TypeError("pools must be e4m3")
-    if k_new.dtype != v_new.dtype or k_new.dtype not in (torch.float32, torch.bfloat16):
-        raise TypeError("new rows must be float32 or bfloat16")
-    if k_scales.dtype != torch.float32 or v_scales.dtype != torch.float32:
-        raise TypeError("scales are float32")
-    nb, hkv, bs, d = k_pool.shape
-    B = block_tables.shape[0]
     _check("pkv_kv_append_quant", load().pkv_kv_append_quant(
         _ptr(k_pool), _ptr(v_pool), _ptr(k_scales), _ptr(v_scales), _ptr(k_new), _ptr(v_new),
         dtype_code(k_new.dtype), _ptr(block_tables), _ptr(context_lens), _ptr(query_start_loc), B,
@@ -479,8 +570,10 @@ class BlockManager:
 
 def copy_blocks(k_pool, v_pool, pairs, k_scales=None, v_scales=None, stream=None):
     """Run copy-on-write copies: pairs int32 [n, 2] (src, dst) on the device."""
+    nb, hkv, bs, d = _want_pools(k_pool, v_pool)
+    _want("pairs", pairs, _I32, (None, 2))
+    _want_scales(k_scales, v_scales, nb, hkv)
     _need_cuda(k_pool, v_pool, pairs, k_scales, v_scales)
-    nb, hkv, bs, d = k_pool.shape
     _check("pkv_copy_blocks", load().pkv_copy_blocks(
         _ptr(k_pool), _ptr(v_pool), _ptr(k_scales), _ptr(v_scales), _ptr(pairs),
         pairs.shape[0] if pairs.numel() else 0, nb, hkv, d, bs, dtype_code(k_pool.dtype),
@@ -491,6 +584,7 @@ def stream_read(src, num_workgroups, out=None, stream=None):
     """Read every byte of src once (pkv_stream_read, a bandwidth measurement);
     returns out, int32 [pkv_stream_read_out_words(num_workgroups)], whose XOR
     is the XOR of src's 32-bit words."""
+    _want("out", out, _I32, (None,), optional=True)
     _need_cuda(src, out)
     words = int(load().pkv_stream_read_out_words(num_workgroups))
     if words == 0:
@@ -506,8 +600,11 @@ def stream_read(src, num_workgroups, out=None, stream=None):
 
 def mla_append(latent_pool, latent_new, block_tables, context_lens, stream=None):
     """Write each sequence's new 576-number row into slot ctx-1 (pkv_mla_append)."""
-    _need_cuda(latent_pool, latent_new, block_tables, context_lens)
+    _want("latent_pool", latent_pool, (torch.bfloat16,), (None, None, None))
     nb, bs, d = latent_pool.shape
+    B = _want_tables(block_tables, context_lens)
+    _want("latent_new", latent_new, (torch.bfloat16,), (B, d))
+    _need_cuda(latent_pool, latent_new, block_tables, context_lens)
     _check("pkv_mla_append", load().pkv_mla_append(
         _ptr(latent_pool), _ptr(latent_new), _ptr(block_tables), _ptr(context_lens),
         block_tables.shape[0], d, bs, nb, block_tables.shape[1], _stream(stream)))
@@ -519,9 +616,14 @@ def mla_decode_attention(out, q, latent_pool, block_tables, context_lens, max_co
     """out [B, H, 512] bf16: absorbed MLA decode of q [B, H, 576] over the paged
     latent rows (pkv_mla_decode_attention); partition_size PKV_PARTITION_BALANCED
     splits the batch's work into balanced chunks."""
+    _want("latent_pool", latent_pool, (torch.bfloat16,), (None, None, None))
+    nb, bs, d = latent_pool.shape
+    B = _want_tables(block_tables, context_lens)
+    _want("q", q, (torch.bfloat16,), (B, None, d))
+    H = q.shape[1]
+    _want("out", out, (torch.bfloat16,), (B, H, kv_lora_rank))
+    _want_workspace(workspace)
     _need_cuda(out, q, latent_pool, block_tables, context_lens, workspace)
-    B, H, d = q.shape
-    nb, bs, _ = latent_pool.shape
     if workspace is None:
         n = int(load().pkv_mla_workspace_bytes(B, H, kv_lora_rank, max_context_len,
                                                partition_size))
@@ -529,7 +631,7 @@ def mla_decode_attention(out, q, latent_pool, block_tables, context_lens, max_co
     _check("pkv_mla_decode_attention", load().pkv_mla_decode_attention(
         _ptr(out), _ptr(q), _ptr(latent_pool), _ptr(block_tables), _ptr(context_lens), B, H,
         kv_lora_rank, d - kv_lora_rank, bs, nb, block_tables.shape[1], int(max_context_len),
-        float(softmax_scale), int(partition_size), _ptr(workspace), workspace.numel(),
+        float(softmax_scale), int(partition_size), _ptr(workspace), _nbytes(workspace),
         _stream(stream)))
     return out
 
@@ -537,9 +639,14 @@ def mla_decode_attention(out, q, latent_pool, block_tables, context_lens, max_co
 def mla_decode_partials(partial_out, partial_lse, q, latent_pool, block_tables, context_lens,
                         softmax_scale, partition_size=512, kv_lora_rank=512, stream=None):
     """Unmerged MLA split-KV results: partial_out [B, H, P, 512], partial_lse [B, H, P]."""
+    _want("latent_pool", latent_pool, (torch.bfloat16,), (None, None, None))
+    nb, bs, d = latent_pool.shape
+    B = _want_tables(block_tables, context_lens)
+    _want("q", q, (torch.bfloat16,), (B, None, d))
+    H = q.shape[1]
+    _want("partial_out", partial_out, _F32, (B, H, None, kv_lora_rank))
+    _want("partial_lse", partial_lse, _F32, (B, H, partial_out.shape[2]))
     _need_cuda(partial_out, partial_lse, q, latent_pool, block_tables, context_lens)
-    B, H, d = q.shape
-    nb, bs, _ = latent_pool.shape
     _check("pkv_mla_decode_partials", load().pkv_mla_decode_partials(
         _ptr(partial_out), _ptr(partial_lse), partial_out.shape[2], _ptr(q), _ptr(latent_pool),
         _ptr(block_tables), _ptr(context_lens), B, H, kv_lora_rank, d - kv_lora_rank, bs, nb,

@@ -117,20 +117,54 @@ def abs_v_attention(inp, seqs=None, pools=None):
                                q_dtype=inp.q_dtype, kv_dtype=inp.kv_dtype, seqs=seqs)
 
 
-def check_guard(inp, gpu, ref, label, seqs=None, pools=None):
+def check_guard(inp, gpu, ref, label, seqs=None, pools=None, absv=None):
     """A bound from the kernels' own arithmetic, much tighter than the bars:
     fp32 products, sums and softmax (relative error ~1e-6), the output rounded
     once to its dtype (2^-9 relative for bf16) and, on the matrix-core path,
-    every weight rounded to bf16 (at most 2^-9 A).  Margins of 2x."""
+    every weight rounded to bf16 (at most 2^-9 A).  Margins of 2x.  ``absv``:
+    A already computed (abs_v_attention of the same sequences)."""
     out_r = 2.0 ** -8 if inp.q_dtype == "bf16" else 0.0
     bound = out_r * np.abs(ref) + 2e-5 * (1.0 + np.abs(ref))
     if uses_matrix_cores(inp):
-        bound = bound + 2.0 ** -8 * abs_v_attention(inp, seqs, pools)
+        if absv is None:
+            absv = abs_v_attention(inp, seqs, pools)
+        bound = bound + 2.0 ** -8 * absv
     err = np.abs(gpu - ref)
     worst = float((err / bound).max()) if err.size else 0.0
     assert (err <= bound).all(), f"{label}: error exceeds the arithmetic bound ({worst:.2f}x)"
     log(f"[guard] {label}: max err / bound = {worst:.3f}")
     return worst
+
+
+class FullReference:
+    """A full-size workload with its oracle results, built once per process and
+    shared by every test that runs it (the fixed and balanced splits, the two
+    calls and the fused step): the inputs, the pools after the append, the
+    oracle output of every sequence and, for the matrix-core path, A of
+    check_guard.  The oracle runs one sequence at a time, so host memory holds
+    one sequence's gathered float64 cache at most, and each sequence logs."""
+
+    _cache: dict = {}
+
+    @classmethod
+    def get(cls, key, make):
+        if key not in cls._cache:
+            cls._cache[key] = cls(key, make())
+        return cls._cache[key]
+
+    def __init__(self, key, inp):
+        self.inp = inp
+        self.pools = pa.kv_append(inp.k_pool, inp.v_pool, inp.k_new, inp.v_new,
+                                  inp.block_tables, inp.context_lens, inp.block_size)
+        refs, absv = [], []
+        for b in range(inp.num_seqs):
+            refs.append(oracle_out(inp, seqs=[b], pools=self.pools)[0])
+            if uses_matrix_cores(inp):
+                absv.append(abs_v_attention(inp, [b], self.pools)[0])
+            if b % 16 == 15 or b == inp.num_seqs - 1:
+                log(f"[oracle] {key}: {b + 1}/{inp.num_seqs} sequences")
+        self.ref = np.stack(refs)
+        self.absv = np.stack(absv) if absv else None
 
 
 def check_tolerance(kv_dtype, gpu, ref, label="", out_dtype="f32"):
