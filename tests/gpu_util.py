@@ -161,7 +161,7 @@ class FullReference:
             refs.append(oracle_out(inp, seqs=[b], pools=self.pools)[0])
             if uses_matrix_cores(inp):
                 absv.append(abs_v_attention(inp, [b], self.pools)[0])
-            if b % 16 == 15 or b == inp.num_seqs - 1:
+            if b % 16 == 15 or b == inp.num_seqs - 1 or inp.num_seqs <= 16:
                 log(f"[oracle] {key}: {b + 1}/{inp.num_seqs} sequences")
         self.ref = np.stack(refs)
         self.absv = np.stack(absv) if absv else None
