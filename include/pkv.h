@@ -225,6 +225,35 @@ pkv_status_t pkv_paged_decode_step(
     size_t workspace_bytes, pkv_dtype_t q_dtype, pkv_dtype_t kv_dtype, void* stream);
 
 /*
+ * pkv_paged_decode_step_noalloc - pkv_paged_decode_step without a workspace
+ * argument, for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ *
+ * The split-KV partial results (and the balanced split's plan) go to a
+ * device array inside the library, PKV_NOALLOC_SCRATCH_BYTES bytes on each
+ * GPU it runs on, held until the process ends.  The call allocates nothing
+ * (no hipMalloc, hipFree or allocating library routine); the first call on a
+ * device looks the array's address up with that device current.  Same
+ * arguments, kernels and results as pkv_paged_decode_step with a caller
+ * workspace.  Returns PKV_ERR_WORKSPACE, and launches nothing, when the call
+ * needs more than PKV_NOALLOC_SCRATCH_BYTES of workspace (the exact layout
+ * of this call, at most pkv_decode_workspace_bytes(...); e.g. 6.3 MB for
+ * batch 64 x 32 q heads x head dim 128 with PKV_PARTITION_BALANCED), and
+ * PKV_ERR_HIP when the address lookup fails.  Every call on one GPU shares
+ * that GPU's array and leaves its results there: calls that overlap on one
+ * GPU (different streams, or different host threads without ordering) race
+ * and give undefined results.  Nothing in the array needs to start at zero.
+ */
+#define PKV_NOALLOC_SCRATCH_BYTES (32u << 20)
+pkv_status_t pkv_paged_decode_step_noalloc(
+    void* out, const void* q, void* k_pool, void* v_pool, const void* k_new, const void* v_new,
+    const float* k_scales, const float* v_scales, const int32_t* block_tables,
+    const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+    int32_t head_dim, int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
+    int32_t max_context_len, float softmax_scale, int32_t partition_size, pkv_dtype_t q_dtype,
+    pkv_dtype_t kv_dtype, void* stream);
+
+/*
  * pkv_paged_decode_partials - the split-KV half of pkv_paged_decode_attention
  * on its own: per-partition attention results, not merged.
  *

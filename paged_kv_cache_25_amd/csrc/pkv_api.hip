@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "pkv_launch.h"
 #include "stream_read.h"
 
@@ -927,6 +929,84 @@ pkv_status_t pkv_paged_decode_step(
                         max_blocks_per_seq, max_context_len, softmax_scale, partition_size,
                         workspace, workspace_bytes, q_dtype, kv_dtype, stream, k_new, v_new,
                         k_pool, v_pool);
+}
+
+}  // extern "C"
+
+namespace {
+
+// The device memory pkv_paged_decode_step_noalloc uses instead of a caller's
+// workspace: one copy per GPU, in the library's code object, alive until the
+// process ends.  Host code never passes this name to a kernel (on the host it
+// is only a stand-in for the symbol); it uses the address that
+// hipGetSymbolAddress reports for the current device.
+static __device__ __align__(256) unsigned char scratch[PKV_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's address of `scratch`, looked up once per device with
+// that device current.  Null on failure.
+void* scratch_for_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    g_scratch_ptr[dev] = p;
+  }
+  return g_scratch_ptr[dev];
+}
+
+// Workspace bytes one decode step needs with these sizes (the exact layout
+// of attention_impl, not pkv_decode_workspace_bytes' upper bound).
+size_t step_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                            int32_t head_dim, int32_t max_context_len, int32_t partition_size,
+                            pkv_dtype_t q_dtype, pkv_dtype_t kv_dtype) {
+  if (partition_size == PKV_PARTITION_BALANCED) {
+    const int64_t slots =
+        decode_slots_for(num_seqs, num_q_heads, num_kv_heads, head_dim, q_dtype, kv_dtype);
+    return decode_balanced_layout(num_seqs, num_q_heads, head_dim, slots).total;
+  }
+  const int64_t maxp = max_partitions(max_context_len, partition_size);
+  return maxp <= 1 ? 0 : part_layout(num_seqs, num_q_heads, head_dim, maxp).total;
+}
+
+}  // namespace
+
+extern "C" {
+
+pkv_status_t pkv_paged_decode_step_noalloc(
+    void* out, const void* q, void* k_pool, void* v_pool, const void* k_new, const void* v_new,
+    const float* k_scales, const float* v_scales, const int32_t* block_tables,
+    const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+    int32_t head_dim, int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
+    int32_t max_context_len, float softmax_scale, int32_t partition_size, pkv_dtype_t q_dtype,
+    pkv_dtype_t kv_dtype, void* stream) {
+  // The size checks of pkv_paged_decode_step, so the workspace size below is
+  // computed from valid sizes only.
+  if (max_context_len < 0) return PKV_ERR_INVALID_ARG;
+  const bool balanced = partition_size == PKV_PARTITION_BALANCED;
+  const pkv_status_t st0 = check_decode(q, k_pool, v_pool, k_scales, v_scales, block_tables,
+                                        context_lens, num_seqs, num_q_heads, num_kv_heads,
+                                        head_dim, block_size, num_blocks, max_blocks_per_seq,
+                                        softmax_scale, balanced ? 0 : partition_size, q_dtype,
+                                        kv_dtype);
+  if (st0 != PKV_OK || num_seqs == 0) return st0;
+  if (!out || !aligned16(out) || !k_new || !v_new || !aligned16(k_new) || !aligned16(v_new))
+    return PKV_ERR_INVALID_ARG;
+  if (step_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len,
+                           partition_size, q_dtype, kv_dtype) > PKV_NOALLOC_SCRATCH_BYTES)
+    return PKV_ERR_WORKSPACE;
+  void* ws = scratch_for_current_device();
+  if (!ws) return PKV_ERR_HIP;
+  return pkv_paged_decode_step(out, q, k_pool, v_pool, k_new, v_new, k_scales, v_scales,
+                               block_tables, context_lens, num_seqs, num_q_heads, num_kv_heads,
+                               head_dim, block_size, num_blocks, max_blocks_per_seq,
+                               max_context_len, softmax_scale, partition_size, ws,
+                               PKV_NOALLOC_SCRATCH_BYTES, q_dtype, kv_dtype, stream);
 }
 
 pkv_status_t pkv_paged_decode_partials(

@@ -56,6 +56,9 @@ def load():
     L.pkv_paged_decode_step.restype = ctypes.c_int
     L.pkv_paged_decode_step.argtypes = [P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, F, I,
                                         P, Z, ctypes.c_int, ctypes.c_int, P]
+    L.pkv_paged_decode_step_noalloc.restype = ctypes.c_int
+    L.pkv_paged_decode_step_noalloc.argtypes = [P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I,
+                                                I, F, I, ctypes.c_int, ctypes.c_int, P]
     L.pkv_paged_decode_partials.restype = ctypes.c_int
     L.pkv_paged_decode_partials.argtypes = [P, P, I, P, P, P, P, P, P, P, I, I, I, I, I, I, I, F, I,
                                             ctypes.c_int, ctypes.c_int, P]
@@ -402,6 +405,32 @@ def decode_step(out, q, k_pool, v_pool, k_new, v_new, block_tables, context_lens
         block_tables.shape[1], int(max_context_len), float(softmax_scale), int(partition_size),
         _ptr(workspace), _nbytes(workspace), dtype_code(q.dtype), dtype_code(k_pool.dtype),
         _stream(stream)))
+    return out
+
+
+PKV_NOALLOC_SCRATCH_BYTES = 32 << 20
+
+
+def decode_step_noalloc(out, q, k_pool, v_pool, k_new, v_new, block_tables, context_lens,
+                        max_context_len, softmax_scale, partition_size=PKV_PARTITION_BALANCED,
+                        k_scales=None, v_scales=None, stream=None):
+    """pkv_paged_decode_step_noalloc: the fused decode step with the partial
+    results in the library's own per-GPU device array (no workspace, nothing
+    allocated); calls that overlap on one GPU race on that array."""
+    nb, hkv, bs, d = _want_pools(k_pool, v_pool)
+    B = _want_tables(block_tables, context_lens)
+    _want_query(q, out, B)
+    _want("q", q, None, (B, None, d))
+    _want("k_new", k_new, (k_pool.dtype,), (B, hkv, d))
+    _want("v_new", v_new, (k_pool.dtype,), (B, hkv, d))
+    _want_scales(k_scales, v_scales, nb, hkv)
+    _need_cuda(out, q, k_pool, v_pool, k_new, v_new, block_tables, context_lens, k_scales,
+               v_scales)
+    _check("pkv_paged_decode_step_noalloc", load().pkv_paged_decode_step_noalloc(
+        _ptr(out), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(k_new), _ptr(v_new), _ptr(k_scales),
+        _ptr(v_scales), _ptr(block_tables), _ptr(context_lens), B, q.shape[1], hkv, d, bs, nb,
+        block_tables.shape[1], int(max_context_len), float(softmax_scale), int(partition_size),
+        dtype_code(q.dtype), dtype_code(k_pool.dtype), _stream(stream)))
     return out
 
 

@@ -33,7 +33,8 @@ def lib():
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted([
         "pkv_abi_version", "pkv_status_string", "pkv_kv_append", "pkv_decode_workspace_bytes",
-        "pkv_paged_decode_attention", "pkv_paged_decode_step", "pkv_paged_decode_partials",
+        "pkv_paged_decode_attention", "pkv_paged_decode_step", "pkv_paged_decode_step_noalloc",
+        "pkv_paged_decode_partials",
         "pkv_merge_partials", "pkv_kv_append_tokens", "pkv_multi_query_workspace_bytes",
         "pkv_paged_multi_query_attention", "pkv_paged_multi_query_partials",
         "pkv_kv_append_quant", "pkv_bm_create", "pkv_bm_destroy", "pkv_bm_add_seq",
@@ -143,6 +144,31 @@ def test_step_validation(lib):
     assert _step(lib, d=96) == UNSUPPORTED
     assert _step(lib) == WORKSPACE
     assert _step(lib, B=0, kn=None, q=None) == OK
+
+
+def _step_noalloc(lib, **over):
+    a = dict(out=FAKE, q=FAKE, kp=FAKE, vp=FAKE, kn=FAKE, vn=FAKE, ks=None, vs=None, tables=FAKE,
+             lens=FAKE, B=2, hq=8, hkv=2, d=128, bs=16, nb=8, mbps=4, maxctx=64, scale=0.088,
+             P=16, qt=ops.PKV_BF16, kvt=ops.PKV_BF16)
+    a.update(over)
+    return lib.pkv_paged_decode_step_noalloc(
+        a["out"], a["q"], a["kp"], a["vp"], a["kn"], a["vn"], a["ks"], a["vs"], a["tables"],
+        a["lens"], a["B"], a["hq"], a["hkv"], a["d"], a["bs"], a["nb"], a["mbps"], a["maxctx"],
+        a["scale"], a["P"], a["qt"], a["kvt"], None)
+
+
+def test_step_noalloc_validation(lib):
+    """Argument checks and the size limit come before the device is touched."""
+    assert _step_noalloc(lib, kn=None) == INVALID
+    assert _step_noalloc(lib, out=ctypes.c_void_p(0x10008)) == INVALID
+    assert _step_noalloc(lib, q=None) == INVALID
+    assert _step_noalloc(lib, hq=6, hkv=4) == INVALID
+    assert _step_noalloc(lib, d=96) == UNSUPPORTED
+    assert _step_noalloc(lib, B=0, kn=None, q=None) == OK
+    # 256 sequences x 32 heads x head dim 128 with up to 64 partitions of 512
+    # tokens: 270 MB of partials, past the 32 MiB array
+    assert _step_noalloc(lib, B=256, hq=32, hkv=8, mbps=2048, maxctx=32768, P=512) == WORKSPACE
+    assert ops.PKV_NOALLOC_SCRATCH_BYTES == 32 << 20
 
 
 def _partials(lib, **over):
