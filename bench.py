@@ -70,6 +70,9 @@ def parse():
     ap.add_argument("--mla", default=None,
                     help="time absorbed MLA decode on a named latent-cache workload instead "
                          "(deepseek_mla_b64, deepseek_lite_mla_b8)")
+    ap.add_argument("--vector-decode", action="store_true",
+                    help="load libpkv_vector.so: every decode on the vector kernel (the "
+                         "baseline the matrix-core kernel is measured against)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only time a plain device-to-device copy of this many MiB (the "
                          "reference kernel for scaling FETCH_SIZE / WRITE_SIZE counters)")
@@ -98,6 +101,8 @@ def copy_calibration(mib, reps):
 
 def main():
     args = parse()
+    if args.vector_decode:
+        os.environ["PKV_LIB"] = os.path.join(ROOT, "paged_kv_cache_25_amd", "libpkv_vector.so")
     if args.gpus != 1:
         print(json.dumps({"error": "bench.py runs on one GPU only: the decode path "
                           "shards by sequence or KV head with no exchange, so N GPUs run N "
@@ -286,7 +291,10 @@ def main():
     roof_bytes = tr["kv_bytes"] + tr["scale_bytes"]
     kernel_gbps = roof_bytes / (decode_ms * 1e-3) / 1e9
 
-    traffic_bytes = measured_traffic(inp.name, P) if args.seed is None else None
+    mfma = (inp.q_dtype == "bf16" and inp.kv_dtype == "bf16" and Hq // Hkv >= 2
+            and not args.vector_decode)
+    kernel_name = "paged_decode_mfma_kernel" if mfma else "paged_decode_kernel"
+    traffic_bytes = measured_traffic(inp.name, P, kernel_name) if args.seed is None else None
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(inp, args.cpu_budget_s)
@@ -315,9 +323,7 @@ def main():
                       ("plan_and_merge" if balanced else "merge"): round(merge_ms * 1e3, 2),
                       "attention_call": round(att_ms * 1e3, 2),
                       "step_as_two_calls": round(two_call_ms * 1e3, 2)},
-        "roofline": {"kernel": ("paged_decode_mfma_kernel" if (inp.q_dtype == "bf16" and
-                                inp.kv_dtype == "bf16" and Hq // Hkv >= 2)
-                                else "paged_decode_kernel") + f"<{D}>",
+        "roofline": {"kernel": f"{kernel_name}<{D}>",
                      "bound": "hbm",
                      "achieved": round(kernel_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(kernel_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic_bytes,
@@ -467,7 +473,8 @@ def main_multi(args):
     if balanced:
         ws_bytes = int(lib.pkv_multi_query_balanced_workspace_bytes(B, mq, Hq, Hkv, D, qcode,
                                                                     kvcode))
-        maxp = 1                         # (no partials call: the balanced call is timed whole)
+        slots = int(lib.pkv_multi_query_plan_slots(B, mq, Hq, Hkv, D, qcode, kvcode))
+        maxp = 1
     else:
         ws_bytes = ops.multi_query_workspace_bytes(R, Hq, D, mcl, P)
         maxp = max(1, -(-mcl // P)) if P else 1
@@ -491,16 +498,31 @@ def main_multi(args):
                ptr(c["qsl"]), B, R, mq, Hq, Hkv, D, 16, NB, MB, mcl,
                ctypes.c_float(inp.softmax_scale), P, ptr(c["ws"]),
                ctypes.c_size_t(c["ws"].numel()), qcode, kvcode, sp)
-        # the decode kernel alone (same grid and work, partials for every row)
-        c["parts"] = torch.empty(lse_off + R * Hq * maxp * 4, dtype=torch.uint8, device=dev)
-        prt = (V(c["parts"].data_ptr()), V(c["parts"].data_ptr() + lse_off), maxp, ptr(c["q"]),
-               ptr(c["k_pool"]), ptr(c["v_pool"]), ptr(c["k_scales"]), ptr(c["v_scales"]),
-               ptr(c["tables"]), ptr(c["lens"]), ptr(c["qsl"]), B, R, mq, Hq, Hkv, D, 16, NB, MB,
-               ctypes.c_float(inp.softmax_scale), P, qcode, kvcode, sp)
+        if balanced:
+            # the decode kernel alone on the call's slots: chunk rows [R, max_q, Hq, D]
+            rows = slots * mq * Hq
+            b_lse = ((rows * D * 4 + 255) // 256) * 256
+            c["parts"] = torch.empty(b_lse + rows * 4, dtype=torch.uint8, device=dev)
+            c["plan"] = torch.empty(int(lib.pkv_decode_plan_bytes(B, slots)), dtype=torch.uint8,
+                                    device=dev)
+            prt = (V(c["parts"].data_ptr()), V(c["parts"].data_ptr() + b_lse), ptr(c["plan"]),
+                   ctypes.c_size_t(c["plan"].numel()), slots, ptr(c["q"]), ptr(c["k_pool"]),
+                   ptr(c["v_pool"]), ptr(c["k_scales"]), ptr(c["v_scales"]), ptr(c["tables"]),
+                   ptr(c["lens"]), ptr(c["qsl"]), B, R, mq, Hq, Hkv, D, 16, NB, MB,
+                   ctypes.c_float(inp.softmax_scale), qcode, kvcode, sp)
+        else:
+            # the decode kernel alone (same grid and work, partials for every row)
+            c["parts"] = torch.empty(lse_off + R * Hq * maxp * 4, dtype=torch.uint8, device=dev)
+            prt = (V(c["parts"].data_ptr()), V(c["parts"].data_ptr() + lse_off), maxp,
+                   ptr(c["q"]), ptr(c["k_pool"]), ptr(c["v_pool"]), ptr(c["k_scales"]),
+                   ptr(c["v_scales"]), ptr(c["tables"]), ptr(c["lens"]), ptr(c["qsl"]), B, R, mq,
+                   Hq, Hkv, D, 16, NB, MB, ctypes.c_float(inp.softmax_scale), P, qcode, kvcode,
+                   sp)
         calls.append((app, att, prt))
 
     f_app, f_att = lib.pkv_kv_append_tokens, lib.pkv_paged_multi_query_attention
-    f_prt = lib.pkv_paged_multi_query_partials
+    f_prt = (lib.pkv_paged_multi_query_partials_planned if balanced
+             else lib.pkv_paged_multi_query_partials)
 
     def step(i):
         app, att, _ = calls[i % n_copies]
@@ -529,12 +551,11 @@ def main_multi(args):
 
     reps = args.kernel_reps
     att_ms = timed(att_only, reps)
-    # The balanced split has no partials entry point for several tokens: its
-    # roofline is taken over the whole call (decode kernel planning its
-    # chunks, then the merge), a lower bound on the decode kernel's own rate.
-    decode_ms = att_ms if balanced else timed(decode_only, reps)
+    # the decode kernel alone: the partials call (the balanced split's plans
+    # its chunks inside the kernel, as the attention call does)
+    decode_ms = timed(decode_only, reps)
     append_ms = timed(append_only, reps)
-    merge_ms = max(att_ms - decode_ms, 0.0) if maxp > 1 else 0.0
+    merge_ms = max(att_ms - decode_ms, 0.0) if (maxp > 1 or balanced) else 0.0
 
     t_new = np.diff(inp.query_start_loc)
     tr = traffic.multi_query_traffic(inp.context_lens, t_new, num_q_heads=Hq, num_kv_heads=Hkv,
@@ -565,13 +586,10 @@ def main_multi(args):
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "steps_per_s": round(1e3 / step_ms, 1),
         "new_tokens_per_s": round(R * 1e3 / step_ms, 1),
-        "kernel_us": ({"append": round(append_ms * 1e3, 2),
-                       "attention_call": round(att_ms * 1e3, 2)} if balanced else
-                      {"append": round(append_ms * 1e3, 2), "decode": round(decode_ms * 1e3, 2),
-                       "merge": round(merge_ms * 1e3, 2), "attention_call": round(att_ms * 1e3, 2)}),
+        "kernel_us": {"append": round(append_ms * 1e3, 2), "decode": round(decode_ms * 1e3, 2),
+                      "merge": round(merge_ms * 1e3, 2), "attention_call": round(att_ms * 1e3, 2)},
         "roofline": {"kernel": ("paged_decode_mfma_kernel" if mfma else "paged_decode_kernel")
-                               + f"<{D}> (several new tokens)"
-                               + (" + merge_kernel" if balanced else ""),
+                               + f"<{D}> (several new tokens)",
                      "bound": "hbm", "achieved": round(kernel_gbps, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(kernel_gbps / HBM_PEAK_GBPS, 4),
                      "traffic": None, "algorithmic_bytes_per_launch": tr["kv_bytes"],
@@ -911,33 +929,44 @@ def cpu_baseline_multi(inp, budget_s):
             "new_tokens_per_s": round(int(t_new.sum()) / elapsed, 3)}
 
 
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "paged_decode_mfma_llama3_8b_b64_traffic.txt")
-KERNEL_SOURCES = ("paged_kv_cache_25_amd/csrc/paged_decode_mfma.hip",
-                  "paged_kv_cache_25_amd/csrc/pkv_device.h",
-                  "paged_kv_cache_25_amd/csrc/pkv_launch.h")
+PROFILES = os.path.join(ROOT, "profiles")
 
 
-def measured_traffic(workload, partition_size):
-    """HBM bytes per decode launch from the committed rocprofv3 counter summary,
-    or None when the workload or partition differs or the kernel sources
-    changed since."""
-    import hashlib
-    if workload != "llama3_8b_b64" or not os.path.exists(TRAFFIC_FILE):
-        return None
+def _traffic_fields(path):
+    """The machine-readable 'key: value' lines of a profiles/*_traffic.txt summary."""
     fields = {}
-    for line in open(TRAFFIC_FILE):
+    for line in open(path):
         if ":" in line and line.split(":", 1)[0].strip().replace("_", "").isalnum():
             k, v = line.split(":", 1)
             fields[k.strip()] = v.strip()
-    if fields.get("partition_size") != str(partition_size):
-        return None
+    return fields
+
+
+def sources_sha256(rels):
+    import hashlib
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in rels:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
-    if fields.get("kernel_source_sha256") != h.hexdigest():
-        return None
-    return int(fields["traffic_bytes_per_launch"])
+    return h.hexdigest()
+
+
+def measured_traffic(workload, partition_size, kernel):
+    """HBM bytes per launch of ``kernel`` (a name prefix: paged_decode_mfma_kernel,
+    paged_decode_kernel, mla_decode_kernel) on ``workload`` at ``partition_size``,
+    from a committed rocprofv3 counter summary (profiles/*_traffic.txt, copy
+    calibrated); None when no summary matches or the kernel's sources, listed
+    in the summary, no longer hash to what was measured."""
+    import glob
+    for path in sorted(glob.glob(os.path.join(PROFILES, "*_traffic.txt"))):
+        f = _traffic_fields(path)
+        if (f.get("workload") != workload or f.get("kernel") != kernel
+                or f.get("partition_size") != str(partition_size)):
+            continue
+        rels = [r.strip() for r in f.get("kernel_sources", "").split(",") if r.strip()]
+        if rels and sources_sha256(rels) == f.get("kernel_source_sha256"):
+            return int(f["traffic_bytes_per_launch"])
+    return None
 
 
 def host_description():

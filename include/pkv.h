@@ -502,6 +502,49 @@ pkv_status_t pkv_paged_multi_query_partials(
     pkv_dtype_t q_dtype, pkv_dtype_t kv_dtype, void* stream);
 
 /*
+ * The balanced split with several new tokens per sequence, decode half alone
+ * (what pkv_paged_multi_query_attention with PKV_PARTITION_BALANCED runs
+ * before its merge; for callers that time the decode kernel or merge chunk
+ * results themselves).
+ *
+ * pkv_multi_query_plan_slots - R, the chunk slots that call uses for this
+ * shape, max_query_len and dtype pair (see PKV_PARTITION_BALANCED: S = 3072,
+ * or 2048 when a wave holds two 16-column tiles, divided by num_kv_heads x
+ * column chunks); 0 for invalid arguments.
+ *
+ * pkv_paged_multi_query_partials_planned - schedules the batch over
+ * num_slots slots exactly as pkv_paged_decode_partials_planned does (plan
+ * [device, written], its layout and the PKV_ERR_WORKSPACE rule as there) and
+ * runs the chunks.  For slot s of sequence b and its new token j < t_b it
+ * writes, for every query head i, the normalised partial output over the
+ * chunk's tokens that token j sees (positions up to ctx_b - t_b + j) to
+ * partial_out[s][j][i][:] and their natural-log log-sum-exp to
+ * partial_lse[s][j][i] (-inf when it sees none of them; partial_out then
+ * holds nothing meaningful); rows j >= t_b and slots past the last chunk are
+ * not written.  The
+ * log-sum-exp merge of a row over its sequence's slots chunk_first[b] ..
+ * chunk_first[b+1]-1 gives pkv_paged_multi_query_attention's output.
+ *   KV-cache post, "A KV cache in PyTorch" (the shifted causal mask of
+ *   attn_cached); serving lesson, "Where it shows up" (split-KV decoding).
+ *
+ * partial_out float32 [num_slots, max_query_len, num_q_heads, head_dim] and
+ * partial_lse float32 [num_slots, max_query_len, num_q_heads] [device,
+ * written]; num_slots >= num_seqs; the rest as for
+ * pkv_paged_multi_query_attention.
+ */
+int32_t pkv_multi_query_plan_slots(int32_t num_seqs, int32_t max_query_len,
+                                   int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                   pkv_dtype_t q_dtype, pkv_dtype_t kv_dtype);
+pkv_status_t pkv_paged_multi_query_partials_planned(
+    float* partial_out, float* partial_lse, void* plan, size_t plan_bytes, int32_t num_slots,
+    const void* q, const void* k_pool, const void* v_pool, const float* k_scales,
+    const float* v_scales, const int32_t* block_tables, const int32_t* context_lens,
+    const int32_t* query_start_loc, int32_t num_seqs, int32_t num_tokens, int32_t max_query_len,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+    int32_t num_blocks, int32_t max_blocks_per_seq, float softmax_scale, pkv_dtype_t q_dtype,
+    pkv_dtype_t kv_dtype, void* stream);
+
+/*
  * pkv_kv_append_quant - append new K/V rows given in bf16 or float32 to an
  * e4m3 cache, quantising them with their (block, KV head) scale: the code of
  * a value x is encode(f32(x / s)), one correctly rounded float32 division

@@ -3,6 +3,12 @@
 ``python -m paged_kv_cache_25_amd.build`` compiles every ``csrc/*.hip`` with
 hipcc (and the host-only ``csrc/*.cpp`` with g++) into objects under
 ``_build/`` and links ``libpkv.so`` next to this file.  Packed-fp32 instructions are disabled for the device code.
+
+It also links ``libpkv_vector.so``: the same objects except ``pkv_api.hip``
+compiled with ``-DPKV_DECODE_VECTOR_ONLY``, which sends every decode to the
+vector kernel (bf16 query groups included).  It is the baseline the
+matrix-core kernel is profiled against; ``PKV_LIB`` (or ``bench.py
+--vector-decode``) loads it in place of ``libpkv.so``.
 """
 
 from __future__ import annotations
@@ -20,6 +26,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libpkv.so")
+LIB_VECTOR = os.path.join(PKG, "libpkv_vector.so")
+VECTOR_SRC = "pkv_api.hip"
 ARCH = os.environ.get("PKV_OFFLOAD_ARCH", "gfx950")
 
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
@@ -34,32 +42,40 @@ CXX = shutil.which("g++") or "g++"
 CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", f"-I{INCLUDE}"]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
+def _compile(src: str, defines=(), suffix="") -> str:
+    obj = os.path.join(BUILD, os.path.basename(src) + suffix + ".o")
     if src.endswith(".cpp"):                  # host-only code (the block allocator)
         cmd = [CXX, *CXX_FLAGS, "-c", src, "-o", obj]
     else:
-        cmd = [HIPCC, *FLAGS, "-c", src, "-o", obj]
+        cmd = [HIPCC, *FLAGS, *[f"-D{d}" for d in defines], "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
-    workers = min(len(srcs), int(os.environ.get("MAX_JOBS", "8")))
-    with concurrent.futures.ThreadPoolExecutor(max_workers=workers) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB + ".tmp"
+def _link(objs, lib):
+    tmp = lib + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
+    workers = min(len(srcs) + 1, int(os.environ.get("MAX_JOBS", "8")))
+    api = os.path.join(CSRC, VECTOR_SRC)
+    with concurrent.futures.ThreadPoolExecutor(max_workers=workers) as ex:
+        vec = ex.submit(_compile, api, ("PKV_DECODE_VECTOR_ONLY",), ".vector")
+        objs = list(ex.map(_compile, srcs))
+        vec_obj = vec.result()
+    _link(objs, LIB)
+    _link([vec_obj if os.path.basename(o) == VECTOR_SRC + ".o" else o for o in objs], LIB_VECTOR)
     if verbose:
-        print(f"built {LIB} from {len(srcs)} sources")
+        print(f"built {LIB} and {os.path.basename(LIB_VECTOR)} from {len(srcs)} sources")
     return LIB
 
 

@@ -1,16 +1,17 @@
 // Log-sum-exp merge of split-KV partial results, for gfx950.
 //
-// One workgroup per (sequence, query head): one wave when every sequence's
-// partition rows fit in one batch or the batch is large, else 256 threads.  A row group reads one
-// partition row with 16-byte loads (D/4 threads for float32 rows, D/8 for
-// the bf16 rows of the balanced MLA split) and keeps eight rows in flight
-// (four for bf16 rows; 64 rows per 256 threads for D=128); the
-// first batch is issued together with the pass that finds M = max lse over the
-// partitions that count.  Each group accumulates sum_p exp(lse_p - M) o_p over
-// its partitions, and the groups are summed in LDS and divided by the summed
-// weights.  Partitions that do not count (past
-// the sequence's count, or with lse = -inf) are skipped, never multiplied by a
-// zero weight, so whatever they hold cannot reach the output.
+// For each merged (row, head) item: M = max lse over the partitions that
+// count, out = sum_p exp(lse_p - M) o_p / sum_p exp(lse_p - M).  Partitions
+// that do not count (past the row's count, or with lse = -inf) are skipped,
+// never multiplied by a zero weight, so whatever they hold cannot reach the
+// output.  A row group of D/4 threads (D/8 for the bf16 rows of the balanced
+// MLA split) reads one partition row with 16-byte loads, several rows in
+// flight.  Two launch shapes:
+//   - very many items with few partitions each (several new tokens per
+//     sequence): merge_items_kernel, several items per 256-thread workgroup,
+//     one row group per item reading all of its partitions;
+//   - otherwise merge_kernel, one workgroup per item, its row groups taking
+//     every kGroups-th partition, summed in LDS.
 //   learn.mohebi.ai serving lesson, "PagedAttention" and "Where it shows up":
 //   partial attention results merged with the online-softmax update.
 #include "pkv_device.h"
@@ -21,40 +22,29 @@ namespace {
 
 constexpr int kThreads = 256;
 
-template <int N>
-struct VecF {
-  float v[N];
+// The merged row of grid item `item` = (row, head) (with several new tokens
+// per sequence: (sequence, new token j, head)) and where its partitions lie.
+// False: nothing to merge (no such token, or a single partition the decode
+// kernel already wrote as the final output).
+struct MergeItem {
+  size_t row;          // row of out: b * num_q_heads + head
+  int np;              // partitions that may count
+  size_t base, stride; // partition p of the row: partial row base + p * stride
 };
 
-template <int D, typename OT, bool kBf16Part>
-__global__ __launch_bounds__(kThreads) void merge_kernel(MergeArgs a) {
-  constexpr int kVec = kBf16Part ? 8 : 4;         // 16 bytes of a row per thread and load
-  constexpr int kRowThreads = D / kVec;           // threads covering one partition row
-  constexpr int kMaxGroups = kThreads / kRowThreads;
-  constexpr int kUnroll = kBf16Part ? 4 : 8;      // rows in flight per row group
-  using Vec = VecF<kVec>;
-  __shared__ Vec s_acc[kMaxGroups][kRowThreads];
-  __shared__ float s_w[kMaxGroups];
-  __shared__ float s_max[kThreads / kWave];
-  const int kGroups = blockDim.x / kRowThreads;   // row groups in this launch
-  const int n_waves = blockDim.x / kWave;
-
-  const int qh = blockIdx.x % a.num_q_heads;
-  const int b = blockIdx.x / a.num_q_heads;
-  const int t = threadIdx.x;
-  const int g = t / kRowThreads, c = t % kRowThreads;
-
-  // Row b's sequence (several new tokens per sequence: the last s with
-  // q_start[s] <= b) and its new token j there.
-  int seq = b, j = 0;
-  if (a.q_start && (a.chunk_first || a.context_lens)) {
-    int lo = 0, hi = a.num_batch - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (a.q_start[mid] <= b) lo = mid; else hi = mid - 1;
-    }
-    seq = lo;
-    j = b - a.q_start[seq];
+__device__ inline bool merge_item(const MergeArgs& a, int item, MergeItem& it) {
+  const int qh = item % a.num_q_heads;
+  // The row (b) and, with several new tokens per sequence, its sequence and
+  // new token j there: the row is q_start[seq] + j, loaded together with the
+  // sequence's partition bounds.
+  int b = item / a.num_q_heads, seq = b, j = 0;
+  if (a.q_start) {
+    const int sj = b;                              // seq * rows_per_seq + j
+    seq = sj / a.rows_per_seq;
+    j = sj - seq * a.rows_per_seq;
+    const int r0 = a.q_start[seq];
+    if (j >= a.q_start[seq + 1] - r0) return false;    // no such token
+    b = r0 + j;
   }
   const int slot_rows = a.slot_rows > 1 ? a.slot_rows : 1;
   int np = a.max_partitions;
@@ -70,35 +60,67 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(MergeArgs a) {
     np = ctx <= 0 ? 0 : (ctx + a.partition_size - 1) / a.partition_size;
   }
   np = np < 0 ? 0 : (np > a.max_partitions ? a.max_partitions : np);
-  if (a.skip_single && np == 1) return;           // already final (uniform: whole block)
-
-  const size_t row = size_t(b) * a.num_q_heads + qh;
+  if (a.skip_single && np == 1) return false;     // already final
+  it.row = size_t(b) * a.num_q_heads + qh;
+  it.np = np;
   // Partition p of this row: rows [b, H, max_partitions] (stride 1), or, for
   // a balanced split, chunk slot chunk_first[seq] + p of rows [slot,
   // slot_rows, H] (stride slot_rows * H).
-  const size_t base = a.chunk_first ? (size_t(first) * slot_rows + j) * a.num_q_heads + qh
-                                    : row * a.max_partitions;
-  const size_t stride = a.chunk_first ? size_t(slot_rows) * a.num_q_heads : 1;
-  const float* lse_base = a.part_lse + base;
-  const size_t o_off = base * D + size_t(kVec) * c;        // elements, float32 or bf16
-  auto lse_at = [&](int p) { return lse_base[size_t(p) * stride]; };
-  auto row_at = [&](int p) {
-    Vec r;
-    if constexpr (kBf16Part) {
-      const uint4 w = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.part_o) +
-                                                      o_off + size_t(p) * stride * D);
-      const uint32_t x[4] = {w.x, w.y, w.z, w.w};
+  it.base = a.chunk_first ? (size_t(first) * slot_rows + j) * a.num_q_heads + qh
+                          : it.row * a.max_partitions;
+  it.stride = a.chunk_first ? size_t(slot_rows) * a.num_q_heads : 1;
+  return true;
+}
+
+template <int N>
+struct VecF {
+  float v[N];
+};
+
+// Partition p's 16 bytes of row data for thread c of a row group: float32
+// rows, or bf16 rows widened to float32.
+template <int D, bool kBf16Part>
+__device__ __forceinline__ VecF<kBf16Part ? 8 : 4> merge_row_at(const MergeArgs& a,
+                                                                const MergeItem& it, int c, int p) {
+  constexpr int kVec = kBf16Part ? 8 : 4;
+  const size_t off = (it.base + size_t(p) * it.stride) * D + size_t(kVec) * c;
+  VecF<kVec> r;
+  if constexpr (kBf16Part) {
+    const uint4 w = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.part_o) + off);
+    const uint32_t x[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        r.v[2 * e] = __uint_as_float(x[e] << 16);
-        r.v[2 * e + 1] = __uint_as_float(x[e] & 0xffff0000u);
-      }
-    } else {
-      const float4 f = *reinterpret_cast<const float4*>(a.part_o + o_off + size_t(p) * stride * D);
-      r.v[0] = f.x; r.v[1] = f.y; r.v[2] = f.z; r.v[3] = f.w;
+    for (int e = 0; e < 4; ++e) {
+      r.v[2 * e] = __uint_as_float(x[e] << 16);
+      r.v[2 * e + 1] = __uint_as_float(x[e] & 0xffff0000u);
     }
-    return r;
-  };
+  } else {
+    const float4 f = *reinterpret_cast<const float4*>(a.part_o + off);
+    r.v[0] = f.x; r.v[1] = f.y; r.v[2] = f.z; r.v[3] = f.w;
+  }
+  return r;
+}
+
+template <int D, typename OT, bool kBf16Part>
+__global__ __launch_bounds__(kThreads) void merge_kernel(MergeArgs a) {
+  constexpr int kVec = kBf16Part ? 8 : 4;         // 16 bytes of a row per thread and load
+  constexpr int kRowThreads = D / kVec;           // threads covering one partition row
+  constexpr int kMaxGroups = kThreads / kRowThreads;
+  constexpr int kUnroll = kBf16Part ? 4 : 8;      // rows in flight per row group
+  using Vec = VecF<kVec>;
+  __shared__ Vec s_acc[kMaxGroups][kRowThreads];
+  __shared__ float s_w[kMaxGroups];
+  __shared__ float s_max[kThreads / kWave];
+  const int kGroups = blockDim.x / kRowThreads;   // row groups in this launch
+  const int n_waves = blockDim.x / kWave;
+  const int t = threadIdx.x;
+  const int g = t / kRowThreads, c = t % kRowThreads;
+
+  MergeItem it;
+  if (!merge_item(a, blockIdx.x, it)) return;     // uniform: the whole block
+  const int np = it.np;
+  const size_t row = it.row;
+  auto lse_at = [&](int p) { return a.part_lse[it.base + size_t(p) * it.stride]; };
+  auto row_at = [&](int p) { return merge_row_at<D, kBf16Part>(a, it, c, p); };
   const Vec zero = {};
 
   // First batch of rows and their lse, issued together with the max pass.
@@ -169,9 +191,73 @@ struct OutBF16 {
   }
 };
 
+// Rows with few partitions: several (row, head) items per workgroup, one row
+// group of D/4 threads (D/8 for bf16 rows) per item, which reads all of the
+// item's partitions itself (kUnroll rows in flight) and needs no LDS or
+// barrier.  Fewer, fuller workgroups than one per item: at 16 new tokens per
+// sequence a step has 32,768 items of two partitions each.
+template <int D, typename OT, bool kBf16Part>
+__global__ __launch_bounds__(kThreads) void merge_items_kernel(MergeArgs a, int n_items) {
+  constexpr int kVec = kBf16Part ? 8 : 4;
+  constexpr int kRowThreads = D / kVec;
+  constexpr int kItems = kThreads / kRowThreads;  // items per workgroup
+  constexpr int kUnroll = kBf16Part ? 4 : 8;
+  using Vec = VecF<kVec>;
+  const int item = blockIdx.x * kItems + threadIdx.x / kRowThreads;
+  const int c = threadIdx.x % kRowThreads;
+  if (item >= n_items) return;
+  MergeItem it;
+  if (!merge_item(a, item, it)) return;           // uniform over the row group
+  const int np = it.np;
+  auto lse_at = [&](int p) { return a.part_lse[it.base + size_t(p) * it.stride]; };
+  const Vec zero = {};
+
+  // First batch of rows with their lse; the maximum over every partition.
+  Vec rowv[kUnroll];
+  float lp[kUnroll];
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u) {
+    lp[u] = u < np ? lse_at(u) : -INFINITY;
+    rowv[u] = u < np ? merge_row_at<D, kBf16Part>(a, it, c, u) : zero;
+  }
+  float M = -INFINITY;
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u) M = fmaxf(M, lp[u]);
+  for (int p = kUnroll; p < np; ++p) M = fmaxf(M, lse_at(p));
+
+  // -inf partitions never count.
+  Vec acc = zero;
+  float wsum = 0.0f;
+  if (M > -INFINITY) {
+    for (int p0 = 0;;) {
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        if (lp[u] == -INFINITY) continue;
+        const float w = __expf(lp[u] - M);
+        wsum += w;
+#pragma unroll
+        for (int e = 0; e < kVec; ++e) acc.v[e] = fmaf(w, rowv[u].v[e], acc.v[e]);
+      }
+      p0 += kUnroll;
+      if (p0 >= np) break;
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const int p = p0 + u;
+        lp[u] = p < np ? lse_at(p) : -INFINITY;
+        rowv[u] = p < np ? merge_row_at<D, kBf16Part>(a, it, c, p) : zero;
+      }
+    }
+  }
+  const float inv = wsum > 0.0f ? 1.0f / wsum : 0.0f;
+  char* orow = reinterpret_cast<char*>(a.out) + it.row * D * sizeof(typename OT::Storage);
+#pragma unroll
+  for (int e = 0; e < kVec; ++e) OT::store(orow, kVec * c + e, acc.v[e] * inv);
+}
+
 template <int D, bool kBf16Part = false>
 hipError_t launch_d(const MergeArgs& a, DType out_dtype, hipStream_t stream) {
-  const size_t grid = size_t(a.num_seqs) * a.num_q_heads;
+  const size_t grid = (a.q_start ? size_t(a.num_batch) * a.rows_per_seq : size_t(a.num_seqs)) *
+                      a.num_q_heads;
   if (grid == 0) return hipSuccess;
   if (grid > 0x7fffffffu) return hipErrorInvalidConfiguration;
   // One wave per (sequence, head) when its rows fit one batch (kUnroll rows
@@ -182,6 +268,22 @@ hipError_t launch_d(const MergeArgs& a, DType out_dtype, hipStream_t stream) {
                                  : a.max_partitions;     // partial rows per merged row
   constexpr int kRowThreads = D / (kBf16Part ? 8 : 4);   // 16 bytes of a row per thread
   constexpr int kUnroll = kBf16Part ? 4 : 8;              // rows in flight per row group
+  // Very many items with few partitions each (16 new tokens per sequence:
+  // 32,768 items of two partitions): several items per workgroup, a row group
+  // each.  Measured at 12.2 us there against 16.2 us one workgroup per item;
+  // at 8,192 items (MLA) the two shapes tie, at 2,048 (one new token) the
+  // workgroup per item is faster (4.7 against 5.2 us).
+  if (kRowThreads <= kWave && rows <= 2 * kUnroll && grid >= 16384) {
+    constexpr int kItems = kThreads / kRowThreads;
+    const size_t blocks = (grid + kItems - 1) / kItems;
+    if (out_dtype == DType::F32)
+      hipLaunchKernelGGL((merge_items_kernel<D, OutF32, kBf16Part>), dim3(unsigned(blocks)),
+                         dim3(kThreads), 0, stream, a, int(grid));
+    else
+      hipLaunchKernelGGL((merge_items_kernel<D, OutBF16, kBf16Part>), dim3(unsigned(blocks)),
+                         dim3(kThreads), 0, stream, a, int(grid));
+    return hipGetLastError();
+  }
   const bool one_batch = rows * kRowThreads <= kUnroll * kWave;
   int threads = (one_batch || grid >= 4096) ? kWave : kThreads;
   threads = threads < kRowThreads ? kRowThreads : threads;   // one row group reads a whole row

@@ -581,9 +581,18 @@ pkv_status_t check_decode(const void* q, const void* k_pool, const void* v_pool,
 
 // bf16 queries over a bf16 cache run on the matrix cores when 2 or more
 // queries share each KV head (the group's heads times the new tokens); every
-// other combination on the vector kernel.
+// other combination on the vector kernel.  Built with
+// -DPKV_DECODE_VECTOR_ONLY (libpkv_vector.so), every decode runs on the
+// vector kernel: the build that the matrix-core choice is measured against.
 bool uses_mfma(pkv_dtype_t q_dtype, pkv_dtype_t kv_dtype, int64_t columns) {
+#ifdef PKV_DECODE_VECTOR_ONLY
+  (void)q_dtype;
+  (void)kv_dtype;
+  (void)columns;
+  return false;
+#else
   return q_dtype == PKV_BF16 && kv_dtype == PKV_BF16 && columns >= 2;
+#endif
 }
 
 pkv::DecodeArgs decode_args(const void* q, const void* k_pool, const void* v_pool,
@@ -1217,6 +1226,7 @@ pkv_status_t pkv_paged_multi_query_attention(
     m.skip_single = 1;
     m.q_start = query_start_loc;
     m.num_batch = num_seqs;
+    m.rows_per_seq = max_query_len;
     m.chunk_first = reinterpret_cast<const int32_t*>(plan);
     m.slot_rows = max_query_len;
     return pkv::launch_merge(m, head_dim, to_internal(q_dtype), st) == hipSuccess ? PKV_OK
@@ -1260,6 +1270,7 @@ pkv_status_t pkv_paged_multi_query_attention(
   m.skip_single = 1;
   m.q_start = query_start_loc;
   m.num_batch = num_seqs;
+  m.rows_per_seq = max_query_len;
   return pkv::launch_merge(m, head_dim, to_internal(q_dtype), st) == hipSuccess ? PKV_OK
                                                                                 : PKV_ERR_HIP;
 }
@@ -1293,6 +1304,57 @@ pkv_status_t pkv_paged_multi_query_partials(
   a.mark_empty = 1;
   return launch_decode(a, head_dim, ms.tile, ms.mfma, q_dtype, kv_dtype,
                        static_cast<hipStream_t>(stream)) == hipSuccess
+             ? PKV_OK
+             : PKV_ERR_HIP;
+}
+
+int32_t pkv_multi_query_plan_slots(int32_t num_seqs, int32_t max_query_len,
+                                   int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                   pkv_dtype_t q_dtype, pkv_dtype_t kv_dtype) {
+  if (num_seqs <= 0 || max_query_len <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
+      num_q_heads % num_kv_heads != 0 || !head_dim_ok(head_dim) || !dtype_ok(q_dtype) ||
+      !dtype_ok(kv_dtype) || q_dtype == PKV_FP8_E4M3)
+    return 0;
+  const MultiKind k =
+      multi_kind(max_query_len, num_q_heads, num_kv_heads, head_dim, q_dtype, kv_dtype);
+  const int64_t slots =
+      decode_balanced_slots(num_seqs, int64_t(num_kv_heads) * k.chunks, multi_resident_waves(k));
+  return slots > 0x7fffffff ? 0 : int32_t(slots);
+}
+
+pkv_status_t pkv_paged_multi_query_partials_planned(
+    float* partial_out, float* partial_lse, void* plan, size_t plan_bytes, int32_t num_slots,
+    const void* q, const void* k_pool, const void* v_pool, const float* k_scales,
+    const float* v_scales, const int32_t* block_tables, const int32_t* context_lens,
+    const int32_t* query_start_loc, int32_t num_seqs, int32_t num_tokens, int32_t max_query_len,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+    int32_t num_blocks, int32_t max_blocks_per_seq, float softmax_scale, pkv_dtype_t q_dtype,
+    pkv_dtype_t kv_dtype, void* stream) {
+  if (num_slots <= 0 || num_slots < num_seqs) return PKV_ERR_INVALID_ARG;
+  MultiSetup ms;
+  const pkv_status_t st0 = multi_setup(
+      ms, q, k_pool, v_pool, k_scales, v_scales, block_tables, context_lens, query_start_loc,
+      num_seqs, num_tokens, max_query_len, num_q_heads, num_kv_heads, head_dim, block_size,
+      num_blocks, max_blocks_per_seq, softmax_scale, 0, q_dtype, kv_dtype);
+  if (st0 != PKV_OK || ms.nothing) return st0;
+  if (!plan || !aligned16(plan) || !partial_out || !partial_lse || !aligned16(partial_out) ||
+      !aligned4(partial_lse))
+    return PKV_ERR_INVALID_ARG;
+  if (int64_t(max_blocks_per_seq) * block_size > 0x7fffffff) return PKV_ERR_INVALID_ARG;
+  if (plan_bytes < plan_layout(num_seqs, num_slots).total) return PKV_ERR_WORKSPACE;
+  pkv::DecodeArgs& a = ms.a;
+  if (int64_t(num_slots) * num_kv_heads * a.head_chunks > 0x7fffffff) return PKV_ERR_INVALID_ARG;
+  a.out = nullptr;
+  a.part_o = partial_out;
+  a.part_lse = partial_lse;
+  a.blocks_per_partition = max_blocks_per_seq;
+  a.max_partitions = num_slots;
+  a.write_final = 0;
+  a.final_single = 0;
+  a.mark_empty = 1;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (!plan_decode(a, static_cast<char*>(plan), num_slots, block_size, st)) return PKV_ERR_HIP;
+  return launch_decode(a, head_dim, ms.tile, ms.mfma, q_dtype, kv_dtype, st) == hipSuccess
              ? PKV_OK
              : PKV_ERR_HIP;
 }

@@ -368,9 +368,12 @@ struct MergeArgs {
   int skip_single;                 // 1: sequences with one partition were written by the decode kernel
   // Several new tokens per sequence: row r (num_seqs above counts rows) belongs
   // to the sequence s with q_start[s] <= r < q_start[s+1], whose context_lens
-  // entry sets its partition count.  Null: row r is sequence r.
+  // entry sets its partition count.  Null: row r is sequence r.  The grid then
+  // runs (sequence, new token j < rows_per_seq, head): row q_start[s] + j,
+  // none for j >= q_start[s+1] - q_start[s].
   const int32_t* q_start;
   int num_batch;                   // sequences, when q_start is set
+  int rows_per_seq;                // most new tokens of a sequence, when q_start is set
   // Balanced split: partitions of sequence b are the chunk slots
   // chunk_first[b] .. chunk_first[b+1]-1; rows [slot, slot_rows, num_q_heads]
   // (slot_rows: the most new tokens of a sequence; 0 or 1 for one each).

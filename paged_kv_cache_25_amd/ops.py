@@ -14,7 +14,9 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libpkv.so")
+# PKV_LIB names another build of the library to load instead (libpkv_vector.so:
+# every decode on the vector kernel, the baseline of the matrix-core kernel).
+LIB_PATH = os.environ.get("PKV_LIB") or os.path.join(_HERE, "libpkv.so")
 
 PKV_F32, PKV_BF16, PKV_FP8_E4M3 = 0, 1, 2
 PKV_SCALE_FIXED, PKV_SCALE_RUNNING_AMAX = 0, 1
@@ -86,6 +88,12 @@ def load():
     L.pkv_paged_multi_query_attention.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I,
                                                   I, I, I, F, I, P, Z, ctypes.c_int,
                                                   ctypes.c_int, P]
+    L.pkv_multi_query_plan_slots.restype = I
+    L.pkv_multi_query_plan_slots.argtypes = [I, I, I, I, I, ctypes.c_int, ctypes.c_int]
+    L.pkv_paged_multi_query_partials_planned.restype = ctypes.c_int
+    L.pkv_paged_multi_query_partials_planned.argtypes = [P, P, P, Z, I, P, P, P, P, P, P, P, P, I,
+                                                         I, I, I, I, I, I, I, I, F, ctypes.c_int,
+                                                         ctypes.c_int, P]
     L.pkv_paged_multi_query_partials.restype = ctypes.c_int
     L.pkv_paged_multi_query_partials.argtypes = [P, P, I, P, P, P, P, P, P, P, P, I, I, I, I, I,
                                                  I, I, I, I, F, I, ctypes.c_int, ctypes.c_int, P]
@@ -509,6 +517,44 @@ def paged_multi_query_partials(partial_out, partial_lse, q, k_pool, v_pool, bloc
         _ptr(query_start_loc), B, T, int(max_query_len), hq, hkv, d, bs, nb,
         block_tables.shape[1], float(softmax_scale), int(partition_size), dtype_code(q.dtype),
         dtype_code(k_pool.dtype), _stream(stream)))
+    return partial_out, partial_lse
+
+
+def multi_query_plan_slots(num_seqs, max_query_len, num_q_heads, num_kv_heads, head_dim, q_dtype,
+                           kv_dtype):
+    """Chunk slots of a balanced multi-token split for this shape (pkv_multi_query_plan_slots)."""
+    n = int(load().pkv_multi_query_plan_slots(num_seqs, max_query_len, num_q_heads, num_kv_heads,
+                                              head_dim, dtype_code(q_dtype), dtype_code(kv_dtype)))
+    if n <= 0:
+        raise PkvError("pkv_multi_query_plan_slots", 1)
+    return n
+
+
+def paged_multi_query_partials_planned(partial_out, partial_lse, plan, q, k_pool, v_pool,
+                                       block_tables, context_lens, query_start_loc,
+                                       max_query_len, softmax_scale, k_scales=None,
+                                       v_scales=None, stream=None):
+    """Chunk results of a balanced multi-token split over R = partial_out.shape[0]
+    slots: partial_out [R, max_query_len, Hq, D] fp32, partial_lse [R,
+    max_query_len, Hq] fp32; the schedule is written into ``plan`` (uint8,
+    pkv_decode_plan_bytes(B, R) bytes)."""
+    nb, hkv, bs, d = _want_pools(k_pool, v_pool)
+    B = _want_tables(block_tables, context_lens)
+    _want("query_start_loc", query_start_loc, _I32, (B + 1,))
+    _want("q", q, _Q_DTYPES, (None, None, d))
+    T, hq, _ = q.shape
+    _want("partial_out", partial_out, _F32, (None, int(max_query_len), hq, d))
+    _want("partial_lse", partial_lse, _F32, (partial_out.shape[0], int(max_query_len), hq))
+    _want("plan", plan, (torch.uint8,), (None,))
+    _want_scales(k_scales, v_scales, nb, hkv)
+    _need_cuda(partial_out, partial_lse, plan, q, k_pool, v_pool, block_tables, context_lens,
+               query_start_loc, k_scales, v_scales)
+    _check("pkv_paged_multi_query_partials_planned", load().pkv_paged_multi_query_partials_planned(
+        _ptr(partial_out), _ptr(partial_lse), _ptr(plan), _nbytes(plan), partial_out.shape[0],
+        _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(k_scales), _ptr(v_scales), _ptr(block_tables),
+        _ptr(context_lens), _ptr(query_start_loc), B, T, int(max_query_len), hq, hkv, d, bs, nb,
+        block_tables.shape[1], float(softmax_scale), dtype_code(q.dtype), dtype_code(k_pool.dtype),
+        _stream(stream)))
     return partial_out, partial_lse
 
 

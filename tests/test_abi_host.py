@@ -37,6 +37,7 @@ def test_header_declares_the_entry_points():
         "pkv_paged_decode_partials",
         "pkv_merge_partials", "pkv_kv_append_tokens", "pkv_multi_query_workspace_bytes",
         "pkv_paged_multi_query_attention", "pkv_paged_multi_query_partials",
+        "pkv_multi_query_plan_slots", "pkv_paged_multi_query_partials_planned",
         "pkv_kv_append_quant", "pkv_bm_create", "pkv_bm_destroy", "pkv_bm_add_seq",
         "pkv_bm_fork", "pkv_bm_free_seq", "pkv_bm_append_slots", "pkv_bm_num_free",
         "pkv_bm_refcount", "pkv_bm_seq_len", "pkv_bm_free_list", "pkv_bm_block_tables",
