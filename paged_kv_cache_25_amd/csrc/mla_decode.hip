@@ -76,14 +76,20 @@ static_assert(kBlockSlices * kWave >= kBlockSize * kSlotsPerRow, "a block's rows
 
 // Maximum over lanes l, l ^ 16, l ^ 32 and l ^ 48 (the four token groups of a
 // head): each lane swap returns the two halves it exchanged, whose larger
-// element is the pairwise maximum in every lane.
+// element is the pairwise maximum in every lane.  (The swap's two results are
+// copied to scalars before the float casts: hipcc's __builtin_bit_cast of an
+// element of the returned vector reads element 0 whatever the index.)
+__device__ __forceinline__ float max_of_swap(int lo, int hi) {
+  return fmaxf(__builtin_bit_cast(float, lo), __builtin_bit_cast(float, hi));
+}
 __device__ __forceinline__ float max_over_groups(float v) {
   const int x = __builtin_bit_cast(int, v);
   const auto a = __builtin_amdgcn_permlane32_swap(x, x, false, false);
-  const float w = fmaxf(__builtin_bit_cast(float, a[0]), __builtin_bit_cast(float, a[1]));
-  const int y = __builtin_bit_cast(int, w);
+  const int a0 = a[0], a1 = a[1];
+  const int y = __builtin_bit_cast(int, max_of_swap(a0, a1));
   const auto b = __builtin_amdgcn_permlane16_swap(y, y, false, false);
-  return fmaxf(__builtin_bit_cast(float, b[0]), __builtin_bit_cast(float, b[1]));
+  const int b0 = b[0], b1 = b[1];
+  return max_of_swap(b0, b1);
 }
 
 // Two floats to bf16 (round to nearest even), low one first.
@@ -92,61 +98,62 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
          (uint32_t(__builtin_bit_cast(uint16_t, __bf16(hi))) << 16);
 }
 
-template <int WAVES>
-__global__ __launch_bounds__(WAVES * kWave) void mla_decode_kernel(MlaArgs a) {
-  constexpr int kThreads = WAVES * kWave;
-  __shared__ __attribute__((aligned(16))) uint16_t s_k0[kBufElems];
-  __shared__ __attribute__((aligned(16))) uint16_t s_k1[kBufElems];
-  constexpr int kSlicesPerWave = (kSlices + WAVES - 1) / WAVES;
-
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);   // uniform
-  const int lane = threadIdx.x % kWave;
-  const int g = lane >> 4, c = lane & 15;
-  const int cap = a.max_blocks_per_seq * kBlockSize;
-
-  // The workgroup's head chunk, sequence and blocks [blk_begin, blk_end); its
-  // partial rows are slot * num_heads + head with slot = the partition of the
-  // sequence (fixed partitions: rows [b, H, max_partitions]) or the chunk
-  // slot (balanced split: rows [slot, H]).
-  int chunk, b, blk_begin, blk_end, n_blk_seq, ctx;
+// The work of one workgroup: its head chunk, sequence b, context ctx and
+// blocks [blk_begin, blk_end); its partial rows are slot_row + head *
+// slot_stride with slot = the partition of the sequence (fixed partitions:
+// rows [b, H, max_partitions]) or the chunk slot (balanced split: rows
+// [slot, H]); final_out: the sequence has one chunk or partition, so the
+// output is written directly.
+struct MlaWork {
+  int chunk, b, blk_begin, blk_end, ctx;
   size_t slot_row, slot_stride;
   bool final_out;
+};
+
+// Derives the workgroup's work (the balanced split planned by wave 0 and
+// shared through LDS, or read from chunk_first, or a fixed partition).
+// False: nothing to do (uniform over the workgroup); a fixed partition past
+// its sequence's end then marks its partial rows empty when asked to
+// (kHeadsPerWave heads per wave).
+template <int WAVES, int kHeadsPerWave>
+__device__ __forceinline__ bool mla_work(const MlaArgs& a, int wave, int lane, MlaWork& w) {
+  constexpr int kThreads = WAVES * kWave;
+  const int cap = a.max_blocks_per_seq * kBlockSize;
+  int n_blk_seq;
   if (a.plan_first) {
     // Wave 0 plans the workgroup's chunk (pairs of blocks) and shares it.
-    chunk = blockIdx.x % a.head_chunks;
+    w.chunk = blockIdx.x % a.head_chunks;
     const int cs = blockIdx.x / a.head_chunks;           // chunk slot
-    const int cap_tok = a.max_blocks_per_seq * kBlockSize;
     __shared__ int s_plan[4];                            // sequence (-1: none), first pair, end pair, chunks
     if (wave == 0) {
       PlanChunk pc;
       int total_chunks;
-      const bool any = plan_slot(a.context_lens, a.num_seqs, cap_tok, 2 * kBlockSize,
+      const bool any = plan_slot(a.context_lens, a.num_seqs, cap, 2 * kBlockSize,
                                  a.max_partitions, cs, pc, total_chunks);
       if (lane == 0) {
         s_plan[0] = any ? pc.b : -1;
         s_plan[1] = pc.u_begin;
         s_plan[2] = pc.u_end;
         s_plan[3] = pc.n;
-        if (any && pc.u_begin == 0 && chunk == 0) {      // the sequence's first chunk
+        if (any && pc.u_begin == 0 && w.chunk == 0) {    // the sequence's first chunk
           a.plan_first[pc.b] = cs;
           if (pc.b == a.num_seqs - 1) a.plan_first[a.num_seqs] = total_chunks;
         }
       }
     }
     __syncthreads();
-    b = s_plan[0];
-    if (b < 0) return;                                   // a slot past the last chunk: uniform
-    const int raw_ctx = a.context_lens[b];
-    ctx = raw_ctx < 0 ? 0 : (raw_ctx > cap_tok ? cap_tok : raw_ctx);
-    n_blk_seq = (ctx + kBlockSize - 1) / kBlockSize;
-    blk_begin = 2 * s_plan[1];
-    blk_end = 2 * s_plan[2];
-    blk_end = blk_end < n_blk_seq ? blk_end : n_blk_seq;
-    final_out = s_plan[3] == 1;                          // (also a sequence with nothing to attend)
-    slot_row = size_t(cs) * a.num_heads;
-    slot_stride = 1;
+    w.b = s_plan[0];
+    if (w.b < 0) return false;                           // a slot past the last chunk
+    const int raw_ctx = a.context_lens[w.b];
+    w.ctx = raw_ctx < 0 ? 0 : (raw_ctx > cap ? cap : raw_ctx);
+    n_blk_seq = (w.ctx + kBlockSize - 1) / kBlockSize;
+    w.blk_begin = 2 * s_plan[1];
+    w.blk_end = 2 * s_plan[2];
+    w.final_out = s_plan[3] == 1;                        // (also a sequence with nothing to attend)
+    w.slot_row = size_t(cs) * a.num_heads;
+    w.slot_stride = 1;
   } else if (a.chunk_first) {
-    chunk = blockIdx.x % a.head_chunks;
+    w.chunk = blockIdx.x % a.head_chunks;
     const int cs = blockIdx.x / a.head_chunks;           // chunk slot (grid: every slot exists)
     __shared__ int s_seq;
     if (threadIdx.x == 0) s_seq = -1;
@@ -154,47 +161,120 @@ __global__ __launch_bounds__(WAVES * kWave) void mla_decode_kernel(MlaArgs a) {
     for (int s = threadIdx.x; s < a.num_seqs; s += kThreads)
       if (a.chunk_first[s] <= cs && cs < a.chunk_first[s + 1]) s_seq = s;
     __syncthreads();
-    b = s_seq;
-    if (b < 0) return;                                   // a slot past the last chunk: uniform
-    const int n_b = a.chunk_first[b + 1] - a.chunk_first[b];
-    const int k = cs - a.chunk_first[b];
-    const int raw_ctx = a.context_lens[b];
-    ctx = raw_ctx < 0 ? 0 : (raw_ctx > cap ? cap : raw_ctx);
-    n_blk_seq = (ctx + kBlockSize - 1) / kBlockSize;
+    w.b = s_seq;
+    if (w.b < 0) return false;                           // a slot past the last chunk
+    const int n_b = a.chunk_first[w.b + 1] - a.chunk_first[w.b];
+    const int k = cs - a.chunk_first[w.b];
+    const int raw_ctx = a.context_lens[w.b];
+    w.ctx = raw_ctx < 0 ? 0 : (raw_ctx > cap ? cap : raw_ctx);
+    n_blk_seq = (w.ctx + kBlockSize - 1) / kBlockSize;
     const int pairs = (n_blk_seq + 1) / 2;                // chunk k: pairs [k u / n, (k+1) u / n)
-    blk_begin = 2 * int(int64_t(k) * pairs / n_b);
-    blk_end = 2 * int(int64_t(k + 1) * pairs / n_b);
-    blk_end = blk_end < n_blk_seq ? blk_end : n_blk_seq;
-    final_out = n_b == 1;                                // (also a sequence with nothing to attend)
-    slot_row = size_t(cs) * a.num_heads;
-    slot_stride = 1;
+    w.blk_begin = 2 * int(int64_t(k) * pairs / n_b);
+    w.blk_end = 2 * int(int64_t(k + 1) * pairs / n_b);
+    w.final_out = n_b == 1;                              // (also a sequence with nothing to attend)
+    w.slot_row = size_t(cs) * a.num_heads;
+    w.slot_stride = 1;
   } else {
     int unit;
-    if (!decode_unit(blockIdx.x, a.head_chunks, a.num_seqs * a.max_partitions, chunk, unit)) return;
-    b = unit % a.num_seqs;
+    if (!decode_unit(blockIdx.x, a.head_chunks, a.num_seqs * a.max_partitions, w.chunk, unit))
+      return false;
+    w.b = unit % a.num_seqs;
     const int part = unit / a.num_seqs;
-    const int raw_ctx = a.context_lens[b];
-    ctx = raw_ctx < 0 ? 0 : (raw_ctx > cap ? cap : raw_ctx);
-    n_blk_seq = (ctx + kBlockSize - 1) / kBlockSize;
-    blk_begin = part * a.blocks_per_partition;
-    blk_end = blk_begin + a.blocks_per_partition;
-    blk_end = blk_end < n_blk_seq ? blk_end : n_blk_seq;
-    final_out = a.write_final || (a.final_single && n_blk_seq <= a.blocks_per_partition);
-    slot_row = size_t(b) * a.num_heads * a.max_partitions + part;
-    slot_stride = a.max_partitions;
+    const int raw_ctx = a.context_lens[w.b];
+    w.ctx = raw_ctx < 0 ? 0 : (raw_ctx > cap ? cap : raw_ctx);
+    n_blk_seq = (w.ctx + kBlockSize - 1) / kBlockSize;
+    w.blk_begin = part * a.blocks_per_partition;
+    w.blk_end = w.blk_begin + a.blocks_per_partition;
+    w.final_out = a.write_final || (a.final_single && n_blk_seq <= a.blocks_per_partition);
+    w.slot_row = size_t(w.b) * a.num_heads * a.max_partitions + part;
+    w.slot_stride = a.max_partitions;
     // (b, part) is uniform over the workgroup: every wave returns here or none.
-    if (blk_begin >= blk_end && !(a.write_final && part == 0)) {    // partition past the end
-      const int h = (chunk * WAVES + wave) * 16 + lane;
-      if (a.mark_empty && lane < 16 && h < a.num_heads)
-        a.part_lse[slot_row + size_t(h) * slot_stride] = -INFINITY;
-      return;
+    const int end = w.blk_end < n_blk_seq ? w.blk_end : n_blk_seq;
+    if (w.blk_begin >= end && !(a.write_final && part == 0)) {    // partition past the end
+      const int h = (w.chunk * WAVES + wave) * kHeadsPerWave + lane;
+      if (a.mark_empty && lane < kHeadsPerWave && h < a.num_heads)
+        a.part_lse[w.slot_row + size_t(h) * w.slot_stride] = -INFINITY;
+      return false;
     }
   }
+  w.blk_end = w.blk_end < n_blk_seq ? w.blk_end : n_blk_seq;
+  return true;
+}
+
+// Copies pairs of blocks into LDS.  Block ids of the workgroup's run, 64 at a
+// time in lane registers (lane i holds entry seg + i); a pair's two ids are
+// broadcast with readlane, so addresses and validity flags are wave-uniform.
+// Pair p goes to dst as 38 slices, one direct-to-LDS load of 64 16-byte
+// slots each, slice sl of block sl / 19, taken by wave sl % WAVES; lanes
+// whose slot is row padding, past the attended tokens (limit) or in a block
+// with a bad table entry load nothing.
+template <int WAVES>
+struct PairStage {
+  const int32_t* table;
+  const char* pool;
+  int blk_begin, blk_end, limit, num_blocks, wave, lane;
+  int seg = -kWave, my_id = 0;
+  uint64_t ok_mask = 0;
+
+  __device__ __forceinline__ void ids(int p, int& phys0, int& phys1, bool& ok0, bool& ok1) {
+    const int rel = 2 * p;                               // first block of the pair, from blk_begin
+    if (rel >= seg + kWave) {
+      seg = rel - rel % kWave;
+      const int blk = blk_begin + seg + lane;
+      my_id = blk < blk_end ? table[blk] : -1;
+      ok_mask = __ballot(unsigned(my_id) < unsigned(num_blocks));
+    }
+    const int k = rel - seg;
+    phys0 = __builtin_amdgcn_readlane(my_id, k);
+    phys1 = __builtin_amdgcn_readlane(my_id, k + 1);
+    ok0 = (ok_mask >> k) & 1;
+    ok1 = k + 1 < kWave && ((ok_mask >> (k + 1)) & 1);
+  }
+
+  __device__ __forceinline__ void stage(int p, uint16_t* dst, bool& ok0, bool& ok1) {
+    constexpr int kSlicesPerWave = (kSlices + WAVES - 1) / WAVES;
+    int phys0, phys1;
+    ids(p, phys0, phys1, ok0, ok1);
+    const int rem0 = limit - (blk_begin + 2 * p) * kBlockSize;   // rows of block 0 attended
+    const char* base0 = pool + size_t(unsigned(phys0)) * kBlockBytes;
+    const char* base1 = pool + size_t(unsigned(phys1)) * kBlockBytes;
+#pragma unroll
+    for (int r = 0; r < kSlicesPerWave; ++r) {
+      const int sl = wave + r * WAVES;
+      if (sl >= kSlices) break;
+      const bool blk1 = sl >= kBlockSlices;
+      if (!(blk1 ? ok1 : ok0)) continue;
+      const int rem = blk1 ? rem0 - kBlockSize : rem0;
+      const int local = (sl - (blk1 ? kBlockSlices : 0)) * kWave + lane;
+      const int row = local / kSlotsPerRow, ch = local - row * kSlotsPerRow;
+      if (row < rem && row < kBlockSize && ch < kChunksPerRow) {
+        // (a named pointer: as a direct argument of the builtin this sum
+        // makes the host pass drop the kernel's launch stub)
+        const char* src = (blk1 ? base1 : base0) + (row * kRowBytes + ch * 16);
+        __builtin_amdgcn_global_load_lds(src, (lds_void*)(dst + sl * kWave * 8), 16, 0, 0);
+      }
+    }
+  }
+};
+
+template <int WAVES>
+__global__ __launch_bounds__(WAVES * kWave) void mla_decode_kernel(MlaArgs a) {
+  constexpr int kThreads = WAVES * kWave;
+  __shared__ __attribute__((aligned(16))) uint16_t s_k0[kBufElems];
+  __shared__ __attribute__((aligned(16))) uint16_t s_k1[kBufElems];
+
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);   // uniform
+  const int lane = threadIdx.x % kWave;
+  const int g = lane >> 4, c = lane & 15;
+
+  MlaWork w;
+  if (!mla_work<WAVES, 16>(a, wave, lane, w)) return;
+  const int chunk = w.chunk, b = w.b, blk_begin = w.blk_begin, blk_end = w.blk_end, ctx = w.ctx;
+  const size_t slot_row = w.slot_row, slot_stride = w.slot_stride;
+  const bool final_out = w.final_out;
   const int h0 = (chunk * WAVES + wave) * 16;            // first head of this wave
 
   const int limit = ctx < blk_end * kBlockSize ? ctx : blk_end * kBlockSize;   // tokens attended
-  const int32_t* table = a.block_tables + size_t(b) * a.max_blocks_per_seq;
-  const char* pool = static_cast<const char*>(a.pool);
 
   // Clear both buffers, so that slots never loaded read as zeros.
   for (int i = threadIdx.x; i < kBufElems / 8; i += kThreads) {
@@ -221,52 +301,9 @@ __global__ __launch_bounds__(WAVES * kWave) void mla_decode_kernel(MlaArgs a) {
 
   const int n_pairs = (blk_end - blk_begin + 1) / 2;
 
-  // Block ids of the partition, 64 at a time in lane registers (lane i holds
-  // entry seg + i); a pair's two ids are broadcast with readlane, so the
-  // addresses and validity flags are wave-uniform scalars.
-  int seg = -kWave, my_id = 0;
-  uint64_t ok_mask = 0;
-  auto pair_ids = [&](int p, int& phys0, int& phys1, bool& ok0, bool& ok1) {
-    const int rel = 2 * p;                             // first block of the pair, from blk_begin
-    if (rel >= seg + kWave) {
-      seg = rel - rel % kWave;
-      const int blk = blk_begin + seg + lane;
-      my_id = blk < blk_end ? table[blk] : -1;
-      ok_mask = __ballot(unsigned(my_id) < unsigned(a.num_blocks));
-    }
-    const int k = rel - seg;
-    phys0 = __builtin_amdgcn_readlane(my_id, k);
-    phys1 = __builtin_amdgcn_readlane(my_id, k + 1);
-    ok0 = (ok_mask >> k) & 1;
-    ok1 = k + 1 < kWave && ((ok_mask >> (k + 1)) & 1);
-  };
-
-  // Pair p into dst: slice sl is one direct-to-LDS load of 64 slots of block
-  // sl / 19; lanes whose row is padding, past the attended tokens or in a
-  // block with a bad table entry load nothing.
-  auto stage = [&](int p, uint16_t* dst, bool& ok0, bool& ok1) {
-    int phys0, phys1;
-    pair_ids(p, phys0, phys1, ok0, ok1);
-    const int rem0 = limit - (blk_begin + 2 * p) * kBlockSize;   // rows of block 0 attended
-    const char* base0 = pool + size_t(unsigned(phys0)) * kBlockBytes;
-    const char* base1 = pool + size_t(unsigned(phys1)) * kBlockBytes;
-#pragma unroll
-    for (int r = 0; r < kSlicesPerWave; ++r) {
-      const int sl = wave + r * WAVES;
-      if (sl >= kSlices) break;
-      const bool blk1 = sl >= kBlockSlices;
-      if (!(blk1 ? ok1 : ok0)) continue;
-      const int rem = blk1 ? rem0 - kBlockSize : rem0;
-      const int local = (sl - (blk1 ? kBlockSlices : 0)) * kWave + lane;
-      const int row = local / kSlotsPerRow, ch = local - row * kSlotsPerRow;
-      if (row < rem && row < kBlockSize && ch < kChunksPerRow) {
-        // (a named pointer: as a direct argument of the builtin this sum
-        // makes the host pass drop the kernel's launch stub)
-        const char* src = (blk1 ? base1 : base0) + (row * kRowBytes + ch * 16);
-        __builtin_amdgcn_global_load_lds(src, (lds_void*)(dst + sl * kWave * 8), 16, 0, 0);
-      }
-    }
-  };
+  PairStage<WAVES> st{a.block_tables + size_t(b) * a.max_blocks_per_seq,
+                      static_cast<const char*>(a.pool), blk_begin, blk_end, limit, a.num_blocks,
+                      wave, lane};
 
   // Pair p, staged in kb, with its blocks' validity flags.
   auto compute = [&](const uint16_t* kb, int p, bool ok0, bool ok1) {
@@ -372,14 +409,14 @@ __global__ __launch_bounds__(WAVES * kWave) void mla_decode_kernel(MlaArgs a) {
   // body does not fit in the registers.)
   __syncthreads();                                    // buffers cleared
   bool ok0 = false, ok1 = false;
-  if (n_pairs > 0) stage(0, s_k0, ok0, ok1);
+  if (n_pairs > 0) st.stage(0, s_k0, ok0, ok1);
   __builtin_amdgcn_s_waitcnt(0);                      // this wave's copies have landed
   __syncthreads();                                    // and everyone's
   for (int p = 0; p < n_pairs; ++p) {
     bool nk0 = false, nk1 = false;
     uint16_t* cur = (p & 1) ? s_k1 : s_k0;
     uint16_t* nxt = (p & 1) ? s_k0 : s_k1;
-    if (p + 1 < n_pairs) stage(p + 1, nxt, nk0, nk1);
+    if (p + 1 < n_pairs) st.stage(p + 1, nxt, nk0, nk1);
     compute(cur, p, ok0, ok1);
     ok0 = nk0;
     ok1 = nk1;

@@ -12,6 +12,7 @@ import torch
 import oracle.mla as mla
 from paged_kv_cache_25_amd import ops
 from tests.gpu_util import check_tolerance, dev_tensor, host_storage, log
+from workloads.configs import _to_storage
 from workloads.mla import make_mla_inputs, named_mla
 
 pytestmark = pytest.mark.gpu
@@ -76,6 +77,26 @@ def test_edge_context_lengths():
         gpu = DevMLA(inp).step(P)
         assert np.all(gpu[0] == 0)                       # ctx 0: zeros
         check_tolerance("bf16", gpu, _oracle(inp), f"mla edges P={P}", out_dtype="bf16")
+
+
+@pytest.mark.parametrize("heads", [64, 128])
+def test_scores_growing_within_a_chunk(heads):
+    """Latent rows planted late in a sequence that score far above everything
+    before them for some heads (100 to 400 in log2 units of the softmax):
+    the kernels' running reference maxima must follow them, by rescaling or
+    by running the chunk again, or the weights overflow.  Fixed partitions of
+    64 tokens put each planted row in the second pair of its partition."""
+    inp = make_mla_inputs(num_seqs=2, num_heads=heads, ctx=("fixed", [1500, 700]), seed=61)
+    qf = torch.from_numpy(inp.q.view(np.int16)).view(torch.bfloat16).float().numpy()
+    for b, pos, head, mult in ((0, 40, 5, 3.0), (0, 1000, 5, 5.0), (0, 1250, heads - 3, 4.0),
+                               (1, 600, 17, 6.0)):
+        row = _to_storage(mult * qf[b, head], inp.dtype)
+        inp.latent_pool[inp.block_tables[b, pos // 16], pos % 16] = row
+    for P in (64, ops.PKV_PARTITION_BALANCED):
+        log(f"[case] mla growing scores H={heads} P={P}")
+        gpu = DevMLA(inp).step(P)
+        assert np.all(np.isfinite(gpu))
+        check_tolerance("bf16", gpu, _oracle(inp), f"mla growing H={heads} P={P}", out_dtype="bf16")
 
 
 def test_lite_workload():
