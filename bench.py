@@ -420,14 +420,45 @@ def attainable_read(ops, stream, reps=20):
     return best
 
 
+GATHER_WORKGROUPS = 6144          # two rounds of the 3,072 resident decode waves
+GATHER_PER_WORKGROUP = 26         # about one decode workgroup's blocks on the batch-64 layer
+
+
+def attainable_gather(ops, stream, reps=20):
+    """The read ceiling of the decode kernels' access pattern: pkv_gather_read
+    over 6,144 x 26 distinct 4 KiB chunks (654 MB) scattered at random over a
+    2 GiB buffer, timed with HIP events on ``stream``; returns GB/s."""
+    import torch
+    n_chunks = STREAM_READ_BYTES // 4096
+    buf = torch.arange(STREAM_READ_BYTES // 4, dtype=torch.int32, device="cuda")
+    perm = np.random.default_rng(11).permutation(n_chunks)[:GATHER_WORKGROUPS * GATHER_PER_WORKGROUP]
+    ids = torch.from_numpy(perm.astype(np.int32)).cuda()
+    out = torch.empty(64 * GATHER_WORKGROUPS, dtype=torch.int32, device="cuda")
+    run = lambda i: ops.gather_read(buf, ids, GATHER_PER_WORKGROUP, out=out, stream=stream)
+    for i in range(3):
+        run(i)
+    timed = event_timer(stream)
+    ms = min(timed(run, reps) for _ in range(2))
+    del buf, ids, out
+    torch.cuda.empty_cache()
+    return len(perm) * 4096 / (ms * 1e-3) / 1e9
+
+
 def attainable_entry(ops, stream, kernel_gbps):
-    """The ``attainable`` object of the JSON line: the read ceiling and the
-    roofline kernel's rate as a fraction of it."""
+    """The ``attainable`` object of the JSON line: the read ceilings (one
+    large buffer in order; scattered 4 KiB chunks, the decode kernels' own
+    unit) and the roofline kernel's rate as a fraction of each."""
     gbps, grid = attainable_read(ops, stream)
     print(f"[bench] stream read: {gbps:.1f} GB/s ({grid} workgroups)", file=sys.stderr, flush=True)
+    gather = attainable_gather(ops, stream)
+    print(f"[bench] gather read of 4 KiB chunks: {gather:.1f} GB/s", file=sys.stderr, flush=True)
     return {"kernel": "stream_read_kernel", "bytes": STREAM_READ_BYTES, "workgroups": grid,
             "read_gbps": round(gbps, 1), "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4),
-            "roofline_kernel_frac_of_attainable": round(kernel_gbps / gbps, 4)}
+            "roofline_kernel_frac_of_attainable": round(kernel_gbps / gbps, 4),
+            "gather_kernel": "gather_read_kernel",
+            "gather_bytes": GATHER_WORKGROUPS * GATHER_PER_WORKGROUP * 4096,
+            "gather_read_gbps": round(gather, 1),
+            "roofline_kernel_frac_of_gather": round(kernel_gbps / gather, 4)}
 
 
 def main_multi(args):
@@ -870,7 +901,10 @@ def main_mla(args):
                                 + "mla_decode_kernel + merge_kernel"
                                 if balanced else "mla_decode_kernel"), "bound": "hbm",
                      "achieved": round(kernel_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(kernel_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "frac": round(kernel_gbps / HBM_PEAK_GBPS, 4),
+                     "traffic": measured_traffic(inp.name, P, "mla_decode_kernel"),
+                     "traffic_unit": "HBM bytes per launch of mla_decode_kernel (rocprofv3 "
+                                     "FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
                      "algorithmic_bytes_per_launch": tr["kv_bytes"],
                      "mfma": {"achieved_tflops": round(tflops, 1), "peak_tflops": 2500.0,
                               "frac": round(tflops / 2500.0, 4),

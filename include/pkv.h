@@ -696,6 +696,23 @@ pkv_status_t pkv_copy_blocks(void* k_pool, void* v_pool, float* k_scales, float*
 pkv_status_t pkv_stream_read(uint32_t* out, const void* src, size_t bytes,
                              int32_t num_workgroups, void* stream);
 
+/* pkv_gather_read - the same folded read over scattered 4 KiB chunks, the
+ * unit a decode workgroup reads (one block of 16 tokens x 128 dims of one KV
+ * head in bf16, anywhere in the pool): the practical read ceiling of that
+ * access pattern.  src [device, read; 16-byte aligned] is bytes long, a
+ * multiple of 4096; chunk_ids int32 [num_chunks] [device, read] lists chunk
+ * c = bytes [4096 c, 4096 c + 4096); ids outside [0, bytes / 4096) read
+ * nothing.  One-wave workgroups take chunks_per_workgroup consecutive
+ * entries each (num_chunks a multiple of it, at most
+ * PKV_STREAM_READ_MAX_WORKGROUPS workgroups), two chunks in registers, 16
+ * bytes per lane and load; out uint32 [64 x num_chunks /
+ * chunks_per_workgroup] [device, written]: lane l of workgroup w writes
+ * out[64 w + l], the XOR of the 32-bit words it read.
+ * PKV_ERR_INVALID_ARG for a bad count, size or pointer. */
+pkv_status_t pkv_gather_read(uint32_t* out, const void* src, size_t bytes,
+                             const int32_t* chunk_ids, int32_t num_chunks,
+                             int32_t chunks_per_workgroup, void* stream);
+
 /* Words pkv_stream_read writes for num_workgroups workgroups (one per wave);
  * 0 for a count outside 1 .. PKV_STREAM_READ_MAX_WORKGROUPS. */
 int32_t pkv_stream_read_out_words(int32_t num_workgroups);

@@ -305,6 +305,22 @@ pkv_status_t pkv_stream_read(uint32_t* out, const void* src, size_t bytes,
              : PKV_ERR_HIP;
 }
 
+pkv_status_t pkv_gather_read(uint32_t* out, const void* src, size_t bytes,
+                             const int32_t* chunk_ids, int32_t num_chunks,
+                             int32_t chunks_per_workgroup, void* stream) {
+  if (num_chunks < 0 || chunks_per_workgroup <= 0 || bytes % 4096 != 0 ||
+      bytes / 4096 > 0x7fffffff || num_chunks % chunks_per_workgroup != 0 ||
+      num_chunks / chunks_per_workgroup > PKV_STREAM_READ_MAX_WORKGROUPS)
+    return PKV_ERR_INVALID_ARG;
+  if (num_chunks == 0) return PKV_OK;
+  if (!out || !aligned4(out) || !chunk_ids || !aligned4(chunk_ids) || !src || !aligned16(src))
+    return PKV_ERR_INVALID_ARG;
+  return pkv::launch_gather_read(out, src, bytes, chunk_ids, num_chunks, chunks_per_workgroup,
+                                 static_cast<hipStream_t>(stream)) == hipSuccess
+             ? PKV_OK
+             : PKV_ERR_HIP;
+}
+
 int32_t pkv_stream_read_out_words(int32_t num_workgroups) {
   if (num_workgroups <= 0 || num_workgroups > PKV_STREAM_READ_MAX_WORKGROUPS) return 0;
   return num_workgroups * pkv::stream_read_waves_per_workgroup();

@@ -11,6 +11,10 @@
 // last, partial pass.  Every word read is folded with
 // XOR, so no load can be dropped, and each wave writes its fold to out: the
 // XOR of all out words equals the XOR of the buffer's 32-bit words.
+//
+// A second kernel reads a list of scattered 4 KiB chunks the same way: the
+// read rate of the decode kernels' own access pattern (one block's slice of
+// one KV head, anywhere in the pool), without any attention arithmetic.
 #include "stream_read.h"
 
 #include "pkv_device.h"
@@ -47,7 +51,48 @@ __global__ __launch_bounds__(kThreads) void stream_read_kernel(uint32_t* out, co
     out[size_t(blockIdx.x) * (kThreads / kWave) + threadIdx.x / kWave] = acc;
 }
 
+// The same folded read over scattered 4 KiB chunks, the unit the decode
+// kernels read (16 tokens x 128 dims x 2 bytes of one block and KV head):
+// one wave per workgroup, chunks ids[wg * per_wg ...] in order, two chunks in
+// registers (one in flight while the other is folded), 16 bytes per lane and
+// load.  An id outside [0, n_chunks) reads nothing.
+__global__ __launch_bounds__(kWave) void gather_read_kernel(uint32_t* out, const char* src,
+                                                            const int32_t* ids, int per_wg,
+                                                            int n_chunks) {
+  constexpr int kChunk = 4096;
+  const int lane = threadIdx.x;
+  const int32_t* my = ids + size_t(blockIdx.x) * per_wg;
+  uint32_t acc = 0;
+  uint4 r[2][4];
+  auto fetch = [&](int k, uint4* d) {
+    const int id = my[k];
+    const bool ok = unsigned(id) < unsigned(n_chunks);
+    const char* c = src + size_t(ok ? id : 0) * kChunk + 16 * lane;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) d[j] = ok ? load_streamed<uint4>(c + 1024 * j) : make_uint4(0, 0, 0, 0);
+  };
+  if (per_wg > 0) fetch(0, r[0]);
+  for (int k = 0; k < per_wg; k += 2) {
+#pragma unroll
+    for (int d = 0; d < 2; ++d) {
+      if (k + d + 1 < per_wg) fetch(k + d + 1, r[d ^ 1]);
+      if (k + d < per_wg)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc ^= r[d][j].x ^ r[d][j].y ^ r[d][j].z ^ r[d][j].w;
+    }
+  }
+  out[size_t(blockIdx.x) * kWave + lane] = acc;
+}
+
 }  // namespace
+
+hipError_t launch_gather_read(uint32_t* out, const void* src, size_t bytes, const int32_t* ids,
+                              int num_ids, int per_workgroup, hipStream_t stream) {
+  const int workgroups = num_ids / per_workgroup;
+  hipLaunchKernelGGL(gather_read_kernel, dim3(unsigned(workgroups)), dim3(kWave), 0, stream, out,
+                     static_cast<const char*>(src), ids, per_workgroup, int(bytes / 4096));
+  return hipGetLastError();
+}
 
 int stream_read_waves_per_workgroup() { return kThreads / kWave; }
 

@@ -127,6 +127,8 @@ def load():
     L.pkv_copy_blocks.argtypes = [P, P, P, P, P, I, I, I, I, I, ctypes.c_int, P]
     L.pkv_stream_read.restype = ctypes.c_int
     L.pkv_stream_read.argtypes = [P, P, Z, I, P]
+    L.pkv_gather_read.restype = ctypes.c_int
+    L.pkv_gather_read.argtypes = [P, P, Z, P, I, I, P]
     L.pkv_stream_read_out_words.restype = I
     L.pkv_stream_read_out_words.argtypes = [I]
     L.pkv_mla_append.restype = ctypes.c_int
@@ -670,6 +672,28 @@ def stream_read(src, num_workgroups, out=None, stream=None):
         raise ValueError(f"out holds {out.numel()} words, {words} needed")
     _check("pkv_stream_read", load().pkv_stream_read(
         _ptr(out), _ptr(src), src.numel() * src.element_size(), num_workgroups, _stream(stream)))
+    return out
+
+
+def gather_read(src, chunk_ids, chunks_per_workgroup, out=None, stream=None):
+    """Read the 4 KiB chunks chunk_ids (int32) of src once (pkv_gather_read, a
+    bandwidth measurement of the decode kernels' access pattern); returns out,
+    int32 [64 * len(chunk_ids) / chunks_per_workgroup]: lane l of workgroup w
+    holds the XOR of the 32-bit words it read."""
+    _want("chunk_ids", chunk_ids, _I32, (None,))
+    _want("out", out, _I32, (None,), optional=True)
+    _need_cuda(src, chunk_ids, out)
+    n = chunk_ids.shape[0]
+    if chunks_per_workgroup <= 0 or n % chunks_per_workgroup:
+        raise ValueError("the chunk count must be a multiple of chunks_per_workgroup")
+    words = 64 * (n // chunks_per_workgroup)
+    if out is None:
+        out = torch.empty(words, dtype=torch.int32, device=src.device)
+    elif out.numel() < words:
+        raise ValueError(f"out holds {out.numel()} words, {words} needed")
+    _check("pkv_gather_read", load().pkv_gather_read(
+        _ptr(out), _ptr(src), _nbytes(src), _ptr(chunk_ids), n, int(chunks_per_workgroup),
+        _stream(stream)))
     return out
 
 

@@ -45,7 +45,7 @@ def test_header_declares_the_entry_points():
         "pkv_mla_decode_attention", "pkv_mla_decode_partials", "pkv_decode_plan_slots",
         "pkv_decode_plan_bytes", "pkv_decode_plan", "pkv_paged_decode_partials_planned",
         "pkv_merge_partials_planned", "pkv_multi_query_balanced_workspace_bytes",
-        "pkv_stream_read", "pkv_stream_read_out_words"])
+        "pkv_stream_read", "pkv_stream_read_out_words", "pkv_gather_read"])
 
 
 def test_every_declared_symbol_is_exported(lib):

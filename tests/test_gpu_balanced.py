@@ -387,3 +387,34 @@ def test_planned_partials_and_merge(kv, q):
     # Sequences of two or more chunks go through the same kernels either way.
     multi = [b for b in range(len(lens)) if first[b + 1] - first[b] >= 2]
     assert multi and torch.equal(merged[multi], whole[multi])
+
+
+def test_workspace_reuse_across_sizes():
+    """One workspace, sized for the largest call, serves calls of different
+    sizes and kinds in turn (balanced calls on 12 sequences of the
+    Llama-3-8B layer and on 9 sequences with 8 q / 2 kv heads, a
+    fixed-partition call between them, each leaving its partial rows and plan
+    behind for the next): every result matches the oracle."""
+    a = named_config(2, num_seqs=12)
+    b = make_inputs(num_seqs=9, num_q_heads=8, num_kv_heads=2, head_dim=128,
+                    ctx=("fixed", [1, 40, 700, 1500, 17, 3000, 260, 33, 900]),
+                    pool=("used_fraction", 0.9), q_dtype="bf16", kv_dtype="bf16", seed=97)
+    n = max(ops.workspace_bytes(a.num_seqs, a.num_q_heads, a.head_dim, a.max_context_len, BAL),
+            ops.workspace_bytes(a.num_seqs, a.num_q_heads, a.head_dim, a.max_context_len, 512),
+            ops.workspace_bytes(b.num_seqs, b.num_q_heads, b.head_dim, b.max_context_len, BAL))
+    ws = torch.full((n,), 0xFF, dtype=torch.uint8, device="cuda")
+    refs = {}
+    devs = {}
+    for name, inp in (("a", a), ("b", b)):
+        d = DeviceStep(inp)
+        d.append()
+        devs[name] = d
+        refs[name] = oracle_out(inp)
+    for name, P in (("a", BAL), ("b", BAL), ("a", 512), ("a", BAL), ("b", BAL)):
+        d, inp = devs[name], devs[name].inp
+        log(f"[case] workspace reuse: {name} P={P}")
+        d.out.fill_(float("nan"))
+        ops.paged_decode_attention(d.out, d.q, d.k_pool, d.v_pool, d.tables, d.lens,
+                                   inp.max_context_len, inp.softmax_scale, P, workspace=ws)
+        torch.cuda.synchronize()
+        check_tolerance("bf16", d.out_f64(), refs[name], f"reuse {name} P={P}", out_dtype="bf16")

@@ -180,28 +180,31 @@ def test_chunked_prefill_equals_one_pass():
     check_tolerance("bf16", gpu, ref, "chunked prefill")
 
 
-def test_speculative_verify_workload_sampled():
-    """The Llama-3-8B batch-64 layer with 4 new tokens per sequence (three
-    drafts and the token before them, as a verify pass sees them), at full
-    size in the launch configuration the benchmark times; sampled rows
-    against the oracle."""
-    inp = named_config(2, new_tokens=("const", 4), name="llama3_8b_b64_t4")
+@pytest.mark.parametrize("t", [4, 16])
+def test_batch64_new_tokens_full(t):
+    """The Llama-3-8B batch-64 layer with t new tokens per sequence (t = 4: three
+    drafts and the token before them, as a verify pass sees them; t = 16: a
+    chunk of a prompt), at full size in the launch configuration the
+    benchmark times (the balanced split; at t = 16 its 32,768 merged rows go
+    through the merge's several-items-per-workgroup shape): every row of every
+    sequence against the oracle."""
+    inp = named_config(2, new_tokens=("const", t), name=f"llama3_8b_b64_t{t}")
     dev = DeviceMultiStep(inp)
     gpu = dev.step().detach().float().cpu().double().numpy()
-    rng = np.random.default_rng(0)
-    seqs = sorted(rng.choice(inp.num_seqs, 6, replace=False).tolist())
     pools = pa.kv_append_tokens(inp.k_pool, inp.v_pool, inp.k_new, inp.v_new, inp.block_tables,
                                 inp.context_lens, inp.query_start_loc, inp.block_size)
     assert _same_bits(host_storage(dev.k_pool), pools[0])
     assert _same_bits(host_storage(dev.v_pool), pools[1])
-    for b in seqs:
+    ref = np.zeros_like(gpu)
+    for b in range(inp.num_seqs):
         q0, q1 = int(inp.query_start_loc[b]), int(inp.query_start_loc[b + 1])
-        ref = pa.multi_query_attention(inp.q[q0:q1], pools[0], pools[1],
-                                       inp.block_tables[b:b + 1], inp.context_lens[b:b + 1],
-                                       np.array([0, q1 - q0]), block_size=inp.block_size,
-                                       softmax_scale=inp.softmax_scale, q_dtype=inp.q_dtype,
-                                       kv_dtype=inp.kv_dtype)
-        check_tolerance("bf16", gpu[q0:q1], ref, f"verify t=4 seq {b} ctx {inp.context_lens[b]}")
+        ref[q0:q1] = pa.multi_query_attention(inp.q[q0:q1], pools[0], pools[1],
+                                              inp.block_tables[b:b + 1], inp.context_lens[b:b + 1],
+                                              np.array([0, q1 - q0]), block_size=inp.block_size,
+                                              softmax_scale=inp.softmax_scale, q_dtype=inp.q_dtype,
+                                              kv_dtype=inp.kv_dtype)
+    check_tolerance("bf16", gpu, ref, f"batch-64 t={t} (all {inp.num_seqs} sequences)",
+                    out_dtype="bf16")
 
 
 @pytest.mark.parametrize("kv,q,P", [("bf16", "bf16", 64), ("f32", "f32", 32),

@@ -41,3 +41,27 @@ def test_stream_read_rejects_bad_arguments():
         ops.stream_read(src[:-1], 8)                      # 4092 bytes: not a multiple of 16
     with pytest.raises(ValueError):
         ops.stream_read(src, 0)
+
+
+@pytest.mark.parametrize("per_wg", [1, 3, 26])
+def test_gather_read_folds_each_lanes_words(per_wg):
+    """pkv_gather_read: lane l of workgroup w folds, over the workgroup's chunks,
+    the 16 bytes at 1024 j + 16 l of each 4 KiB chunk (j = 0..3); ids outside
+    the buffer (here -1 and past the end) read nothing."""
+    n_chunks, n_wg = 64, 10
+    rng = np.random.default_rng(per_wg)
+    host = rng.integers(0, 2 ** 32, size=n_chunks * 1024, dtype=np.uint32)
+    ids = rng.integers(-2, n_chunks + 2, size=n_wg * per_wg).astype(np.int32)
+    log(f"[case] gather_read per_wg={per_wg}")
+    src = torch.from_numpy(host.view(np.int32)).cuda()
+    out = torch.full((n_wg * 64 + 64,), SENTINEL, dtype=torch.int32, device="cuda")
+    ops.gather_read(src, torch.from_numpy(ids).cuda(), per_wg, out=out)
+    got = out.cpu().numpy().view(np.uint32)
+    words = host.reshape(n_chunks, 4, 64, 4)              # [chunk, quarter j, lane, word]
+    for w in range(n_wg):
+        want = np.zeros(64, np.uint32)
+        for c in ids[w * per_wg:(w + 1) * per_wg]:
+            if 0 <= c < n_chunks:
+                want ^= np.bitwise_xor.reduce(words[c].reshape(4, 64, 4), axis=(0, 2))
+        assert np.array_equal(got[64 * w:64 * w + 64], want), w
+    assert (got[n_wg * 64:] == SENTINEL).all()
