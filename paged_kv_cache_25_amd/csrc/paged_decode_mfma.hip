@@ -440,6 +440,252 @@ void paged_decode_mfma_kernel(DecodeArgs a) {
   }
 }
 
+// Several new tokens per sequence, head dim 128, four or more column tiles
+// per KV head: one workgroup of W waves per unit (KV head, chunk slot or
+// partition) covers W x NT column tiles, and the unit's blocks are read from
+// HBM once, into LDS, for all of them (the kernel above gives each two-tile
+// chunk its own workgroup, so every chunk loads every block).  Each wave
+// loads its share of a block's K and V slices (8 KiB; 8 / W pieces of 1 KiB)
+// into registers two blocks ahead of the one computed, writes it into one of
+// two LDS stages, and after a barrier every wave reads the whole block's
+// operands from LDS in the register layout of BlockRegs and runs
+// MfmaDecode::block on its NT tiles.  Rows are stored with their 16-byte
+// chunks rotated (chunk q of row r at position q ^ (r & 15)), so the K reads
+// of 16 rows and the V reads of one row hit 16 distinct bank groups.  The
+// block table of the unit goes to LDS first, up to kIdWindow entries at a
+// time.  Measured at 16 new tokens on the batch-64 layer: 131 us against 166
+// us for the kernel above; copying the blocks with direct-to-LDS loads
+// instead, 145 us (the copies alone took 142 us at any ring depth), and
+// three or four blocks in registers instead of two, 133 and 135 us.
+constexpr int kIdWindow = 512;
+#ifndef PKV_MULTI_LDS
+#define PKV_MULTI_LDS 1
+#endif
+
+template <int NT, int W>
+__global__ __launch_bounds__(W * kWave)
+__attribute__((amdgpu_waves_per_eu(2)))
+void paged_decode_lds_kernel(DecodeArgs a) {
+  constexpr int D = 128;
+  using T = MfmaTile<D>;
+  constexpr int kStage = 2 * T::kSliceBytes;           // K slice then V slice: 8 KiB
+  constexpr int kPieces = kStage / (16 * kWave);       // 1 KiB pieces of a block (8)
+  constexpr int P = kPieces / W;                       // per wave
+  static_assert(kPieces % W == 0, "pieces per wave");
+  __shared__ __attribute__((aligned(16))) uint8_t s_ring[2 * kStage];
+  __shared__ int32_t s_ids[kIdWindow];
+
+  DecodeItem it;
+  if (!decode_item(a, it)) return;                     // uniform over the workgroup
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int lane = threadIdx.x % kWave;
+  const int r = lane >> 4, c = lane & 15;
+  const int h = it.h, b = it.b, part = it.part;
+
+  const int32_t* table = a.block_tables + size_t(b) * a.max_blocks_per_seq;
+  const int blk_begin = it.blk_begin;
+  const int raw_ctx = a.context_lens[b];
+  int ctx = raw_ctx < 0 ? 0 : raw_ctx;
+  const int cap = a.max_blocks_per_seq * kBlockSize;
+  ctx = ctx > cap ? cap : ctx;
+  const int n_blk_seq = (ctx + kBlockSize - 1) / kBlockSize;
+  const int blk_end = it.blk_end < n_blk_seq ? it.blk_end : n_blk_seq;
+  Columns cols;
+  cols.group = a.group;
+  cols.num_q_heads = a.num_q_heads;
+  cols.kv_head = h;
+  cols.row0 = a.q_start[b];
+  cols.t = a.q_start[b + 1] - cols.row0;
+  auto row_of = [&](int n) -> size_t { return cols.row(n); };
+  const int n0 = (it.chunk * W + wave) * kHeadTile * NT;   // this wave's first column
+  const bool has_cols = cols.valid(n0);                // uniform per wave
+
+  const bool final_out =
+      a.write_final ||
+      (a.final_single && (a.balanced() ? it.n_parts == 1 : n_blk_seq <= a.blocks_per_partition));
+  if (blk_begin >= blk_end && !(a.write_final && part == 0) &&
+      !(a.balanced() && final_out)) {                  // uniform: nothing to attend
+    if (has_cols) {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+        if ((a.mark_empty || a.balanced()) && lane < kHeadTile && cols.valid(n0 + 16 * nt + c) &&
+            partial_row_ok(a, row_of(n0 + 16 * nt + c), cols.row0))
+          a.part_lse[partial_row(a, it, row_of(n0 + 16 * nt + c), cols.row0)] = -INFINITY;
+    }
+    return;
+  }
+  int my_vis[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int n = n0 + 16 * nt + c;
+    my_vis[nt] = cols.valid(n) ? cols.visible(n, ctx) : ctx;
+  }
+  const int min_vis = cols.visible(n0, ctx);
+
+  MfmaDecode<D> dec[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int n = n0 + 16 * nt + c;
+    const bool ok = cols.valid(n);
+    const char* qrow = reinterpret_cast<const char*>(a.q) + (ok ? row_of(n) : 0) * T::kRowBytes;
+#pragma unroll
+    for (int j = 0; j < T::kSlabs; ++j) {
+      uint4 w = ok ? *reinterpret_cast<const uint4*>(qrow + 64 * j + 16 * r) : make_uint4(0, 0, 0, 0);
+      dec[nt].q[j] = __builtin_bit_cast(bf16x8, w);
+    }
+#pragma unroll
+    for (int t = 0; t < T::kTiles; ++t) dec[nt].o[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    dec[nt].m = -INFINITY;
+    dec[nt].l = 0.0f;
+  }
+  // The queries are waited for here, before any copy is in flight: a wait
+  // for them inside the block loop would also wait for every copy.
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+    for (int j = 0; j < T::kSlabs; ++j) asm volatile("" ::"v"(dec[nt].q[j]));
+
+  const char* kbase = reinterpret_cast<const char*>(a.k_pool);
+  const char* vbase = reinterpret_cast<const char*>(a.v_pool);
+  const size_t head_off = size_t(h) * T::kSliceBytes;
+  const size_t block_stride = size_t(a.num_kv_heads) * T::kSliceBytes;
+  const float k_mul = a.scale_log2;
+  // Operands of the block in stage st, in BlockRegs' layout.
+  auto read_block = [&](BlockRegs<D>& br, int st) {
+    const uint8_t* kb = s_ring + st * kStage;
+    const uint8_t* vb = kb + T::kSliceBytes;
+#pragma unroll
+    for (int j = 0; j < T::kSlabs; ++j)
+      br.k[j] = *reinterpret_cast<const uint4*>(kb + c * T::kRowBytes + (((4 * j + r) ^ c) << 4));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 4 * r + i;
+      const uint4 w = *reinterpret_cast<const uint4*>(vb + row * T::kRowBytes + ((c ^ row) << 4));
+      br.v[i][0] = w.x; br.v[i][1] = w.y; br.v[i][2] = w.z; br.v[i][3] = w.w;
+    }
+  };
+
+  // Attends block k of the window from ring stage st.
+  auto compute = [&](int win, int k, int st) {
+    const int id = s_ids[k];
+    const bool ok = unsigned(id) < unsigned(a.num_blocks);
+    BlockRegs<D> br;
+    read_block(br, st);
+    const int first = (win + k) * kBlockSize;
+    int valid = ctx - first;
+    valid = valid < kBlockSize ? valid : kBlockSize;
+    valid = ok ? valid : 0;
+    const bool need_mask = !ok || first + kBlockSize > min_vis;
+    if (valid < kBlockSize) zero_v_tail<D>(br, valid, lane);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+      dec[nt].template block<true, false>(br, valid, ok ? my_vis[nt] - first : 0, need_mask,
+                                          k_mul, lane);
+  };
+  // The wave's pieces of block kb of the window: piece m (m = wave,
+  // wave + W, ...) holds K rows 4m..4m+3 (m < 4) or V rows 4(m-4).. (m >= 4),
+  // lane i the 16 bytes that go to position i & 15 of row 4m + (i >> 4),
+  // i.e. chunk (i & 15) ^ row.  A bad table entry loads block 0 (its tokens
+  // are masked).  Scheduling fences keep each block's loads together and in
+  // program order, so the compiler counts the loads in flight exactly and
+  // waits for one block, not both, before a store.
+  auto load_regs = [&](uint4 (&rb)[P], int kb) {
+    int phys = __builtin_amdgcn_readfirstlane(s_ids[kb]);
+    phys = unsigned(phys) < unsigned(a.num_blocks) ? phys : 0;
+    const size_t off = size_t(phys) * block_stride + head_off;
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < P; ++i) {
+      const int m = wave + i * W;
+      const int row = 4 * (m & 3) + r;
+      rb[i] = load_streamed<uint4, true>((m < 4 ? kbase : vbase) + off + row * T::kRowBytes +
+                                         ((c ^ row) << 4));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto store_regs = [&](const uint4 (&rb)[P], int st) {
+#pragma unroll
+    for (int i = 0; i < P; ++i)
+      *reinterpret_cast<uint4*>(s_ring + st * kStage + (wave + i * W) * 1024 + 16 * lane) = rb[i];
+  };
+
+  for (int win = blk_begin; win < blk_end; win += kIdWindow) {   // uniform
+    const int wn = (blk_end - win) < kIdWindow ? (blk_end - win) : kIdWindow;
+    for (int i = threadIdx.x; i < wn; i += W * kWave) s_ids[i] = table[win + i];
+    __syncthreads();                                   // ids written; no copy in flight
+    // Stages 0 and 1 take even and odd blocks; R = 2 blocks ahead of the one
+    // computed are in flight in registers (rb[(k + 1) % R] holds block
+    // k + 1 until it is stored, then loads block k + 1 + R).  The loads and
+    // stores run unconditionally, past the window's end on its last block
+    // again (an L2 hit, never computed), and the loop has one exit at the
+    // bottom: with a conditional load or an early exit, the compiler could
+    // not count the loads in flight on every path and would wait for all
+    // of them before a store.
+    constexpr int R = 2;
+    const int last = wn - 1;
+    uint4 rb[R][P];
+#pragma unroll
+    for (int u = 0; u < R; ++u) load_regs(rb[u], u < last ? u : last);
+    store_regs(rb[0], 0);
+    load_regs(rb[0], R < last ? R : last);
+    for (int k0 = 0; k0 < wn; k0 += 2 * R) {
+#pragma unroll
+      for (int u = 0; u < 2 * R; ++u) {
+        const int k = k0 + u;
+        // Stage u % 2 holds block k for every wave; every read of the
+        // other stage (block k - 1) is done.
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        store_regs(rb[(u + 1) % R], (u + 1) % 2);
+        load_regs(rb[(u + 1) % R], k + 1 + R < last ? k + 1 + R : last);
+        if (has_cols && k < wn) compute(win, k, u % 2);
+      }
+    }
+    __syncthreads();                                   // ring and ids free for the next window
+  }
+  if (!has_cols) return;
+
+  constexpr int kDimsPerLane = D / 16;
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const MfmaDecode<D>& dt = dec[nt];
+    float lt = dt.l + __shfl_xor(dt.l, 16);
+    lt += __shfl_xor(lt, 32);
+    float l_row[4], m_row[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      l_row[i] = __shfl(lt, 4 * r + i);
+      m_row[i] = __shfl(dt.m, 4 * r + i);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int n = n0 + 16 * nt + 4 * r + i;
+      if (!cols.valid(n)) continue;
+      const size_t qrow = row_of(n);
+      const bool empty = l_row[i] == 0.0f;
+      const float inv = empty ? 0.0f : 1.0f / l_row[i];
+      if (final_out) {
+        uint16_t* orow = reinterpret_cast<uint16_t*>(a.out) + qrow * D + kDimsPerLane * c;
+        uint32_t packed[kDimsPerLane / 2];
+#pragma unroll
+        for (int e = 0; e < kDimsPerLane; e += 2)
+          packed[e / 2] = uint32_t(f32_to_bf16_rne(dt.o[e][i] * inv)) |
+                          (uint32_t(f32_to_bf16_rne(dt.o[e + 1][i] * inv)) << 16);
+        *reinterpret_cast<uint4*>(orow) = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+      } else {
+        if (!partial_row_ok(a, qrow, cols.row0)) continue;
+        const size_t prow = partial_row(a, it, qrow, cols.row0);
+        float* op = a.part_o + prow * D + kDimsPerLane * c;
+#pragma unroll
+        for (int e = 0; e < kDimsPerLane; e += 4)
+          *reinterpret_cast<float4*>(op + e) = make_float4(dt.o[e][i] * inv, dt.o[e + 1][i] * inv,
+                                                           dt.o[e + 2][i] * inv, dt.o[e + 3][i] * inv);
+        if (c == 0)
+          a.part_lse[prow] = empty ? -INFINITY : (m_row[i] + __builtin_amdgcn_logf(l_row[i])) * kLn2;
+      }
+    }
+  }
+}
+
 template <int D>
 hipError_t launch_d(const DecodeArgs& a, hipStream_t stream) {
   const size_t units = (a.balanced() ? size_t(1) : size_t(a.num_seqs)) * a.num_kv_heads * a.max_partitions;
@@ -450,6 +696,19 @@ hipError_t launch_d(const DecodeArgs& a, hipStream_t stream) {
   const bool nt = a.head_chunks == 1 && PKV_NT_LOADS;
   const dim3 g{unsigned(grid)}, blk{unsigned(kWave)};
   if (a.q_start) {
+    // Two or more two-tile chunks per unit at head dim 128: the LDS ring, one
+    // workgroup of two waves per pair of chunks.
+    if constexpr (D == 128) {
+      if (PKV_MULTI_LDS && a.tiles_per_wave == 2 && a.head_chunks >= 2 && !a.k_new) {
+        DecodeArgs b = a;
+        b.head_chunks = (a.head_chunks + 1) / 2;
+        const size_t g2 = decode_grid(units, b.head_chunks);
+        if (g2 > 0x7fffffffu) return hipErrorInvalidConfiguration;
+        hipLaunchKernelGGL((paged_decode_lds_kernel<2, 2>), dim3(unsigned(g2)), dim3(2 * kWave), 0,
+                           stream, b);
+        return hipGetLastError();
+      }
+    }
     if (a.tiles_per_wave == 2) {
       if (nt) hipLaunchKernelGGL((paged_decode_mfma_kernel<D, true, true, 2>), g, blk, 0, stream, a);
       else hipLaunchKernelGGL((paged_decode_mfma_kernel<D, true, false, 2>), g, blk, 0, stream, a);

@@ -15,8 +15,8 @@ import pytest
 import torch
 
 import oracle.paged_attention as pa
-from tests.gpu_util import (DeviceMultiStep, DeviceStep, check_tolerance, host_storage, log,
-                            oracle_multi)
+from tests.gpu_util import (DeviceMultiStep, DeviceStep, check_tolerance, dev_tensor,
+                            host_storage, log, oracle_multi)
 from workloads import make_inputs, named_config
 
 pytestmark = pytest.mark.gpu
@@ -316,3 +316,48 @@ def test_balanced_partials_planned_match_chunk_oracle(kv, q):
                                                got_l[list(slots), j].T)
     check_tolerance(kv, merged, oracle_multi(inp, (kp, vp)), f"multi planned partials {kv}",
                     out_dtype="f32")
+
+
+@pytest.mark.parametrize("P", [0, BAL])
+def test_unit_longer_than_the_table_window(P):
+    """Sixteen new tokens per sequence over contexts of 9,000 and 8,300
+    tokens (563 and 519 blocks): with one partition per sequence a unit walks
+    more blocks than the 512 table entries the LDS-ring kernel holds at once,
+    so it drains the ring and reloads the entries mid-sequence."""
+    inp = named_config(2, seed=120, num_seqs=2, ctx=("fixed", [9000, 8300]),
+                       new_tokens=("const", 16), name="long_unit_t16")
+    _check(inp, f"long unit t=16 P={P}", partition_size=P)
+
+
+@pytest.mark.parametrize("P", [0, 32, BAL])
+def test_bad_table_entry_with_new_tokens(P):
+    """A table entry outside [0, num_blocks) in a sequence with 16 new tokens
+    (64 query columns per KV head: the LDS-ring kernel) is an empty block:
+    the result is the oracle's attention with that block taken out of the
+    table and its 16 tokens out of the context (every new row sees the whole
+    block, so its removal shifts no visibility)."""
+    inp = make_inputs(num_seqs=3, num_q_heads=16, num_kv_heads=4, head_dim=128,
+                      ctx=("fixed", [200, 300, 150]), pool=("used_fraction", 0.8),
+                      q_dtype="bf16", kv_dtype="bf16", seed=121, new_tokens=("const", 16),
+                      name="bad_entry_t16")
+    pools = pa.kv_append_tokens(inp.k_pool, inp.v_pool, inp.k_new, inp.v_new, inp.block_tables,
+                                inp.context_lens, inp.query_start_loc, inp.block_size)
+    good = inp.block_tables.copy()
+    bad_seq, bad_blk = 1, 1
+    inp.block_tables[bad_seq, bad_blk] = inp.num_blocks + 7
+    log(f"[case] bad entry t=16 P={P}")
+    dev = DeviceMultiStep(inp)
+    dev.k_pool = dev_tensor(pools[0], inp.kv_dtype)       # appended already: attend only
+    dev.v_pool = dev_tensor(pools[1], inp.kv_dtype)
+    gpu = dev.attend(P)
+    torch.cuda.synchronize()
+    gpu = gpu.detach().float().cpu().double().numpy()
+    tables = good.copy()
+    row = [x for k, x in enumerate(tables[bad_seq]) if k != bad_blk] + [-1]
+    tables[bad_seq] = np.asarray(row, dtype=tables.dtype)
+    lens = inp.context_lens.copy()
+    lens[bad_seq] -= 16
+    ref = pa.multi_query_attention(inp.q, pools[0], pools[1], tables, lens, inp.query_start_loc,
+                                   block_size=inp.block_size, softmax_scale=inp.softmax_scale,
+                                   q_dtype=inp.q_dtype, kv_dtype=inp.kv_dtype)
+    check_tolerance("bf16", gpu, ref, f"bad entry t=16 P={P}")
