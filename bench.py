@@ -597,6 +597,17 @@ def main_multi(args):
     kernel_gbps = tr["kv_bytes"] / (decode_ms * 1e-3) / 1e9
     mfma = inp.q_dtype == "bf16" and inp.kv_dtype == "bf16" and (Hq // Hkv) * mq >= 2
     cpu = None if args.no_cpu_baseline else cpu_baseline_multi(inp, args.cpu_budget_s)
+    # The decode kernel the library picks: the matrix cores in 16-column tiles
+    # (two per wave past 16 columns per KV head), and at head dim 128 with
+    # four or more tiles one LDS-staged workgroup per unit.
+    columns = mq * (Hq // Hkv)
+    tiles2 = mfma and columns > 16
+    if mfma and tiles2 and D == 128 and -(-columns // 32) >= 2:
+        kprefix, kname = "paged_decode_lds_kernel", "paged_decode_lds_kernel<2, 2>"
+    elif mfma:
+        kprefix, kname = "paged_decode_mfma_kernel", f"paged_decode_mfma_kernel<{D}>"
+    else:
+        kprefix, kname = "paged_decode_kernel", f"paged_decode_kernel<{D}>"
     result = {
         "metric": "paged multi-token attention achieved HBM GB/s (% of peak) and new tokens/s",
         "value": round(value, 1),
@@ -619,11 +630,13 @@ def main_multi(args):
         "new_tokens_per_s": round(R * 1e3 / step_ms, 1),
         "kernel_us": {"append": round(append_ms * 1e3, 2), "decode": round(decode_ms * 1e3, 2),
                       "merge": round(merge_ms * 1e3, 2), "attention_call": round(att_ms * 1e3, 2)},
-        "roofline": {"kernel": ("paged_decode_mfma_kernel" if mfma else "paged_decode_kernel")
-                               + f"<{D}> (several new tokens)",
+        "roofline": {"kernel": kname + " (several new tokens)",
                      "bound": "hbm", "achieved": round(kernel_gbps, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(kernel_gbps / HBM_PEAK_GBPS, 4),
-                     "traffic": None, "algorithmic_bytes_per_launch": tr["kv_bytes"],
+                     "traffic": measured_traffic(inp.name, P, kprefix),
+                     "traffic_unit": f"HBM bytes per launch of {kprefix} (rocprofv3 FETCH_SIZE + "
+                                     "WRITE_SIZE, copy-calibrated)",
+                     "algorithmic_bytes_per_launch": tr["kv_bytes"],
                      "flops_per_launch": tr["flops"]},
         "cpu_baseline": cpu,
         "attainable": attainable_entry(ops, stream, kernel_gbps),

@@ -299,9 +299,10 @@ hipError_t launch_d(const MergeArgs& a, DType out_dtype, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_merge(const MergeArgs& a, int head_dim, DType out_dtype, hipStream_t stream) {
-  if (a.part_bf16) {                              // bf16 partial rows: MLA latent rows only
-    if (head_dim != 512) return hipErrorInvalidValue;
-    return launch_d<512, true>(a, out_dtype, stream);
+  if (a.part_bf16) {      // bf16 partial rows: MLA latent rows, and head dim 128 with several tokens
+    if (head_dim == 512) return launch_d<512, true>(a, out_dtype, stream);
+    if (head_dim == 128) return launch_d<128, true>(a, out_dtype, stream);
+    return hipErrorInvalidValue;
   }
   if (head_dim == 64) return launch_d<64>(a, out_dtype, stream);
   if (head_dim == 512) return launch_d<512>(a, out_dtype, stream);   // MLA latent rows

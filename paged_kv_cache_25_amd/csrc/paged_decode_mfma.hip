@@ -231,6 +231,25 @@ struct MfmaDecode {
   }
 };
 
+// Partial row of column 4r+i (this lane's dims) as bf16, round to nearest
+// even: the balanced split with several new tokens keeps its partial rows in
+// bf16, half the bytes the decode kernel writes and the merge reads.
+template <int D>
+__device__ __forceinline__ void store_bf16_partial(float* part_o, size_t prow, int c,
+                                                   const MfmaDecode<D>& dt, int i, float inv) {
+  constexpr int kDimsPerLane = D / 16;
+  uint16_t* op = reinterpret_cast<uint16_t*>(part_o) + prow * D + kDimsPerLane * c;
+  uint32_t packed[kDimsPerLane / 2];
+#pragma unroll
+  for (int e = 0; e < kDimsPerLane; e += 2)
+    packed[e / 2] = uint32_t(f32_to_bf16_rne(dt.o[e][i] * inv)) |
+                    (uint32_t(f32_to_bf16_rne(dt.o[e + 1][i] * inv)) << 16);
+  if constexpr (kDimsPerLane == 8)
+    *reinterpret_cast<uint4*>(op) = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+  else
+    *reinterpret_cast<uint2*>(op) = make_uint2(packed[0], packed[1]);
+}
+
 // Three waves per SIMD: about 150 VGPRs for head dim 128 with two blocks in registers.
 // kMulti: several new tokens per sequence (per-column visibility); otherwise
 // one new token, whose column sees the whole context.  kNT: K/V loads carry the
@@ -428,11 +447,15 @@ void paged_decode_mfma_kernel(DecodeArgs a) {
       } else {
         if (!partial_row_ok(a, qrow, cols.row0)) continue;
         const size_t prow = partial_row(a, it, qrow, cols.row0);
-        float* op = a.part_o + prow * D + kDimsPerLane * c;
+        if (kMulti && a.part_bf16) {                       // uniform
+          store_bf16_partial<D>(a.part_o, prow, c, dt, i, inv);
+        } else {
+          float* op = a.part_o + prow * D + kDimsPerLane * c;
 #pragma unroll
-        for (int e = 0; e < kDimsPerLane; e += 4)
-          *reinterpret_cast<float4*>(op + e) = make_float4(dt.o[e][i] * inv, dt.o[e + 1][i] * inv,
-                                                           dt.o[e + 2][i] * inv, dt.o[e + 3][i] * inv);
+          for (int e = 0; e < kDimsPerLane; e += 4)
+            *reinterpret_cast<float4*>(op + e) = make_float4(dt.o[e][i] * inv, dt.o[e + 1][i] * inv,
+                                                             dt.o[e + 2][i] * inv, dt.o[e + 3][i] * inv);
+        }
         if (c == 0)
           a.part_lse[prow] = empty ? -INFINITY : (m_row[i] + __builtin_amdgcn_logf(l_row[i])) * kLn2;
       }
@@ -674,11 +697,15 @@ void paged_decode_lds_kernel(DecodeArgs a) {
       } else {
         if (!partial_row_ok(a, qrow, cols.row0)) continue;
         const size_t prow = partial_row(a, it, qrow, cols.row0);
-        float* op = a.part_o + prow * D + kDimsPerLane * c;
+        if (a.part_bf16) {                       // uniform
+          store_bf16_partial<D>(a.part_o, prow, c, dt, i, inv);
+        } else {
+          float* op = a.part_o + prow * D + kDimsPerLane * c;
 #pragma unroll
-        for (int e = 0; e < kDimsPerLane; e += 4)
-          *reinterpret_cast<float4*>(op + e) = make_float4(dt.o[e][i] * inv, dt.o[e + 1][i] * inv,
-                                                           dt.o[e + 2][i] * inv, dt.o[e + 3][i] * inv);
+          for (int e = 0; e < kDimsPerLane; e += 4)
+            *reinterpret_cast<float4*>(op + e) = make_float4(dt.o[e][i] * inv, dt.o[e + 1][i] * inv,
+                                                             dt.o[e + 2][i] * inv, dt.o[e + 3][i] * inv);
+        }
         if (c == 0)
           a.part_lse[prow] = empty ? -INFINITY : (m_row[i] + __builtin_amdgcn_logf(l_row[i])) * kLn2;
       }

@@ -1229,10 +1229,17 @@ pkv_status_t pkv_paged_multi_query_attention(
     a.write_final = 0;
     a.final_single = 1;
     a.mark_empty = 0;
+    // On the matrix cores at head dim 128 the chunks' partial rows pass
+    // through the workspace as bf16 (one more rounding of each partial; the
+    // output is bf16 anyway): half the bytes the decode kernel writes and the
+    // merge reads, 2 x 32,768 rows of 512 bytes at 16 new tokens on the
+    // batch-64 layer.
+    a.part_bf16 = ms.mfma && head_dim == 128 && q_dtype == PKV_BF16 ? 1 : 0;
     if (!plan_decode(a, plan, slots, block_size, st)) return PKV_ERR_HIP;
     if (launch_decode(a, head_dim, ms.tile, ms.mfma, q_dtype, kv_dtype, st) != hipSuccess)
       return PKV_ERR_HIP;
     pkv::MergeArgs m{};
+    m.part_bf16 = a.part_bf16;
     m.out = out;
     m.part_o = a.part_o;
     m.part_lse = a.part_lse;

@@ -131,6 +131,7 @@ struct DecodeArgs {
   int write_final;            // every sequence has one partition: write `out`
   int final_single;           // a sequence with one partition writes `out` (the merge skips it)
   int mark_empty;             // partitions past a sequence's end write lse = -inf
+  int part_bf16;              // partial rows stored as bf16 (several new tokens, matrix cores)
   // Balanced split (null: fixed partitions): the plan's slot_info[slot] =
   // {sequence, first block, end block, chunks of the sequence}; the grid runs
   // max_partitions slots; partial rows are [slot, Hq] and an empty chunk
