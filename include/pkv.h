@@ -18,8 +18,9 @@
  * ---------------------------------------
  * Pointers marked [device] are device memory owned by the caller; the library
  * allocates nothing, keeps no state between calls and never synchronises the
- * host.  Every call enqueues its kernels on `stream` (a hipStream_t; NULL is
- * the default stream) and returns.  Calls on one stream run in order; calls
+ * host.  Every call enqueues its kernels on `stream` (a hipStream_t, passed as
+ * void* so that this header needs no HIP header; NULL is the default stream)
+ * and returns.  Calls on one stream run in order; calls
  * on different streams that touch the same memory race.
  *
  * Layouts (row-major, innermost last):
@@ -90,7 +91,7 @@ typedef enum {
 int pkv_abi_version(void);
 
 /* A static, human-readable name for a status code. */
-const char* pkv_status_string(int status);
+const char* pkv_status_string(pkv_status_t status);
 
 /*
  * pkv_kv_append - write each sequence's new K and V rows into its slot.

@@ -140,7 +140,7 @@ extern "C" {
 
 int pkv_abi_version(void) { return PKV_ABI_VERSION; }
 
-const char* pkv_status_string(int status) {
+const char* pkv_status_string(pkv_status_t status) {
   switch (status) {
     case PKV_OK: return "PKV_OK";
     case PKV_ERR_INVALID_ARG: return "PKV_ERR_INVALID_ARG";
