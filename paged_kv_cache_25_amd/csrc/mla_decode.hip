@@ -98,6 +98,20 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
          (uint32_t(__builtin_bit_cast(uint16_t, __bf16(hi))) << 16);
 }
 
+// Chunk slot cs and head chunk of this workgroup in a balanced grid of
+// slots x head_chunks workgroups.  Workgroups are dealt to the eight XCDs in
+// turn (workgroup i to XCD i % 8); each XCD takes a run of consecutive slots,
+// so the chunks of one sequence, which take consecutive slots, mostly share
+// one L2 and read the sequence's absorbed queries from HBM once.
+__device__ __forceinline__ void slot_of(int head_chunks, int slots, int& chunk, int& cs) {
+  const int bid = blockIdx.x;
+  const int total = slots * head_chunks;
+  int lin = bid;
+  if (total % 8 == 0) lin = (bid & 7) * (total >> 3) + (bid >> 3);
+  chunk = lin % head_chunks;
+  cs = lin / head_chunks;
+}
+
 // The work of one workgroup: its head chunk, sequence b, context ctx and
 // blocks [blk_begin, blk_end); its partial rows are slot_row + head *
 // slot_stride with slot = the partition of the sequence (fixed partitions:
@@ -122,8 +136,8 @@ __device__ __forceinline__ bool mla_work(const MlaArgs& a, int wave, int lane, M
   int n_blk_seq;
   if (a.plan_first) {
     // Wave 0 plans the workgroup's chunk (pairs of blocks) and shares it.
-    w.chunk = blockIdx.x % a.head_chunks;
-    const int cs = blockIdx.x / a.head_chunks;           // chunk slot
+    int cs;                                              // chunk slot
+    slot_of(a.head_chunks, a.max_partitions, w.chunk, cs);
     __shared__ int s_plan[4];                            // sequence (-1: none), first pair, end pair, chunks
     if (wave == 0) {
       PlanChunk pc;
@@ -142,26 +156,27 @@ __device__ __forceinline__ bool mla_work(const MlaArgs& a, int wave, int lane, M
       }
     }
     __syncthreads();
-    w.b = s_plan[0];
+    // (read back through readfirstlane: uniform values in scalar registers)
+    w.b = __builtin_amdgcn_readfirstlane(s_plan[0]);
     if (w.b < 0) return false;                           // a slot past the last chunk
     const int raw_ctx = a.context_lens[w.b];
     w.ctx = raw_ctx < 0 ? 0 : (raw_ctx > cap ? cap : raw_ctx);
     n_blk_seq = (w.ctx + kBlockSize - 1) / kBlockSize;
-    w.blk_begin = 2 * s_plan[1];
-    w.blk_end = 2 * s_plan[2];
-    w.final_out = s_plan[3] == 1;                        // (also a sequence with nothing to attend)
+    w.blk_begin = 2 * __builtin_amdgcn_readfirstlane(s_plan[1]);
+    w.blk_end = 2 * __builtin_amdgcn_readfirstlane(s_plan[2]);
+    w.final_out = __builtin_amdgcn_readfirstlane(s_plan[3]) == 1;                        // (also a sequence with nothing to attend)
     w.slot_row = size_t(cs) * a.num_heads;
     w.slot_stride = 1;
   } else if (a.chunk_first) {
-    w.chunk = blockIdx.x % a.head_chunks;
-    const int cs = blockIdx.x / a.head_chunks;           // chunk slot (grid: every slot exists)
+    int cs;                                              // chunk slot (grid: every slot exists)
+    slot_of(a.head_chunks, a.max_partitions, w.chunk, cs);
     __shared__ int s_seq;
     if (threadIdx.x == 0) s_seq = -1;
     __syncthreads();
     for (int s = threadIdx.x; s < a.num_seqs; s += kThreads)
       if (a.chunk_first[s] <= cs && cs < a.chunk_first[s + 1]) s_seq = s;
     __syncthreads();
-    w.b = s_seq;
+    w.b = __builtin_amdgcn_readfirstlane(s_seq);
     if (w.b < 0) return false;                           // a slot past the last chunk
     const int n_b = a.chunk_first[w.b + 1] - a.chunk_first[w.b];
     const int k = cs - a.chunk_first[w.b];
@@ -260,12 +275,20 @@ struct PairStage {
 template <int WAVES>
 __global__ __launch_bounds__(WAVES * kWave) void mla_decode_kernel(MlaArgs a) {
   constexpr int kThreads = WAVES * kWave;
-  __shared__ __attribute__((aligned(16))) uint16_t s_k0[kBufElems];
-  __shared__ __attribute__((aligned(16))) uint16_t s_k1[kBufElems];
+  __shared__ __attribute__((aligned(16))) uint16_t s_k[2 * kBufElems];
+  uint16_t* const s_k0 = s_k;                            // the two pair buffers, one after the other
+  uint16_t* const s_k1 = s_k + kBufElems;
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);   // uniform
   const int lane = threadIdx.x % kWave;
   const int g = lane >> 4, c = lane & 15;
+
+  // Clear both buffers, so that slots never loaded read as zeros (while wave
+  // 0 plans the chunk).
+  for (int i = threadIdx.x; i < kBufElems / 8; i += kThreads) {
+    reinterpret_cast<uint4*>(s_k0)[i] = make_uint4(0, 0, 0, 0);
+    reinterpret_cast<uint4*>(s_k1)[i] = make_uint4(0, 0, 0, 0);
+  }
 
   MlaWork w;
   if (!mla_work<WAVES, 16>(a, wave, lane, w)) return;
@@ -276,24 +299,7 @@ __global__ __launch_bounds__(WAVES * kWave) void mla_decode_kernel(MlaArgs a) {
 
   const int limit = ctx < blk_end * kBlockSize ? ctx : blk_end * kBlockSize;   // tokens attended
 
-  // Clear both buffers, so that slots never loaded read as zeros.
-  for (int i = threadIdx.x; i < kBufElems / 8; i += kThreads) {
-    reinterpret_cast<uint4*>(s_k0)[i] = make_uint4(0, 0, 0, 0);
-    reinterpret_cast<uint4*>(s_k1)[i] = make_uint4(0, 0, 0, 0);
-  }
-
-  // The absorbed query of head h0 + c, as the B operand of the score product.
-  bf16x8 q[kSlabs];
-  {
-    const bool ok = h0 + c < a.num_heads;
-    const char* qrow = static_cast<const char*>(a.q) +
-                       (size_t(b) * a.num_heads + (ok ? h0 + c : 0)) * kRowBytes;
-#pragma unroll
-    for (int j = 0; j < kSlabs; ++j) {
-      const uint4 w = ok ? *reinterpret_cast<const uint4*>(qrow + 64 * j + 16 * g) : make_uint4(0, 0, 0, 0);
-      q[j] = __builtin_bit_cast(bf16x8, w);
-    }
-  }
+  bf16x8 q[kSlabs];                                   // loaded after the first pair's copy is issued
   f32x4 o[kTiles];
 #pragma unroll
   for (int t = 0; t < kTiles; ++t) o[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
@@ -407,9 +413,21 @@ __global__ __launch_bounds__(WAVES * kWave) void mla_decode_kernel(MlaArgs a) {
   // to name each buffer statically would let the compiler tell the copy of
   // the next pair from the reads of this one, but the second copy of the
   // body does not fit in the registers.)
+  // The first pair's copy, then the queries, both in flight together.
   __syncthreads();                                    // buffers cleared
   bool ok0 = false, ok1 = false;
   if (n_pairs > 0) st.stage(0, s_k0, ok0, ok1);
+  // The absorbed query of head h0 + c, as the B operand of the score product.
+  {
+    const bool ok = h0 + c < a.num_heads;
+    const char* qrow = static_cast<const char*>(a.q) +
+                       (size_t(b) * a.num_heads + (ok ? h0 + c : 0)) * kRowBytes;
+#pragma unroll
+    for (int j = 0; j < kSlabs; ++j) {
+      const uint4 w = ok ? *reinterpret_cast<const uint4*>(qrow + 64 * j + 16 * g) : make_uint4(0, 0, 0, 0);
+      q[j] = __builtin_bit_cast(bf16x8, w);
+    }
+  }
   __builtin_amdgcn_s_waitcnt(0);                      // this wave's copies have landed
   __syncthreads();                                    // and everyone's
   for (int p = 0; p < n_pairs; ++p) {
@@ -433,30 +451,58 @@ __global__ __launch_bounds__(WAVES * kWave) void mla_decode_kernel(MlaArgs a) {
     l_row[i] = __shfl(lt, 4 * g + i);
     m_row[i] = __shfl(m, 4 * g + i);
   }
+  float inv[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int head = h0 + 4 * g + i;
-    if (head >= a.num_heads) continue;
-    const size_t row = size_t(b) * a.num_heads + head;
-    const bool empty = l_row[i] == 0.0f;
-    const float inv = empty ? 0.0f : 1.0f / l_row[i];
-    if (final_out) {
-      uint16_t* orow = static_cast<uint16_t*>(a.out) + row * kDc + c;
+  for (int i = 0; i < 4; ++i) inv[i] = l_row[i] == 0.0f ? 0.0f : 1.0f / l_row[i];
+  if (!final_out) {
 #pragma unroll
-      for (int t = 0; t < kTiles; ++t) orow[16 * t] = f32_to_bf16_rne(o[t][i] * inv);
-    } else {
-      const size_t prow = slot_row + size_t(head) * slot_stride;
-      if (a.part_bf16) {                                 // uniform
-        uint16_t* op = reinterpret_cast<uint16_t*>(a.part_o) + prow * kDc + c;
+    for (int i = 0; i < 4; ++i) {
+      const int head = h0 + 4 * g + i;
+      if (c == 0 && head < a.num_heads)
+        a.part_lse[slot_row + size_t(head) * slot_stride] =
+            l_row[i] == 0.0f ? -INFINITY : (m_row[i] + __builtin_amdgcn_logf(l_row[i])) * kLn2;
+    }
+  }
+  if (final_out || a.part_bf16) {                        // uniform
+    // bf16 rows, through LDS (free once the last pair's barrier has passed):
+    // a wave writes its 16 rows' half of the columns to its own region (rows
+    // 528 bytes apart, so the four row groups of a write fall on distinct
+    // banks) and stores them back 16 bytes per lane, eight stores per half
+    // instead of 64 two-byte ones.
+    constexpr int kRowPitch = 264;                       // bf16 elements per staged row
+    static_assert(WAVES * 16 * kRowPitch <= 2 * kBufElems, "the staged rows fit the pair buffers");
+    uint16_t* region = s_k + wave * 16 * kRowPitch;
+    uint16_t* rows_base = final_out ? static_cast<uint16_t*>(a.out) + (size_t(b) * a.num_heads) * kDc
+                                    : reinterpret_cast<uint16_t*>(a.part_o) + slot_row * kDc;
+    const size_t head_pitch = final_out ? kDc : slot_stride * kDc;
 #pragma unroll
-        for (int t = 0; t < kTiles; ++t) op[16 * t] = f32_to_bf16_rne(o[t][i] * inv);
-      } else {
-        float* op = a.part_o + prow * kDc + c;
+    for (int half = 0; half < 2; ++half) {
 #pragma unroll
-        for (int t = 0; t < kTiles; ++t) op[16 * t] = o[t][i] * inv;
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int tt = 0; tt < kTiles / 2; ++tt)
+          region[(4 * g + i) * kRowPitch + 16 * tt + c] =
+              f32_to_bf16_rne(o[half * kTiles / 2 + tt][i] * inv[i]);
+      __builtin_amdgcn_s_waitcnt(0xc07f);                // lgkmcnt(0): this wave's writes are in LDS
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int k = lane + kWave * j;                  // 16-byte piece: row k / 32, piece k % 32
+        const int r = k >> 5, piece = k & 31;
+        const uint4 v = *reinterpret_cast<const uint4*>(region + r * kRowPitch + 8 * piece);
+        if (h0 + r < a.num_heads)
+          *reinterpret_cast<uint4*>(rows_base + size_t(h0 + r) * head_pitch + half * (kDc / 2) +
+                                    8 * piece) = v;
       }
-      if (c == 0)
-        a.part_lse[prow] = empty ? -INFINITY : (m_row[i] + __builtin_amdgcn_logf(l_row[i])) * kLn2;
+      __builtin_amdgcn_s_waitcnt(0xc07f);                // the reads are done before the next half's writes
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int head = h0 + 4 * g + i;
+      if (head >= a.num_heads) continue;
+      float* op = a.part_o + (slot_row + size_t(head) * slot_stride) * kDc + c;
+#pragma unroll
+      for (int t = 0; t < kTiles; ++t) op[16 * t] = o[t][i] * inv[i];
     }
   }
 }
