@@ -100,9 +100,10 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 
 // Chunk slot cs and head chunk of this workgroup in a balanced grid of
 // slots x head_chunks workgroups.  Workgroups are dealt to the eight XCDs in
-// turn (workgroup i to XCD i % 8); each XCD takes a run of consecutive slots,
-// so the chunks of one sequence, which take consecutive slots, mostly share
-// one L2 and read the sequence's absorbed queries from HBM once.
+// turn (workgroup i to XCD (i + o) mod 8, the offset o carried over from
+// earlier launches); the workgroups i = x mod 8 take a run of consecutive
+// slots, so the chunks of one sequence, which take consecutive slots, mostly
+// share one L2 and read the sequence's absorbed queries from HBM once.
 __device__ __forceinline__ void slot_of(int head_chunks, int slots, int& chunk, int& cs) {
   const int bid = blockIdx.x;
   const int total = slots * head_chunks;
@@ -164,7 +165,8 @@ __device__ __forceinline__ bool mla_work(const MlaArgs& a, int wave, int lane, M
     n_blk_seq = (w.ctx + kBlockSize - 1) / kBlockSize;
     w.blk_begin = 2 * __builtin_amdgcn_readfirstlane(s_plan[1]);
     w.blk_end = 2 * __builtin_amdgcn_readfirstlane(s_plan[2]);
-    w.final_out = __builtin_amdgcn_readfirstlane(s_plan[3]) == 1;                        // (also a sequence with nothing to attend)
+    // (one chunk: also a sequence with nothing to attend)
+    w.final_out = __builtin_amdgcn_readfirstlane(s_plan[3]) == 1;
     w.slot_row = size_t(cs) * a.num_heads;
     w.slot_stride = 1;
   } else if (a.chunk_first) {
