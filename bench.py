@@ -911,7 +911,7 @@ def main_mla(args):
                       {"decode": round(decode_ms * 1e3, 2), "merge": round(merge_ms * 1e3, 2),
                        "attention_call": round(att_ms * 1e3, 2)}),
         "roofline": {"kernel": (("balanced_split_kernel + " if B > 256 else "")
-                                + "mla_decode_kernel + merge_kernel"
+                                + "mla_decode_kernel + merge_wide_kernel"
                                 if balanced else "mla_decode_kernel"), "bound": "hbm",
                      "achieved": round(kernel_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(kernel_gbps / HBM_PEAK_GBPS, 4),

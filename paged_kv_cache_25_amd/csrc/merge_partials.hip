@@ -4,9 +4,11 @@
 // count, out = sum_p exp(lse_p - M) o_p / sum_p exp(lse_p - M).  Partitions
 // that do not count (past the row's count, or with lse = -inf) are skipped,
 // never multiplied by a zero weight, so whatever they hold cannot reach the
-// output.  A row group of D/4 threads (D/8 for the bf16 rows of the balanced
-// MLA split) reads one partition row with 16-byte loads, several rows in
-// flight.  Two launch shapes:
+// output.  A row group of D/4 threads (D/8 for bf16 partial rows) reads one
+// partition row with 16-byte loads, several rows in flight.  Three launch
+// shapes:
+//   - the 512-wide bf16 rows of the balanced MLA split: merge_wide_kernel,
+//     32 threads per item, each two 16-byte pieces of every row;
 //   - very many items with few partitions each (several new tokens per
 //     sequence): merge_items_kernel, several items per 256-thread workgroup,
 //     one row group per item reading all of its partitions;
@@ -254,6 +256,87 @@ __global__ __launch_bounds__(kThreads) void merge_items_kernel(MergeArgs a, int 
   for (int e = 0; e < kVec; ++e) OT::store(orow, kVec * c + e, acc.v[e] * inv);
 }
 
+// bf16 partial rows, wide: a row group of 32 threads per item, each thread
+// D / 256 16-byte pieces of a row (pieces c + 32 i: every load instruction
+// reads contiguous bytes), two items per wave and four rows of an item in
+// flight; the arithmetic is the other kernels' element by element (the
+// maximum over every partition, then the weighted sum in partition order), so
+// the bits are the same.  The absorbed MLA merge (8,192 items of 1 KB rows)
+// runs as 4,096 waves, all resident at once, instead of 8,192 one-wave
+// workgroups: 1.5-2 us less.  (16 or 8 threads per item measured the same
+// within the noise.)
+template <int D, typename OT>
+__global__ __launch_bounds__(kThreads) void merge_wide_kernel(MergeArgs a, int n_items) {
+  constexpr int kRowThreads = 32;
+  constexpr int kPieces = D / 8 / kRowThreads;    // 16-byte pieces per thread and row
+  constexpr int kItems = kThreads / kRowThreads;  // items per workgroup
+  constexpr int kUnroll = 4;
+  static_assert(D % (8 * kRowThreads) == 0, "whole pieces per thread");
+  const int item = blockIdx.x * kItems + threadIdx.x / kRowThreads;
+  const int c = threadIdx.x % kRowThreads;
+  if (item >= n_items) return;
+  MergeItem it;
+  if (!merge_item(a, item, it)) return;           // uniform over the row group
+  const int np = it.np;
+  auto lse_at = [&](int p) { return a.part_lse[it.base + size_t(p) * it.stride]; };
+  auto piece_at = [&](int p, int i) {
+    const size_t off = (it.base + size_t(p) * it.stride) * D + 8 * size_t(c + kRowThreads * i);
+    return *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.part_o) + off);
+  };
+
+  uint4 rowv[kUnroll][kPieces];
+  float lp[kUnroll];
+  auto load_batch = [&](int p0) {
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int p = p0 + u;
+      lp[u] = p < np ? lse_at(p) : -INFINITY;
+#pragma unroll
+      for (int i = 0; i < kPieces; ++i) rowv[u][i] = p < np ? piece_at(p, i) : make_uint4(0, 0, 0, 0);
+    }
+  };
+  load_batch(0);
+  float M = -INFINITY;
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u) M = fmaxf(M, lp[u]);
+  for (int p = kUnroll; p < np; ++p) M = fmaxf(M, lse_at(p));
+
+  float acc[kPieces][8];
+#pragma unroll
+  for (int i = 0; i < kPieces; ++i)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[i][e] = 0.0f;
+  float wsum = 0.0f;
+  if (M > -INFINITY) {
+    for (int p0 = 0;;) {
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        if (lp[u] == -INFINITY) continue;
+        const float w = __expf(lp[u] - M);
+        wsum += w;
+#pragma unroll
+        for (int i = 0; i < kPieces; ++i) {
+          const uint32_t x[4] = {rowv[u][i].x, rowv[u][i].y, rowv[u][i].z, rowv[u][i].w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            acc[i][2 * e] = fmaf(w, __uint_as_float(x[e] << 16), acc[i][2 * e]);
+            acc[i][2 * e + 1] = fmaf(w, __uint_as_float(x[e] & 0xffff0000u), acc[i][2 * e + 1]);
+          }
+        }
+      }
+      p0 += kUnroll;
+      if (p0 >= np) break;
+      load_batch(p0);
+    }
+  }
+  const float inv = wsum > 0.0f ? 1.0f / wsum : 0.0f;
+  char* orow = reinterpret_cast<char*>(a.out) + it.row * D * sizeof(typename OT::Storage);
+#pragma unroll
+  for (int i = 0; i < kPieces; ++i)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) OT::store(orow, 8 * (c + kRowThreads * i) + e, acc[i][e] * inv);
+}
+
 template <int D, bool kBf16Part = false>
 hipError_t launch_d(const MergeArgs& a, DType out_dtype, hipStream_t stream) {
   const size_t grid = (a.q_start ? size_t(a.num_batch) * a.rows_per_seq : size_t(a.num_seqs)) *
@@ -273,6 +356,17 @@ hipError_t launch_d(const MergeArgs& a, DType out_dtype, hipStream_t stream) {
   // each.  Measured at 12.2 us there against 16.2 us one workgroup per item;
   // at 8,192 items (MLA) the two shapes tie, at 2,048 (one new token) the
   // workgroup per item is faster (4.7 against 5.2 us).
+  if constexpr (kBf16Part && D == 512) {                 // MLA latent rows
+    constexpr int kItems = kThreads / 32;
+    const size_t blocks = (grid + kItems - 1) / kItems;
+    if (out_dtype == DType::F32)
+      hipLaunchKernelGGL((merge_wide_kernel<D, OutF32>), dim3(unsigned(blocks)), dim3(kThreads), 0,
+                         stream, a, int(grid));
+    else
+      hipLaunchKernelGGL((merge_wide_kernel<D, OutBF16>), dim3(unsigned(blocks)), dim3(kThreads), 0,
+                         stream, a, int(grid));
+    return hipGetLastError();
+  }
   if (kRowThreads <= kWave && rows <= 2 * kUnroll && grid >= 16384) {
     constexpr int kItems = kThreads / kRowThreads;
     const size_t blocks = (grid + kItems - 1) / kItems;
