@@ -7,8 +7,9 @@
 // output.  A row group of D/4 threads (D/8 for bf16 partial rows) reads one
 // partition row with 16-byte loads, several rows in flight.  Three launch
 // shapes:
-//   - the 512-wide bf16 rows of the balanced MLA split: merge_wide_kernel,
-//     32 threads per item, each two 16-byte pieces of every row;
+//   - bf16 rows (the balanced MLA split; several new tokens per sequence):
+//     merge_wide_kernel, 32 or 8 threads per item, each two 16-byte pieces
+//     of every row;
 //   - very many items with few partitions each (several new tokens per
 //     sequence): merge_items_kernel, several items per 256-thread workgroup,
 //     one row group per item reading all of its partitions;
@@ -256,18 +257,19 @@ __global__ __launch_bounds__(kThreads) void merge_items_kernel(MergeArgs a, int 
   for (int e = 0; e < kVec; ++e) OT::store(orow, kVec * c + e, acc.v[e] * inv);
 }
 
-// bf16 partial rows, wide: a row group of 32 threads per item, each thread
-// D / 256 16-byte pieces of a row (pieces c + 32 i: every load instruction
-// reads contiguous bytes), two items per wave and four rows of an item in
+// bf16 partial rows, wide: a row group of kRowThreads threads per item, each
+// thread D / (8 kRowThreads) 16-byte pieces of a row (pieces c + kRowThreads
+// i: every load instruction reads contiguous bytes), four rows of an item in
 // flight; the arithmetic is the other kernels' element by element (the
 // maximum over every partition, then the weighted sum in partition order), so
-// the bits are the same.  The absorbed MLA merge (8,192 items of 1 KB rows)
-// runs as 4,096 waves, all resident at once, instead of 8,192 one-wave
-// workgroups: 1.5-2 us less.  (16 or 8 threads per item measured the same
-// within the noise.)
-template <int D, typename OT>
+// the bits are the same.  Fewer, fuller waves, all resident at once: the
+// absorbed MLA merge (8,192 items of 1 KB rows, 32 threads each) runs as
+// 4,096 waves instead of 8,192 one-wave workgroups, 12.4 -> 10.5 us (16 or 8
+// threads per item measured the same within the noise); 16 new tokens per
+// sequence (32,768 items of 256-byte rows, 8 threads each) as 4,096 waves
+// instead of 8,192, 5.9-6.4 -> 4.4-4.6 us.
+template <int D, typename OT, int kRowThreads = 32>
 __global__ __launch_bounds__(kThreads) void merge_wide_kernel(MergeArgs a, int n_items) {
-  constexpr int kRowThreads = 32;
   constexpr int kPieces = D / 8 / kRowThreads;    // 16-byte pieces per thread and row
   constexpr int kItems = kThreads / kRowThreads;  // items per workgroup
   constexpr int kUnroll = 4;
@@ -356,6 +358,17 @@ hipError_t launch_d(const MergeArgs& a, DType out_dtype, hipStream_t stream) {
   // each.  Measured at 12.2 us there against 16.2 us one workgroup per item;
   // at 8,192 items (MLA) the two shapes tie, at 2,048 (one new token) the
   // workgroup per item is faster (4.7 against 5.2 us).
+  if constexpr (kBf16Part && D == 128) {                 // several new tokens per sequence
+    constexpr int kItems = kThreads / 8;
+    const size_t blocks = (grid + kItems - 1) / kItems;
+    if (out_dtype == DType::F32)
+      hipLaunchKernelGGL((merge_wide_kernel<D, OutF32, 8>), dim3(unsigned(blocks)), dim3(kThreads), 0,
+                         stream, a, int(grid));
+    else
+      hipLaunchKernelGGL((merge_wide_kernel<D, OutBF16, 8>), dim3(unsigned(blocks)), dim3(kThreads), 0,
+                         stream, a, int(grid));
+    return hipGetLastError();
+  }
   if constexpr (kBf16Part && D == 512) {                 // MLA latent rows
     constexpr int kItems = kThreads / 32;
     const size_t blocks = (grid + kItems - 1) / kItems;
