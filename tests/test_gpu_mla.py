@@ -177,19 +177,22 @@ def test_partials_and_merge(P):
     assert torch.equal(merged.float().cpu().double(), whole)
 
 
-@pytest.mark.parametrize("case", ["long_and_short", "many_short", "all_empty", "one_long"])
+@pytest.mark.parametrize("case", ["long_and_short", "many_short", "odd_slots", "all_empty", "one_long"])
 def test_balanced_split(case):
     """The balanced split (PKV_PARTITION_BALANCED) on batches it treats
     differently: one sequence far longer than the rest (many chunks for it,
-    one for the others), more sequences than chunk slots (one chunk each),
-    every context empty (zeros), and a single sequence of 6,000 tokens split
-    over up to 256 chunks of one pair of blocks or more."""
+    one for the others), more sequences than chunk slots (one chunk each:
+    600 slots of 16-head workgroups, and 301 of 128-head ones, which the
+    eight XCDs cannot share in equal runs), every context empty (zeros), and
+    a single sequence of 6,000 tokens split over up to 256 chunks of one pair
+    of blocks or more."""
     spec = {"long_and_short": dict(num_seqs=9, ctx=("fixed", [3000, 5, 17, 64, 1, 33, 100, 0, 48])),
             "many_short": dict(num_seqs=600, ctx=("uniform", 0, 40)),
+            "odd_slots": dict(num_seqs=301, ctx=("uniform", 0, 90)),
             "all_empty": dict(num_seqs=4, ctx=("fixed", [0, 0, 0, 0])),
             "one_long": dict(num_seqs=1, ctx=("fixed", [6000]))}[case]
     heads = 16 if case == "many_short" else 128
-    seed = {"long_and_short": 51, "many_short": 52, "all_empty": 53, "one_long": 54}[case]
+    seed = {"long_and_short": 51, "many_short": 52, "odd_slots": 55, "all_empty": 53, "one_long": 54}[case]
     inp = make_mla_inputs(num_heads=heads, seed=seed, pool_used_fraction=0.9, **spec)
     log(f"[case] mla balanced {case}")
     dev = DevMLA(inp)
